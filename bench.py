@@ -1,0 +1,180 @@
+#!/usr/bin/env python3
+"""Throughput of the LSA memory-indexer selection path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic inputs
+already resident in HBM: project (memory-indexer and native queries), score +
+select, OR-union + compact, native top-k inside the subset, and gather of the
+union rows. The default workload is three indexer layers x 8 sequences x
+125,000 compressed entries (bf16 keys, d_h = 128, n_h = 64). That is the
+N = 125K configuration whose key stream (768 MB) does not fit in the 256 MB
+Infinity Cache.
+
+Output: one JSON line. `value` is entries scored+selected per second over the
+whole step (sum over layers and sequences of N_b, divided by the step time).
+`roofline` describes the dominant kernel (score_select), from HIP events on
+its stream. `cpu_baseline` is the CPU oracle on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_select_traffic.json")
+SCORE_SOURCES = ["score.hip", "scorer.hpp", "common.hpp", "kernels.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def score_source_hash() -> str:
+    h = hashlib.sha256()
+    for s in SCORE_SOURCES:
+        with open(os.path.join(ROOT, "sparse_kv_retrieval_amd", "csrc", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, lengths) -> dict:
+    """Bytes the score+select pass must move: every key once, its fp8 scale, one mask bit, plus q and w once per (b, l)."""
+    esz = {"f32": 4, "bf16": 2, "fp8": 1}[w.key_dtype]
+    per_entry = w.d_h * esz + (4 if w.key_dtype == "fp8" else 0)
+    n = int(np.sum(lengths))
+    words = int(np.sum((lengths + 63) // 64))
+    qw = w.B * (w.n_h * w.d_h + w.n_h) * 4
+    total = w.L * (n * per_entry + words * 8 + qw)
+    return {"per_entry_bytes": per_entry + 0.125, "bytes_per_launch": total, "entries_per_launch": w.L * n}
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The CPU oracle as it stands, timed over whole sequences of the same workload until about `budget_s`."""
+    from oracle import lsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w = inp.workload
+    done_entries = 0
+    seqs = 0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        O.run_path(inp, sequences=[b])
+        done_entries += int(inp.lengths[b]) * w.L
+        seqs += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done_entries / el, "unit": "entries/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{seqs} of {w.B} sequences x {w.L} layers of the {w.name} workload, full path "
+                      f"(project, score, select, union, compact, top-k, gather), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="three_layer_b8")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode (each GPU would score its own "
+              "sequences; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_kv_retrieval_amd import synth
+    from sparse_kv_retrieval_amd.pipeline import Pipeline
+
+    w = synth.WORKLOADS[args.workload]
+    log(f"[bench] generating {w.name}")
+    t = time.perf_counter()
+    inp = synth.make(w)
+    log(f"[bench] generated in {time.perf_counter() - t:.1f}s; uploading")
+    p = Pipeline(inp, "cuda:0", with_scores=False)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        p.run()
+    torch.cuda.synchronize()
+
+    names = ["project", "score_select", "union_compact", "topk", "gather"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        e = ev[s]
+        e[0].record(stream)
+        p.project(); e[1].record(stream)
+        p.score_select(); e[2].record(stream)
+        p.union_compact(); e[3].record(stream)
+        p.topk(); e[4].record(stream)
+        p.gather(); e[5].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+                for i, n in enumerate(names)}
+
+    counts = p.count.cpu().numpy()
+    rows = int(inp.key_offsets[-1])
+    entries = int(np.sum(inp.lengths)) * w.L
+    ab = algorithmic_bytes(w, inp.lengths)
+    score_s = stage_ms["score_select"] / 1e3
+    achieved = ab["bytes_per_launch"] / score_s / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_hash") == score_source_hash() and tr.get("workload") == w.name:
+            traffic = tr.get("traffic_bytes_per_launch")
+
+    out = {
+        "metric": "compressed entries scored+selected/sec and HBM GB/s at N=125K (1 GPU)",
+        "value": entries / (ms_per_step / 1e3),
+        "unit": "entries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.key_dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "L": w.L, "N_per_seq": int(inp.lengths.max()) if w.N else "ragged",
+                   "total_entries_per_layer": rows, "key_dtype": w.key_dtype, "n_h": w.n_h, "d_h": w.d_h,
+                   "d": w.d, "r": w.r, "k": w.k, "threshold": w.threshold, "pool_row_bytes": w.pool_dim * 2},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "kernel": "score_select_kernel",
+                     "bytes_per_launch": ab["bytes_per_launch"], "per_entry_bytes": ab["per_entry_bytes"],
+                     "avg_launch_us": stage_ms["score_select"] * 1e3},
+        "stages_us": {k: v * 1e3 for k, v in stage_ms.items()},
+        "selection": {"union_fraction": float(counts.sum()) / rows, "union_per_seq_mean": float(counts.mean())},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline")
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

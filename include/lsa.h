@@ -1,0 +1,236 @@
+/*
+ * lsa.h: C-ABI of the MI355X (gfx950) LSA memory-indexer selection path.
+ *
+ * The library implements one trigger of the Lookahead Sparse Attention memory
+ * indexer. The method is described in the write-up "arXiv'26 |
+ * FlashMemory-DeepSeek-V4: 用 13.5% 的显存干 100% 的活, 超长上下文推理的 less is
+ * more" (marsggbo.github.io, cited below as [BLOG]) and in the hyper.ai digest
+ * of the same report (section "方法", cited as [HYPER]). The steps are:
+ *
+ *   lsa_project        c = h W^DQ, q = c W^IUQ, w = h W^w        [BLOG] §3.1
+ *   lsa_score_select   I_s = sigma(sum_j w_j ReLU(q_j . K_s)), keep I_s >= theta
+ *                                                                [BLOG] §3.1
+ *   lsa_union_compact  OR over the indexer layers, ascending index list
+ *                                                    [BLOG] §4.2, [HYPER] 方法
+ *   lsa_topk           native Lightning-Indexer top-k inside the subset
+ *                                                    [BLOG] §2.2, §3.2
+ *   lsa_gather         copy the selected compressed-KV rows into a compact buffer
+ *                                                    [HYPER] 方法 (load C^MemComp)
+ *
+ * Conventions shared by every call:
+ *  - Ownership: the caller allocates every buffer. Pointers marked "dev" are
+ *    device memory on the current HIP device; pointers marked "host" are host
+ *    memory read during the call only. The library never allocates, frees or
+ *    synchronises. Its only scratch space is the caller's top-k workspace.
+ *  - Asynchrony: kernels are enqueued on `stream` and the call returns at once.
+ *    Results are valid once the stream reaches that point. Calls are reentrant.
+ *  - Errors: every argument is checked on the host before anything is enqueued.
+ *    A bad argument returns LSA_ERR_INVALID_ARG and an unsupported shape or
+ *    dtype returns LSA_ERR_UNSUPPORTED. In both cases nothing is launched and
+ *    lsa_last_error() describes the problem. A failed launch returns
+ *    LSA_ERR_HIP. Device-side values such as indices, counts and offsets are
+ *    not range-checked beyond what each call states.
+ *  - Sequences: B sequences are stored back to back. Sequence b owns rows
+ *    [key_offsets[b], key_offsets[b+1]) of every per-entry buffer. Entry indices
+ *    are sequence-local int32 values in [0, N_b), where
+ *    N_b = key_offsets[b+1] - key_offsets[b].
+ *  - Masks: bit (s % 64) of word mask_word_offsets[b] + s/64 is entry s of
+ *    sequence b. Region b is exactly ceil(N_b/64) words, so no two sequences
+ *    share a word. Bits at or beyond N_b are written as 0.
+ *  - Layers: L indexer layers per call, 1 <= L <= LSA_MAX_LAYERS. The pages use
+ *    three, at transformer layers 10, 12 and 20 ([BLOG] §4.2).
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LSA_MAX_LAYERS 8
+#define LSA_MAX_HEADS 64
+#define LSA_VERSION 1
+
+typedef enum {
+  LSA_F32 = 0,      /* IEEE binary32 */
+  LSA_BF16 = 1,     /* bfloat16 */
+  LSA_FP8_E4M3 = 2  /* OCP FP8 E4M3 ("e4m3fn"), keys only, one fp32 scale per entry */
+} lsa_dtype;
+
+typedef enum {
+  LSA_OK = 0,
+  LSA_ERR_INVALID_ARG = -1,
+  LSA_ERR_UNSUPPORTED = -2,
+  LSA_ERR_HIP = -3,
+  LSA_ERR_WORKSPACE = -4
+} lsa_status;
+
+/* ------------------------------------------------------------------------
+ * lsa_project: the indexer query and head gates of each layer ([BLOG] §3.1,
+ * the down-projection, the up-projection and the head-routing weights).
+ *
+ *   c = h W^DQ (rank r), q = c W^IUQ viewed as [n_h, d_h] (head j is columns
+ *   j*d_h ... (j+1)*d_h - 1), and w = h W^w.
+ *
+ * Weights are stored "out x in" (each output's weights are contiguous):
+ *   w_dq  [r, d]         row n = column n of W^DQ
+ *   w_iuq [n_h*d_h, r]   row m = column m of W^IUQ
+ *   w_w   [n_h, d]       row j = column j of W^w
+ * h is [B, d] row-major. h and all weights share `dtype` (LSA_F32 or LSA_BF16).
+ * Outputs are fp32 and row-major: c_out [B, r], q_out [B, n_h, d_h],
+ * w_out [B, n_h]. c_out is both an output and the input of the second stage,
+ * so it must not alias the other buffers.
+ * Supported shapes: 1 <= B <= 128; d and r multiples of 32 (of 4 for LSA_F32);
+ * n_h * d_h a multiple of 16; 1 <= n_h <= LSA_MAX_HEADS.
+ * Accumulation is fp32. With LSA_BF16, c enters the second product as
+ * bf16 hi + lo, which keeps about 16 significant bits.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const void* h;      /* dev [B, d]          */
+  const void* w_dq;   /* dev [r, d]          */
+  const void* w_iuq;  /* dev [n_h*d_h, r]    */
+  const void* w_w;    /* dev [n_h, d]        */
+  float* c_out;       /* dev [B, r]   fp32   */
+  float* q_out;       /* dev [B, n_h, d_h] fp32 */
+  float* w_out;       /* dev [B, n_h] fp32   */
+} lsa_proj_layer;
+
+lsa_status lsa_project(const lsa_proj_layer* layers /* host [L] */, int32_t L, int32_t B,
+                       int32_t d, int32_t r, int32_t n_h, int32_t d_h, lsa_dtype dtype,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * lsa_score_select: the lookahead index score and the loading rule
+ * ([BLOG] §3.1; [HYPER] 方法: entries whose score reaches or exceeds the
+ * threshold are fetched).
+ *
+ *   x_s = sum_j w_j * ReLU(q_j . K_s),   I_s = 1 / (1 + exp(-x_s)),
+ *   selected  <=>  I_s >= threshold  <=>  x_s >= ln(threshold / (1 - threshold)).
+ *
+ * The comparison is made on the fp32 logit against the logit threshold, which
+ * is computed in double precision on the host (exactly 0 for threshold 0.5),
+ * so rounding in the sigmoid never decides membership. A sum that is exactly
+ * zero (every head's dot product <= 0, or every gate 0) selects the entry.
+ * Keys: [rows, d_h], in LSA_F32, LSA_BF16 or LSA_FP8_E4M3. For FP8 the key is
+ * key_scale[s] * e4m3(K8_s), and the scale must be positive and finite. One key
+ * serves all heads. q and w come from lsa_project or any other source: q is
+ * [B, n_h, d_h] fp32 and w is [B, n_h] fp32. score_out, if non-NULL, receives I_s
+ * as fp32 for every entry. mask_out receives the selection bits (see "Masks").
+ * Supported: d_h in {32, 64, 128}; 1 <= n_h <= 64; 0 < threshold < 1.
+ * Sequences with N_b = 0 are allowed and write nothing.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const float* q;          /* dev [B, n_h, d_h] fp32 */
+  const float* w;          /* dev [B, n_h] fp32 */
+  const void* keys;        /* dev [rows, d_h] */
+  const float* key_scale;  /* dev [rows] fp32 for LSA_FP8_E4M3, else NULL */
+  uint64_t* mask_out;      /* dev, words [mask_word_offsets[0], mask_word_offsets[B]) */
+  float* score_out;        /* dev [rows] fp32, or NULL */
+} lsa_score_layer;
+
+lsa_status lsa_score_select(const lsa_score_layer* layers /* host [L] */, int32_t L, int32_t B,
+                            const int64_t* key_offsets /* dev [B+1] */,
+                            const int64_t* key_offsets_host /* host [B+1] */,
+                            const int64_t* mask_word_offsets /* dev [B+1] */,
+                            const int64_t* mask_word_offsets_host /* host [B+1] */,
+                            int32_t n_h, int32_t d_h, lsa_dtype key_dtype, float threshold,
+                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * lsa_union_compact: OR-mode routing over the indexer layers. Entry s is
+ * fetched if any layer selected it ([BLOG] §4.2; [HYPER] 方法). The union is
+ * then compacted into the subset C^MemComp as an ascending list of
+ * sequence-local indices.
+ *
+ * idx_out region b starts at key_offsets[b] and holds up to N_b int32 values.
+ * The first count_out[b] are written in ascending order and the rest are left
+ * untouched. union_mask_out (optional) receives the OR of the masks in the
+ * mask layout.
+ * ---------------------------------------------------------------------- */
+lsa_status lsa_union_compact(const uint64_t* const* masks /* host [L] of dev pointers */, int32_t L,
+                             int32_t B, const int64_t* key_offsets /* dev [B+1] */,
+                             const int64_t* key_offsets_host /* host [B+1] */,
+                             const int64_t* mask_word_offsets /* dev [B+1] */,
+                             const int64_t* mask_word_offsets_host /* host [B+1] */,
+                             int32_t* idx_out /* dev [rows] */, int32_t* count_out /* dev [B] */,
+                             uint64_t* union_mask_out /* dev or NULL */, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * lsa_topk: the native Lightning Indexer's fine selection inside the loaded
+ * subset ([BLOG] §3.2 second level; §2.2 for the native score, which is a
+ * head-gated ReLU sum with no sigmoid).
+ *
+ * For each layer l and sequence b, and for each s in the subset
+ * idx[key_offsets[b] .. key_offsets[b] + count[b]), the call scores
+ *   y_s = sum_j w'_j * ReLU(q'_j . K^l_s),
+ * with the layer's native query q' [B, n_h, d_h] and gates w' [B, n_h]. It
+ * keeps the min(k, count[b]) entries that come first in the order (-y_s, s),
+ * so ties go to the lower index. topk_idx_out[b*k .. b*k + k) receives them in
+ * ascending index order, padded with -1. topk_score_out (optional) receives
+ * the matching y values, padded with -inf. topk_count_out[l*B + b] receives
+ * min(k, count[b]). idx must be ascending within each sequence, which is what
+ * lsa_union_compact writes.
+ *
+ * The workspace must hold at least lsa_topk_workspace_size(...) bytes of
+ * device memory. Its contents on entry do not matter. It holds the subset
+ * scores, one fp32 per (layer, row). Supported: 1 <= k <= 65536; B <= 4096;
+ * the key dtypes and head shapes of lsa_score_select.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const float* q;          /* dev [B, n_h, d_h] fp32 (native query q') */
+  const float* w;          /* dev [B, n_h] fp32 (native gates w') */
+  const void* keys;        /* dev [rows, d_h] (this layer's K^l) */
+  const float* key_scale;  /* dev [rows] for LSA_FP8_E4M3, else NULL */
+  int32_t* topk_idx_out;   /* dev [B, k] */
+  float* topk_score_out;   /* dev [B, k] or NULL */
+} lsa_topk_layer;
+
+size_t lsa_topk_workspace_size(int32_t L, int32_t B, int64_t total_rows, int32_t k);
+
+lsa_status lsa_topk(const lsa_topk_layer* layers /* host [L] */, int32_t L, int32_t B,
+                    const int64_t* key_offsets /* dev [B+1] */,
+                    const int64_t* key_offsets_host /* host [B+1] */,
+                    const int32_t* idx /* dev [rows] */, const int32_t* count /* dev [B] */,
+                    int32_t n_h, int32_t d_h, lsa_dtype key_dtype, int32_t k,
+                    int32_t* topk_count_out /* dev [L, B] */, void* workspace /* dev */,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * lsa_gather: load the selected entries' compressed-KV rows into a compact
+ * device buffer ([HYPER] 方法: the subset C^MemComp is loaded into GPU memory).
+ * Here the pool is already in device memory, so this is an HBM-to-HBM row copy.
+ *
+ * Row i < count[b] of sequence b is pool row pool_row_offsets[b] + idx[idx_offsets[b] + i].
+ * It is copied byte for byte, as row_bytes bytes, to output row o_b + i:
+ *   - packed mode (out_row_offsets == NULL): o_b = count[0] + ... + count[b-1].
+ *     The sequences are packed back to back, which is the compact buffer.
+ *   - explicit mode: o_b = out_row_offsets[b], and at most
+ *     out_row_offsets[b+1] - out_row_offsets[b] rows are written for b.
+ * Output rows at or beyond out_capacity_rows are never written. Rows that do
+ * not fit are dropped. row_bytes must be a positive multiple of 16. pool and
+ * out must be 16-byte aligned. idx values must lie in [0, N_b) of the pool
+ * region; this is not checked on the device.
+ * ---------------------------------------------------------------------- */
+lsa_status lsa_gather(const void* pool /* dev */, int64_t row_bytes, int32_t B,
+                      const int64_t* pool_row_offsets /* dev [B+1] */,
+                      const int64_t* pool_row_offsets_host /* host [B+1] */,
+                      const int32_t* idx /* dev */, const int64_t* idx_offsets /* dev [B] */,
+                      const int32_t* count /* dev [B] */, void* out /* dev */,
+                      const int64_t* out_row_offsets /* dev [B+1] or NULL */,
+                      int64_t out_capacity_rows, hipStream_t stream);
+
+/* Text describing the last non-OK status returned on the calling thread. */
+const char* lsa_last_error(void);
+
+/* LSA_VERSION of the built library. */
+int32_t lsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSA_H */

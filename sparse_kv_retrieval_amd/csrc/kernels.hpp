@@ -1,0 +1,135 @@
+// Kernel argument blocks and launchers shared between the kernels and the
+// C-ABI host layer.
+#pragma once
+
+#include "common.hpp"
+
+#define LSA_TOPK_MAX_B 4096
+
+namespace lsa {
+
+struct ScoreArgs {
+  const float* q[LSA_MAX_LAYERS];
+  const float* w[LSA_MAX_LAYERS];
+  const void* keys[LSA_MAX_LAYERS];
+  const float* scale[LSA_MAX_LAYERS];
+  uint64_t* mask[LSA_MAX_LAYERS];
+  float* score[LSA_MAX_LAYERS];
+  const int64_t* key_off;  // [B+1]
+  const int64_t* mwo;      // [B+1]
+  int64_t word_base;       // mwo[0]
+  int64_t words_per_layer; // mwo[B] - mwo[0]
+  int64_t total_words;     // L * words_per_layer
+  int32_t B, n_h;
+  float thr;               // logit threshold
+};
+
+struct TopkScoreArgs {
+  const float* q[LSA_MAX_LAYERS];
+  const float* w[LSA_MAX_LAYERS];
+  const void* keys[LSA_MAX_LAYERS];
+  const float* scale[LSA_MAX_LAYERS];
+  float* ys;                // workspace scores [L][rows_total]
+  const int32_t* idx;       // union lists, region b at key_off[b]
+  const int32_t* count;     // [B]
+  const int64_t* key_off;   // [B+1]
+  int64_t rows_total;
+  int32_t B, L, n_h;
+};
+
+struct TopkSelectArgs {
+  const float* ys;
+  const int32_t* idx;
+  const int32_t* count;
+  const int64_t* key_off;
+  int32_t* out_idx[LSA_MAX_LAYERS];
+  float* out_score[LSA_MAX_LAYERS];
+  int32_t* out_count;       // [L, B]
+  int64_t rows_total;
+  int32_t B, k;
+};
+
+struct UnionArgs {
+  const uint64_t* mask[LSA_MAX_LAYERS];
+  const int64_t* key_off;
+  const int64_t* mwo;
+  int32_t* idx_out;
+  int32_t* count_out;
+  uint64_t* union_out;
+  int32_t L;
+};
+
+struct GatherArgs {
+  const char* pool;
+  const int64_t* pool_off;   // [B+1]
+  const int32_t* idx;
+  const int64_t* idx_off;    // [B]
+  const int32_t* count;      // [B]
+  char* out;
+  const int64_t* out_off;    // [B+1] or null (packed)
+  int64_t out_capacity;
+  int64_t row_bytes;
+  int32_t B;
+};
+
+struct ProjArgs {
+  const void* h[LSA_MAX_LAYERS];
+  const void* w_dq[LSA_MAX_LAYERS];
+  const void* w_iuq[LSA_MAX_LAYERS];
+  const void* w_w[LSA_MAX_LAYERS];
+  float* c[LSA_MAX_LAYERS];
+  float* q[LSA_MAX_LAYERS];
+  float* w[LSA_MAX_LAYERS];
+  int32_t B, d, r, n_h, d_h;
+};
+
+hipError_t launch_score_select(const ScoreArgs& a, int key_kind, int d_h, int grid, hipStream_t st);
+hipError_t launch_topk_score(const TopkScoreArgs& a, int key_kind, int d_h, int grid, hipStream_t st);
+hipError_t launch_topk_select(const TopkSelectArgs& a, int L, hipStream_t st);
+hipError_t launch_union_compact(const UnionArgs& a, int B, int64_t max_words, hipStream_t st);
+hipError_t launch_gather(const GatherArgs& a, int grid, hipStream_t st);
+hipError_t launch_project(const ProjArgs& a, int L, bool f32, hipStream_t st);
+
+// ------------------------------------------------------------ block helpers
+// Exclusive prefix sum over the threads of a block (blockDim.x a multiple of
+// 64, at most 1024). Every thread of the block must call it.
+__device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* total) {
+  __shared__ int64_t wsum[16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nwv = blockDim.x >> 6;
+  int64_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int64_t off = 0, tot = 0;
+  for (int i = 0; i < nwv; ++i) {
+    const int64_t s = wsum[i];
+    off += i < w ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  if (total) *total = tot;
+  return off + x - v;
+}
+
+// tp[b] = sum over b' < b of ceil(count[b'] / 32), for b = 0..B (B <= LSA_TOPK_MAX_B).
+__device__ __forceinline__ void block_tile_prefix(const int32_t* __restrict__ count, int B, int32_t* tp) {
+  const int nt = blockDim.x, tid = threadIdx.x;
+  const int per = (B + nt - 1) / nt;
+  const int lo = min(B, tid * per), hi = min(B, lo + per);
+  int64_t s = 0;
+  for (int b = lo; b < hi; ++b) s += (count[b] + 31) >> 5;
+  int64_t tot;
+  int64_t run = block_exclusive_scan(s, &tot);
+  for (int b = lo; b < hi; ++b) {
+    tp[b] = (int32_t)run;
+    run += (count[b] + 31) >> 5;
+  }
+  if (tid == 0) tp[B] = (int32_t)tot;
+  __syncthreads();
+}
+
+}  // namespace lsa

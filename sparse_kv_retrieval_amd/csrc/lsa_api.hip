@@ -1,0 +1,268 @@
+// C-ABI host layer. It validates the arguments, sizes the grids and launches
+// the kernels. Every check runs before any HIP call, so a rejected call
+// touches neither the device nor the stream. No allocation, no
+// synchronisation.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "kernels.hpp"
+
+using namespace lsa;
+
+namespace {
+
+thread_local std::string g_err;
+
+lsa_status fail(lsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+lsa_status hip_fail(const char* where, hipError_t e) {
+  return fail(LSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  const int x = std::atoi(v);
+  return x > 0 ? x : dflt;
+}
+
+// Checks an offsets mirror: off[0] >= 0 and non-decreasing. Also returns the total.
+lsa_status check_offsets(const int64_t* off_host, int32_t B, const char* name) {
+  if (!off_host) return fail(LSA_ERR_INVALID_ARG, "%s_host is NULL", name);
+  if (off_host[0] < 0) return fail(LSA_ERR_INVALID_ARG, "%s_host[0] < 0", name);
+  for (int32_t b = 0; b < B; ++b)
+    if (off_host[b + 1] < off_host[b]) return fail(LSA_ERR_INVALID_ARG, "%s_host is decreasing at %d", name, b);
+  return LSA_OK;
+}
+
+lsa_status check_seq_layout(int32_t B, const int64_t* key_offsets, const int64_t* key_offsets_host,
+                            const int64_t* mwo, const int64_t* mwo_host) {
+  if (B < 1) return fail(LSA_ERR_INVALID_ARG, "B must be >= 1 (got %d)", B);
+  if (!key_offsets || !mwo) return fail(LSA_ERR_INVALID_ARG, "device offset array is NULL");
+  lsa_status s;
+  if ((s = check_offsets(key_offsets_host, B, "key_offsets")) != LSA_OK) return s;
+  if ((s = check_offsets(mwo_host, B, "mask_word_offsets")) != LSA_OK) return s;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t n = key_offsets_host[b + 1] - key_offsets_host[b];
+    if (n > INT32_MAX) return fail(LSA_ERR_UNSUPPORTED, "sequence %d has %lld entries (> 2^31-1)", b, (long long)n);
+    if (mwo_host[b + 1] - mwo_host[b] != (n + 63) / 64)
+      return fail(LSA_ERR_INVALID_ARG, "mask region of sequence %d must be ceil(N_b/64) = %lld words", b,
+                  (long long)((n + 63) / 64));
+  }
+  return LSA_OK;
+}
+
+lsa_status check_heads(int32_t n_h, int32_t d_h) {
+  if (n_h < 1 || n_h > LSA_MAX_HEADS) return fail(LSA_ERR_UNSUPPORTED, "n_h must be in [1, %d] (got %d)", LSA_MAX_HEADS, n_h);
+  if (d_h != 32 && d_h != 64 && d_h != 128) return fail(LSA_ERR_UNSUPPORTED, "d_h must be 32, 64 or 128 (got %d)", d_h);
+  return LSA_OK;
+}
+
+lsa_status key_kind_of(lsa_dtype dt, int* kind) {
+  switch (dt) {
+    case LSA_F32: *kind = KEY_F32; return LSA_OK;
+    case LSA_BF16: *kind = KEY_BF16; return LSA_OK;
+    case LSA_FP8_E4M3: *kind = KEY_FP8; return LSA_OK;
+    default: return fail(LSA_ERR_UNSUPPORTED, "unknown key dtype %d", (int)dt);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lsa_last_error(void) { return g_err.c_str(); }
+
+int32_t lsa_version(void) { return LSA_VERSION; }
+
+lsa_status lsa_project(const lsa_proj_layer* layers, int32_t L, int32_t B, int32_t d, int32_t r, int32_t n_h,
+                       int32_t d_h, lsa_dtype dtype, hipStream_t stream) {
+  if (!layers) return fail(LSA_ERR_INVALID_ARG, "layers is NULL");
+  if (L < 1 || L > LSA_MAX_LAYERS) return fail(LSA_ERR_INVALID_ARG, "L must be in [1, %d] (got %d)", LSA_MAX_LAYERS, L);
+  if (B < 1 || B > 128) return fail(LSA_ERR_UNSUPPORTED, "B must be in [1, 128] (got %d)", B);
+  if (dtype != LSA_F32 && dtype != LSA_BF16) return fail(LSA_ERR_UNSUPPORTED, "projection dtype must be LSA_F32 or LSA_BF16");
+  const int kq = dtype == LSA_F32 ? 4 : 32;
+  if (d < kq || d % kq || r < kq || r % kq)
+    return fail(LSA_ERR_UNSUPPORTED, "d and r must be positive multiples of %d (got d=%d r=%d)", kq, d, r);
+  if (n_h < 1 || n_h > LSA_MAX_HEADS || d_h < 1) return fail(LSA_ERR_UNSUPPORTED, "bad head shape n_h=%d d_h=%d", n_h, d_h);
+  if ((int64_t)n_h * d_h % 16) return fail(LSA_ERR_UNSUPPORTED, "n_h*d_h must be a multiple of 16");
+  ProjArgs a{};
+  for (int l = 0; l < L; ++l) {
+    const lsa_proj_layer& p = layers[l];
+    if (!p.h || !p.w_dq || !p.w_iuq || !p.w_w || !p.c_out || !p.q_out || !p.w_out)
+      return fail(LSA_ERR_INVALID_ARG, "layer %d: a pointer is NULL", l);
+    if (!aligned16(p.h) || !aligned16(p.w_dq) || !aligned16(p.w_iuq) || !aligned16(p.c_out))
+      return fail(LSA_ERR_INVALID_ARG, "layer %d: h, w_dq, w_iuq and c_out must be 16-byte aligned", l);
+    if ((const void*)p.c_out == (const void*)p.q_out || (const void*)p.c_out == (const void*)p.w_out)
+      return fail(LSA_ERR_INVALID_ARG, "layer %d: c_out aliases another output", l);
+    a.h[l] = p.h; a.w_dq[l] = p.w_dq; a.w_iuq[l] = p.w_iuq; a.w_w[l] = p.w_w;
+    a.c[l] = p.c_out; a.q[l] = p.q_out; a.w[l] = p.w_out;
+  }
+  a.B = B; a.d = d; a.r = r; a.n_h = n_h; a.d_h = d_h;
+  const hipError_t e = launch_project(a, L, dtype == LSA_F32, stream);
+  return e == hipSuccess ? LSA_OK : hip_fail("lsa_project launch", e);
+}
+
+lsa_status lsa_score_select(const lsa_score_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
+                            const int64_t* key_offsets_host, const int64_t* mask_word_offsets,
+                            const int64_t* mask_word_offsets_host, int32_t n_h, int32_t d_h, lsa_dtype key_dtype,
+                            float threshold, hipStream_t stream) {
+  if (!layers) return fail(LSA_ERR_INVALID_ARG, "layers is NULL");
+  if (L < 1 || L > LSA_MAX_LAYERS) return fail(LSA_ERR_INVALID_ARG, "L must be in [1, %d] (got %d)", LSA_MAX_LAYERS, L);
+  lsa_status s;
+  if ((s = check_seq_layout(B, key_offsets, key_offsets_host, mask_word_offsets, mask_word_offsets_host)) != LSA_OK) return s;
+  if ((s = check_heads(n_h, d_h)) != LSA_OK) return s;
+  int kind;
+  if ((s = key_kind_of(key_dtype, &kind)) != LSA_OK) return s;
+  if (!(threshold > 0.0f && threshold < 1.0f)) return fail(LSA_ERR_INVALID_ARG, "threshold must lie in (0, 1)");
+  ScoreArgs a{};
+  for (int l = 0; l < L; ++l) {
+    const lsa_score_layer& p = layers[l];
+    if (!p.q || !p.w || !p.keys || !p.mask_out) return fail(LSA_ERR_INVALID_ARG, "layer %d: q, w, keys and mask_out must be set", l);
+    if (kind == KEY_FP8 && !p.key_scale) return fail(LSA_ERR_INVALID_ARG, "layer %d: fp8 keys need key_scale", l);
+    if (kind != KEY_FP8 && p.key_scale) return fail(LSA_ERR_INVALID_ARG, "layer %d: key_scale is only for fp8 keys", l);
+    if (!aligned16(p.q) || !aligned16(p.keys)) return fail(LSA_ERR_INVALID_ARG, "layer %d: q and keys must be 16-byte aligned", l);
+    a.q[l] = p.q; a.w[l] = p.w; a.keys[l] = p.keys; a.scale[l] = p.key_scale;
+    a.mask[l] = p.mask_out; a.score[l] = p.score_out;
+  }
+  const double t = std::log((double)threshold / (1.0 - (double)threshold));
+  a.key_off = key_offsets; a.mwo = mask_word_offsets;
+  a.word_base = mask_word_offsets_host[0];
+  a.words_per_layer = mask_word_offsets_host[B] - mask_word_offsets_host[0];
+  a.total_words = a.words_per_layer * L;
+  a.B = B; a.n_h = n_h; a.thr = (float)t;
+  if (a.total_words == 0) return LSA_OK;
+  const int64_t waves = std::min<int64_t>(a.total_words, (int64_t)cu_count() * env_int("LSA_SCORE_WAVES_PER_CU", 8));
+  const int grid = (int)((waves + 3) / 4);
+  const hipError_t e = launch_score_select(a, kind, d_h, grid, stream);
+  return e == hipSuccess ? LSA_OK : hip_fail("lsa_score_select launch", e);
+}
+
+lsa_status lsa_union_compact(const uint64_t* const* masks, int32_t L, int32_t B, const int64_t* key_offsets,
+                             const int64_t* key_offsets_host, const int64_t* mask_word_offsets,
+                             const int64_t* mask_word_offsets_host, int32_t* idx_out, int32_t* count_out,
+                             uint64_t* union_mask_out, hipStream_t stream) {
+  if (!masks) return fail(LSA_ERR_INVALID_ARG, "masks is NULL");
+  if (L < 1 || L > LSA_MAX_LAYERS) return fail(LSA_ERR_INVALID_ARG, "L must be in [1, %d] (got %d)", LSA_MAX_LAYERS, L);
+  if (B > 65535) return fail(LSA_ERR_UNSUPPORTED, "B must be <= 65535");
+  lsa_status s;
+  if ((s = check_seq_layout(B, key_offsets, key_offsets_host, mask_word_offsets, mask_word_offsets_host)) != LSA_OK) return s;
+  if (!idx_out || !count_out) return fail(LSA_ERR_INVALID_ARG, "idx_out and count_out must be set");
+  UnionArgs a{};
+  for (int l = 0; l < L; ++l) {
+    if (!masks[l]) return fail(LSA_ERR_INVALID_ARG, "masks[%d] is NULL", l);
+    a.mask[l] = masks[l];
+  }
+  int64_t max_words = 0;
+  for (int b = 0; b < B; ++b) max_words = std::max(max_words, mask_word_offsets_host[b + 1] - mask_word_offsets_host[b]);
+  a.key_off = key_offsets; a.mwo = mask_word_offsets; a.idx_out = idx_out; a.count_out = count_out;
+  a.union_out = union_mask_out; a.L = L;
+  const hipError_t e = launch_union_compact(a, B, max_words, stream);
+  return e == hipSuccess ? LSA_OK : hip_fail("lsa_union_compact launch", e);
+}
+
+size_t lsa_topk_workspace_size(int32_t L, int32_t B, int64_t total_rows, int32_t k) {
+  (void)B; (void)k;
+  if (L < 1 || total_rows < 0) return 0;
+  return (size_t)L * (size_t)total_rows * sizeof(float);
+}
+
+lsa_status lsa_topk(const lsa_topk_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
+                    const int64_t* key_offsets_host, const int32_t* idx, const int32_t* count, int32_t n_h, int32_t d_h,
+                    lsa_dtype key_dtype, int32_t k, int32_t* topk_count_out, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  if (!layers) return fail(LSA_ERR_INVALID_ARG, "layers is NULL");
+  if (L < 1 || L > LSA_MAX_LAYERS) return fail(LSA_ERR_INVALID_ARG, "L must be in [1, %d] (got %d)", LSA_MAX_LAYERS, L);
+  if (B < 1 || B > LSA_TOPK_MAX_B) return fail(LSA_ERR_UNSUPPORTED, "B must be in [1, %d] (got %d)", LSA_TOPK_MAX_B, B);
+  if (!key_offsets) return fail(LSA_ERR_INVALID_ARG, "key_offsets is NULL");
+  lsa_status s;
+  if ((s = check_offsets(key_offsets_host, B, "key_offsets")) != LSA_OK) return s;
+  if ((s = check_heads(n_h, d_h)) != LSA_OK) return s;
+  int kind;
+  if ((s = key_kind_of(key_dtype, &kind)) != LSA_OK) return s;
+  if (k < 1 || k > 65536) return fail(LSA_ERR_UNSUPPORTED, "k must be in [1, 65536] (got %d)", k);
+  if (!idx || !count || !topk_count_out) return fail(LSA_ERR_INVALID_ARG, "idx, count and topk_count_out must be set");
+  const int64_t rows = key_offsets_host[B];
+  for (int32_t b = 0; b < B; ++b)
+    if (key_offsets_host[b + 1] - key_offsets_host[b] > INT32_MAX) return fail(LSA_ERR_UNSUPPORTED, "sequence too long");
+  const size_t need = lsa_topk_workspace_size(L, B, rows, k);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(LSA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  TopkScoreArgs sa{};
+  TopkSelectArgs ta{};
+  for (int l = 0; l < L; ++l) {
+    const lsa_topk_layer& p = layers[l];
+    if (!p.q || !p.w || !p.keys || !p.topk_idx_out) return fail(LSA_ERR_INVALID_ARG, "layer %d: q, w, keys and topk_idx_out must be set", l);
+    if (kind == KEY_FP8 && !p.key_scale) return fail(LSA_ERR_INVALID_ARG, "layer %d: fp8 keys need key_scale", l);
+    if (kind != KEY_FP8 && p.key_scale) return fail(LSA_ERR_INVALID_ARG, "layer %d: key_scale is only for fp8 keys", l);
+    if (!aligned16(p.q) || !aligned16(p.keys)) return fail(LSA_ERR_INVALID_ARG, "layer %d: q and keys must be 16-byte aligned", l);
+    sa.q[l] = p.q; sa.w[l] = p.w; sa.keys[l] = p.keys; sa.scale[l] = p.key_scale;
+    ta.out_idx[l] = p.topk_idx_out; ta.out_score[l] = p.topk_score_out;
+  }
+  sa.ys = (float*)workspace; sa.idx = idx; sa.count = count; sa.key_off = key_offsets; sa.rows_total = rows;
+  sa.B = B; sa.L = L; sa.n_h = n_h;
+  ta.ys = (const float*)workspace; ta.idx = idx; ta.count = count; ta.key_off = key_offsets;
+  ta.out_count = topk_count_out; ta.rows_total = rows; ta.B = B; ta.k = k;
+  hipError_t e;
+  if (rows > 0) {
+    int64_t tiles = 0;
+    for (int32_t b = 0; b < B; ++b) tiles += (key_offsets_host[b + 1] - key_offsets_host[b] + 31) / 32;
+    const int64_t waves = std::max<int64_t>(1, std::min<int64_t>(tiles * L, (int64_t)cu_count() * 8));
+    if ((e = launch_topk_score(sa, kind, d_h, (int)((waves + 3) / 4), stream)) != hipSuccess)
+      return hip_fail("lsa_topk score launch", e);
+  }
+  if ((e = launch_topk_select(ta, L, stream)) != hipSuccess) return hip_fail("lsa_topk select launch", e);
+  return LSA_OK;
+}
+
+lsa_status lsa_gather(const void* pool, int64_t row_bytes, int32_t B, const int64_t* pool_row_offsets,
+                      const int64_t* pool_row_offsets_host, const int32_t* idx, const int64_t* idx_offsets,
+                      const int32_t* count, void* out, const int64_t* out_row_offsets, int64_t out_capacity_rows,
+                      hipStream_t stream) {
+  if (B < 1 || B > LSA_TOPK_MAX_B) return fail(LSA_ERR_UNSUPPORTED, "B must be in [1, %d] (got %d)", LSA_TOPK_MAX_B, B);
+  if (row_bytes <= 0 || row_bytes % 16) return fail(LSA_ERR_INVALID_ARG, "row_bytes must be a positive multiple of 16");
+  if (!pool || !pool_row_offsets || !idx || !idx_offsets || !count || !out)
+    return fail(LSA_ERR_INVALID_ARG, "pool, pool_row_offsets, idx, idx_offsets, count and out must be set");
+  if (!aligned16(pool) || !aligned16(out)) return fail(LSA_ERR_INVALID_ARG, "pool and out must be 16-byte aligned");
+  if (out_capacity_rows < 0) return fail(LSA_ERR_INVALID_ARG, "out_capacity_rows < 0");
+  lsa_status s;
+  if ((s = check_offsets(pool_row_offsets_host, B, "pool_row_offsets")) != LSA_OK) return s;
+  const int64_t bound = std::min<int64_t>(out_capacity_rows, pool_row_offsets_host[B] - pool_row_offsets_host[0]);
+  if (bound == 0) {
+    // Nothing can be written, but the call is still well formed.
+    return LSA_OK;
+  }
+  GatherArgs a{};
+  a.pool = (const char*)pool; a.pool_off = pool_row_offsets; a.idx = idx; a.idx_off = idx_offsets; a.count = count;
+  a.out = (char*)out; a.out_off = out_row_offsets; a.out_capacity = out_capacity_rows; a.row_bytes = row_bytes; a.B = B;
+  const int64_t waves = std::min<int64_t>(bound, (int64_t)cu_count() * 16);
+  const hipError_t e = launch_gather(a, (int)((waves + 3) / 4), stream);
+  return e == hipSuccess ? LSA_OK : hip_fail("lsa_gather launch", e);
+}
+
+}  // extern "C"

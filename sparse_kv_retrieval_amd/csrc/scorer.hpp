@@ -1,0 +1,141 @@
+// MFMA micro-kernel for the head-gated ReLU score of 32 entries by one wave.
+//
+//   x_s = sum_j w_j * ReLU(q_j . K_s)
+//
+// This is the lookahead index score before its sigmoid ([BLOG] §3.1 of the
+// FlashMemory-DeepSeek-V4 write-up) and also the native Lightning-Indexer
+// score ([BLOG] §2.2). The contraction q_j . K_s is a [heads x d_h] x
+// [d_h x 32 entries] matrix product on the matrix cores. Heads are the MFMA
+// rows, so each lane ends up holding one entry's dot products for 16 heads per
+// 32-head block, and the gate/ReLU/head-sum epilogue needs one cross-lane add.
+//
+// Operand layout (wave64, 32x32 MFMA, one block):
+//   A (query):  lane l supplies row (l % 32), k-group (l / 32)
+//   B (keys):   lane l supplies column (l % 32), k-group (l / 32)
+//   D:          lane l holds column (l % 32), rows 8*(i/4) + 4*(l/32) + (i%4), i < 16
+// The order of the k sum is free, so lane group g = l/32 owns the contiguous
+// half [g*d_h/2, (g+1)*d_h/2) of the head dimension. Each lane then reads one
+// contiguous half-row of its key (64..256 bytes) with 16-byte loads.
+//
+// Precision: bf16 keys (and fp8 keys, widened exactly to bf16) multiply a
+// query split into bf16 hi + lo parts, which keeps about 16 bits of q, with
+// fp32 accumulation. fp32 keys use the fp32 MFMA directly.
+#pragma once
+
+#include "common.hpp"
+
+namespace lsa {
+
+template <int KT, int DH, int NHB>
+struct Scorer {
+  static_assert(DH == 32 || DH == 64 || DH == 128, "d_h");
+  static_assert(NHB == 1 || NHB == 2, "heads per block");
+  static constexpr int HALF = DH / 2;                         // k values per lane group
+  static constexpr int ESZ = KT == KEY_F32 ? 4 : (KT == KEY_BF16 ? 2 : 1);
+  static constexpr int ROW_BYTES = DH * ESZ;
+  static constexpr int HALF_BYTES = HALF * ESZ;
+  static constexpr int NLD = HALF_BYTES / 16;                 // 16-byte loads per lane
+  static constexpr int STEPS = KT == KEY_F32 ? HALF : HALF / 8;  // MFMAs per head block (per part)
+  static constexpr bool SPLIT = KT != KEY_F32;
+
+  // query fragments (bf16 hi/lo) or fp32 values
+  bf16x8 qa[SPLIT ? NHB : 1][SPLIT ? STEPS : 1][2];
+  float qf[SPLIT ? 1 : NHB][SPLIT ? 1 : STEPS];
+  float gate[NHB][16];
+  // key fragment of the current 32-entry tile
+  u32x4 kraw[NLD];
+
+  // Load q[b] and w[b] (fp32) of one (sequence, layer).
+  __device__ __forceinline__ void load_query(const float* __restrict__ q, const float* __restrict__ w,
+                                             int b, int n_h) {
+    const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
+#pragma unroll
+    for (int mb = 0; mb < NHB; ++mb) {
+      const int head = mb * 32 + n;
+      const bool ok = head < n_h;
+      const float* qrow = q + ((int64_t)b * n_h + (ok ? head : 0)) * DH + g * HALF;
+      if constexpr (SPLIT) {
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+          float v[8];
+          f32x4 v0 = ok ? *(const f32x4*)(qrow + 8 * t) : f32x4{0, 0, 0, 0};
+          f32x4 v1 = ok ? *(const f32x4*)(qrow + 8 * t + 4) : f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { v[i] = v0[i]; v[4 + i] = v1[i]; }
+          split8(v, qa[mb][t][0], qa[mb][t][1]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < STEPS; t += 4) {
+          f32x4 v = ok ? *(const f32x4*)(qrow + t) : f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) qf[mb][t + i] = v[i];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int h = mb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+        gate[mb][i] = h < n_h ? w[(int64_t)b * n_h + h] : 0.0f;
+      }
+    }
+  }
+
+  // Load this lane's half of one key row (row pointer already at the half).
+  __device__ __forceinline__ void load_keys(const char* __restrict__ p, bool valid) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i)
+      kraw[i] = valid ? __builtin_nontemporal_load((const u32x4*)p + i) : u32x4{0, 0, 0, 0};
+  }
+
+  __device__ __forceinline__ void mma(f32x16 (&acc)[NHB]) const {
+#pragma unroll
+    for (int mb = 0; mb < NHB; ++mb) acc[mb] = f32x16{};
+    if constexpr (KT == KEY_BF16) {
+#pragma unroll
+      for (int t = 0; t < STEPS; ++t) {
+        const bf16x8 kb = as_bf16x8(kraw[t]);
+#pragma unroll
+        for (int mb = 0; mb < NHB; ++mb) {
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][t][0], kb, acc[mb], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][t][1], kb, acc[mb], 0, 0, 0);
+        }
+      }
+    } else if constexpr (KT == KEY_FP8) {
+#pragma unroll
+      for (int t = 0; t < STEPS; ++t) {
+        const u32x4 raw = kraw[t >> 1];
+        const int o = (t & 1) * 2;
+        const u32x2 lo = e4m3x4_to_bf16x4(raw[o]);
+        const u32x2 hi = e4m3x4_to_bf16x4(raw[o + 1]);
+        const bf16x8 kb = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+        for (int mb = 0; mb < NHB; ++mb) {
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][t][0], kb, acc[mb], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][t][1], kb, acc[mb], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < STEPS; ++t) {
+        const float kv = __uint_as_float(kraw[t >> 2][t & 3]);
+#pragma unroll
+        for (int mb = 0; mb < NHB; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(qf[mb][t], kv, acc[mb], 0, 0, 0);
+      }
+    }
+  }
+
+  // Gate, ReLU and head sum. Lanes l and l^32 hold complementary heads of the
+  // same entry. After one swap both lanes have the full sum. Addition is
+  // commutative, so both lanes hold the identical value.
+  __device__ __forceinline__ float logit(const f32x16 (&acc)[NHB]) const {
+    float part = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < NHB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part = fmaf(gate[mb][i], fmaxf(acc[mb][i], 0.0f), part);
+    return part + __shfl_xor(part, 32);
+  }
+};
+
+}  // namespace lsa

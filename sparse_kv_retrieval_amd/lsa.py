@@ -1,0 +1,169 @@
+"""Python binding for `liblsa.so` (the C-ABI declared in include/lsa.h).
+
+This module only marshals arguments. Every step of the selection path runs in
+the library's HIP kernels. Tensors are passed by `data_ptr()`, `*_host` offset
+arrays are int64 numpy arrays (or CPU tensors), and the stream defaults to
+torch's current stream. If the library has not been built, importing this
+module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblsa.so")
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+MAX_LAYERS = 8
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4
+
+
+class LsaError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build the HIP library first (__graft_entry__.build())")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp = ctypes.c_void_p
+_i32, _i64, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class ProjLayer(ctypes.Structure):
+    _fields_ = [("h", _vp), ("w_dq", _vp), ("w_iuq", _vp), ("w_w", _vp),
+                ("c_out", _vp), ("q_out", _vp), ("w_out", _vp)]
+
+
+class ScoreLayer(ctypes.Structure):
+    _fields_ = [("q", _vp), ("w", _vp), ("keys", _vp), ("key_scale", _vp),
+                ("mask_out", _vp), ("score_out", _vp)]
+
+
+class TopkLayer(ctypes.Structure):
+    _fields_ = [("q", _vp), ("w", _vp), ("keys", _vp), ("key_scale", _vp),
+                ("topk_idx_out", _vp), ("topk_score_out", _vp)]
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_project = _sig("lsa_project", _i32, [ctypes.POINTER(ProjLayer), _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp])
+_score_select = _sig("lsa_score_select", _i32, [ctypes.POINTER(ScoreLayer), _i32, _i32, _vp, _vp, _vp, _vp,
+                                                 _i32, _i32, _i32, _f32, _vp])
+_union_compact = _sig("lsa_union_compact", _i32, [ctypes.POINTER(_vp), _i32, _i32, _vp, _vp, _vp, _vp,
+                                                   _vp, _vp, _vp, _vp])
+_topk_ws = _sig("lsa_topk_workspace_size", _sz, [_i32, _i32, _i64, _i32])
+_topk = _sig("lsa_topk", _i32, [ctypes.POINTER(TopkLayer), _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                 _i32, _vp, _vp, _sz, _vp])
+_gather = _sig("lsa_gather", _i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp])
+_last_error = _sig("lsa_last_error", ctypes.c_char_p, [])
+_version = _sig("lsa_version", _i32, [])
+
+EXPORTED = ("lsa_project", "lsa_score_select", "lsa_union_compact", "lsa_topk_workspace_size", "lsa_topk",
+            "lsa_gather", "lsa_last_error", "lsa_version")
+
+
+def last_error() -> str:
+    return _last_error().decode()
+
+
+def version() -> int:
+    return int(_version())
+
+
+def _p(t):
+    """Device pointer of a tensor (or None/int passthrough)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _host64(a):
+    """Host int64 array -> (keep-alive object, pointer)."""
+    if a is None:
+        return None, None
+    if hasattr(a, "numpy"):
+        a = a.detach().cpu().numpy()
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+    return arr, arr.ctypes.data
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, st):
+    if st != OK:
+        raise LsaError(fn, st, last_error())
+
+
+def project(layers, *, B, d, r, n_h, d_h, dtype, stream=None):
+    """lsa_project. `layers`: list of dicts with h, w_dq, w_iuq, w_w, c_out, q_out, w_out tensors."""
+    arr = (ProjLayer * len(layers))(*[ProjLayer(*[_p(x[k]) for k in ("h", "w_dq", "w_iuq", "w_w", "c_out",
+                                                                      "q_out", "w_out")]) for x in layers])
+    _check("lsa_project", _project(arr, len(layers), B, d, r, n_h, d_h, DTYPES.get(dtype, dtype), _stream(stream)))
+
+
+def score_select(layers, *, B, key_offsets, key_offsets_host, mask_word_offsets, mask_word_offsets_host,
+                 n_h, d_h, key_dtype, threshold=0.5, stream=None):
+    """lsa_score_select. `layers`: dicts with q, w, keys, key_scale (fp8), mask_out, score_out (optional)."""
+    arr = (ScoreLayer * len(layers))(*[ScoreLayer(_p(x["q"]), _p(x["w"]), _p(x["keys"]), _p(x.get("key_scale")),
+                                                  _p(x["mask_out"]), _p(x.get("score_out"))) for x in layers])
+    ko, kop = _host64(key_offsets_host)
+    mo, mop = _host64(mask_word_offsets_host)
+    _check("lsa_score_select", _score_select(arr, len(layers), B, _p(key_offsets), kop, _p(mask_word_offsets), mop,
+                                             n_h, d_h, DTYPES.get(key_dtype, key_dtype), float(threshold),
+                                             _stream(stream)))
+
+
+def union_compact(masks, *, B, key_offsets, key_offsets_host, mask_word_offsets, mask_word_offsets_host,
+                  idx_out, count_out, union_mask_out=None, stream=None):
+    """lsa_union_compact over a list of per-layer mask tensors."""
+    marr = (_vp * len(masks))(*[_p(m) for m in masks])
+    ko, kop = _host64(key_offsets_host)
+    mo, mop = _host64(mask_word_offsets_host)
+    _check("lsa_union_compact", _union_compact(marr, len(masks), B, _p(key_offsets), kop, _p(mask_word_offsets),
+                                               mop, _p(idx_out), _p(count_out), _p(union_mask_out),
+                                               _stream(stream)))
+
+
+def topk_workspace_size(L, B, total_rows, k) -> int:
+    return int(_topk_ws(L, B, total_rows, k))
+
+
+def topk(layers, *, B, key_offsets, key_offsets_host, idx, count, n_h, d_h, key_dtype, k, topk_count_out,
+         workspace, stream=None):
+    """lsa_topk. `layers`: dicts with q, w, keys, key_scale (fp8), topk_idx_out, topk_score_out (optional)."""
+    arr = (TopkLayer * len(layers))(*[TopkLayer(_p(x["q"]), _p(x["w"]), _p(x["keys"]), _p(x.get("key_scale")),
+                                                _p(x["topk_idx_out"]), _p(x.get("topk_score_out"))) for x in layers])
+    ko, kop = _host64(key_offsets_host)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("lsa_topk", _topk(arr, len(layers), B, _p(key_offsets), kop, _p(idx), _p(count), n_h, d_h,
+                             DTYPES.get(key_dtype, key_dtype), k, _p(topk_count_out), _p(workspace), nbytes,
+                             _stream(stream)))
+
+
+def gather(pool, *, row_bytes, B, pool_row_offsets, pool_row_offsets_host, idx, idx_offsets, count, out,
+           out_row_offsets=None, out_capacity_rows, stream=None):
+    """lsa_gather (packed mode when out_row_offsets is None)."""
+    po, pop = _host64(pool_row_offsets_host)
+    _check("lsa_gather", _gather(_p(pool), int(row_bytes), B, _p(pool_row_offsets), pop, _p(idx), _p(idx_offsets),
+                                 _p(count), _p(out), _p(out_row_offsets), int(out_capacity_rows), _stream(stream)))

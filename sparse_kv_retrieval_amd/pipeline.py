@@ -1,0 +1,140 @@
+"""Device-resident buffers for one workload, and one pass of the whole path.
+
+`Pipeline(inputs)` copies a seeded input set (from `synth.make`) into HBM and
+allocates every output and the top-k workspace once. `run()` then enqueues the
+five library calls on the current stream, with no allocation and no host
+synchronisation:
+
+  lsa_project        memory-indexer and native query/gates for every layer (one call, 2L layers)
+  lsa_score_select   masks (and optional sigmoid scores) for every (layer, sequence)
+  lsa_union_compact  OR over the layers -> ascending index list + count per sequence
+  lsa_topk           native top-k inside the union, per (layer, sequence)
+  lsa_gather         the union rows of the compressed-KV pool -> packed compact buffer
+
+This module only wires buffers. All arithmetic happens in the HIP kernels.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import lsa
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    elif a.dtype == np.uint64:
+        a = a.view(np.int64)
+    return torch.from_numpy(a).to(device)
+
+
+class Pipeline:
+    def __init__(self, inp, device="cuda", *, with_scores=False, with_topk_scores=True, gather_capacity=None):
+        w = inp.workload
+        self.w = w
+        self.inp = inp
+        dev = torch.device(device)
+        self.device = dev
+        B, L = w.B, w.L
+        self.rows = int(inp.key_offsets[-1])
+        self.words = int(inp.mask_word_offsets[-1])
+        self.key_off_h = inp.key_offsets.astype(np.int64)
+        self.mwo_h = inp.mask_word_offsets.astype(np.int64)
+        self.key_off = _dev(self.key_off_h, dev)
+        self.mwo = _dev(self.mwo_h, dev)
+
+        self.h = [_dev(inp.h[l], dev) for l in range(L)]
+        self.mem = [tuple(_dev(x, dev) for x in (lw.w_dq, lw.w_iuq, lw.w_w)) for lw in inp.mem_w]
+        self.nat = [tuple(_dev(x, dev) for x in (lw.w_dq, lw.w_iuq, lw.w_w)) for lw in inp.nat_w]
+        self.keys = [_dev(inp.keys[l], dev) for l in range(L)]
+        self.scale = [None if inp.key_scale[l] is None else _dev(inp.key_scale[l], dev) for l in range(L)]
+        self.pool = None if inp.pool is None else _dev(inp.pool, dev)
+
+        f32 = dict(dtype=torch.float32, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        # 2L projection outputs: first L for the memory indexer, next L for the native indexer
+        self.c = [torch.empty(B, w.r, **f32) for _ in range(2 * L)]
+        self.q = [torch.empty(B, w.n_h, w.d_h, **f32) for _ in range(2 * L)]
+        self.g = [torch.empty(B, w.n_h, **f32) for _ in range(2 * L)]
+        self.masks = [torch.empty(max(self.words, 1), dtype=torch.int64, device=dev) for _ in range(L)]
+        self.scores = [torch.empty(max(self.rows, 1), **f32) for _ in range(L)] if with_scores else None
+        self.idx = torch.empty(max(self.rows, 1), **i32)
+        self.count = torch.empty(B, **i32)
+        self.union_mask = torch.empty(max(self.words, 1), dtype=torch.int64, device=dev)
+        self.topk_idx = [torch.empty(B, w.k, **i32) for _ in range(L)]
+        self.topk_score = [torch.empty(B, w.k, **f32) for _ in range(L)] if with_topk_scores else None
+        self.topk_count = torch.empty(L, B, **i32)
+        ws = lsa.topk_workspace_size(L, B, self.rows, w.k)
+        self.workspace = torch.empty(max(ws, 4), dtype=torch.uint8, device=dev)
+        self.gather_capacity = self.rows if gather_capacity is None else int(gather_capacity)
+        if self.pool is not None:
+            self.gathered = torch.empty(max(self.gather_capacity, 1), w.pool_dim, dtype=torch.int16, device=dev)
+
+    # ------------------------------------------------------------- stages
+    def project(self, stream=None):
+        w, L = self.w, self.w.L
+        layers = []
+        for j in range(2 * L):
+            wdq, wiuq, ww = (self.mem if j < L else self.nat)[j % L]
+            layers.append(dict(h=self.h[j % L], w_dq=wdq, w_iuq=wiuq, w_w=ww, c_out=self.c[j], q_out=self.q[j],
+                               w_out=self.g[j]))
+        lsa.project(layers, B=w.B, d=w.d, r=w.r, n_h=w.n_h, d_h=w.d_h, dtype=w.act_dtype, stream=stream)
+
+    def score_select(self, stream=None):
+        w = self.w
+        layers = [dict(q=self.q[l], w=self.g[l], keys=self.keys[l], key_scale=self.scale[l], mask_out=self.masks[l],
+                       score_out=None if self.scores is None else self.scores[l]) for l in range(w.L)]
+        lsa.score_select(layers, B=w.B, key_offsets=self.key_off, key_offsets_host=self.key_off_h,
+                         mask_word_offsets=self.mwo, mask_word_offsets_host=self.mwo_h, n_h=w.n_h, d_h=w.d_h,
+                         key_dtype=w.key_dtype, threshold=w.threshold, stream=stream)
+
+    def union_compact(self, stream=None):
+        w = self.w
+        lsa.union_compact(self.masks, B=w.B, key_offsets=self.key_off, key_offsets_host=self.key_off_h,
+                          mask_word_offsets=self.mwo, mask_word_offsets_host=self.mwo_h, idx_out=self.idx,
+                          count_out=self.count, union_mask_out=self.union_mask, stream=stream)
+
+    def topk(self, stream=None):
+        w, L = self.w, self.w.L
+        layers = [dict(q=self.q[L + l], w=self.g[L + l], keys=self.keys[l], key_scale=self.scale[l],
+                       topk_idx_out=self.topk_idx[l],
+                       topk_score_out=None if self.topk_score is None else self.topk_score[l]) for l in range(L)]
+        lsa.topk(layers, B=w.B, key_offsets=self.key_off, key_offsets_host=self.key_off_h, idx=self.idx,
+                 count=self.count, n_h=w.n_h, d_h=w.d_h, key_dtype=w.key_dtype, k=w.k,
+                 topk_count_out=self.topk_count, workspace=self.workspace, stream=stream)
+
+    def gather(self, stream=None):
+        if self.pool is None:
+            return
+        w = self.w
+        lsa.gather(self.pool, row_bytes=w.pool_dim * 2, B=w.B, pool_row_offsets=self.key_off,
+                   pool_row_offsets_host=self.key_off_h, idx=self.idx, idx_offsets=self.key_off, count=self.count,
+                   out=self.gathered, out_capacity_rows=self.gather_capacity, stream=stream)
+
+    def run(self, stream=None):
+        self.project(stream)
+        self.score_select(stream)
+        self.union_compact(stream)
+        self.topk(stream)
+        self.gather(stream)
+
+    # ------------------------------------------------------------- readback
+    def masks_bool(self, l):
+        """Unpack layer l's mask words into one bool array per sequence."""
+        words = self.masks[l][: self.words].cpu().numpy().view(np.uint64)
+        return self._unpack(words)
+
+    def union_bool(self):
+        return self._unpack(self.union_mask[: self.words].cpu().numpy().view(np.uint64))
+
+    def _unpack(self, words):
+        out = []
+        bits = np.unpackbits(words.view(np.uint8), bitorder="little")
+        for b in range(self.w.B):
+            w0, w1 = int(self.mwo_h[b]), int(self.mwo_h[b + 1])
+            n = int(self.key_off_h[b + 1] - self.key_off_h[b])
+            seg = bits[w0 * 64: w1 * 64]
+            out.append((seg[:n].astype(bool), seg[n:].astype(bool)))
+        return out

@@ -1,0 +1,147 @@
+"""Host-side C-ABI checks. They need no GPU: every call here is rejected by
+argument validation before anything touches the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lsa.h")
+
+
+@pytest.fixture(scope="module")
+def lsa():
+    from sparse_kv_retrieval_amd import lsa as mod
+    return mod
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(lsa_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_five_calls():
+    fns = declared_functions()
+    for f in ("lsa_project", "lsa_score_select", "lsa_union_compact", "lsa_topk", "lsa_gather",
+              "lsa_topk_workspace_size", "lsa_last_error", "lsa_version"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol(lsa):
+    lib = ctypes.CDLL(lsa.LIB_PATH)
+    for f in declared_functions():
+        assert hasattr(lib, f), f
+    out = subprocess.run(["nm", "-D", "--defined-only", lsa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (lsa_\w+)", out))
+    assert set(declared_functions()) == exported, exported ^ set(declared_functions())
+    assert set(lsa.EXPORTED) == exported
+
+
+def test_version(lsa):
+    assert lsa.version() == 1
+
+
+def _offs(n):
+    ko = np.zeros(len(n) + 1, np.int64)
+    ko[1:] = np.cumsum(n)
+    mw = np.zeros(len(n) + 1, np.int64)
+    mw[1:] = np.cumsum((np.asarray(n) + 63) // 64)
+    return ko, mw
+
+
+FAKE = 1 << 20  # non-null, 16-byte aligned stand-in address (never dereferenced: validation fails first)
+
+
+def _score_layer(**kw):
+    d = dict(q=FAKE, w=FAKE, keys=FAKE, key_scale=None, mask_out=FAKE, score_out=None)
+    d.update(kw)
+    return d
+
+
+def _expect(lsa, status, fn, *a, match=None, **kw):
+    with pytest.raises(lsa.LsaError) as ei:
+        fn(*a, **kw)
+    assert ei.value.status == status, str(ei.value)
+    if match:
+        assert re.search(match, str(ei.value)), str(ei.value)
+
+
+def test_score_select_validation(lsa):
+    ko, mw = _offs([100, 0, 65])
+    base = dict(B=3, key_offsets=FAKE, key_offsets_host=ko, mask_word_offsets=FAKE, mask_word_offsets_host=mw,
+                n_h=64, d_h=128, key_dtype="bf16", threshold=0.5, stream=0)
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.score_select, [_score_layer(q=None)], **base, match="must be set")
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.score_select, [_score_layer()], **{**base, "d_h": 96}, match="d_h")
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.score_select, [_score_layer()], **{**base, "n_h": 65}, match="n_h")
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.score_select, [_score_layer()], **{**base, "key_dtype": 7})
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.score_select, [_score_layer()], **{**base, "threshold": 1.0})
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.score_select, [_score_layer()], **{**base, "threshold": 0.0})
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.score_select, [_score_layer()] * 9, **base, match="L must")
+    bad = ko.copy(); bad[2] = 50
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.score_select, [_score_layer()], **{**base, "key_offsets_host": bad},
+            match="decreasing")
+    badw = mw.copy(); badw[1] += 1; badw[2] += 1; badw[3] += 1
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.score_select, [_score_layer()], **{**base, "mask_word_offsets_host": badw},
+            match="ceil")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.score_select, [_score_layer()], **{**base, "key_dtype": "fp8"},
+            match="key_scale")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.score_select, [_score_layer(key_scale=FAKE)], **base, match="only for fp8")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.score_select, [_score_layer(keys=FAKE + 4)], **base, match="aligned")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.score_select, [_score_layer()], **{**base, "B": 0})
+    assert "B must" in lsa.last_error()
+
+
+def test_project_validation(lsa):
+    lay = dict(h=FAKE, w_dq=FAKE, w_iuq=FAKE, w_w=FAKE, c_out=FAKE + 4096, q_out=FAKE + 8192, w_out=FAKE + 16384)
+    base = dict(B=8, d=4096, r=2048, n_h=64, d_h=128, dtype="bf16", stream=0)
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.project, [{**lay, "h": None}], **base)
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.project, [lay], **{**base, "d": 4001}, match="multiples")
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.project, [lay], **{**base, "B": 129})
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.project, [lay], **{**base, "dtype": "fp8"})
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.project, [{**lay, "q_out": lay["c_out"]}], **base, match="alias")
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.project, [lay], **{**base, "n_h": 3, "d_h": 5})
+
+
+def test_union_topk_gather_validation(lsa):
+    ko, mw = _offs([10, 20])
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.union_compact, [FAKE, None], B=2, key_offsets=FAKE, key_offsets_host=ko,
+            mask_word_offsets=FAKE, mask_word_offsets_host=mw, idx_out=FAKE, count_out=FAKE, stream=0)
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.union_compact, [FAKE], B=2, key_offsets=FAKE, key_offsets_host=ko,
+            mask_word_offsets=FAKE, mask_word_offsets_host=mw, idx_out=None, count_out=FAKE, stream=0)
+    tl = dict(q=FAKE, w=FAKE, keys=FAKE, key_scale=None, topk_idx_out=FAKE, topk_score_out=None)
+    tb = dict(B=2, key_offsets=FAKE, key_offsets_host=ko, idx=FAKE, count=FAKE, n_h=64, d_h=128, key_dtype="bf16",
+              k=2048, topk_count_out=FAKE, stream=0)
+
+    class _WS:  # a workspace tensor stand-in that is too small
+        def numel(self):
+            return 4
+
+        def element_size(self):
+            return 1
+
+        def data_ptr(self):
+            return FAKE
+    _expect(lsa, lsa.ERR_WORKSPACE, lsa.topk, [tl], **tb, workspace=_WS(), match="workspace")
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.topk, [tl], **{**tb, "k": 0}, workspace=_WS())
+    assert lsa.topk_workspace_size(3, 2, 30, 2048) == 3 * 30 * 4
+    gb = dict(row_bytes=1024, B=2, pool_row_offsets=FAKE, pool_row_offsets_host=ko, idx=FAKE, idx_offsets=FAKE,
+              count=FAKE, out=FAKE, out_capacity_rows=30, stream=0)
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.gather, FAKE, **{**gb, "row_bytes": 1000}, match="multiple of 16")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.gather, None, **gb)
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.gather, FAKE + 8, **gb, match="aligned")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.gather, FAKE, **{**gb, "out_capacity_rows": -1})
+
+
+def test_binding_has_no_oracle_import():
+    """The product path (binding, pipeline, library sources) never refers to the oracle."""
+    pkg = os.path.join(ROOT, "sparse_kv_retrieval_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", txt, re.M), f
+                assert "lsa_oracle" not in txt, f

@@ -1,0 +1,139 @@
+"""HIP path vs the CPU oracle, through the C-ABI (marked gpu).
+
+Small cases span several tiles, ragged tails, empty and one-entry sequences,
+k above and below the subset size, and every key dtype and head shape.
+The full-size cases run the five workloads at their real sizes, with the
+launch configuration that bench.py times. There the oracle checks sampled
+outputs, and properties that hold at any size cover the rest.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from sparse_kv_retrieval_amd import synth
+from tests import parity as P
+
+W = synth.WORKLOADS
+
+SMALL = {
+    "tiny_f32": W["tiny_f32"],
+    "tiny_f32_k_over": dataclasses.replace(W["tiny_f32"], k=4096, name="tiny_k_over"),
+    "single_bf16_tail": synth.scaled(W["single_layer_500k"], N=(4099,), k=256),
+    "three_layer_mixed": synth.scaled(W["three_layer_b8"], N=(3000, 0, 1, 64, 65, 700), k=128),
+    "fp8_two_seq": synth.scaled(W["fp8_1m"], N=(5000, 63), k=512),
+    "ragged_small": synth.scaled(W["ragged_b32"], N=(2000, 1500, 127, 0, 129), k=100),
+    "bf16_16heads_d64": dataclasses.replace(
+        synth.scaled(W["three_layer_b8"], N=(2100, 333), k=64), n_h=16, d_h=64, d=512, r=256, name="h16d64"),
+    "fp8_8heads_d32": dataclasses.replace(
+        synth.scaled(W["fp8_1m"], N=(1000,), k=32), n_h=8, d_h=32, d=256, r=128, L=2, name="h8d32"),
+    "f32_d128_48heads": dataclasses.replace(
+        synth.scaled(W["three_layer_b8"], N=(777, 64), k=50), key_dtype="f32", act_dtype="f32", n_h=48, d=256,
+        r=128, L=2, name="f32h48"),
+    "single_k_ge_count": synth.scaled(W["three_layer_b8"], N=(600, 200), k=4096),
+}
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    return torch
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", list(SMALL))
+def test_small_parity(case, torch_cuda):
+    from sparse_kv_retrieval_amd.pipeline import Pipeline
+    w = SMALL[case]
+    P.say(f"[parity] case={case} B={w.B} L={w.L} N={w.N} dtype={w.key_dtype} n_h={w.n_h} d_h={w.d_h} k={w.k}")
+    inp = synth.make(w)
+    p = Pipeline(inp, "cuda", with_scores=True)
+    p.run()
+    torch_cuda.cuda.synchronize()
+    st, counts = P.full_check(p, inp)
+    P.say(f"[parity] case={case} ok counts={counts.tolist()} band={st['band']} "
+          f"band_mismatch={st['mismatch_in_band']} max_dI={st['max_dI']:.2e}")
+
+
+@pytest.mark.gpu
+def test_repeat_is_deterministic(torch_cuda):
+    """Two runs give bit-identical masks, lists, top-k and gather."""
+    from sparse_kv_retrieval_amd.pipeline import Pipeline
+    w = SMALL["three_layer_mixed"]
+    P.say("[parity] determinism")
+    inp = synth.make(w)
+    p = Pipeline(inp, "cuda", with_scores=True)
+    snaps = []
+    for _ in range(2):
+        p.run()
+        torch_cuda.cuda.synchronize()
+        snaps.append([t.clone() for t in (p.masks + p.scores + [p.idx[: p.rows], p.count, p.topk_count]
+                                          + p.topk_idx + p.topk_score + [p.gathered])])
+    for a, b in zip(*snaps):
+        assert torch_cuda.equal(a, b)
+
+
+def _full_sampled(name, torch_cuda, sample=2048):
+    from oracle import lsa_oracle as O
+    from sparse_kv_retrieval_amd.pipeline import Pipeline
+    w = W[name]
+    P.say(f"[full] case={name}: generating")
+    inp = synth.make(w)
+    P.say(f"[full] case={name}: rows={int(inp.key_offsets[-1])} running")
+    p = Pipeline(inp, "cuda", with_scores=True)
+    p.run()
+    torch_cuda.cuda.synchronize()
+    P.say(f"[full] case={name}: checking")
+    rng = np.random.default_rng(0)
+    masks = [p.masks_bool(l) for l in range(w.L)]
+    # sampled entries of every (sequence, layer) against the oracle, one by one
+    checked = 0
+    for b in range(w.B):
+        s0, s1 = int(inp.key_offsets[b]), int(inp.key_offsets[b + 1])
+        n = s1 - s0
+        if n == 0:
+            continue
+        ent = np.unique(np.concatenate([rng.choice(n, min(n, sample), replace=False), np.arange(min(n, 64)),
+                                        np.arange(max(0, n - 64), n)]))
+        for l in range(w.L):
+            mw = inp.mem_w[l]
+            H = O.decode_act(inp.h[l][b:b + 1], w.act_dtype)
+            _, q, g = O.project(H, O.decode_act(mw.w_dq, w.act_dtype), O.decode_act(mw.w_iuq, w.act_dtype),
+                                O.decode_act(mw.w_w, w.act_dtype), w.n_h, w.d_h)
+            sc = None if inp.key_scale[l] is None else inp.key_scale[l][s0 + ent]
+            K = O.decode_keys(inp.keys[l][s0 + ent], w.key_dtype, sc)
+            x = O.logits(q[0], g[0], K)
+            band = np.abs(x) <= P.BAND
+            m, tail = masks[l][b]
+            assert not tail.any()
+            assert np.array_equal(m[ent][~band], O.select(x, w.threshold)[~band]), f"mask b={b} l={l}"
+            I = p.scores[l][s0 + ent].cpu().numpy() if len(ent) else np.zeros(0)
+            assert np.abs(I - O.sigmoid(x)).max() <= P.SCORE_TOL
+            checked += len(ent)
+    # compaction is integer work: bit-exact against the GPU's own masks, all sequences
+    counts, lists = P.gpu_union_lists(p, inp)
+    for b in range(w.B):
+        U = O.union([masks[l][b][0] for l in range(w.L)])
+        assert np.array_equal(lists[b], O.compact(U))
+    # top-k against the oracle for the first and last sequence (full subset re-scored)
+    sel = sorted({0, w.B - 1})
+    ref = {}
+    for b in sel:
+        s0, s1 = int(inp.key_offsets[b]), int(inp.key_offsets[b + 1])
+        ref[b] = {"qn": {}, "wn": {}}
+        for l in range(w.L):
+            nw = inp.nat_w[l]
+            H = O.decode_act(inp.h[l][b:b + 1], w.act_dtype)
+            _, qn, wn = O.project(H, O.decode_act(nw.w_dq, w.act_dtype), O.decode_act(nw.w_iuq, w.act_dtype),
+                                  O.decode_act(nw.w_w, w.act_dtype), w.n_h, w.d_h)
+            ref[b]["qn"][l], ref[b]["wn"][l] = qn[0], wn[0]
+    P.check_topk(p, inp, ref, lists)
+    P.check_gather(p, inp, lists, sample=512, rng=rng)
+    frac = counts.sum() / max(1, int(inp.key_offsets[-1]))
+    P.say(f"[full] case={name}: ok, {checked} sampled entries, union fraction {frac:.4f}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", ["single_layer_500k", "three_layer_b8", "fp8_1m", "ragged_b32"])
+def test_full_size_sampled(name, torch_cuda):
+    _full_sampled(name, torch_cuda)
