@@ -67,6 +67,16 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t four) {
   return r;
 }
 
+// Values the whole wave agrees on, pinned to scalar registers. Loads from memory
+// are vector loads, and without this the compiler keeps their results (and
+// everything derived from them) in VGPRs.
+__device__ __forceinline__ int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // ----------------------------------------------------------------- search
 // Largest b in [0, n) with off[b] <= x, given off[0] <= x < off[n] and off
 // non-decreasing. It also skips over empty sequences (off[b] == off[b+1]).

@@ -83,7 +83,7 @@ struct ProjArgs {
   int32_t B, d, r, n_h, d_h;
 };
 
-hipError_t launch_score_select(const ScoreArgs& a, int key_kind, int d_h, int grid, hipStream_t st);
+hipError_t launch_score_select(const ScoreArgs& a, int key_kind, int d_h, int pairs, hipStream_t st);
 hipError_t launch_topk_score(const TopkScoreArgs& a, int key_kind, int d_h, int grid, hipStream_t st);
 hipError_t launch_topk_select(const TopkSelectArgs& a, int L, hipStream_t st);
 hipError_t launch_union_compact(const UnionArgs& a, int B, int64_t max_words, hipStream_t st);

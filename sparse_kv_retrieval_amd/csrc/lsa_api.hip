@@ -157,9 +157,9 @@ lsa_status lsa_score_select(const lsa_score_layer* layers, int32_t L, int32_t B,
   a.total_words = a.words_per_layer * L;
   a.B = B; a.n_h = n_h; a.thr = (float)t;
   if (a.total_words == 0) return LSA_OK;
-  const int64_t waves = std::min<int64_t>(a.total_words, (int64_t)cu_count() * env_int("LSA_SCORE_WAVES_PER_CU", 8));
-  const int grid = (int)((waves + 3) / 4);
-  const hipError_t e = launch_score_select(a, kind, d_h, grid, stream);
+  // one block per pair of waves; each pair takes a contiguous run of mask words
+  const int64_t pairs = std::min<int64_t>(a.total_words, (int64_t)cu_count() * env_int("LSA_SCORE_PAIRS_PER_CU", 4));
+  const hipError_t e = launch_score_select(a, kind, d_h, (int)pairs, stream);
   return e == hipSuccess ? LSA_OK : hip_fail("lsa_score_select launch", e);
 }
 

@@ -14,53 +14,268 @@
 
 namespace lsa {
 
-template <int KT, int DH, int NHB>
-__global__ __launch_bounds__(256) void score_select_kernel(const ScoreArgs a) {
-  using S_t = Scorer<KT, DH, NHB>;
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+template <int STEP>
+__device__ __forceinline__ void vm_wait_pending(int pending) {
+  // Vector-memory loads complete in issue order, so "at most STEP*pending
+  // outstanding" means every tile older than the last `pending` tiles has
+  // landed in LDS.
+  switch (pending) {
+    case 0: vm_wait<0>(); break;
+    case 1: vm_wait<STEP>(); break;
+    case 2: vm_wait<2 * STEP>(); break;
+    default: vm_wait<3 * STEP>(); break;
+  }
+  asm volatile("" ::: "memory");
+}
+
+#define LSA_AS3(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Block barrier for LDS traffic only. __syncthreads() also fences global memory,
+// so it waits for every outstanding vector load (vmcnt(0)), and that would drain
+// the key DMAs still in flight. Here the LDS operations of this wave
+// (lgkmcnt) complete first, and the barrier is then the bare s_barrier. The
+// DMAs that a tile depends on are waited for explicitly with vm_wait_pending.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima (no wait)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Sequence table lookups. For up to SEQ_TAB entries the key and word offsets
+// are copied to LDS once per block. A lookup is then an LDS read, which never
+// waits on the vector-memory counter that tracks the key DMAs.
+constexpr int SEQ_TAB = 256;
+
+struct SeqTab {
+  const int64_t* koff;  // LDS or global
+  const int64_t* mwo;
+};
+
+// Wave-uniform cursor over the mask words of one wave: (layer, sequence, word).
+// It advances one word at a time, so there is no division or search in the
+// steady state. A search runs only when the cursor is placed.
+struct WordCursor {
+  int l, b;
+  int64_t word;     // word index in the mask layout
+  int64_t seq_hi;   // first word after sequence b
+  int64_t e0;       // entry index (within sequence b) of the word's first bit
+  int64_t row0, nb; // sequence b's first key row and entry count
+
+  __device__ __forceinline__ void load_seq(const SeqTab& t) {
+    const int64_t lo = uni(t.mwo[b]);
+    seq_hi = uni(t.mwo[b + 1]);
+    row0 = uni(t.koff[b]);
+    nb = uni(t.koff[b + 1]) - row0;
+    e0 = (word - lo) * 64;
+  }
+  __device__ __forceinline__ void place(const ScoreArgs& a, const SeqTab& t, int64_t gw) {
+    l = uni((int32_t)(gw / a.words_per_layer));
+    word = uni(a.word_base + (gw - (int64_t)l * a.words_per_layer));
+    b = uni(upper_seq(t.mwo, a.B, word));
+    load_seq(t);
+  }
+  __device__ __forceinline__ void next(const ScoreArgs& a, const SeqTab& t) {
+    ++word;
+    e0 += 64;
+    if (word == seq_hi) {
+      if (word == a.word_base + a.words_per_layer) {
+        ++l;
+        word = a.word_base;
+        b = 0;
+      } else {
+        ++b;
+      }
+      while (uni(t.mwo[b + 1]) == uni(t.mwo[b])) ++b;  // skip empty sequences
+      load_seq(t);
+    }
+  }
+};
+
+// Score + select: keys streamed HBM -> registers -> LDS -> MFMA, two waves per tile.
+//
+// A block is one pair of waves and owns a contiguous run of mask words. Each
+// word is two 32-entry tiles. Wave h loads half of every tile with coalesced
+// 16-byte vector loads (each load instruction covers 1 KiB of contiguous key
+// rows) and keeps D tiles in flight in registers. When a tile's turn comes, it
+// writes the tile into one of two LDS stages. fp8 keys are widened to bf16 on
+// the way (exact), so both waves then run the bf16 MFMA on the same
+// operands. In LDS, 16-byte chunk c of row r sits at position c ^ (r % CPR), so
+// the operand reads (lane n reads row n) are free of bank conflicts.
+//
+// Wave h scores heads [32h, 32h+32). Wave 1 passes its gate/ReLU partial sums
+// to wave 0 through LDS, and wave 0 finishes tile j-1 (threshold, ballot,
+// mask word, optional sigmoid) in iteration j. There is one barrier per tile.
+// After it, tile j is complete in LDS, the previous partial is visible, and
+// the stage written next iteration is no longer being read.
+template <int KT, int DH>
+struct TileIO {
+  static constexpr int GESZ = KT == KEY_F32 ? 4 : (KT == KEY_BF16 ? 2 : 1);  // stored element
+  static constexpr int LESZ = KT == KEY_F32 ? 4 : 2;                         // element in LDS
+  static constexpr int GRB = DH * GESZ;      // stored row bytes
+  static constexpr int LRB = DH * LESZ;      // LDS row bytes
+  static constexpr int GSUB = 32 * GRB;      // stored tile bytes
+  static constexpr int LSUB = 32 * LRB;      // LDS tile bytes
+  static constexpr int NLI = GSUB / 1024;    // 1 KiB load instructions per tile (>= 1)
+  static constexpr int NLW = NLI >= 2 ? NLI / 2 : 1;  // per wave
+  static constexpr int GCPR = GRB / 16;      // stored 16-byte chunks per row
+  static constexpr int LCPR = LRB / 16;      // LDS 16-byte chunks per row
+};
+
+template <int KT, int DH, int D>
+__global__ __launch_bounds__(128) void score_select_kernel(const ScoreArgs a) {
+  using IO = TileIO<KT, DH>;
+  using S_t = Scorer<KT == KEY_F32 ? KEY_F32 : KEY_BF16, DH, 1>;
+  static_assert(S_t::ROW_BYTES == IO::LRB, "LDS row layout");
+  __shared__ __attribute__((aligned(16))) char stage[2][IO::LSUB];
+  __shared__ float xpart[2][32];
+  __shared__ int64_t tab[2][SEQ_TAB + 1];
+
   const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
-  const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
-  const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave_in_block;
-  int64_t gw = wid * a.total_words / nw;
-  const int64_t gend = (wid + 1) * a.total_words / nw;
+  const int h = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // which half of the heads
+  SeqTab t{a.key_off, a.mwo};
+  if (a.B < SEQ_TAB) {
+    for (int i = threadIdx.x; i <= a.B; i += 128) {
+      tab[0][i] = a.key_off[i];
+      tab[1][i] = a.mwo[i];
+    }
+    __syncthreads();
+    t.koff = tab[0];
+    t.mwo = tab[1];
+  }
+  const int64_t np = gridDim.x;
+  const int64_t gbeg = (int64_t)blockIdx.x * a.total_words / np;
+  const int64_t gend = ((int64_t)blockIdx.x + 1) * a.total_words / np;
+  const int J = (int)(2 * (gend - gbeg));  // tiles of this pair
+  if (J == 0) return;
+
+  // This wave's load instructions: [i0, i0 + NLW), or none for 1 KiB tiles on wave 1.
+  const int i0 = IO::NLI >= 2 ? h * IO::NLW : 0;
+  const bool loads = IO::NLI >= 2 || h == 0;
+  // per instruction: row within the tile, and the stored chunk of that row
+  int lrow[IO::NLW], lchunk[IO::NLW];
+#pragma unroll
+  for (int i = 0; i < IO::NLW; ++i) {
+    const int p = (i0 + i) * 1024 + lane * 16;
+    lrow[i] = p / IO::GRB;
+    lchunk[i] = (p % IO::GRB) / 16;
+  }
+
+  u32x4 R[D][IO::NLW];
+  float SC[D];
+  WordCursor ic, cc;
+  ic.place(a, t, gbeg);
+  cc = ic;
 
   S_t S;
   int cur_l = -1, cur_b = -1;
-  int64_t seq_lo = 0, seq_hi = -1, row0 = 0, nb = 0;
-  const char* keys = nullptr;
-  for (; gw < gend; ++gw) {
-    const int l = (int)(gw / a.words_per_layer);
-    const int64_t word = a.word_base + (gw - (int64_t)l * a.words_per_layer);
-    if (l != cur_l || word < seq_lo || word >= seq_hi) {
-      const int b = upper_seq(a.mwo, a.B, word);
-      seq_lo = a.mwo[b];
-      seq_hi = a.mwo[b + 1];
-      row0 = a.key_off[b];
-      nb = a.key_off[b + 1] - row0;
-      keys = (const char*)a.keys[l];
-      if (l != cur_l || b != cur_b) {
-        S.load_query(a.q[l], a.w[l], b, a.n_h);
-        cur_l = l;
-        cur_b = b;
-      }
-    }
-    const int64_t s0 = (word - seq_lo) * 64;
-    uint32_t bits[2];
+  float pprev = 0.0f;
+  bool vprev = false;
+  int64_t rprev = 0, wprev = 0;
+  int lprev = 0;
+  uint32_t bits0 = 0;
+
+#define LSA_LOAD_TILE(SLOT, JJ)                                                                     \
+  do {                                                                                              \
+    const int64_t e_ = ic.e0 + ((JJ) & 1) * 32;                                                     \
+    const int64_t last_ = ic.row0 + ic.nb - 1;                                                      \
+    const char* kb_ = (const char*)a.keys[ic.l];                                                    \
+    if (loads) {                                                                                    \
+      _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i) {                                         \
+        const int64_t row_ = min(ic.row0 + e_ + lrow[i], last_);                                    \
+        R[SLOT][i] = __builtin_nontemporal_load((const u32x4*)(kb_ + row_ * IO::GRB + lchunk[i] * 16)); \
+      }                                                                                             \
+    }                                                                                               \
+    if constexpr (KT == KEY_FP8) SC[SLOT] = a.scale[ic.l][min(ic.row0 + e_ + n, last_)];            \
+    if ((JJ) & 1) ic.next(a, t);                                                                    \
+  } while (0)
+
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int64_t s = s0 + sub * 32 + n;
-      const bool valid = s < nb;
-      const int64_t row = row0 + (valid ? s : 0);
-      S.load_keys(keys + row * S_t::ROW_BYTES + g * S_t::HALF_BYTES, valid);
-      f32x16 acc[NHB];
+  for (int s = 0; s < D; ++s)
+    if (s < J) LSA_LOAD_TILE(s, s);
+
+  for (int j0 = 0; j0 < J; j0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      const int j = j0 + s;
+      if (j >= J) break;
+      char* st = &stage[j & 1][0];
+      // write this wave's half of tile j into LDS (waits for its loads)
+      if (loads) {
+#pragma unroll
+        for (int i = 0; i < IO::NLW; ++i) {
+          const int r = lrow[i];
+          char* rowp = st + r * IO::LRB;
+          if constexpr (KT == KEY_FP8) {
+            const u32x4 v = R[s][i];
+            const u32x2 b0 = e4m3x4_to_bf16x4(v[0]), b1 = e4m3x4_to_bf16x4(v[1]);
+            const u32x2 b2 = e4m3x4_to_bf16x4(v[2]), b3 = e4m3x4_to_bf16x4(v[3]);
+            const int c0 = 2 * lchunk[i], c1 = c0 + 1;
+            *(u32x4*)(rowp + ((c0 ^ (r % IO::LCPR)) * 16)) = u32x4{b0[0], b0[1], b1[0], b1[1]};
+            *(u32x4*)(rowp + ((c1 ^ (r % IO::LCPR)) * 16)) = u32x4{b2[0], b2[1], b3[0], b3[1]};
+          } else {
+            *(u32x4*)(rowp + ((lchunk[i] ^ (r % IO::LCPR)) * 16)) = R[s][i];
+          }
+        }
+      }
+      float scale = 1.0f;
+      if constexpr (KT == KEY_FP8) scale = SC[s];
+      // refill this slot with tile j + D
+      if (j + D < J) LSA_LOAD_TILE(s, j + D);
+      lds_barrier();  // tile j complete in LDS; wave 1's partial of tile j-1 visible
+      S.read_keys_lds(st);
+
+      if (h == 0 && j > 0) {
+        // finish tile j-1: both halves of the head sum, threshold, ballot, stores
+        const float x = pprev + xpart[(j - 1) & 1][n];
+        const uint32_t bits = (uint32_t)__ballot(vprev && x >= a.thr);
+        float* so = a.score[lprev];
+        if (so != nullptr && g == 0 && vprev) so[rprev] = 1.0f / (1.0f + __expf(-x));
+        if ((j - 1) & 1) {
+          if (lane == 0) a.mask[lprev][wprev] = (uint64_t)bits0 | ((uint64_t)bits << 32);
+        } else {
+          bits0 = bits;
+        }
+      }
+      if (cc.l != cur_l || cc.b != cur_b) {
+        S.load_query(a.q[cc.l], a.w[cc.l], cc.b, a.n_h, 32 * h);
+        cur_l = cc.l;
+        cur_b = cc.b;
+      }
+      f32x16 acc[1];
       S.mma(acc);
-      float x = S.logit(acc);
-      if constexpr (KT == KEY_FP8) x *= valid ? a.scale[l][row] : 0.0f;
-      bits[sub] = (uint32_t)__ballot(valid && x >= a.thr);
-      float* so = a.score[l];
-      if (so != nullptr && g == 0 && valid) so[row] = 1.0f / (1.0f + __expf(-x));
+      float p = S.partial(acc);
+      p += __shfl_xor(p, 32);
+      if constexpr (KT == KEY_FP8) p *= scale;
+      const int64_t se = cc.e0 + (j & 1) * 32 + n;
+      if (h == 1) {
+        if (g == 0) xpart[j & 1][n] = p;
+      } else {
+        pprev = p;
+        vprev = se < cc.nb;
+        rprev = cc.row0 + se;
+        wprev = cc.word;
+        lprev = cc.l;
+      }
+      if (j & 1) cc.next(a, t);
     }
-    if (lane == 0) a.mask[l][word] = (uint64_t)bits[0] | ((uint64_t)bits[1] << 32);
+  }
+#undef LSA_LOAD_TILE
+  lds_barrier();
+  if (h == 0) {
+    const int j = J;
+    const float x = pprev + xpart[(j - 1) & 1][n];
+    const uint32_t bits = (uint32_t)__ballot(vprev && x >= a.thr);
+    float* so = a.score[lprev];
+    if (so != nullptr && g == 0 && vprev) so[rprev] = 1.0f / (1.0f + __expf(-x));
+    if (lane == 0) a.mask[lprev][wprev] = (uint64_t)bits0 | ((uint64_t)bits << 32);  // J is even: tile J-1 is odd
   }
 }
 
@@ -109,8 +324,10 @@ __global__ __launch_bounds__(256) void topk_score_kernel(const TopkScoreArgs a) 
 
 // ------------------------------------------------------------------ launch
 template <int KT, int DH, int NHB>
-static hipError_t launch_score_t(const ScoreArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((score_select_kernel<KT, DH, NHB>), dim3(grid), dim3(256), 0, st, a);
+static hipError_t launch_score_t(const ScoreArgs& a, int pairs, hipStream_t st) {
+  // one block = one pair of waves; D tiles in flight per wave in registers
+  constexpr int D = TileIO<KT, DH>::GSUB > 8192 ? 2 : 4;
+  hipLaunchKernelGGL((score_select_kernel<KT, DH, D>), dim3(pairs), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 template <int KT, int DH, int NHB>
@@ -136,9 +353,9 @@ static hipError_t launch_tscore_t(const TopkScoreArgs& a, int grid, hipStream_t 
     }                                                                               \
   } while (0)
 
-hipError_t launch_score_select(const ScoreArgs& a, int key_kind, int d_h, int grid, hipStream_t st) {
+hipError_t launch_score_select(const ScoreArgs& a, int key_kind, int d_h, int pairs, hipStream_t st) {
   const int nhb = a.n_h > 32 ? 2 : 1;
-  LSA_DISPATCH(launch_score_t, key_kind, d_h, nhb, a, grid, st);
+  LSA_DISPATCH(launch_score_t, key_kind, d_h, nhb, a, pairs, st);
 }
 
 hipError_t launch_topk_score(const TopkScoreArgs& a, int key_kind, int d_h, int grid, hipStream_t st) {

@@ -45,13 +45,13 @@ struct Scorer {
   // key fragment of the current 32-entry tile
   u32x4 kraw[NLD];
 
-  // Load q[b] and w[b] (fp32) of one (sequence, layer).
+  // Load q[b] and w[b] (fp32) of one (sequence, layer), heads head0 .. head0 + 32*NHB - 1.
   __device__ __forceinline__ void load_query(const float* __restrict__ q, const float* __restrict__ w,
-                                             int b, int n_h) {
+                                             int b, int n_h, int head0 = 0) {
     const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
 #pragma unroll
     for (int mb = 0; mb < NHB; ++mb) {
-      const int head = mb * 32 + n;
+      const int head = head0 + mb * 32 + n;
       const bool ok = head < n_h;
       const float* qrow = q + ((int64_t)b * n_h + (ok ? head : 0)) * DH + g * HALF;
       if constexpr (SPLIT) {
@@ -74,7 +74,7 @@ struct Scorer {
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int h = mb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+        const int h = head0 + mb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
         gate[mb][i] = h < n_h ? w[(int64_t)b * n_h + h] : 0.0f;
       }
     }
@@ -85,6 +85,19 @@ struct Scorer {
 #pragma unroll
     for (int i = 0; i < NLD; ++i)
       kraw[i] = valid ? __builtin_nontemporal_load((const u32x4*)p + i) : u32x4{0, 0, 0, 0};
+  }
+
+  // Read this lane's half-row of a 32-row tile staged in LDS with the chunk
+  // swizzle used by the DMA (16-byte chunk c of row r stored at c ^ (r % CPR)).
+  static constexpr int CPR = ROW_BYTES / 16;
+  __device__ __forceinline__ void read_keys_lds(const char* tile) {
+    const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
+    const char* row = tile + n * ROW_BYTES;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int c = g * (CPR / 2) + i;
+      kraw[i] = *(const u32x4*)(row + ((c ^ (n % CPR)) * 16));
+    }
   }
 
   __device__ __forceinline__ void mma(f32x16 (&acc)[NHB]) const {
@@ -127,13 +140,27 @@ struct Scorer {
 
   // Gate, ReLU and head sum. Lanes l and l^32 hold complementary heads of the
   // same entry. After one swap both lanes have the full sum. Addition is
-  // commutative, so both lanes hold the identical value.
+  // commutative, so both lanes hold the identical value. The ReLU is
+  // max(int(x), 0) on the float's bits: exact for IEEE floats (every negative
+  // value, -0 included, becomes +0) and free of NaN canonicalisation.
+  // This lane's share of the head sum (its 16*NHB heads), before the lane swap.
+  __device__ __forceinline__ float partial(const f32x16 (&acc)[NHB]) const {
+    float part = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < NHB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        part = fmaf(gate[mb][i], __int_as_float(max(__float_as_int(acc[mb][i]), 0)), part);
+    return part;
+  }
+
   __device__ __forceinline__ float logit(const f32x16 (&acc)[NHB]) const {
     float part = 0.0f;
 #pragma unroll
     for (int mb = 0; mb < NHB; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) part = fmaf(gate[mb][i], fmaxf(acc[mb][i], 0.0f), part);
+      for (int i = 0; i < 16; ++i)
+        part = fmaf(gate[mb][i], __int_as_float(max(__float_as_int(acc[mb][i]), 0)), part);
     return part + __shfl_xor(part, 32);
   }
 };
