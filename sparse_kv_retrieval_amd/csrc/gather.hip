@@ -3,18 +3,31 @@
 // GPU memory). This version copies HBM to HBM.
 //
 // Each block computes, in LDS, where every sequence's rows land: a prefix sum
-// of min(count, capacity) in explicit mode, or of count in packed mode. The
-// output rows are then numbered 0..total-1 and the waves stride over them.
-// One wave copies one row with 16-byte non-temporal loads and stores, so a
-// 1 KiB latent row is a single fully coalesced wave access.
+// of min(count, capacity) in explicit mode, or of count in packed mode. For up
+// to GA_TAB sequences it also keeps the per-sequence pool, list and output
+// offsets in LDS. The output rows are numbered 0..total-1, and each wave moves
+// GA_ROWS consecutive ones per iteration. Lanes 0..GA_ROWS-1 resolve one row
+// each (sequence, source row, destination row) and broadcast it, so a row costs
+// one dependent global load (its list entry) before the copy. The copy itself
+// issues all the rows' 16-byte non-temporal loads before their stores, so each
+// 1 KiB latent row is one fully coalesced wave access and GA_ROWS KiB per wave
+// are in flight.
 #include "kernels.hpp"
 
 namespace lsa {
 
 static constexpr int GA_THREADS = 256;
+static constexpr int GA_ROWS = 8;    // rows per wave per iteration
+static constexpr int GA_TAB = 1024;  // sequences whose offsets are cached in LDS
 
+// Dynamic LDS: pre[B+1], then (for B <= GA_TAB) t_pool[B], t_idx[B], t_out[B], all int64.
 __global__ __launch_bounds__(GA_THREADS) void gather_kernel(const GatherArgs a) {
-  __shared__ int64_t pre[LSA_TOPK_MAX_B + 1];
+  extern __shared__ int64_t dyn[];
+  const bool cached = a.B <= GA_TAB;
+  int64_t* pre = dyn;
+  int64_t* t_pool = dyn + a.B + 1;
+  int64_t* t_idx = t_pool + a.B;
+  int64_t* t_out = t_idx + a.B;
   const int tid = threadIdx.x;
   {
     const int per = (a.B + GA_THREADS - 1) / GA_THREADS;
@@ -36,27 +49,61 @@ __global__ __launch_bounds__(GA_THREADS) void gather_kernel(const GatherArgs a) 
       run += rows_of(b);
     }
     if (tid == 0) pre[a.B] = tot;
+    if (cached) {
+      for (int b = tid; b < a.B; b += GA_THREADS) {
+        t_pool[b] = a.pool_off[b];
+        t_idx[b] = a.idx_off[b];
+        t_out[b] = a.out_off ? a.out_off[b] : 0;
+      }
+    }
     __syncthreads();
   }
   const int64_t total = pre[a.B];
   const int lane = tid & 63;
   const int wave_in_block = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t nw = (int64_t)gridDim.x * (GA_THREADS / 64);
-  for (int64_t r = (int64_t)blockIdx.x * (GA_THREADS / 64) + wave_in_block; r < total; r += nw) {
-    const int b = upper_seq(pre, a.B, r);
-    const int64_t i = r - pre[b];
-    const int64_t dst_row = a.out_off ? a.out_off[b] + i : r;
-    if (dst_row >= a.out_capacity) continue;
-    const int64_t src_row = a.pool_off[b] + a.idx[a.idx_off[b] + i];
-    const u32x4* src = (const u32x4*)(a.pool + src_row * a.row_bytes);
-    u32x4* dst = (u32x4*)(a.out + dst_row * a.row_bytes);
-    const int64_t n16 = a.row_bytes >> 4;
-    for (int64_t j = lane; j < n16; j += 64) __builtin_nontemporal_store(__builtin_nontemporal_load(src + j), dst + j);
+  const int n16 = (int)(a.row_bytes >> 4);
+  for (int64_t r0 = ((int64_t)blockIdx.x * (GA_THREADS / 64) + wave_in_block) * GA_ROWS; r0 < total;
+       r0 += nw * GA_ROWS) {
+    // lane u < GA_ROWS resolves output row r0 + u
+    int64_t src_row = 0, dst_row = 0;
+    int ok = 0;
+    if (lane < GA_ROWS) {
+      const int64_t r = r0 + lane;
+      if (r < total) {
+        const int b = upper_seq(pre, a.B, r);
+        const int64_t i = r - pre[b];
+        const int64_t po = cached ? t_pool[b] : a.pool_off[b];
+        const int64_t io = cached ? t_idx[b] : a.idx_off[b];
+        dst_row = a.out_off ? (cached ? t_out[b] : a.out_off[b]) + i : r;
+        ok = dst_row < a.out_capacity;
+        src_row = po + a.idx[io + i];
+      }
+    }
+    const char* src[GA_ROWS];
+    char* dst[GA_ROWS];
+    bool okr[GA_ROWS];
+#pragma unroll
+    for (int u = 0; u < GA_ROWS; ++u) {
+      okr[u] = __shfl(ok, u) != 0;
+      src[u] = a.pool + (int64_t)__shfl(src_row, u) * a.row_bytes;
+      dst[u] = a.out + (int64_t)__shfl(dst_row, u) * a.row_bytes;
+    }
+    for (int j = lane; j < n16; j += 64) {
+      u32x4 v[GA_ROWS];
+#pragma unroll
+      for (int u = 0; u < GA_ROWS; ++u)
+        if (okr[u]) v[u] = __builtin_nontemporal_load((const u32x4*)src[u] + j);
+#pragma unroll
+      for (int u = 0; u < GA_ROWS; ++u)
+        if (okr[u]) __builtin_nontemporal_store(v[u], (u32x4*)dst[u] + j);
+    }
   }
 }
 
 hipError_t launch_gather(const GatherArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(GA_THREADS), 0, st, a);
+  const size_t lds = sizeof(int64_t) * ((size_t)a.B + 1 + (a.B <= GA_TAB ? 3 * (size_t)a.B : 0));
+  hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(GA_THREADS), lds, st, a);
   return hipGetLastError();
 }
 

@@ -232,8 +232,8 @@ lsa_status lsa_topk(const lsa_topk_layer* layers, int32_t L, int32_t B, const in
   if (rows > 0) {
     int64_t tiles = 0;
     for (int32_t b = 0; b < B; ++b) tiles += (key_offsets_host[b + 1] - key_offsets_host[b] + 31) / 32;
-    const int64_t waves = std::max<int64_t>(1, std::min<int64_t>(tiles * L, (int64_t)cu_count() * 8));
-    if ((e = launch_topk_score(sa, kind, d_h, (int)((waves + 3) / 4), stream)) != hipSuccess)
+    const int64_t pairs = std::max<int64_t>(1, std::min<int64_t>(tiles * L, (int64_t)cu_count() * 4));
+    if ((e = launch_topk_score(sa, kind, d_h, (int)pairs, stream)) != hipSuccess)
       return hip_fail("lsa_topk score launch", e);
   }
   if ((e = launch_topk_select(ta, L, stream)) != hipSuccess) return hip_fail("lsa_topk select launch", e);
@@ -260,7 +260,7 @@ lsa_status lsa_gather(const void* pool, int64_t row_bytes, int32_t B, const int6
   GatherArgs a{};
   a.pool = (const char*)pool; a.pool_off = pool_row_offsets; a.idx = idx; a.idx_off = idx_offsets; a.count = count;
   a.out = (char*)out; a.out_off = out_row_offsets; a.out_capacity = out_capacity_rows; a.row_bytes = row_bytes; a.B = B;
-  const int64_t waves = std::min<int64_t>(bound, (int64_t)cu_count() * 16);
+  const int64_t waves = std::min<int64_t>((bound + 7) / 8, (int64_t)cu_count() * 16);
   const hipError_t e = launch_gather(a, (int)((waves + 3) / 4), stream);
   return e == hipSuccess ? LSA_OK : hip_fail("lsa_gather launch", e);
 }

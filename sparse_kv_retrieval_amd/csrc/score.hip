@@ -281,44 +281,180 @@ __global__ __launch_bounds__(128) void score_select_kernel(const ScoreArgs a) {
 
 // Gathered scoring for the top-k: y = sum_j w'_j ReLU(q'_j . K_s) for each s in
 // the union list ([BLOG] §3.2: the native indexer works only inside the loaded
-// subset). The 32-entry tiles of all (layer, sequence) lists are numbered
-// consecutively, and each wave takes a contiguous run of tiles.
-template <int KT, int DH, int NHB>
-__global__ __launch_bounds__(256) void topk_score_kernel(const TopkScoreArgs a) {
-  using S_t = Scorer<KT, DH, NHB>;
-  __shared__ int32_t tp[LSA_TOPK_MAX_B + 1];  // tile prefix over sequences
+// subset).
+//
+// The 32-entry tiles of all (layer, sequence) lists are numbered
+// consecutively, and each pair of waves takes a contiguous run of them. The
+// pipeline is the one of score_select: register-staged loads D tiles ahead,
+// a double-buffered swizzled LDS stage, 32 heads per wave, and one barrier per
+// tile. The key rows are gathered through the index list. A load instruction
+// covers four whole 256-byte rows, so every row is fetched fully coalesced.
+// Each tile's indices are loaded D tiles before its keys. The key loads then
+// never wait on a load issued after the older loads still in flight.
+struct TileCursor {
+  int l, b;
+  int32_t jt, nt;     // tile within sequence b, tiles of sequence b
+  int64_t base;       // first row of sequence b (also where its list starts)
+  int32_t cnt;        // entries in b's list
+  __device__ __forceinline__ void load_seq(const TopkScoreArgs& a, const int32_t* tp) {
+    nt = uni(tp[b + 1]) - uni(tp[b]);
+    base = uni(a.key_off[b]);
+    cnt = uni(a.count[b]);
+  }
+  __device__ __forceinline__ void place(const TopkScoreArgs& a, const int32_t* tp, int64_t t) {
+    const int64_t tpl = uni(tp[a.B]);
+    l = uni((int32_t)(t / tpl));
+    const int32_t tt = (int32_t)(t - (int64_t)l * tpl);
+    b = uni(upper_seq(tp, a.B, tt));
+    jt = tt - uni(tp[b]);
+    load_seq(a, tp);
+  }
+  __device__ __forceinline__ void next(const TopkScoreArgs& a, const int32_t* tp) {
+    if (++jt < nt) return;
+    jt = 0;
+    do {
+      if (++b == a.B) {
+        b = 0;
+        ++l;
+      }
+    } while (uni(tp[b + 1]) == uni(tp[b]));
+    load_seq(a, tp);
+  }
+};
+
+template <int KT, int DH, int D>
+__global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) {
+  using IO = TileIO<KT, DH>;
+  using S_t = Scorer<KT == KEY_F32 ? KEY_F32 : KEY_BF16, DH, 1>;
+  static_assert(IO::GRB == 16 * (IO::GRB / 16), "row size");
+  __shared__ __attribute__((aligned(16))) char stage[2][IO::LSUB];
+  __shared__ float xpart[2][32];
+  __shared__ int32_t tp[LSA_TOPK_MAX_B + 1];
+
   const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
+  const int h = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   block_tile_prefix(a.count, a.B, tp);
-  const int64_t tiles_per_layer = tp[a.B];
-  const int64_t total = tiles_per_layer * a.L;
-  const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
-  const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave_in_block;
-  int64_t t = wid * total / nw;
-  const int64_t tend = (wid + 1) * total / nw;
+  const int64_t total = (int64_t)tp[a.B] * a.L;
+  const int64_t np = gridDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * total / np;
+  const int64_t t1 = ((int64_t)blockIdx.x + 1) * total / np;
+  const int J = (int)(t1 - t0);
+  if (J == 0) return;
+
+  const int i0 = IO::NLI >= 2 ? h * IO::NLW : 0;
+  const bool loads = IO::NLI >= 2 || h == 0;
+  int lrow[IO::NLW], lchunk[IO::NLW];
+#pragma unroll
+  for (int i = 0; i < IO::NLW; ++i) {
+    const int p = (i0 + i) * 1024 + lane * 16;
+    lrow[i] = p / IO::GRB;
+    lchunk[i] = (p % IO::GRB) / 16;
+  }
+
+  u32x4 R[D][IO::NLW];
+  float SC[D];
+  int32_t IX[2 * D][IO::NLW];  // list entries of the rows this lane loads, 2D tiles deep
+  int32_t IXS[2 * D];          // (fp8) list entry of row n, for the scale
+  TileCursor xc, ic, cc;       // index, key and compute cursors
+  xc.place(a, tp, t0);
+  ic = xc;
+  cc = xc;
+
+#define LSA_LOAD_IDX(SLOT)                                                                     \
+  do {                                                                                         \
+    const int32_t e_ = xc.jt * 32;                                                             \
+    const int32_t* il_ = a.idx + xc.base;                                                      \
+    _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i) IX[SLOT][i] = il_[min(e_ + lrow[i], xc.cnt - 1)]; \
+    if constexpr (KT == KEY_FP8) IXS[SLOT] = il_[min(e_ + n, xc.cnt - 1)];                     \
+    xc.next(a, tp);                                                                            \
+  } while (0)
+#define LSA_LOAD_KEYS(SLOT, XSLOT)                                                             \
+  do {                                                                                         \
+    const char* kb_ = (const char*)a.keys[ic.l] + ic.base * IO::GRB;                           \
+    if (loads) {                                                                               \
+      _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i)                                      \
+        R[SLOT][i] = __builtin_nontemporal_load(                                               \
+            (const u32x4*)(kb_ + (int64_t)IX[XSLOT][i] * IO::GRB + lchunk[i] * 16));           \
+    }                                                                                          \
+    if constexpr (KT == KEY_FP8) SC[SLOT] = a.scale[ic.l][ic.base + IXS[XSLOT]];               \
+    ic.next(a, tp);                                                                            \
+  } while (0)
+
+  // prologue: indices for tiles 0 .. 2D-1, keys for tiles 0 .. D-1
+#pragma unroll
+  for (int s = 0; s < 2 * D; ++s)
+    if (s < J) LSA_LOAD_IDX(s);
+#pragma unroll
+  for (int s = 0; s < D; ++s)
+    if (s < J) LSA_LOAD_KEYS(s, s);
 
   S_t S;
   int cur_l = -1, cur_b = -1;
-  for (; t < tend; ++t) {
-    const int l = (int)(t / tiles_per_layer);
-    const int32_t tt = (int32_t)(t - (int64_t)l * tiles_per_layer);
-    const int b = upper_seq(tp, a.B, tt);
-    if (l != cur_l || b != cur_b) {
-      S.load_query(a.q[l], a.w[l], b, a.n_h);
-      cur_l = l;
-      cur_b = b;
+  float pprev = 0.0f;
+  bool vprev = false;
+  int64_t oprev = 0;
+
+  for (int j0 = 0; j0 < J; j0 += 2 * D) {
+#pragma unroll
+    for (int s = 0; s < 2 * D; ++s) {
+      const int j = j0 + s;
+      if (j >= J) break;
+      const int rs = s % D;  // register slot of tile j
+      char* st = &stage[j & 1][0];
+      if (loads) {
+#pragma unroll
+        for (int i = 0; i < IO::NLW; ++i) {
+          const int r = lrow[i];
+          char* rowp = st + r * IO::LRB;
+          if constexpr (KT == KEY_FP8) {
+            const u32x4 v = R[rs][i];
+            const u32x2 b0 = e4m3x4_to_bf16x4(v[0]), b1 = e4m3x4_to_bf16x4(v[1]);
+            const u32x2 b2 = e4m3x4_to_bf16x4(v[2]), b3 = e4m3x4_to_bf16x4(v[3]);
+            const int c0 = 2 * lchunk[i], c1 = c0 + 1;
+            *(u32x4*)(rowp + ((c0 ^ (r % IO::LCPR)) * 16)) = u32x4{b0[0], b0[1], b1[0], b1[1]};
+            *(u32x4*)(rowp + ((c1 ^ (r % IO::LCPR)) * 16)) = u32x4{b2[0], b2[1], b3[0], b3[1]};
+          } else {
+            *(u32x4*)(rowp + ((lchunk[i] ^ (r % IO::LCPR)) * 16)) = R[rs][i];
+          }
+        }
+      }
+      float scale = 1.0f;
+      if constexpr (KT == KEY_FP8) scale = SC[rs];
+      if (j + D < J) LSA_LOAD_KEYS(rs, (s + D) % (2 * D));
+      if (j + 2 * D < J) LSA_LOAD_IDX(s);
+      lds_barrier();
+      S.read_keys_lds(st);
+      if (h == 0 && j > 0) {
+        const float y = pprev + xpart[(j - 1) & 1][n];
+        if (g == 0 && vprev) a.ys[oprev] = y;
+      }
+      if (cc.l != cur_l || cc.b != cur_b) {
+        S.load_query(a.q[cc.l], a.w[cc.l], cc.b, a.n_h, 32 * h);
+        cur_l = cc.l;
+        cur_b = cc.b;
+      }
+      f32x16 acc[1];
+      S.mma(acc);
+      float p = S.partial(acc);
+      p += __shfl_xor(p, 32);
+      if constexpr (KT == KEY_FP8) p *= scale;
+      const int32_t e = cc.jt * 32 + n;
+      if (h == 1) {
+        if (g == 0) xpart[j & 1][n] = p;
+      } else {
+        pprev = p;
+        vprev = e < cc.cnt;
+        oprev = (int64_t)cc.l * a.rows_total + cc.base + e;
+      }
+      cc.next(a, tp);
     }
-    const int64_t base = a.key_off[b];
-    const int32_t cnt = a.count[b];
-    const int32_t i = (tt - tp[b]) * 32 + n;
-    const bool valid = i < cnt;
-    const int64_t row = base + (valid ? a.idx[base + i] : 0);
-    S.load_keys((const char*)a.keys[l] + row * S_t::ROW_BYTES + g * S_t::HALF_BYTES, valid);
-    f32x16 acc[NHB];
-    S.mma(acc);
-    float y = S.logit(acc);
-    if constexpr (KT == KEY_FP8) y *= valid ? a.scale[l][row] : 0.0f;
-    if (g == 0 && valid) a.ys[(int64_t)l * a.rows_total + base + i] = y;
+  }
+#undef LSA_LOAD_IDX
+#undef LSA_LOAD_KEYS
+  lds_barrier();
+  if (h == 0) {
+    const float y = pprev + xpart[(J - 1) & 1][n];
+    if (g == 0 && vprev) a.ys[oprev] = y;
   }
 }
 
@@ -331,8 +467,9 @@ static hipError_t launch_score_t(const ScoreArgs& a, int pairs, hipStream_t st) 
   return hipGetLastError();
 }
 template <int KT, int DH, int NHB>
-static hipError_t launch_tscore_t(const TopkScoreArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((topk_score_kernel<KT, DH, NHB>), dim3(grid), dim3(256), 0, st, a);
+static hipError_t launch_tscore_t(const TopkScoreArgs& a, int pairs, hipStream_t st) {
+  constexpr int D = TileIO<KT, DH>::GSUB >= 8192 ? 2 : 4;
+  hipLaunchKernelGGL((topk_score_kernel<KT, DH, D>), dim3(pairs), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 

@@ -3,68 +3,184 @@
 // Indexer picks the final top-k core entries inside C^MemComp).
 //
 // One block per (sequence, layer). The scores y are in the workspace, in
-// subset order, which is ascending entry order. The k-th largest key is found
-// by a 4-pass MSB-first radix select over order-preserving uint32 keys, using
-// 256-bin LDS histograms. A final ordered pass keeps every entry above the
-// k-th key, plus the lowest-index entries equal to it. That matches the
-// (-y, s) order, and the output stays ascending because the pass walks the
-// list in order.
+// subset order, which is ascending entry order. A radix select over
+// order-preserving uint32 keys finds T, the key of the k-th largest score, and
+// how many entries equal to T must be kept. The output keeps every entry above
+// T plus the lowest-index entries equal to it, in list order, which matches
+// the (-y, s) order and keeps the output ascending.
 #include "kernels.hpp"
 
 namespace lsa {
 
 static constexpr int TS_THREADS = 1024;
+static constexpr int TS_VMAX = 80;  // values per thread held in registers (lists up to 81,920)
 
-__global__ __launch_bounds__(TS_THREADS) void topk_select_kernel(const TopkSelectArgs a) {
-  const int b = blockIdx.x, l = blockIdx.y, tid = threadIdx.x;
-  const int64_t base = a.key_off[b];
-  const int32_t M = a.count[b];
-  const int32_t k = a.k;
-  const float* ys = a.ys + (int64_t)l * a.rows_total + base;
-  const int32_t* idx = a.idx + base;
-  int32_t* out = a.out_idx[l] + (int64_t)b * k;
-  float* outs = a.out_score[l] ? a.out_score[l] + (int64_t)b * k : nullptr;
-
-  if (M <= k) {
-    for (int32_t i = tid; i < k; i += TS_THREADS) {
-      out[i] = i < M ? idx[i] : -1;
-      if (outs) outs[i] = i < M ? ys[i] : -INFINITY;
+// The digit d with (count of digits > d) < krem <= (count of digits >= d),
+// over an LDS histogram of nbins (1024 or 2048) bins. It writes d and the
+// new krem (how many of the entries with digit d are still to be taken).
+__device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, uint32_t krem, uint32_t* sh_digit,
+                                           uint32_t* sh_krem) {
+  const int tid = threadIdx.x;
+  const int per = nbins / TS_THREADS;
+  uint32_t own = 0;
+  for (int i = 0; i < per; ++i) own += hist[tid * per + i];
+  int64_t tot;
+  const int64_t below = block_exclusive_scan((int64_t)own, &tot);  // bins below this thread's bins
+  const uint32_t suf = (uint32_t)(tot - below);                    // bins >= tid*per
+  const uint32_t above = suf - own;                                // bins above this thread's bins
+  if (above < krem && krem <= suf) {
+    uint32_t cum = above;
+    for (int i = per - 1; i >= 0; --i) {
+      const uint32_t c = hist[tid * per + i];
+      if (cum + c >= krem) {
+        *sh_digit = (uint32_t)(tid * per + i);
+        *sh_krem = krem - cum;
+        break;
+      }
+      cum += c;
     }
-    if (tid == 0) a.out_count[l * gridDim.x + b] = M;
-    return;
   }
+  __syncthreads();
+}
 
-  __shared__ uint32_t hist[256];
+// Number of set bits of m in the lanes below this one.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Exclusive scan, in place, of an LDS table of n <= 2 * TS_THREADS counts.
+__device__ __forceinline__ void table_exclusive_scan(uint32_t* tab, int n) {
+  const int tid = threadIdx.x;
+  const int j0 = 2 * tid;
+  const uint32_t a0 = j0 < n ? tab[j0] : 0u, a1 = j0 + 1 < n ? tab[j0 + 1] : 0u;
+  int64_t tot;
+  const int64_t ex = block_exclusive_scan((int64_t)(a0 + a1), &tot);
+  if (j0 < n) tab[j0] = (uint32_t)ex;
+  if (j0 + 1 < n) tab[j0 + 1] = (uint32_t)(ex + a0);
+  __syncthreads();
+}
+
+// Radix select over a list held in registers.
+//
+// Thread t = 64 w + lane holds the list entries i = t + 1024 v (v < V), so
+// every load is coalesced. Three histogram passes over bits 31..21, 20..10
+// and 9..0 of the keys touch only registers and a 2048-bin LDS histogram, and
+// find T, the key of the k-th largest score. The list order is (v, w, lane).
+// An entry's rank among the entries before it is therefore a count of lanes
+// below it in its wave (ballot + mbcnt) plus an exclusive scan of the
+// per-(v, w) counts held in a small LDS table. One such scan ranks the entries
+// equal to T, which settles ties toward the lower index. A second one places
+// each kept entry at its ascending output position.
+__device__ __forceinline__ void select_in_registers(const float* __restrict__ ys, const int32_t* __restrict__ idx,
+                                                    int32_t M, int32_t k, int32_t* out, float* outs) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int NW = TS_THREADS / 64;
+  const int V = (M + TS_THREADS - 1) / TS_THREADS;
+  // Key 0 pads the tail. It sorts below every real key (the smallest real key,
+  // -inf, maps to 0x007FFFFF), so padding never reaches the selected bins or
+  // the output, and the passes need no bounds test.
+  uint32_t key[TS_VMAX];
+#pragma unroll
+  for (int v = 0; v < TS_VMAX; ++v)
+    if (v < V) {
+      const int i = tid + TS_THREADS * v;
+      key[v] = i < M ? order_key(ys[i]) : 0u;
+    }
+
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t tab[TS_VMAX * NW], tab2[TS_VMAX * NW];
   __shared__ uint32_t sh_digit, sh_krem;
-  uint32_t prefix = 0, pmask = 0;
-  uint32_t krem = (uint32_t)k;  // how many of the remaining candidates to take
+  uint32_t prefix = 0, pmask = 0, krem = (uint32_t)k;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 2 ? 1024 : 2048;
+    for (int i = tid; i < 2048; i += TS_THREADS) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < TS_VMAX; ++v)
+      if (v < V && (key[v] & pmask) == prefix) atomicAdd(&hist[(key[v] >> sh) & (nb - 1)], 1u);
+    __syncthreads();
+    find_digit(hist, nb, krem, &sh_digit, &sh_krem);
+    prefix |= sh_digit << sh;
+    pmask |= (uint32_t)(nb - 1) << sh;
+    krem = sh_krem;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+
+  // Ballots are recomputed in each loop rather than kept, so registers hold only the keys.
+  // tab holds per-(v, w) counts of entries equal to T, then their exclusive scan;
+  // tab2 the same for kept entries.
+#pragma unroll
+  for (int v = 0; v < TS_VMAX; ++v)
+    if (v < V) {
+      const uint64_t m = __ballot(key[v] == T);
+      if (lane == 0) tab[v * NW + w] = (uint32_t)__popcll(m);
+    }
+  __syncthreads();
+  table_exclusive_scan(tab, V * NW);
+#pragma unroll
+  for (int v = 0; v < TS_VMAX; ++v)
+    if (v < V) {
+      const uint64_t meq = __ballot(key[v] == T);
+      const bool take = key[v] > T || (key[v] == T && tab[v * NW + w] + lanes_below(meq) < krem);
+      const uint64_t mt = __ballot(take);
+      if (lane == 0) tab2[v * NW + w] = (uint32_t)__popcll(mt);
+    }
+  __syncthreads();
+  table_exclusive_scan(tab2, V * NW);
+#pragma unroll
+  for (int v = 0; v < TS_VMAX; ++v)
+    if (v < V) {
+      const uint64_t meq = __ballot(key[v] == T);
+      const bool take = key[v] > T || (key[v] == T && tab[v * NW + w] + lanes_below(meq) < krem);
+      const uint64_t mt = __ballot(take);
+      if (take) {
+        const int i = tid + TS_THREADS * v;
+        const uint32_t pos = tab2[v * NW + w] + lanes_below(mt);
+        out[pos] = idx[i];
+        if (outs) outs[pos] = ys[i];
+      }
+    }
+}
+
+// Radix select that re-reads the scores from memory on every pass (lists of
+// any length): four 8-bit passes, then an ordered output pass in chunks of
+// 1024 entries.
+__device__ __forceinline__ void select_streaming(const float* __restrict__ ys, const int32_t* __restrict__ idx,
+                                                 int32_t M, int32_t k, int32_t* out, float* outs) {
+  const int tid = threadIdx.x;
+  __shared__ uint32_t hist8[256];
+  __shared__ uint32_t sd, sk;
+  uint32_t prefix = 0, pmask = 0, krem = (uint32_t)k;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
+    if (tid < 256) hist8[tid] = 0;
     __syncthreads();
     for (int32_t i = tid; i < M; i += TS_THREADS) {
       const uint32_t u = order_key(ys[i]);
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+      if ((u & pmask) == prefix) atomicAdd(&hist8[(u >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (tid < 64) {
       // lane j owns bins 4j..4j+3; suffix sums from the top bin down
       uint32_t s4[4], own = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { s4[i] = hist[4 * tid + i]; own += s4[i]; }
-      uint32_t suf = own;  // inclusive suffix over lanes >= tid
+      for (int i = 0; i < 4; ++i) { s4[i] = hist8[4 * tid + i]; own += s4[i]; }
+      uint32_t suf = own;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const uint32_t y = __shfl_down(suf, o);
         if (tid + o < 64) suf += y;
       }
-      const uint32_t above = suf - own;  // candidates in bins of higher lanes
+      const uint32_t above = suf - own;
       if (above < krem && krem <= suf) {
         uint32_t cum = above;
         for (int i = 3; i >= 0; --i) {
           if (cum + s4[i] >= krem) {
-            sh_digit = 4 * tid + i;
-            sh_krem = krem - cum;
+            sd = 4 * tid + i;
+            sk = krem - cum;
             break;
           }
           cum += s4[i];
@@ -72,13 +188,12 @@ __global__ __launch_bounds__(TS_THREADS) void topk_select_kernel(const TopkSelec
       }
     }
     __syncthreads();
-    prefix |= sh_digit << shift;
+    prefix |= sd << shift;
     pmask |= 255u << shift;
-    krem = sh_krem;
+    krem = sk;
     __syncthreads();
   }
-  const uint32_t T = prefix;  // key of the k-th largest score; take `krem` entries equal to it
-
+  const uint32_t T = prefix;
   int64_t run_out = 0, run_eq = 0;
   for (int32_t base_i = 0; base_i < M; base_i += TS_THREADS) {
     const int32_t i = base_i + tid;
@@ -98,7 +213,28 @@ __global__ __launch_bounds__(TS_THREADS) void topk_select_kernel(const TopkSelec
     run_out += tot_take;
     run_eq += tot_eq;
   }
-  if (tid == 0) a.out_count[l * gridDim.x + b] = k;
+}
+
+__global__ __launch_bounds__(TS_THREADS) void topk_select_kernel(const TopkSelectArgs a) {
+  const int b = blockIdx.x, l = blockIdx.y, tid = threadIdx.x;
+  const int64_t base = a.key_off[b];
+  const int32_t M = a.count[b];
+  const int32_t k = a.k;
+  const float* ys = a.ys + (int64_t)l * a.rows_total + base;
+  const int32_t* idx = a.idx + base;
+  int32_t* out = a.out_idx[l] + (int64_t)b * k;
+  float* outs = a.out_score[l] ? a.out_score[l] + (int64_t)b * k : nullptr;
+  if (M <= k) {
+    for (int32_t i = tid; i < k; i += TS_THREADS) {
+      out[i] = i < M ? idx[i] : -1;
+      if (outs) outs[i] = i < M ? ys[i] : -INFINITY;
+    }
+  } else if (M <= TS_THREADS * TS_VMAX) {
+    select_in_registers(ys, idx, M, k, out, outs);
+  } else {
+    select_streaming(ys, idx, M, k, out, outs);
+  }
+  if (tid == 0) a.out_count[l * gridDim.x + b] = M < k ? M : k;
 }
 
 hipError_t launch_topk_select(const TopkSelectArgs& a, int L, hipStream_t st) {
