@@ -19,6 +19,8 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 instructions in any generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the epilogues read them without v_accvgpr_read copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 _NOISE = "is not a recognized feature for this target"
 

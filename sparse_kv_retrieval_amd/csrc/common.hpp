@@ -44,27 +44,62 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ------------------------------------------------------------- e4m3fn -> bf16
-// Exact widening of 4 OCP e4m3fn bytes (one dword) to 4 bfloat16 values (two
-// dwords). For exponent field e >= 1 the value is 2^(e-7) (1 + m/8). Placing
-// the 7 exponent/mantissa bits at float32 bit 20 gives 2^(e-127) (1 + m/8),
-// and multiplying by 2^120 rescales it exactly. Subnormal bytes (e = 0) become
-// float32 subnormals m/8 2^-126, and the same multiply gives m 2^-9. Every
-// result has at most 4 significant bits, so truncating to the high half is
-// exact. Finite inputs only: the NaN byte is not a valid key.
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t two) {
-  // `two` holds two bytes in bits 0..7 and 8..15.
-  float f0 = __uint_as_float((two & 0x7Fu) << 20) * 0x1p120f;
-  float f1 = __uint_as_float(((two >> 8) & 0x7Fu) << 20) * 0x1p120f;
-  uint32_t b0 = (__float_as_uint(f0) >> 16) | ((two & 0x80u) << 8);
-  uint32_t b1 = (__float_as_uint(f1) >> 16) | (((two >> 8) & 0x80u) << 8);
-  return b0 | (b1 << 16);
-}
-
+// Widening of 4 OCP e4m3fn bytes (one dword) to 4 bfloat16 values (two
+// dwords, byte i -> element i) with the gfx950 conversion instruction
+// (v_cvt_scalef32_pk_bf16_fp8, scale 1). Every finite e4m3fn value has at most
+// 4 significant bits and an exponent in [-9, 8], so bf16 holds it exactly; a
+// one-launch check over all 256 codes matched the format's definition.
+// Finite inputs only: the NaN byte is not a valid key.
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t four) {
   u32x2 r;
-  r[0] = e4m3x2_to_bf16x2(four & 0xFFFFu);
-  r[1] = e4m3x2_to_bf16x2(four >> 16);
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(four, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(four, 1.0f, true));
   return r;
+}
+
+// ------------------------------------------------------------- buffer loads
+// Raw buffer resource over [base, base + bytes). A load at an offset >= bytes
+// returns zeros without a memory access. The streaming kernels use this to
+// issue the same loads on every path: a slot with nothing to fetch (past the
+// end of a wave's work, or the tail of a ragged tile) gets an out-of-range
+// offset instead of a branch. The compiler's wait counts then stay exact, and
+// no wait drains the loads still in flight. Callers keep bytes < 2^31.
+constexpr uint32_t BUF_OOB = 0x80000000u;
+constexpr int BUF_NT = 2;  // cache policy: non-temporal
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, BUF_NT));
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+// ------------------------------------------------------------- LDS tile layout
+// Position of 16-byte chunk c of row r in a 32-row tile staged in LDS, with
+// CPR chunks per row. Rows are XOR-swizzled (chunk c of row r at c ^ (r % CPR))
+// so that 8 lanes reading the same chunk of 8 consecutive rows hit 8 distinct
+// 16-byte bank groups. With ROT the chunk index is first rotated right by one
+// bit, c -> (c >> 1) | ((c & 1) * CPR / 2). This is for fp8 tiles, where each
+// lane writes the two LDS chunks 2j and 2j + 1 that one 16-byte load widens
+// to, and 8 lanes write chunks 2j, j = 0..7, of one row. Rotated, those land
+// on 8 distinct bank groups too.
+template <int CPR, bool ROT>
+__device__ __forceinline__ int lds_chunk(int c, int r) {
+  if constexpr (ROT) c = (c >> 1) | ((c & 1) * (CPR / 2));
+  return c ^ (r % CPR);
+}
+
+// Sum of a lane's value and the value of lane l ^ 32 (the other half of the
+// wave), in both halves. v_permlane32_swap exchanges the upper half of one
+// register with the lower half of the other, so with both operands equal to x
+// the two results hold x[l] and x[l ^ 32] at every lane; the add is the same
+// low-half + high-half sum in both halves.
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Values the whole wave agrees on, pinned to scalar registers. Loads from memory

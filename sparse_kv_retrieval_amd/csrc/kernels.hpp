@@ -22,6 +22,7 @@ struct ScoreArgs {
   int64_t total_words;     // L * words_per_layer
   int32_t B, n_h;
   float thr;               // logit threshold
+  int32_t group;           // pairs per interleave group (grid size is a multiple)
 };
 
 struct TopkScoreArgs {
@@ -83,8 +84,8 @@ struct ProjArgs {
   int32_t B, d, r, n_h, d_h;
 };
 
-hipError_t launch_score_select(const ScoreArgs& a, int key_kind, int d_h, int pairs, hipStream_t st);
-hipError_t launch_topk_score(const TopkScoreArgs& a, int key_kind, int d_h, int grid, hipStream_t st);
+hipError_t launch_score_select(const ScoreArgs& a, int key_kind, int d_h, int pairs, int depth, hipStream_t st);
+hipError_t launch_topk_score(const TopkScoreArgs& a, int key_kind, int d_h, int grid, int depth, hipStream_t st);
 hipError_t launch_topk_select(const TopkSelectArgs& a, int L, hipStream_t st);
 hipError_t launch_union_compact(const UnionArgs& a, int B, int64_t max_words, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, int grid, hipStream_t st);

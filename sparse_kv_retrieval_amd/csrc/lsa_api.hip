@@ -92,6 +92,17 @@ lsa_status key_kind_of(lsa_dtype dt, int* kind) {
   }
 }
 
+// The kernels address one sequence's keys with 32-bit byte offsets.
+lsa_status check_key_bytes(int32_t B, const int64_t* key_offsets_host, int32_t d_h, int kind) {
+  const int64_t row = (int64_t)d_h * (kind == KEY_F32 ? 4 : kind == KEY_BF16 ? 2 : 1);
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t n = key_offsets_host[b + 1] - key_offsets_host[b];
+    if (n * row > INT32_MAX)
+      return fail(LSA_ERR_UNSUPPORTED, "sequence %d holds %lld bytes of keys (> 2^31-1)", b, (long long)(n * row));
+  }
+  return LSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -139,6 +150,7 @@ lsa_status lsa_score_select(const lsa_score_layer* layers, int32_t L, int32_t B,
   if ((s = check_heads(n_h, d_h)) != LSA_OK) return s;
   int kind;
   if ((s = key_kind_of(key_dtype, &kind)) != LSA_OK) return s;
+  if ((s = check_key_bytes(B, key_offsets_host, d_h, kind)) != LSA_OK) return s;
   if (!(threshold > 0.0f && threshold < 1.0f)) return fail(LSA_ERR_INVALID_ARG, "threshold must lie in (0, 1)");
   ScoreArgs a{};
   for (int l = 0; l < L; ++l) {
@@ -157,9 +169,11 @@ lsa_status lsa_score_select(const lsa_score_layer* layers, int32_t L, int32_t B,
   a.total_words = a.words_per_layer * L;
   a.B = B; a.n_h = n_h; a.thr = (float)t;
   if (a.total_words == 0) return LSA_OK;
-  // one block per pair of waves; each pair takes a contiguous run of mask words
-  const int64_t pairs = std::min<int64_t>(a.total_words, (int64_t)cu_count() * env_int("LSA_SCORE_PAIRS_PER_CU", 4));
-  const hipError_t e = launch_score_select(a, kind, d_h, (int)pairs, stream);
+  // One block per pair of waves. Groups of `group` pairs take interleaved words of a contiguous run.
+  int64_t pairs = std::min<int64_t>(a.total_words, (int64_t)cu_count() * env_int("LSA_SCORE_PAIRS_PER_CU", 4));
+  a.group = (int32_t)std::max<int64_t>(1, std::min<int64_t>(env_int("LSA_SCORE_GROUP", 1), pairs));
+  pairs = std::max<int64_t>(a.group, pairs / a.group * a.group);
+  const hipError_t e = launch_score_select(a, kind, d_h, (int)pairs, env_int("LSA_SCORE_DEPTH", 0), stream);
   return e == hipSuccess ? LSA_OK : hip_fail("lsa_score_select launch", e);
 }
 
@@ -205,6 +219,7 @@ lsa_status lsa_topk(const lsa_topk_layer* layers, int32_t L, int32_t B, const in
   if ((s = check_heads(n_h, d_h)) != LSA_OK) return s;
   int kind;
   if ((s = key_kind_of(key_dtype, &kind)) != LSA_OK) return s;
+  if ((s = check_key_bytes(B, key_offsets_host, d_h, kind)) != LSA_OK) return s;
   if (k < 1 || k > 65536) return fail(LSA_ERR_UNSUPPORTED, "k must be in [1, 65536] (got %d)", k);
   if (!idx || !count || !topk_count_out) return fail(LSA_ERR_INVALID_ARG, "idx, count and topk_count_out must be set");
   const int64_t rows = key_offsets_host[B];
@@ -232,8 +247,8 @@ lsa_status lsa_topk(const lsa_topk_layer* layers, int32_t L, int32_t B, const in
   if (rows > 0) {
     int64_t tiles = 0;
     for (int32_t b = 0; b < B; ++b) tiles += (key_offsets_host[b + 1] - key_offsets_host[b] + 31) / 32;
-    const int64_t pairs = std::max<int64_t>(1, std::min<int64_t>(tiles * L, (int64_t)cu_count() * 4));
-    if ((e = launch_topk_score(sa, kind, d_h, (int)pairs, stream)) != hipSuccess)
+    const int64_t pairs = std::max<int64_t>(1, std::min<int64_t>(tiles * L, (int64_t)cu_count() * env_int("LSA_TOPK_PAIRS_PER_CU", 4)));
+    if ((e = launch_topk_score(sa, kind, d_h, (int)pairs, env_int("LSA_TOPK_DEPTH", 0), stream)) != hipSuccess)
       return hip_fail("lsa_topk score launch", e);
   }
   if ((e = launch_topk_select(ta, L, stream)) != hipSuccess) return hip_fail("lsa_topk select launch", e);

@@ -66,15 +66,16 @@ struct WordCursor {
   int l, b;
   int64_t word;     // word index in the mask layout
   int64_t seq_hi;   // first word after sequence b
-  int64_t e0;       // entry index (within sequence b) of the word's first bit
-  int64_t row0, nb; // sequence b's first key row and entry count
+  int32_t e0;       // entry index (within sequence b) of the word's first bit
+  int32_t nb;       // sequence b's entry count (< 2^31, checked on the host)
+  int64_t row0;     // sequence b's first key row
 
   __device__ __forceinline__ void load_seq(const SeqTab& t) {
     const int64_t lo = uni(t.mwo[b]);
     seq_hi = uni(t.mwo[b + 1]);
     row0 = uni(t.koff[b]);
-    nb = uni(t.koff[b + 1]) - row0;
-    e0 = (word - lo) * 64;
+    nb = uni((int32_t)(uni(t.koff[b + 1]) - row0));
+    e0 = uni((int32_t)((word - lo) * 64));
   }
   __device__ __forceinline__ void place(const ScoreArgs& a, const SeqTab& t, int64_t gw) {
     l = uni((int32_t)(gw / a.words_per_layer));
@@ -97,6 +98,9 @@ struct WordCursor {
       load_seq(t);
     }
   }
+  __device__ __forceinline__ void advance(const ScoreArgs& a, const SeqTab& t, int g) {
+    for (int i = 0; i < g; ++i) next(a, t);
+  }
 };
 
 // Score + select: keys streamed HBM -> registers -> LDS -> MFMA, two waves per tile.
@@ -106,9 +110,10 @@ struct WordCursor {
 // 16-byte vector loads (each load instruction covers 1 KiB of contiguous key
 // rows) and keeps D tiles in flight in registers. When a tile's turn comes, it
 // writes the tile into one of two LDS stages. fp8 keys are widened to bf16 on
-// the way (exact), so both waves then run the bf16 MFMA on the same
-// operands. In LDS, 16-byte chunk c of row r sits at position c ^ (r % CPR), so
-// the operand reads (lane n reads row n) are free of bank conflicts.
+// the way (exact, one conversion instruction per two values), so both waves
+// then run the bf16 MFMA on the same operands. The LDS layout (lds_chunk)
+// swizzles 16-byte chunks so that the stores and the operand reads (lane n
+// reads row n) are free of bank conflicts.
 //
 // Wave h scores heads [32h, 32h+32). Wave 1 passes its gate/ReLU partial sums
 // to wave 0 through LDS, and wave 0 finishes tile j-1 (threshold, ballot,
@@ -127,12 +132,38 @@ struct TileIO {
   static constexpr int NLW = NLI >= 2 ? NLI / 2 : 1;  // per wave
   static constexpr int GCPR = GRB / 16;      // stored 16-byte chunks per row
   static constexpr int LCPR = LRB / 16;      // LDS 16-byte chunks per row
+  // fp8 rows of 8+ stored chunks: one 8-lane write group covers one row
+  static constexpr bool ROT = KT == KEY_FP8 && GCPR >= 8;
 };
+
+// Where a scored tile's results go: entry n of the tile is row `row` (valid
+// if the entry exists), in mask word `word` of layer `l`.
+struct TileMeta {
+  bool valid = false;
+  int64_t row = 0, word = 0;
+  int l = 0;
+  float scale = 1.0f;  // fp8 keys: the entry's scale
+};
+
+// Threshold, ballot and stores of one tile, given its full logit x (lane n of
+// both lane groups holds entry n). Tiles come in pairs per 64-bit mask word:
+// the even tile's ballot waits in bits0 for the odd one.
+__device__ __forceinline__ void finish_tile(const ScoreArgs& a, const TileMeta& m, float x, int odd,
+                                            uint32_t& bits0, int lane, int g) {
+  const uint32_t bits = (uint32_t)__ballot(m.valid && x >= a.thr);
+  float* so = a.score[m.l];
+  if (so != nullptr && g == 0 && m.valid) so[m.row] = 1.0f / (1.0f + __expf(-x));
+  if (odd) {
+    if (lane == 0) a.mask[m.l][m.word] = (uint64_t)bits0 | ((uint64_t)bits << 32);
+  } else {
+    bits0 = bits;
+  }
+}
 
 template <int KT, int DH, int D>
 __global__ __launch_bounds__(128) void score_select_kernel(const ScoreArgs a) {
   using IO = TileIO<KT, DH>;
-  using S_t = Scorer<KT == KEY_F32 ? KEY_F32 : KEY_BF16, DH, 1>;
+  using S_t = Scorer<KT == KEY_F32 ? KEY_F32 : KEY_BF16, DH, 1, TileIO<KT, DH>::ROT>;
   static_assert(S_t::ROW_BYTES == IO::LRB, "LDS row layout");
   __shared__ __attribute__((aligned(16))) char stage[2][IO::LSUB];
   __shared__ float xpart[2][32];
@@ -150,10 +181,17 @@ __global__ __launch_bounds__(128) void score_select_kernel(const ScoreArgs a) {
     t.koff = tab[0];
     t.mwo = tab[1];
   }
-  const int64_t np = gridDim.x;
-  const int64_t gbeg = (int64_t)blockIdx.x * a.total_words / np;
-  const int64_t gend = ((int64_t)blockIdx.x + 1) * a.total_words / np;
-  const int J = (int)(2 * (gend - gbeg));  // tiles of this pair
+  // Pairs form groups of G. A group owns a contiguous run of mask words, and
+  // its pairs take every G-th word of the run. The G pairs then stream
+  // neighbouring tiles, which keeps DRAM accesses local, while each pair stays
+  // inside one (layer, sequence) for long stretches.
+  const int G = a.group;
+  const int64_t ng = gridDim.x / G;
+  const int64_t grp = blockIdx.x / G, off = blockIdx.x % G;
+  const int64_t gbeg = grp * a.total_words / ng;
+  const int64_t gend = (grp + 1) * a.total_words / ng;
+  const int64_t nwords = gend - gbeg > off ? (gend - gbeg - off + G - 1) / G : 0;
+  const int J = (int)(2 * nwords);  // tiles of this pair
   if (J == 0) return;
 
   // This wave's load instructions: [i0, i0 + NLW), or none for 1 KiB tiles on wave 1.
@@ -161,54 +199,71 @@ __global__ __launch_bounds__(128) void score_select_kernel(const ScoreArgs a) {
   const bool loads = IO::NLI >= 2 || h == 0;
   // per instruction: row within the tile, and the stored chunk of that row
   int lrow[IO::NLW], lchunk[IO::NLW];
+  uint32_t loff[IO::NLW];  // byte offset within the tile (out of range: this wave loads nothing)
 #pragma unroll
   for (int i = 0; i < IO::NLW; ++i) {
     const int p = (i0 + i) * 1024 + lane * 16;
     lrow[i] = p / IO::GRB;
     lchunk[i] = (p % IO::GRB) / 16;
+    loff[i] = loads ? (uint32_t)p : BUF_OOB;
   }
 
   u32x4 R[D][IO::NLW];
   float SC[D];
   WordCursor ic, cc;
-  ic.place(a, t, gbeg);
+  ic.place(a, t, gbeg + off);
   cc = ic;
 
   S_t S;
   int cur_l = -1, cur_b = -1;
-  float pprev = 0.0f;
-  bool vprev = false;
-  int64_t rprev = 0, wprev = 0;
-  int lprev = 0;
+  f32x16 acc[1];        // MFMA result of the last tile issued
+  TileMeta m1, m2;      // tiles j-1 and j-2 (wave 0 finishes them)
+  float p2 = 0.0f;      // wave 0's half of the head sum of tile j-2
   uint32_t bits0 = 0;
 
-#define LSA_LOAD_TILE(SLOT, JJ)                                                                     \
+  // Loads of tile JJ into register slot SLOT. Every slot issues the same
+  // loads whether or not it is LIVE (a tile of this pair). The buffer
+  // resource covers exactly the tile's existing rows (none for a dead slot),
+  // so the rows past a sequence's end read as zeros. With the resource based
+  // at the tile, each lane's offsets are constants.
+#define LSA_LOAD_TILE(SLOT, JJ, LIVE)                                                                 \
   do {                                                                                              \
-    const int64_t e_ = ic.e0 + ((JJ) & 1) * 32;                                                     \
-    const int64_t last_ = ic.row0 + ic.nb - 1;                                                      \
-    const char* kb_ = (const char*)a.keys[ic.l];                                                    \
-    if (loads) {                                                                                    \
-      _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i) {                                         \
-        const int64_t row_ = min(ic.row0 + e_ + lrow[i], last_);                                    \
-        R[SLOT][i] = __builtin_nontemporal_load((const u32x4*)(kb_ + row_ * IO::GRB + lchunk[i] * 16)); \
-      }                                                                                             \
+    const bool live_ = (LIVE);                                                                      \
+    const int kl_ = live_ ? ic.l : 0;                                                               \
+    const int32_t e_ = ic.e0 + ((JJ) & 1) * 32;                                                     \
+    const int64_t row_ = ic.row0 + e_;                                                              \
+    const uint32_t nr_ = live_ ? (uint32_t)uni(max(0, min(32, ic.nb - e_))) : 0u;                     \
+    const auto rk_ = buf_rsrc((const char*)a.keys[kl_] + row_ * IO::GRB, nr_ * IO::GRB);            \
+    _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i) R[SLOT][i] = buf_load16_nt(rk_, loff[i]);   \
+    if constexpr (KT == KEY_FP8) {                                                                  \
+      const auto rs_ = buf_rsrc(a.scale[kl_] + row_, nr_ * 4);                                      \
+      SC[SLOT] = __uint_as_float(buf_load4(rs_, n * 4));                                            \
     }                                                                                               \
-    if constexpr (KT == KEY_FP8) SC[SLOT] = a.scale[ic.l][min(ic.row0 + e_ + n, last_)];            \
-    if ((JJ) & 1) ic.next(a, t);                                                                    \
+    if (live_ && ((JJ) & 1)) ic.advance(a, t, G);                                                   \
   } while (0)
 
+  // The prologue keeps its slots in issue order (the sched barrier), so slot
+  // s is always the oldest load group when tile s is written.
 #pragma unroll
-  for (int s = 0; s < D; ++s)
-    if (s < J) LSA_LOAD_TILE(s, s);
+  for (int s = 0; s < D; ++s) {
+    LSA_LOAD_TILE(s, s, s < J);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
-  for (int j0 = 0; j0 < J; j0 += D) {
+  // The loop runs whole groups of D slots. A slot past the last tile (j >= J)
+  // only issues its (out-of-range) refill. With no early exit, every path
+  // around the loop issues the same loads, so the compiler's wait before
+  // writing tile j covers tile j's loads only, and the D - 1 younger tiles
+  // stay in flight.
+  const int NIT = (J + D - 1) / D;
+  for (int it = 0; it < NIT; ++it) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
-      const int j = j0 + s;
-      if (j >= J) break;
+      const int j = it * D + s;
+      const bool live = j < J;
       char* st = &stage[j & 1][0];
       // write this wave's half of tile j into LDS (waits for its loads)
-      if (loads) {
+      if (live && loads) {
 #pragma unroll
         for (int i = 0; i < IO::NLW; ++i) {
           const int r = lrow[i];
@@ -218,30 +273,38 @@ __global__ __launch_bounds__(128) void score_select_kernel(const ScoreArgs a) {
             const u32x2 b0 = e4m3x4_to_bf16x4(v[0]), b1 = e4m3x4_to_bf16x4(v[1]);
             const u32x2 b2 = e4m3x4_to_bf16x4(v[2]), b3 = e4m3x4_to_bf16x4(v[3]);
             const int c0 = 2 * lchunk[i], c1 = c0 + 1;
-            *(u32x4*)(rowp + ((c0 ^ (r % IO::LCPR)) * 16)) = u32x4{b0[0], b0[1], b1[0], b1[1]};
-            *(u32x4*)(rowp + ((c1 ^ (r % IO::LCPR)) * 16)) = u32x4{b2[0], b2[1], b3[0], b3[1]};
+            *(u32x4*)(rowp + lds_chunk<IO::LCPR, IO::ROT>(c0, r) * 16) = u32x4{b0[0], b0[1], b1[0], b1[1]};
+            *(u32x4*)(rowp + lds_chunk<IO::LCPR, IO::ROT>(c1, r) * 16) = u32x4{b2[0], b2[1], b3[0], b3[1]};
           } else {
-            *(u32x4*)(rowp + ((lchunk[i] ^ (r % IO::LCPR)) * 16)) = R[s][i];
+            *(u32x4*)(rowp + lds_chunk<IO::LCPR, IO::ROT>(lchunk[i], r) * 16) = R[s][i];
           }
         }
       }
       float scale = 1.0f;
       if constexpr (KT == KEY_FP8) scale = SC[s];
       // refill this slot with tile j + D
-      if (j + D < J) LSA_LOAD_TILE(s, j + D);
-      lds_barrier();  // tile j complete in LDS; wave 1's partial of tile j-1 visible
+      LSA_LOAD_TILE(s, j + D, j + D < J);
+      if (!live) continue;
+      // Tile j's MFMAs are issued at the end of iteration j. Their result is
+      // consumed one iteration later (gate/ReLU partial of tile j-1, below),
+      // so the MFMA chain runs while this wave writes and loads the next
+      // tile. Wave 0 finishes a tile one iteration after that, once wave 1's
+      // half of the head sum is in LDS.
+      lds_barrier();  // tile j complete in LDS; wave 1's partial of tile j-2 visible
       S.read_keys_lds(st);
-
-      if (h == 0 && j > 0) {
-        // finish tile j-1: both halves of the head sum, threshold, ballot, stores
-        const float x = pprev + xpart[(j - 1) & 1][n];
-        const uint32_t bits = (uint32_t)__ballot(vprev && x >= a.thr);
-        float* so = a.score[lprev];
-        if (so != nullptr && g == 0 && vprev) so[rprev] = 1.0f / (1.0f + __expf(-x));
-        if ((j - 1) & 1) {
-          if (lane == 0) a.mask[lprev][wprev] = (uint64_t)bits0 | ((uint64_t)bits << 32);
+      // keep the partial below the barrier and the operand reads: it is what
+      // waits for tile j-1's MFMA chain
+      __builtin_amdgcn_sched_barrier(0);
+      if (j > 0) {
+        float p = S.partial(acc);
+        p = sum_halves(p);
+        if constexpr (KT == KEY_FP8) p *= m1.scale;
+        if (h == 1) {
+          if (g == 0) xpart[(j - 1) & 1][n] = p;
         } else {
-          bits0 = bits;
+          if (j > 1) finish_tile(a, m2, p2 + xpart[(j - 2) & 1][n], (j - 2) & 1, bits0, lane, g);
+          p2 = p;
+          m2 = m1;
         }
       }
       if (cc.l != cur_l || cc.b != cur_b) {
@@ -249,34 +312,34 @@ __global__ __launch_bounds__(128) void score_select_kernel(const ScoreArgs a) {
         cur_l = cc.l;
         cur_b = cc.b;
       }
-      f32x16 acc[1];
-      S.mma(acc);
-      float p = S.partial(acc);
-      p += __shfl_xor(p, 32);
-      if constexpr (KT == KEY_FP8) p *= scale;
-      const int64_t se = cc.e0 + (j & 1) * 32 + n;
-      if (h == 1) {
-        if (g == 0) xpart[j & 1][n] = p;
-      } else {
-        pprev = p;
-        vprev = se < cc.nb;
-        rprev = cc.row0 + se;
-        wprev = cc.word;
-        lprev = cc.l;
+      {
+        const int32_t se = cc.e0 + (j & 1) * 32 + n;
+        m1.valid = se < cc.nb;
+        m1.row = cc.row0 + se;
+        m1.word = cc.word;
+        m1.l = cc.l;
+        m1.scale = scale;
       }
-      if (j & 1) cc.next(a, t);
+      S.mma(acc);
+      if (j & 1) cc.advance(a, t, G);
     }
   }
 #undef LSA_LOAD_TILE
+  // drain: tile J-2 (partial already taken) and tile J-1 (MFMAs in flight)
   lds_barrier();
-  if (h == 0) {
-    const int j = J;
-    const float x = pprev + xpart[(j - 1) & 1][n];
-    const uint32_t bits = (uint32_t)__ballot(vprev && x >= a.thr);
-    float* so = a.score[lprev];
-    if (so != nullptr && g == 0 && vprev) so[rprev] = 1.0f / (1.0f + __expf(-x));
-    if (lane == 0) a.mask[lprev][wprev] = (uint64_t)bits0 | ((uint64_t)bits << 32);  // J is even: tile J-1 is odd
+  {
+    float p = S.partial(acc);
+    p = sum_halves(p);
+    if constexpr (KT == KEY_FP8) p *= m1.scale;
+    if (h == 1) {
+      if (g == 0) xpart[(J - 1) & 1][n] = p;
+    } else {
+      if (J > 1) finish_tile(a, m2, p2 + xpart[(J - 2) & 1][n], (J - 2) & 1, bits0, lane, g);
+      p2 = p;
+    }
   }
+  lds_barrier();
+  if (h == 0) finish_tile(a, m1, p2 + xpart[(J - 1) & 1][n], (J - 1) & 1, bits0, lane, g);
 }
 
 // Gathered scoring for the top-k: y = sum_j w'_j ReLU(q'_j . K_s) for each s in
@@ -296,9 +359,11 @@ struct TileCursor {
   int32_t jt, nt;     // tile within sequence b, tiles of sequence b
   int64_t base;       // first row of sequence b (also where its list starts)
   int32_t cnt;        // entries in b's list
+  int32_t nrow;       // rows of sequence b
   __device__ __forceinline__ void load_seq(const TopkScoreArgs& a, const int32_t* tp) {
     nt = uni(tp[b + 1]) - uni(tp[b]);
     base = uni(a.key_off[b]);
+    nrow = (int32_t)(uni(a.key_off[b + 1]) - base);
     cnt = uni(a.count[b]);
   }
   __device__ __forceinline__ void place(const TopkScoreArgs& a, const int32_t* tp, int64_t t) {
@@ -325,7 +390,7 @@ struct TileCursor {
 template <int KT, int DH, int D>
 __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) {
   using IO = TileIO<KT, DH>;
-  using S_t = Scorer<KT == KEY_F32 ? KEY_F32 : KEY_BF16, DH, 1>;
+  using S_t = Scorer<KT == KEY_F32 ? KEY_F32 : KEY_BF16, DH, 1, TileIO<KT, DH>::ROT>;
   static_assert(IO::GRB == 16 * (IO::GRB / 16), "row size");
   __shared__ __attribute__((aligned(16))) char stage[2][IO::LSUB];
   __shared__ float xpart[2][32];
@@ -360,33 +425,49 @@ __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) 
   ic = xc;
   cc = xc;
 
-#define LSA_LOAD_IDX(SLOT)                                                                     \
+  // As in score_select, every slot issues its loads whether or not it is LIVE:
+  // a dead slot, or a list entry past the end of a list, reads out of range
+  // and gets zeros (list entry 0: row 0 of the sequence, whose score is
+  // dropped).
+#define LSA_LOAD_IDX(SLOT, LIVE)                                                                \
   do {                                                                                         \
-    const int32_t e_ = xc.jt * 32;                                                             \
-    const int32_t* il_ = a.idx + xc.base;                                                      \
-    _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i) IX[SLOT][i] = il_[min(e_ + lrow[i], xc.cnt - 1)]; \
-    if constexpr (KT == KEY_FP8) IXS[SLOT] = il_[min(e_ + n, xc.cnt - 1)];                     \
-    xc.next(a, tp);                                                                            \
+    const bool live_ = (LIVE);                                                                 \
+    const uint32_t e_ = (uint32_t)xc.jt * 32;                                                  \
+    const auto ri_ = buf_rsrc(a.idx + xc.base, (uint32_t)xc.cnt * 4);                          \
+    _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i)                                        \
+      IX[SLOT][i] = (int32_t)buf_load4(ri_, live_ ? (e_ + lrow[i]) * 4 : BUF_OOB);             \
+    if constexpr (KT == KEY_FP8) IXS[SLOT] = (int32_t)buf_load4(ri_, live_ ? (e_ + n) * 4 : BUF_OOB); \
+    if (live_) xc.next(a, tp);                                                                 \
   } while (0)
-#define LSA_LOAD_KEYS(SLOT, XSLOT)                                                             \
+#define LSA_LOAD_KEYS(SLOT, XSLOT, LIVE)                                                       \
   do {                                                                                         \
-    const char* kb_ = (const char*)a.keys[ic.l] + ic.base * IO::GRB;                           \
-    if (loads) {                                                                               \
-      _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i)                                      \
-        R[SLOT][i] = __builtin_nontemporal_load(                                               \
-            (const u32x4*)(kb_ + (int64_t)IX[XSLOT][i] * IO::GRB + lchunk[i] * 16));           \
+    const bool live_ = (LIVE);                                                                 \
+    const int kl_ = live_ ? ic.l : 0;                                                          \
+    const auto rk_ = buf_rsrc((const char*)a.keys[kl_] + ic.base * IO::GRB, (uint32_t)ic.nrow * IO::GRB); \
+    _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i)                                        \
+      R[SLOT][i] = buf_load16_nt(                                                              \
+          rk_, live_ && loads ? (uint32_t)IX[XSLOT][i] * IO::GRB + lchunk[i] * 16 : BUF_OOB);   \
+    if constexpr (KT == KEY_FP8) {                                                             \
+      const auto rs_ = buf_rsrc(a.scale[kl_] + ic.base, (uint32_t)ic.nrow * 4);                \
+      SC[SLOT] = __uint_as_float(buf_load4(rs_, live_ ? (uint32_t)IXS[XSLOT] * 4 : BUF_OOB));  \
     }                                                                                          \
-    if constexpr (KT == KEY_FP8) SC[SLOT] = a.scale[ic.l][ic.base + IXS[XSLOT]];               \
-    ic.next(a, tp);                                                                            \
+    if (live_) ic.next(a, tp);                                                                 \
   } while (0)
 
-  // prologue: indices for tiles 0 .. 2D-1, keys for tiles 0 .. D-1
+  // prologue: indices for tiles 0 .. 2D-1 and keys for tiles 0 .. D-1, issued
+  // in the order of the steady state (keys of tile s, then indices of tile
+  // s + D), so the waits in the loop are the same for every slot
 #pragma unroll
-  for (int s = 0; s < 2 * D; ++s)
-    if (s < J) LSA_LOAD_IDX(s);
+  for (int s = 0; s < D; ++s) {
+    LSA_LOAD_IDX(s, s < J);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
-  for (int s = 0; s < D; ++s)
-    if (s < J) LSA_LOAD_KEYS(s, s);
+  for (int s = 0; s < D; ++s) {
+    LSA_LOAD_KEYS(s, s, s < J);
+    LSA_LOAD_IDX(D + s, D + s < J);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   S_t S;
   int cur_l = -1, cur_b = -1;
@@ -394,14 +475,17 @@ __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) 
   bool vprev = false;
   int64_t oprev = 0;
 
-  for (int j0 = 0; j0 < J; j0 += 2 * D) {
+  // Whole groups of 2D slots, no early exit (see score_select): a slot past the
+  // last tile only issues its out-of-range refills.
+  const int NIT = (J + 2 * D - 1) / (2 * D);
+  for (int it = 0; it < NIT; ++it) {
 #pragma unroll
     for (int s = 0; s < 2 * D; ++s) {
-      const int j = j0 + s;
-      if (j >= J) break;
+      const int j = it * 2 * D + s;
+      const bool live = j < J;
       const int rs = s % D;  // register slot of tile j
       char* st = &stage[j & 1][0];
-      if (loads) {
+      if (live && loads) {
 #pragma unroll
         for (int i = 0; i < IO::NLW; ++i) {
           const int r = lrow[i];
@@ -411,17 +495,18 @@ __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) 
             const u32x2 b0 = e4m3x4_to_bf16x4(v[0]), b1 = e4m3x4_to_bf16x4(v[1]);
             const u32x2 b2 = e4m3x4_to_bf16x4(v[2]), b3 = e4m3x4_to_bf16x4(v[3]);
             const int c0 = 2 * lchunk[i], c1 = c0 + 1;
-            *(u32x4*)(rowp + ((c0 ^ (r % IO::LCPR)) * 16)) = u32x4{b0[0], b0[1], b1[0], b1[1]};
-            *(u32x4*)(rowp + ((c1 ^ (r % IO::LCPR)) * 16)) = u32x4{b2[0], b2[1], b3[0], b3[1]};
+            *(u32x4*)(rowp + lds_chunk<IO::LCPR, IO::ROT>(c0, r) * 16) = u32x4{b0[0], b0[1], b1[0], b1[1]};
+            *(u32x4*)(rowp + lds_chunk<IO::LCPR, IO::ROT>(c1, r) * 16) = u32x4{b2[0], b2[1], b3[0], b3[1]};
           } else {
-            *(u32x4*)(rowp + ((lchunk[i] ^ (r % IO::LCPR)) * 16)) = R[rs][i];
+            *(u32x4*)(rowp + lds_chunk<IO::LCPR, IO::ROT>(lchunk[i], r) * 16) = R[rs][i];
           }
         }
       }
       float scale = 1.0f;
       if constexpr (KT == KEY_FP8) scale = SC[rs];
-      if (j + D < J) LSA_LOAD_KEYS(rs, (s + D) % (2 * D));
-      if (j + 2 * D < J) LSA_LOAD_IDX(s);
+      LSA_LOAD_KEYS(rs, (s + D) % (2 * D), j + D < J);
+      LSA_LOAD_IDX(s, j + 2 * D < J);
+      if (!live) continue;
       lds_barrier();
       S.read_keys_lds(st);
       if (h == 0 && j > 0) {
@@ -436,7 +521,7 @@ __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) 
       f32x16 acc[1];
       S.mma(acc);
       float p = S.partial(acc);
-      p += __shfl_xor(p, 32);
+      p = sum_halves(p);
       if constexpr (KT == KEY_FP8) p *= scale;
       const int32_t e = cc.jt * 32 + n;
       if (h == 1) {
@@ -459,45 +544,69 @@ __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) 
 }
 
 // ------------------------------------------------------------------ launch
-template <int KT, int DH, int NHB>
-static hipError_t launch_score_t(const ScoreArgs& a, int pairs, hipStream_t st) {
-  // one block = one pair of waves; D tiles in flight per wave in registers
-  constexpr int D = TileIO<KT, DH>::GSUB > 8192 ? 2 : 4;
+// Tiles in flight per wave (D). The default keeps about 16 KiB of key loads in
+// flight per wave pair; `depth` > 0 overrides it for d_h = 128.
+template <int KT, int DH, int D>
+static hipError_t launch_score_d(const ScoreArgs& a, int pairs, hipStream_t st) {
   hipLaunchKernelGGL((score_select_kernel<KT, DH, D>), dim3(pairs), dim3(128), 0, st, a);
   return hipGetLastError();
 }
-template <int KT, int DH, int NHB>
-static hipError_t launch_tscore_t(const TopkScoreArgs& a, int pairs, hipStream_t st) {
-  constexpr int D = TileIO<KT, DH>::GSUB >= 8192 ? 2 : 4;
+template <int KT, int DH>
+static hipError_t launch_score_t(const ScoreArgs& a, int pairs, int depth, hipStream_t st) {
+  constexpr int DDEF = TileIO<KT, DH>::GSUB > 8192 ? 2 : 4;
+  if constexpr (DH == 128) {
+    switch (depth) {
+      case 1: return launch_score_d<KT, DH, 1>(a, pairs, st);
+      case 2: return launch_score_d<KT, DH, 2>(a, pairs, st);
+      case 4: return launch_score_d<KT, DH, 4>(a, pairs, st);
+      case 8: if constexpr (KT == KEY_FP8) return launch_score_d<KT, DH, 8>(a, pairs, st); break;
+      default: break;
+    }
+  }
+  return launch_score_d<KT, DH, DDEF>(a, pairs, st);
+}
+template <int KT, int DH, int D>
+static hipError_t launch_tscore_d(const TopkScoreArgs& a, int pairs, hipStream_t st) {
   hipLaunchKernelGGL((topk_score_kernel<KT, DH, D>), dim3(pairs), dim3(128), 0, st, a);
   return hipGetLastError();
 }
-
-#define LSA_DISPATCH(FN, KT_, DH_, NHB_, ...)                                       \
-  do {                                                                              \
-    if (KT_ == KEY_BF16) {                                                          \
-      if (DH_ == 128) return NHB_ == 1 ? FN<KEY_BF16, 128, 1>(__VA_ARGS__) : FN<KEY_BF16, 128, 2>(__VA_ARGS__); \
-      if (DH_ == 64) return NHB_ == 1 ? FN<KEY_BF16, 64, 1>(__VA_ARGS__) : FN<KEY_BF16, 64, 2>(__VA_ARGS__);    \
-      return NHB_ == 1 ? FN<KEY_BF16, 32, 1>(__VA_ARGS__) : FN<KEY_BF16, 32, 2>(__VA_ARGS__);                   \
-    } else if (KT_ == KEY_FP8) {                                                    \
-      if (DH_ == 128) return NHB_ == 1 ? FN<KEY_FP8, 128, 1>(__VA_ARGS__) : FN<KEY_FP8, 128, 2>(__VA_ARGS__);   \
-      if (DH_ == 64) return NHB_ == 1 ? FN<KEY_FP8, 64, 1>(__VA_ARGS__) : FN<KEY_FP8, 64, 2>(__VA_ARGS__);      \
-      return NHB_ == 1 ? FN<KEY_FP8, 32, 1>(__VA_ARGS__) : FN<KEY_FP8, 32, 2>(__VA_ARGS__);                     \
-    } else {                                                                        \
-      if (DH_ == 128) return NHB_ == 1 ? FN<KEY_F32, 128, 1>(__VA_ARGS__) : FN<KEY_F32, 128, 2>(__VA_ARGS__);   \
-      if (DH_ == 64) return NHB_ == 1 ? FN<KEY_F32, 64, 1>(__VA_ARGS__) : FN<KEY_F32, 64, 2>(__VA_ARGS__);      \
-      return NHB_ == 1 ? FN<KEY_F32, 32, 1>(__VA_ARGS__) : FN<KEY_F32, 32, 2>(__VA_ARGS__);                     \
-    }                                                                               \
-  } while (0)
-
-hipError_t launch_score_select(const ScoreArgs& a, int key_kind, int d_h, int pairs, hipStream_t st) {
-  const int nhb = a.n_h > 32 ? 2 : 1;
-  LSA_DISPATCH(launch_score_t, key_kind, d_h, nhb, a, pairs, st);
+template <int KT, int DH>
+static hipError_t launch_tscore_t(const TopkScoreArgs& a, int pairs, int depth, hipStream_t st) {
+  constexpr int DDEF = TileIO<KT, DH>::GSUB >= 8192 ? 2 : 4;
+  if constexpr (DH == 128) {
+    switch (depth) {
+      case 1: return launch_tscore_d<KT, DH, 1>(a, pairs, st);
+      case 2: return launch_tscore_d<KT, DH, 2>(a, pairs, st);
+      case 4: return launch_tscore_d<KT, DH, 4>(a, pairs, st);
+      default: break;
+    }
+  }
+  return launch_tscore_d<KT, DH, DDEF>(a, pairs, st);
 }
 
-hipError_t launch_topk_score(const TopkScoreArgs& a, int key_kind, int d_h, int grid, hipStream_t st) {
-  const int nhb = a.n_h > 32 ? 2 : 1;
-  LSA_DISPATCH(launch_tscore_t, key_kind, d_h, nhb, a, grid, st);
+#define LSA_DISPATCH(FN, KT_, DH_, ...)                                                   \
+  do {                                                                                    \
+    if (KT_ == KEY_BF16) {                                                                \
+      if (DH_ == 128) return FN<KEY_BF16, 128>(__VA_ARGS__);                              \
+      if (DH_ == 64) return FN<KEY_BF16, 64>(__VA_ARGS__);                                \
+      return FN<KEY_BF16, 32>(__VA_ARGS__);                                               \
+    } else if (KT_ == KEY_FP8) {                                                          \
+      if (DH_ == 128) return FN<KEY_FP8, 128>(__VA_ARGS__);                               \
+      if (DH_ == 64) return FN<KEY_FP8, 64>(__VA_ARGS__);                                 \
+      return FN<KEY_FP8, 32>(__VA_ARGS__);                                                \
+    } else {                                                                              \
+      if (DH_ == 128) return FN<KEY_F32, 128>(__VA_ARGS__);                               \
+      if (DH_ == 64) return FN<KEY_F32, 64>(__VA_ARGS__);                                 \
+      return FN<KEY_F32, 32>(__VA_ARGS__);                                                \
+    }                                                                                     \
+  } while (0)
+
+hipError_t launch_score_select(const ScoreArgs& a, int key_kind, int d_h, int pairs, int depth, hipStream_t st) {
+  LSA_DISPATCH(launch_score_t, key_kind, d_h, a, pairs, depth, st);
+}
+
+hipError_t launch_topk_score(const TopkScoreArgs& a, int key_kind, int d_h, int grid, int depth, hipStream_t st) {
+  LSA_DISPATCH(launch_tscore_t, key_kind, d_h, a, grid, depth, st);
 }
 
 }  // namespace lsa

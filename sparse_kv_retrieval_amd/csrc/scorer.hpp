@@ -17,7 +17,7 @@
 // half [g*d_h/2, (g+1)*d_h/2) of the head dimension. Each lane then reads one
 // contiguous half-row of its key (64..256 bytes) with 16-byte loads.
 //
-// Precision: bf16 keys (and fp8 keys, widened exactly to bf16) multiply a
+// Precision: bf16 keys (and fp8 keys, widened exactly to bf16 in LDS) multiply a
 // query split into bf16 hi + lo parts, which keeps about 16 bits of q, with
 // fp32 accumulation. fp32 keys use the fp32 MFMA directly.
 #pragma once
@@ -26,10 +26,11 @@
 
 namespace lsa {
 
-template <int KT, int DH, int NHB>
+template <int KT, int DH, int NHB, bool ROT = false>
 struct Scorer {
   static_assert(DH == 32 || DH == 64 || DH == 128, "d_h");
   static_assert(NHB == 1 || NHB == 2, "heads per block");
+  static_assert(KT == KEY_F32 || KT == KEY_BF16, "fp8 keys are widened to bf16 before the scorer");
   static constexpr int HALF = DH / 2;                         // k values per lane group
   static constexpr int ESZ = KT == KEY_F32 ? 4 : (KT == KEY_BF16 ? 2 : 1);
   static constexpr int ROW_BYTES = DH * ESZ;
@@ -87,8 +88,8 @@ struct Scorer {
       kraw[i] = valid ? __builtin_nontemporal_load((const u32x4*)p + i) : u32x4{0, 0, 0, 0};
   }
 
-  // Read this lane's half-row of a 32-row tile staged in LDS with the chunk
-  // swizzle used by the DMA (16-byte chunk c of row r stored at c ^ (r % CPR)).
+  // Read this lane's half-row of a 32-row tile staged in LDS in the layout of
+  // lds_chunk<CPR, ROT>.
   static constexpr int CPR = ROW_BYTES / 16;
   __device__ __forceinline__ void read_keys_lds(const char* tile) {
     const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
@@ -96,7 +97,7 @@ struct Scorer {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int c = g * (CPR / 2) + i;
-      kraw[i] = *(const u32x4*)(row + ((c ^ (n % CPR)) * 16));
+      kraw[i] = *(const u32x4*)(row + lds_chunk<CPR, ROT>(c, n) * 16);
     }
   }
 
@@ -107,20 +108,6 @@ struct Scorer {
 #pragma unroll
       for (int t = 0; t < STEPS; ++t) {
         const bf16x8 kb = as_bf16x8(kraw[t]);
-#pragma unroll
-        for (int mb = 0; mb < NHB; ++mb) {
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][t][0], kb, acc[mb], 0, 0, 0);
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][t][1], kb, acc[mb], 0, 0, 0);
-        }
-      }
-    } else if constexpr (KT == KEY_FP8) {
-#pragma unroll
-      for (int t = 0; t < STEPS; ++t) {
-        const u32x4 raw = kraw[t >> 1];
-        const int o = (t & 1) * 2;
-        const u32x2 lo = e4m3x4_to_bf16x4(raw[o]);
-        const u32x2 hi = e4m3x4_to_bf16x4(raw[o + 1]);
-        const bf16x8 kb = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
         for (int mb = 0; mb < NHB; ++mb) {
           acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][t][0], kb, acc[mb], 0, 0, 0);

@@ -79,13 +79,18 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
   // Key 0 pads the tail. It sorts below every real key (the smallest real key,
   // -inf, maps to 0x007FFFFF), so padding never reaches the selected bins or
   // the output, and the passes need no bounds test.
+  // Loads go in chunks of 8 with clamped addresses, so each chunk is one round trip.
   uint32_t key[TS_VMAX];
 #pragma unroll
-  for (int v = 0; v < TS_VMAX; ++v)
-    if (v < V) {
-      const int i = tid + TS_THREADS * v;
-      key[v] = i < M ? order_key(ys[i]) : 0u;
+  for (int c = 0; c < TS_VMAX; c += 8) {
+    if (c < V) {
+      float y[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) y[u] = ys[min(tid + TS_THREADS * (c + u), M - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) key[c + u] = (c + u < V && tid + TS_THREADS * (c + u) < M) ? order_key(y[u]) : 0u;
     }
+  }
 
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t tab[TS_VMAX * NW], tab2[TS_VMAX * NW];
@@ -130,19 +135,39 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
     }
   __syncthreads();
   table_exclusive_scan(tab2, V * NW);
+  // output in chunks of 8: positions first, then all the loads, then all the stores
 #pragma unroll
-  for (int v = 0; v < TS_VMAX; ++v)
-    if (v < V) {
-      const uint64_t meq = __ballot(key[v] == T);
-      const bool take = key[v] > T || (key[v] == T && tab[v * NW + w] + lanes_below(meq) < krem);
-      const uint64_t mt = __ballot(take);
-      if (take) {
-        const int i = tid + TS_THREADS * v;
-        const uint32_t pos = tab2[v * NW + w] + lanes_below(mt);
-        out[pos] = idx[i];
-        if (outs) outs[pos] = ys[i];
+  for (int c = 0; c < TS_VMAX; c += 8) {
+    if (c < V) {
+      int32_t pos[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int v = c + u;
+        pos[u] = -1;
+        if (v < V) {
+          const uint64_t meq = __ballot(key[v] == T);
+          const bool take = key[v] > T || (key[v] == T && tab[v * NW + w] + lanes_below(meq) < krem);
+          const uint64_t mt = __ballot(take);
+          if (take) pos[u] = (int32_t)(tab2[v * NW + w] + lanes_below(mt));
+        }
+      }
+      int32_t iv[8];
+      float yv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = min(tid + TS_THREADS * (c + u), M - 1);
+        iv[u] = pos[u] >= 0 ? idx[i] : 0;
+        yv[u] = (outs && pos[u] >= 0) ? ys[i] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (pos[u] >= 0) {
+          out[pos[u]] = iv[u];
+          if (outs) outs[pos[u]] = yv[u];
+        }
       }
     }
+  }
 }
 
 // Radix select that re-reads the scores from memory on every pass (lists of

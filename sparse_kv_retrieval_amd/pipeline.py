@@ -30,13 +30,20 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(a).to(device)
 
 
+GUARD_BYTES = 4096
+CANARY = 0x5A
+
+
 class Pipeline:
-    def __init__(self, inp, device="cuda", *, with_scores=False, with_topk_scores=True, gather_capacity=None):
+    def __init__(self, inp, device="cuda", *, with_scores=False, with_topk_scores=True, gather_capacity=None,
+                 guard=False):
         w = inp.workload
         self.w = w
         self.inp = inp
         dev = torch.device(device)
         self.device = dev
+        self._guarded = []
+        self.guard = guard
         B, L = w.B, w.L
         self.rows = int(inp.key_offsets[-1])
         self.words = int(inp.mask_word_offsets[-1])
@@ -52,25 +59,48 @@ class Pipeline:
         self.scale = [None if inp.key_scale[l] is None else _dev(inp.key_scale[l], dev) for l in range(L)]
         self.pool = None if inp.pool is None else _dev(inp.pool, dev)
 
-        f32 = dict(dtype=torch.float32, device=dev)
-        i32 = dict(dtype=torch.int32, device=dev)
+        f32, i32, i64, i16 = torch.float32, torch.int32, torch.int64, torch.int16
+        out = self._out
         # 2L projection outputs: first L for the memory indexer, next L for the native indexer
-        self.c = [torch.empty(B, w.r, **f32) for _ in range(2 * L)]
-        self.q = [torch.empty(B, w.n_h, w.d_h, **f32) for _ in range(2 * L)]
-        self.g = [torch.empty(B, w.n_h, **f32) for _ in range(2 * L)]
-        self.masks = [torch.empty(max(self.words, 1), dtype=torch.int64, device=dev) for _ in range(L)]
-        self.scores = [torch.empty(max(self.rows, 1), **f32) for _ in range(L)] if with_scores else None
-        self.idx = torch.empty(max(self.rows, 1), **i32)
-        self.count = torch.empty(B, **i32)
-        self.union_mask = torch.empty(max(self.words, 1), dtype=torch.int64, device=dev)
-        self.topk_idx = [torch.empty(B, w.k, **i32) for _ in range(L)]
-        self.topk_score = [torch.empty(B, w.k, **f32) for _ in range(L)] if with_topk_scores else None
-        self.topk_count = torch.empty(L, B, **i32)
+        self.c = [out((B, w.r), f32) for _ in range(2 * L)]
+        self.q = [out((B, w.n_h, w.d_h), f32) for _ in range(2 * L)]
+        self.g = [out((B, w.n_h), f32) for _ in range(2 * L)]
+        self.masks = [out((max(self.words, 1),), i64) for _ in range(L)]
+        self.scores = [out((max(self.rows, 1),), f32) for _ in range(L)] if with_scores else None
+        self.idx = out((max(self.rows, 1),), i32)
+        self.count = out((B,), i32)
+        self.union_mask = out((max(self.words, 1),), i64)
+        self.topk_idx = [out((B, w.k), i32) for _ in range(L)]
+        self.topk_score = [out((B, w.k), f32) for _ in range(L)] if with_topk_scores else None
+        self.topk_count = out((L, B), i32)
         ws = lsa.topk_workspace_size(L, B, self.rows, w.k)
-        self.workspace = torch.empty(max(ws, 4), dtype=torch.uint8, device=dev)
+        self.workspace = out((max(ws, 4),), torch.uint8)
         self.gather_capacity = self.rows if gather_capacity is None else int(gather_capacity)
         if self.pool is not None:
-            self.gathered = torch.empty(max(self.gather_capacity, 1), w.pool_dim, dtype=torch.int16, device=dev)
+            self.gathered = out((max(self.gather_capacity, 1), w.pool_dim), i16)
+
+    def _out(self, shape, dtype):
+        """An output buffer. With guard=True it sits between two GUARD_BYTES canary bands."""
+        n = 1
+        for s_ in shape:
+            n *= int(s_)
+        if not self.guard:
+            return torch.empty(shape, dtype=dtype, device=self.device)
+        esz = torch.empty(0, dtype=dtype).element_size()
+        nbytes = n * esz
+        raw = torch.full((GUARD_BYTES + nbytes + GUARD_BYTES,), CANARY, dtype=torch.uint8, device=self.device)
+        self._guarded.append((raw, nbytes))
+        return raw[GUARD_BYTES:GUARD_BYTES + nbytes].view(dtype).view(shape)
+
+    def check_guards(self):
+        """Return the indices of output buffers whose canary bands were written."""
+        bad = []
+        for i, (raw, nbytes) in enumerate(self._guarded):
+            head = raw[:GUARD_BYTES]
+            tail = raw[GUARD_BYTES + nbytes:]
+            if not (bool((head == CANARY).all()) and bool((tail == CANARY).all())):
+                bad.append(i)
+        return bad
 
     # ------------------------------------------------------------- stages
     def project(self, stream=None):

@@ -47,9 +47,10 @@ def test_small_parity(case, torch_cuda):
     w = SMALL[case]
     P.say(f"[parity] case={case} B={w.B} L={w.L} N={w.N} dtype={w.key_dtype} n_h={w.n_h} d_h={w.d_h} k={w.k}")
     inp = synth.make(w)
-    p = Pipeline(inp, "cuda", with_scores=True)
+    p = Pipeline(inp, "cuda", with_scores=True, guard=True)
     p.run()
     torch_cuda.cuda.synchronize()
+    assert p.check_guards() == [], f"writes outside an output buffer: {p.check_guards()}"
     st, counts = P.full_check(p, inp)
     P.say(f"[parity] case={case} ok counts={counts.tolist()} band={st['band']} "
           f"band_mismatch={st['mismatch_in_band']} max_dI={st['max_dI']:.2e}")
@@ -80,9 +81,10 @@ def _full_sampled(name, torch_cuda, sample=2048):
     P.say(f"[full] case={name}: generating")
     inp = synth.make(w)
     P.say(f"[full] case={name}: rows={int(inp.key_offsets[-1])} running")
-    p = Pipeline(inp, "cuda", with_scores=True)
+    p = Pipeline(inp, "cuda", with_scores=True, guard=True)
     p.run()
     torch_cuda.cuda.synchronize()
+    assert p.check_guards() == [], f"writes outside an output buffer: {p.check_guards()}"
     P.say(f"[full] case={name}: checking")
     rng = np.random.default_rng(0)
     masks = [p.masks_bool(l) for l in range(w.L)]
