@@ -30,8 +30,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_select_traffic.json")
-SCORE_SOURCES = ["score.hip", "scorer.hpp", "common.hpp", "kernels.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_select_traffic_three_layer_b8.txt")
+# what the score_select kernel is built from: a change to any of these invalidates the measured traffic
+SCORE_SOURCES = ["csrc/score.hip", "csrc/scorer.hpp", "csrc/common.hpp", "csrc/kernels.hpp", "build.py"]
 
 
 def log(*a):
@@ -41,9 +42,27 @@ def log(*a):
 def score_source_hash() -> str:
     h = hashlib.sha256()
     for s in SCORE_SOURCES:
-        with open(os.path.join(ROOT, "sparse_kv_retrieval_amd", "csrc", s), "rb") as f:
+        with open(os.path.join(ROOT, "sparse_kv_retrieval_amd", s), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per score_select launch from the committed PMC summary, if it was taken on these sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith(("#", " ", "|", "`")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != score_source_hash() or kv.get("workload") != workload:
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def algorithmic_bytes(w, lengths) -> dict:
@@ -140,12 +159,7 @@ def main():
     score_s = stage_ms["score_select"] / 1e3
     achieved = ab["bytes_per_launch"] / score_s / 1e9
 
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("source_hash") == score_source_hash() and tr.get("workload") == w.name:
-            traffic = tr.get("traffic_bytes_per_launch")
+    traffic = read_traffic(w.name)
 
     out = {
         "metric": "compressed entries scored+selected/sec and HBM GB/s at N=125K (1 GPU)",

@@ -1,0 +1,137 @@
+"""Helpers for the rocprofv3 evidence of the selection path.
+
+Usage (each step's output is plain text, suitable for a short summary file):
+
+  python -m sparse_kv_retrieval_amd.profiling copy --mib 1024 --reps 5
+      Device-to-device copy of a known size, to calibrate the HBM byte
+      counters: run it under `rocprofv3 --pmc FETCH_SIZE` (then WRITE_SIZE)
+      and compare the counter with the bytes the copy must move.
+
+  python -m sparse_kv_retrieval_amd.profiling stats <dir>
+      Per-kernel call count and average / min / max duration from a
+      `rocprofv3 --kernel-trace --output-format csv` run (its
+      *_kernel_trace.csv), as a markdown table.
+
+  python -m sparse_kv_retrieval_amd.profiling pmc <dir> [--kernel REGEX]
+      Average value per dispatch of every counter in a `rocprofv3 --pmc`
+      run (its *_counter_collection.csv), per kernel.
+
+  python -m sparse_kv_retrieval_amd.profiling traffic --fetch <dir> --write <dir>
+      --copy-fetch <dir> --copy-write <dir> --copy-mib M --kernel REGEX
+      HBM bytes per dispatch of one kernel: FETCH_SIZE and WRITE_SIZE (KiB
+      per dispatch) divided by what the same counters read per byte for the
+      plain copy of M MiB.
+
+Nothing here launches the selection kernels; the copy uses torch.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import os
+import re
+import statistics
+import sys
+from collections import defaultdict
+
+
+def _one(pattern: str) -> str:
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def kernel_stats(run_dir: str) -> list[dict]:
+    """Per-kernel durations (ns) from a kernel-trace csv."""
+    path = _one(os.path.join(run_dir, "**", "*kernel_trace.csv"))
+    durs = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            durs[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = []
+    for name, d in durs.items():
+        out.append({"kernel": name, "calls": len(d), "avg_us": statistics.mean(d) / 1e3,
+                    "min_us": min(d) / 1e3, "max_us": max(d) / 1e3, "total_us": sum(d) / 1e3})
+    out.sort(key=lambda x: -x["total_us"])
+    return out
+
+
+def pmc_means(run_dir: str, kernel: str | None = None) -> dict:
+    """{(kernel, counter): mean value per dispatch} from a counter-collection csv."""
+    path = _one(os.path.join(run_dir, "**", "*counter_collection.csv"))
+    vals = defaultdict(list)
+    rx = re.compile(kernel) if kernel else None
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if rx and not rx.search(r["Kernel_Name"]):
+                continue
+            vals[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+    return {k: (statistics.mean(v), len(v)) for k, v in vals.items()}
+
+
+def _counter(run_dir: str, kernel: str, counter: str) -> float:
+    m = {k: v for k, v in pmc_means(run_dir, kernel).items() if k[1] == counter}
+    if not m:
+        raise KeyError(f"{counter} for /{kernel}/ not in {run_dir}")
+    if len(m) > 1:
+        raise KeyError(f"/{kernel}/ matches several kernels: {[k[0] for k in m]}")
+    return next(iter(m.values()))[0]
+
+
+def copy_run(mib: int, reps: int) -> None:
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {mib} MiB x {reps}", flush=True)
+
+
+def main(argv=None) -> None:
+    ap = argparse.ArgumentParser(prog="python -m sparse_kv_retrieval_amd.profiling")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("copy")
+    c.add_argument("--mib", type=int, default=1024)
+    c.add_argument("--reps", type=int, default=5)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    p = sub.add_parser("pmc")
+    p.add_argument("dir")
+    p.add_argument("--kernel")
+    t = sub.add_parser("traffic")
+    for k in ("fetch", "write", "copy_fetch", "copy_write", "kernel"):
+        t.add_argument("--" + k.replace("_", "-"), required=True)
+    t.add_argument("--copy-mib", type=int, required=True)
+    a = ap.parse_args(argv)
+
+    if a.cmd == "copy":
+        copy_run(a.mib, a.reps)
+    elif a.cmd == "stats":
+        print("| kernel | calls | avg us | min us | max us |")
+        print("|---|---:|---:|---:|---:|")
+        for r in kernel_stats(a.dir):
+            print(f"| `{r['kernel'][:90]}` | {r['calls']} | {r['avg_us']:.1f} | {r['min_us']:.1f} | {r['max_us']:.1f} |")
+    elif a.cmd == "pmc":
+        for (k, ctr), (v, n) in sorted(pmc_means(a.dir, a.kernel).items()):
+            print(f"{k[:90]}\t{ctr}\t{v:.1f}\t(n={n})")
+    else:
+        copy_bytes = a.copy_mib << 20
+        cf = _counter(a.copy_fetch, r"copyBuffer", "FETCH_SIZE") * 1024 / copy_bytes
+        cw = _counter(a.copy_write, r"copyBuffer", "WRITE_SIZE") * 1024 / copy_bytes
+        kf = _counter(a.fetch, a.kernel, "FETCH_SIZE") * 1024
+        kw = _counter(a.write, a.kernel, "WRITE_SIZE") * 1024
+        print(f"copy calibration: FETCH_SIZE reads {cf:.4f} x the copied bytes, WRITE_SIZE {cw:.4f} x")
+        print(f"kernel /{a.kernel}/: FETCH_SIZE {kf / 1e6:.2f} MB, WRITE_SIZE {kw / 1e6:.2f} MB per dispatch (raw)")
+        print(f"traffic_bytes_per_launch: {kf / cf + kw / cw:.0f}")
+        print(f"fetch_bytes_per_launch: {kf / cf:.0f}")
+        print(f"write_bytes_per_launch: {kw / cw:.0f}")
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
