@@ -110,6 +110,8 @@ def check_topk(p, inp, ref, lists):
     tk_idx = [t.cpu().numpy() for t in p.topk_idx]
     tk_sc = None if p.topk_score is None else [t.cpu().numpy() for t in p.topk_score]
     tk_cnt = p.topk_count.cpu().numpy()
+    # the GPU's fp32 score of every union entry, in list order: [l, key_offsets[b] + i]
+    ws = p.workspace[: 4 * w.L * p.rows].cpu().numpy().view(np.float32).reshape(w.L, p.rows)
     for b in ref:
         idx = lists[b]
         s0, s1 = int(inp.key_offsets[b]), int(inp.key_offsets[b + 1])
@@ -126,6 +128,10 @@ def check_topk(p, inp, ref, lists):
             got = got[:n].astype(np.int64)
             assert np.all(np.diff(got) > 0), "top-k output not ascending"
             assert np.all(np.isin(got, idx)), "top-k picked an entry outside the subset"
+            # The integer decision, in the GPU's own precision: its list is exactly the (-y, s)
+            # top-k of its own fp32 scores (ties to the lower index).
+            y_gpu = ws[l, s0:s0 + M].astype(np.float64)
+            assert np.array_equal(got, O.topk(y_gpu, idx, w.k)), f"top-k vs own scores l={l} b={b}"
             if M > w.k:
                 kth = np.sort(y)[::-1][w.k - 1]
                 yv = dict(zip(idx.tolist(), y.tolist()))
