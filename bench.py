@@ -11,6 +11,8 @@ Infinity Cache.
 
 Output: one JSON line. `value` is entries scored+selected per second over the
 whole step (sum over layers and sequences of N_b, divided by the step time).
+Whole steps are timed as replays of one HIP graph holding the five calls;
+`ms_per_step_eager` is the same step launched call by call.
 `roofline` describes the dominant kernel (score_select), from HIP events on
 its stream. `cpu_baseline` is the CPU oracle on a bounded sample of the same
 workload.
@@ -134,9 +136,10 @@ def main():
         p.run()
     torch.cuda.synchronize()
 
+    # Per-stage launch durations: eager calls with HIP events between them, on the launch stream.
     names = ["project", "score_select", "union_compact", "topk", "gather"]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps")
+    log(f"[bench] timing {args.steps} eager steps (per stage)")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -148,10 +151,21 @@ def main():
         p.topk(); e[4].record(stream)
         p.gather(); e[5].record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step_eager = (time.perf_counter() - t0) * 1e3 / args.steps
     stage_ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
                 for i, n in enumerate(names)}
+
+    # Whole steps: the same five calls captured once in a HIP graph, replayed K times.
+    graph = p.capture()
+    for _ in range(args.warmup):
+        graph.replay()
+    log(f"[bench] timing {args.steps} graph-replayed steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
     counts = p.count.cpu().numpy()
     rows = int(inp.key_offsets[-1])
@@ -183,6 +197,7 @@ def main():
                      "bytes_per_launch": ab["bytes_per_launch"], "per_entry_bytes": ab["per_entry_bytes"],
                      "avg_launch_us": stage_ms["score_select"] * 1e3},
         "stages_us": {k: v * 1e3 for k, v in stage_ms.items()},
+        "ms_per_step_eager": ms_per_step_eager,
         "selection": {"union_fraction": float(counts.sum()) / rows, "union_per_seq_mean": float(counts.mean())},
     }
     if not args.no_cpu_baseline:

@@ -150,6 +150,36 @@ class Pipeline:
         self.topk(stream)
         self.gather(stream)
 
+    def capture(self):
+        """Record one run() into a HIP graph and return it (replay with .replay()).
+
+        run() allocates nothing and clears nothing with memset, so the graph holds
+        exactly the kernel launches of the five calls, with these buffers baked in.
+        """
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run()
+        torch.cuda.synchronize()
+        return g
+
+    def outputs(self):
+        """Every output buffer of run(), for comparisons between runs."""
+        out = self.c + self.q + self.g + self.masks + [self.idx, self.count, self.union_mask, self.topk_count]
+        out += self.topk_idx
+        if self.scores is not None:
+            out += self.scores
+        if self.topk_score is not None:
+            out += self.topk_score
+        if self.pool is not None:
+            out.append(self.gathered)
+        return out
+
     # ------------------------------------------------------------- readback
     def masks_bool(self, l):
         """Unpack layer l's mask words into one bool array per sequence."""

@@ -74,6 +74,38 @@ def test_repeat_is_deterministic(torch_cuda):
         assert torch_cuda.equal(a, b)
 
 
+@pytest.mark.gpu
+def test_graph_replay_matches_eager(torch_cuda):
+    """The whole path captured in one HIP graph: every replay equals the eager run bit for bit."""
+    from sparse_kv_retrieval_amd.pipeline import Pipeline
+    w = SMALL["three_layer_mixed"]
+    P.say("[parity] graph replay")
+    inp = synth.make(w)
+    p = Pipeline(inp, "cuda", with_scores=True)
+    p.run()
+    torch_cuda.cuda.synchronize()
+
+    def written():
+        # the parts of the outputs a run writes: union lists hold count_b entries per region,
+        # the gathered buffer holds sum(count) rows; everything else is written in full
+        counts = p.count.cpu().numpy()
+        parts = [t for t in p.outputs() if t is not p.idx and t is not getattr(p, "gathered", None)]
+        parts += [p.idx[int(p.key_off_h[b]): int(p.key_off_h[b]) + int(counts[b])] for b in range(w.B)]
+        parts.append(p.gathered[: int(counts.sum())])
+        return [t.clone() for t in parts]
+
+    want = written()
+    g = p.capture()
+    for rep in range(3):
+        for t in p.outputs():  # eager work between replays: overwrite every output
+            t.view(torch_cuda.uint8).fill_(0xA5 if rep % 2 else 0x3C)
+        torch_cuda.cuda.synchronize()
+        g.replay()
+        torch_cuda.cuda.synchronize()
+        for a, b in zip(written(), want):
+            assert torch_cuda.equal(a, b), f"replay {rep} differs"
+
+
 def _full_sampled(name, torch_cuda, sample=2048):
     from oracle import lsa_oracle as O
     from sparse_kv_retrieval_amd.pipeline import Pipeline
