@@ -8,6 +8,7 @@
  * of the same report (section "方法", cited as [HYPER]). The steps are:
  *
  *   lsa_project        c = h W^DQ, q = c W^IUQ, w = h W^w        [BLOG] §3.1
+ *   (lsa_project_packed, the same with weights packed once by lsa_pack_weights)
  *   lsa_score_select   I_s = sigma(sum_j w_j ReLU(q_j . K_s)), keep I_s >= theta
  *                                                                [BLOG] §3.1
  *   lsa_union_compact  OR over the indexer layers, ascending index list
@@ -102,6 +103,40 @@ typedef struct {
 lsa_status lsa_project(const lsa_proj_layer* layers /* host [L] */, int32_t L, int32_t B,
                        int32_t d, int32_t r, int32_t n_h, int32_t d_h, lsa_dtype dtype,
                        hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * lsa_pack_weights / lsa_project_packed: the same projection ([BLOG] §3.1)
+ * with bf16 weights stored once in the layout the matrix cores read.
+ *
+ * The projection weights are constants of the model, so they can be
+ * rearranged once (at load time) into a layout where every 1 KiB is one
+ * wave's operand of one 16x16x32 MFMA step. A matrix of `rows` x K (out x in,
+ * as for lsa_project) becomes ceil(rows/16) x (K/32) blocks of 1 KiB; block
+ * (rb, ch) holds rows 16rb..16rb+15 and columns 32ch..32ch+31, and its
+ * 16-byte unit l = 16*kg + m is row 16rb+m, columns 32ch+8kg .. 32ch+8kg+7.
+ * Rows past the end are zero.
+ *
+ * lsa_pack_weights_size returns the bytes of the packed form of a rows x K
+ * bf16 matrix (0 if K is not a positive multiple of 32 or rows < 1).
+ * lsa_pack_weights writes it: w is dev [rows, K] bf16 (16-byte aligned),
+ * out is dev memory of out_bytes >= lsa_pack_weights_size(rows, K). The
+ * packed size must stay below 2^31 bytes. Pack W^DQ as (r, d), W^IUQ as
+ * (n_h*d_h, r) and W^w as (n_h, d).
+ *
+ * lsa_project_packed takes lsa_proj_layer entries whose w_dq, w_iuq and w_w
+ * point to packed matrices, and bf16 h. It computes the same c, q and w as
+ * lsa_project (fp32 accumulation, c split into bf16 hi + lo for the second
+ * product); the order of the fp32 sums differs, so results agree to rounding.
+ * Supported: 1 <= B <= 32; d a multiple of 32; r a multiple of 64; n_h*d_h a
+ * multiple of 64; 1 <= n_h <= LSA_MAX_HEADS. Errors as for lsa_project.
+ * ---------------------------------------------------------------------- */
+size_t lsa_pack_weights_size(int32_t rows, int32_t K);
+
+lsa_status lsa_pack_weights(const void* w /* dev [rows, K] bf16 */, int32_t rows, int32_t K,
+                            void* out /* dev */, size_t out_bytes, hipStream_t stream);
+
+lsa_status lsa_project_packed(const lsa_proj_layer* layers /* host [L] */, int32_t L, int32_t B,
+                              int32_t d, int32_t r, int32_t n_h, int32_t d_h, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * lsa_score_select: the lookahead index score and the loading rule

@@ -139,6 +139,51 @@ lsa_status lsa_project(const lsa_proj_layer* layers, int32_t L, int32_t B, int32
   return e == hipSuccess ? LSA_OK : hip_fail("lsa_project launch", e);
 }
 
+size_t lsa_pack_weights_size(int32_t rows, int32_t K) {
+  if (rows < 1 || K < 32 || K % 32) return 0;
+  return (size_t)((rows + 15) / 16) * (size_t)(K / 32) * 1024;
+}
+
+lsa_status lsa_pack_weights(const void* w, int32_t rows, int32_t K, void* out, size_t out_bytes, hipStream_t stream) {
+  if (!w || !out) return fail(LSA_ERR_INVALID_ARG, "w and out must be set");
+  if (rows < 1 || K < 32 || K % 32) return fail(LSA_ERR_UNSUPPORTED, "rows >= 1 and K a positive multiple of 32 (got %d x %d)", rows, K);
+  if (!aligned16(w) || !aligned16(out)) return fail(LSA_ERR_INVALID_ARG, "w and out must be 16-byte aligned");
+  const size_t need = lsa_pack_weights_size(rows, K);
+  if (need > (size_t)INT32_MAX) return fail(LSA_ERR_UNSUPPORTED, "packed matrix of %zu bytes (> 2^31-1)", need);
+  if (out_bytes < need) return fail(LSA_ERR_INVALID_ARG, "out holds %zu bytes, packing needs %zu", out_bytes, need);
+  const hipError_t e = launch_pack_weights(w, rows, K, out, stream);
+  return e == hipSuccess ? LSA_OK : hip_fail("lsa_pack_weights launch", e);
+}
+
+lsa_status lsa_project_packed(const lsa_proj_layer* layers, int32_t L, int32_t B, int32_t d, int32_t r, int32_t n_h,
+                              int32_t d_h, hipStream_t stream) {
+  if (!layers) return fail(LSA_ERR_INVALID_ARG, "layers is NULL");
+  if (L < 1 || L > LSA_MAX_LAYERS) return fail(LSA_ERR_INVALID_ARG, "L must be in [1, %d] (got %d)", LSA_MAX_LAYERS, L);
+  if (B < 1 || B > 32) return fail(LSA_ERR_UNSUPPORTED, "B must be in [1, 32] for packed weights (got %d)", B);
+  if (d < 32 || d % 32 || r < 64 || r % 64)
+    return fail(LSA_ERR_UNSUPPORTED, "d must be a positive multiple of 32 and r of 64 (got d=%d r=%d)", d, r);
+  if (n_h < 1 || n_h > LSA_MAX_HEADS || d_h < 1) return fail(LSA_ERR_UNSUPPORTED, "bad head shape n_h=%d d_h=%d", n_h, d_h);
+  if ((int64_t)n_h * d_h % 64) return fail(LSA_ERR_UNSUPPORTED, "n_h*d_h must be a multiple of 64");
+  if (lsa_pack_weights_size(n_h * d_h, r) > (size_t)INT32_MAX || lsa_pack_weights_size(r, d) > (size_t)INT32_MAX ||
+      (int64_t)B * d * 2 > INT32_MAX || (int64_t)B * r * 4 > INT32_MAX)
+    return fail(LSA_ERR_UNSUPPORTED, "a packed matrix or an activation exceeds 2^31-1 bytes");
+  ProjArgs a{};
+  for (int l = 0; l < L; ++l) {
+    const lsa_proj_layer& p = layers[l];
+    if (!p.h || !p.w_dq || !p.w_iuq || !p.w_w || !p.c_out || !p.q_out || !p.w_out)
+      return fail(LSA_ERR_INVALID_ARG, "layer %d: a pointer is NULL", l);
+    if (!aligned16(p.h) || !aligned16(p.w_dq) || !aligned16(p.w_iuq) || !aligned16(p.w_w) || !aligned16(p.c_out))
+      return fail(LSA_ERR_INVALID_ARG, "layer %d: h, the packed weights and c_out must be 16-byte aligned", l);
+    if ((const void*)p.c_out == (const void*)p.q_out || (const void*)p.c_out == (const void*)p.w_out)
+      return fail(LSA_ERR_INVALID_ARG, "layer %d: c_out aliases another output", l);
+    a.h[l] = p.h; a.w_dq[l] = p.w_dq; a.w_iuq[l] = p.w_iuq; a.w_w[l] = p.w_w;
+    a.c[l] = p.c_out; a.q[l] = p.q_out; a.w[l] = p.w_out;
+  }
+  a.B = B; a.d = d; a.r = r; a.n_h = n_h; a.d_h = d_h;
+  const hipError_t e = launch_project_packed(a, L, stream);
+  return e == hipSuccess ? LSA_OK : hip_fail("lsa_project_packed launch", e);
+}
+
 lsa_status lsa_score_select(const lsa_score_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
                             const int64_t* key_offsets_host, const int64_t* mask_word_offsets,
                             const int64_t* mask_word_offsets_host, int32_t n_h, int32_t d_h, lsa_dtype key_dtype,

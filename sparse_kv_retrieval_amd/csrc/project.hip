@@ -1,6 +1,12 @@
 // Indexer query projection ([BLOG] §3.1 of the FlashMemory-DeepSeek-V4
 // write-up): c = h W^DQ (rank r), q = c W^IUQ, w = h W^w.
 //
+// Two forms. project_kernel reads the weights in their plain "out x in"
+// layout (lsa_project). project_packed_kernel reads weights rearranged once
+// into the MFMA operand layout (lsa_pack_weights, lsa_project_packed), so each
+// weight load is one contiguous 1 KiB wave access; it is the faster form for
+// bf16. The notes below describe the plain form.
+//
 // These are GEMMs with a tiny M (the batch of sequences, B <= 128) and large
 // weights. Their cost is streaming the weights from HBM once. The weights use
 // the "out x in" layout, so each output row's weights are contiguous along the
@@ -196,6 +202,158 @@ __global__ __launch_bounds__(PJ_THREADS) void project_kernel(const ProjArgs a) {
   }
 }
 
+// bf16 weights in the packed operand layout (lsa_pack_weights). A matrix of
+// `rows` x K (out x in) is stored as ceil(rows/16) x (K/32) blocks of 1 KiB.
+// Block (rb, ch) holds rows 16rb..16rb+15 and columns 32ch..32ch+31 in lane
+// order: lane l = 16kg + m owns the 16 bytes of row 16rb+m, columns
+// 32ch+8kg..32ch+8kg+7, which is exactly its A operand of the 16x16x32 MFMA.
+// Rows past the end are zero. Every weight load is then one contiguous 1 KiB
+// wave access, and a wave walking along K streams contiguous memory.
+//
+// W waves per block split the reduction. Each wave streams its slice of K in
+// batches of KU chunks, double-buffered: batch i+1's loads are in flight while
+// batch i's MFMAs run. Every load is a raw buffer load issued on every path:
+// row groups past the end, sequences past B and chunks past the wave's slice
+// read out of range as zeros, which add nothing to the MFMA sums. A block's
+// rows lie in one weight matrix (W^DQ or W^w), so its buffer resource is
+// uniform. The W partial sums are added through LDS in wave order, so the
+// result does not depend on timing.
+template <bool UP, int MB, int NB, int W, int KU>
+__global__ __launch_bounds__(64 * W) void project_packed_kernel(const ProjArgs a) {
+  constexpr int KCH = 32;                 // k per MFMA
+  constexpr int COLS = UP ? 8 : 16;       // sequences per column block (UP: 8 hi + 8 lo columns)
+  constexpr int BV = UP ? 2 : 1;          // 16-byte B loads per chunk (UP: 8 fp32 of c)
+  __shared__ f32x4 red[W - 1][MB][NB][64];
+
+  const int l = blockIdx.y;
+  const int lane = threadIdx.x & 63, m = lane & 15, kg = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int K = UP ? a.r : a.d;
+  const int rows = UP ? a.n_h * a.d_h : a.r + a.n_h;
+  const int rb = blockIdx.x * 16 * MB;
+
+  // packed weight matrix of this block, and this lane's offsets in it
+  const bool gate_rows = !UP && rb >= a.r;
+  const char* wbase = UP ? (const char*)a.w_iuq[l] : gate_rows ? (const char*)a.w_w[l] : (const char*)a.w_dq[l];
+  const int r0 = gate_rows ? a.r : 0;
+  const int nrb = ((UP ? rows : gate_rows ? a.n_h : a.r) + 15) / 16;  // 16-row blocks of the matrix
+  const int chunks = K / KCH;
+  const auto ra = buf_rsrc(wbase, (uint32_t)nrb * chunks * 1024);
+  uint32_t aoff[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int rbk = (rb - r0) / 16 + mb;
+    aoff[mb] = rbk < nrb ? (uint32_t)rbk * chunks * 1024 + 16 * lane : BUF_OOB;
+  }
+  // B operand: h (bf16) or c (fp32), one row per sequence
+  const auto rbuf = UP ? buf_rsrc(a.c[l], (uint32_t)a.B * a.r * 4) : buf_rsrc(a.h[l], (uint32_t)a.B * a.d * 2);
+  uint32_t boff[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+    const int seq = cb * COLS + (UP ? (m & 7) : m);
+    boff[cb] = seq < a.B ? (UP ? (uint32_t)seq * a.r * 4 + 32 * kg : (uint32_t)seq * a.d * 2 + 16 * kg) : BUF_OOB;
+  }
+
+  const int c0 = wv * chunks / W, c1 = (wv + 1) * chunks / W;
+  const int nbat = (c1 - c0 + KU - 1) / KU;
+
+  u32x4 A0[KU][MB], A1[KU][MB], B0[KU][NB][BV], B1[KU][NB][BV];
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) acc[mb][cb] = f32x4{0, 0, 0, 0};
+
+#define LSA_PJ_LOAD(AA, BB, BAT)                                                                    \
+  do {                                                                                            \
+    _Pragma("unroll") for (int u = 0; u < KU; ++u) {                                              \
+      const int ch = c0 + (BAT) * KU + u;                                                         \
+      const bool ok = ch < c1;                                                                    \
+      _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                           \
+        AA[u][mb] = buf_load16_nt(ra, ok && aoff[mb] != BUF_OOB ? aoff[mb] + ch * 1024 : BUF_OOB);    \
+      _Pragma("unroll") for (int cb = 0; cb < NB; ++cb)                                           \
+        _Pragma("unroll") for (int v = 0; v < BV; ++v)                                            \
+          BB[u][cb][v] = buf_load16(rbuf, ok && boff[cb] != BUF_OOB                               \
+                                              ? boff[cb] + ch * KCH * (UP ? 4 : 2) + 16 * v : BUF_OOB); \
+    }                                                                                             \
+  } while (0)
+#define LSA_PJ_MMA(AA, BB)                                                                        \
+  do {                                                                                            \
+    _Pragma("unroll") for (int u = 0; u < KU; ++u) {                                              \
+      bf16x8 bv[NB];                                                                              \
+      _Pragma("unroll") for (int cb = 0; cb < NB; ++cb) {                                         \
+        if constexpr (UP) {                                                                       \
+          float v8[8];                                                                            \
+          _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                         \
+            v8[i] = __uint_as_float(BB[u][cb][0][i]);                                             \
+            v8[4 + i] = __uint_as_float(BB[u][cb][BV - 1][i]);                                    \
+          }                                                                                       \
+          bf16x8 hi, lo;                                                                          \
+          split8(v8, hi, lo);                                                                     \
+          bv[cb] = (m & 8) ? lo : hi;                                                             \
+        } else {                                                                                  \
+          bv[cb] = as_bf16x8(BB[u][cb][0]);                                                       \
+        }                                                                                         \
+      }                                                                                           \
+      _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                           \
+        _Pragma("unroll") for (int cb = 0; cb < NB; ++cb)                                         \
+          acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(AA[u][mb]), bv[cb], acc[mb][cb], 0, 0, 0); \
+    }                                                                                             \
+  } while (0)
+
+  LSA_PJ_LOAD(A0, B0, 0);
+  for (int bat = 0; bat < nbat; bat += 2) {
+    LSA_PJ_LOAD(A1, B1, bat + 1);
+    LSA_PJ_MMA(A0, B0);
+    LSA_PJ_LOAD(A0, B0, bat + 2);
+    LSA_PJ_MMA(A1, B1);
+  }
+#undef LSA_PJ_LOAD
+#undef LSA_PJ_MMA
+
+  // sum the W waves' partial products in wave order
+  if (wv > 0) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) red[wv - 1][mb][cb][lane] = acc[mb][cb];
+  }
+  __syncthreads();
+  if (wv != 0) return;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+      f32x4 s = acc[mb][cb];
+#pragma unroll
+      for (int j = 0; j < W - 1; ++j) {
+        const f32x4 t = red[j][mb][cb][lane];
+        s[0] += t[0]; s[1] += t[1]; s[2] += t[2]; s[3] += t[3];
+      }
+      if constexpr (UP) {
+        // column m holds the hi part (m < 8) or the lo part (m >= 8) of sequence cb*8 + (m&7)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] += __shfl_xor(s[i], 8);
+        if (m & 8) continue;
+      }
+      const int seq = cb * COLS + (UP ? (m & 7) : m);
+      if (seq >= a.B) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = rb + 16 * mb + 4 * kg + i;
+        if (row >= rows) continue;
+        if (UP) {
+          a.q[l][(int64_t)seq * rows + row] = s[i];
+        } else if (row < a.r) {
+          a.c[l][(int64_t)seq * a.r + row] = s[i];
+        } else {
+          a.w[l][(int64_t)seq * a.n_h + (row - a.r)] = s[i];
+        }
+      }
+    }
+  }
+}
+
 template <bool F32, bool UP, int MB, int NBMAX>
 static hipError_t launch_stage(const ProjArgs& a, int L, int nb, hipStream_t st) {
   const int rows = UP ? a.n_h * a.d_h : a.r + a.n_h;
@@ -210,14 +368,67 @@ static hipError_t launch_stage(const ProjArgs& a, int L, int nb, hipStream_t st)
   return hipGetLastError();
 }
 
+// Rearrange a bf16 "out x in" matrix into the packed operand layout: one
+// thread per 16-byte unit of the output.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ w, int rows, int K,
+                                                           u32x4* __restrict__ out, int64_t units) {
+  const int chunks = K / 32;
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (int64_t)gridDim.x * 256) {
+    const int64_t rbk = u / (chunks * 64);
+    const int rem = (int)(u - rbk * chunks * 64);
+    const int ch = rem / 64, lane = rem % 64;
+    const int64_t R = rbk * 16 + (lane & 15);
+    const int k0 = ch * 32 + 8 * (lane >> 4);
+    out[u] = R < rows ? *(const u32x4*)(w + R * K + k0) : u32x4{0, 0, 0, 0};
+  }
+}
+
+hipError_t launch_pack_weights(const void* w, int rows, int K, void* out, hipStream_t st) {
+  const int64_t units = (int64_t)((rows + 15) / 16) * (K / 32) * 64;
+  const int grid = (int)std::min<int64_t>((units + 255) / 256, 65536);
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(grid), dim3(256), 0, st, (const uint16_t*)w, rows, K, (u32x4*)out,
+                     units);
+  return hipGetLastError();
+}
+
+template <bool UP, int MB, int NB, int W, int KU>
+static hipError_t launch_bf16(const ProjArgs& a, int L, hipStream_t st) {
+  const int rows = UP ? a.n_h * a.d_h : a.r + a.n_h;
+  const dim3 grid((rows + 16 * MB - 1) / (16 * MB), L);
+  hipLaunchKernelGGL((project_packed_kernel<UP, MB, NB, W, KU>), grid, dim3(64 * W), 0, st, a);
+  return hipGetLastError();
+}
+
+// Block shapes of the packed projection, per stage and number of column blocks NB
+// (measured on MI355X at B = 8 and B = 32): MB row groups of 16 rows, W waves
+// splitting K, KU chunks per load batch.
+template <bool UP>
+static hipError_t launch_packed_stage(const ProjArgs& a, int L, int nb, hipStream_t st) {
+  if constexpr (UP) {
+    if (nb <= 1) return launch_bf16<true, 2, 1, 4, 4>(a, L, st);
+    if (nb <= 2) return launch_bf16<true, 4, 2, 4, 2>(a, L, st);
+    return launch_bf16<true, 4, 4, 4, 2>(a, L, st);
+  } else {
+    if (nb <= 1) return launch_bf16<false, 1, 1, 4, 4>(a, L, st);
+    return launch_bf16<false, 2, 2, 8, 4>(a, L, st);
+  }
+}
+
+hipError_t launch_project_packed(const ProjArgs& a, int L, hipStream_t st) {
+  hipError_t e;
+  const int nb_down = (a.B + 15) / 16, nb_up = (a.B + 7) / 8;
+  if ((e = launch_packed_stage<false>(a, L, nb_down, st)) != hipSuccess) return e;
+  return launch_packed_stage<true>(a, L, nb_up, st);
+}
+
 hipError_t launch_project(const ProjArgs& a, int L, bool f32, hipStream_t st) {
   hipError_t e;
+  const int nb_down = (a.B + 15) / 16, nb_up = (a.B + 7) / 8;
   if (f32) {
     const int nb = (a.B + 15) / 16;
     if ((e = launch_stage<true, false, 1, 16>(a, L, nb, st)) != hipSuccess) return e;
     return launch_stage<true, true, 1, 16>(a, L, nb, st);
   }
-  const int nb_down = (a.B + 15) / 16, nb_up = (a.B + 7) / 8;
   if ((e = launch_stage<false, false, 1, 16>(a, L, nb_down, st)) != hipSuccess) return e;
   // the up stage reuses each hi/lo split of c across 4 row groups while the B operand stays small
   if (nb_up <= 4) return launch_stage<false, true, 4, 4>(a, L, nb_up, st);

@@ -59,6 +59,10 @@ def _sig(name, res, args):
 
 
 _project = _sig("lsa_project", _i32, [ctypes.POINTER(ProjLayer), _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp])
+_pack_size = _sig("lsa_pack_weights_size", _sz, [_i32, _i32])
+_pack = _sig("lsa_pack_weights", _i32, [_vp, _i32, _i32, _vp, _sz, _vp])
+_project_packed = _sig("lsa_project_packed", _i32, [ctypes.POINTER(ProjLayer), _i32, _i32, _i32, _i32, _i32, _i32,
+                                                     _vp])
 _score_select = _sig("lsa_score_select", _i32, [ctypes.POINTER(ScoreLayer), _i32, _i32, _vp, _vp, _vp, _vp,
                                                  _i32, _i32, _i32, _f32, _vp])
 _union_compact = _sig("lsa_union_compact", _i32, [ctypes.POINTER(_vp), _i32, _i32, _vp, _vp, _vp, _vp,
@@ -70,7 +74,7 @@ _gather = _sig("lsa_gather", _i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _v
 _last_error = _sig("lsa_last_error", ctypes.c_char_p, [])
 _version = _sig("lsa_version", _i32, [])
 
-EXPORTED = ("lsa_project", "lsa_score_select", "lsa_union_compact", "lsa_topk_workspace_size", "lsa_topk",
+EXPORTED = ("lsa_project", "lsa_pack_weights_size", "lsa_pack_weights", "lsa_project_packed", "lsa_score_select", "lsa_union_compact", "lsa_topk_workspace_size", "lsa_topk",
             "lsa_gather", "lsa_last_error", "lsa_version")
 
 
@@ -120,6 +124,25 @@ def project(layers, *, B, d, r, n_h, d_h, dtype, stream=None):
     arr = (ProjLayer * len(layers))(*[ProjLayer(*[_p(x[k]) for k in ("h", "w_dq", "w_iuq", "w_w", "c_out",
                                                                       "q_out", "w_out")]) for x in layers])
     _check("lsa_project", _project(arr, len(layers), B, d, r, n_h, d_h, DTYPES.get(dtype, dtype), _stream(stream)))
+
+
+def pack_weights_size(rows, K) -> int:
+    """lsa_pack_weights_size: bytes of the packed operand layout of a rows x K bf16 matrix."""
+    return int(_pack_size(rows, K))
+
+
+def pack_weights(w, rows, K, out, out_bytes=None, stream=None):
+    """lsa_pack_weights: `w` a [rows, K] bf16 (int16 bits) tensor, `out` a byte tensor of pack_weights_size bytes."""
+    if out_bytes is None:
+        out_bytes = out.numel() * out.element_size()
+    _check("lsa_pack_weights", _pack(_p(w), rows, K, _p(out), int(out_bytes), _stream(stream)))
+
+
+def project_packed(layers, *, B, d, r, n_h, d_h, stream=None):
+    """lsa_project_packed: as project(), with w_dq, w_iuq, w_w packed by pack_weights (bf16)."""
+    arr = (ProjLayer * len(layers))(*[ProjLayer(*[_p(x[k]) for k in ("h", "w_dq", "w_iuq", "w_w", "c_out",
+                                                                      "q_out", "w_out")]) for x in layers])
+    _check("lsa_project_packed", _project_packed(arr, len(layers), B, d, r, n_h, d_h, _stream(stream)))
 
 
 def score_select(layers, *, B, key_offsets, key_offsets_host, mask_word_offsets, mask_word_offsets_host,

@@ -5,7 +5,8 @@ allocates every output and the top-k workspace once. `run()` then enqueues the
 five library calls on the current stream, with no allocation and no host
 synchronisation:
 
-  lsa_project        memory-indexer and native query/gates for every layer (one call, 2L layers)
+  lsa_project        memory-indexer and native query/gates for every layer (one call, 2L layers);
+                     with bf16 weights, lsa_project_packed on weights packed once at set-up
   lsa_score_select   masks (and optional sigmoid scores) for every (layer, sequence)
   lsa_union_compact  OR over the layers -> ascending index list + count per sequence
   lsa_topk           native top-k inside the union, per (layer, sequence)
@@ -36,7 +37,7 @@ CANARY = 0x5A
 
 class Pipeline:
     def __init__(self, inp, device="cuda", *, with_scores=False, with_topk_scores=True, gather_capacity=None,
-                 guard=False):
+                 guard=False, packed=True):
         w = inp.workload
         self.w = w
         self.inp = inp
@@ -55,6 +56,22 @@ class Pipeline:
         self.h = [_dev(inp.h[l], dev) for l in range(L)]
         self.mem = [tuple(_dev(x, dev) for x in (lw.w_dq, lw.w_iuq, lw.w_w)) for lw in inp.mem_w]
         self.nat = [tuple(_dev(x, dev) for x in (lw.w_dq, lw.w_iuq, lw.w_w)) for lw in inp.nat_w]
+        # bf16 projection weights are packed once into the matrix-core operand layout
+        self.packed = packed and w.act_dtype == "bf16" and B <= 32 and w.r % 64 == 0 and (w.n_h * w.d_h) % 64 == 0
+        if self.packed:
+            shapes = ((w.r, w.d), (w.n_h * w.d_h, w.r), (w.n_h, w.d))
+
+            def pack(mats):
+                out = []
+                for m, (rows, K) in zip(mats, shapes):
+                    buf = torch.empty(lsa.pack_weights_size(rows, K), dtype=torch.uint8, device=dev)
+                    lsa.pack_weights(m, rows, K, buf)
+                    out.append(buf)
+                return tuple(out)
+
+            self.mem = [pack(m) for m in self.mem]
+            self.nat = [pack(m) for m in self.nat]
+            torch.cuda.synchronize()
         self.keys = [_dev(inp.keys[l], dev) for l in range(L)]
         self.scale = [None if inp.key_scale[l] is None else _dev(inp.key_scale[l], dev) for l in range(L)]
         self.pool = None if inp.pool is None else _dev(inp.pool, dev)
@@ -110,7 +127,10 @@ class Pipeline:
             wdq, wiuq, ww = (self.mem if j < L else self.nat)[j % L]
             layers.append(dict(h=self.h[j % L], w_dq=wdq, w_iuq=wiuq, w_w=ww, c_out=self.c[j], q_out=self.q[j],
                                w_out=self.g[j]))
-        lsa.project(layers, B=w.B, d=w.d, r=w.r, n_h=w.n_h, d_h=w.d_h, dtype=w.act_dtype, stream=stream)
+        if self.packed:
+            lsa.project_packed(layers, B=w.B, d=w.d, r=w.r, n_h=w.n_h, d_h=w.d_h, stream=stream)
+        else:
+            lsa.project(layers, B=w.B, d=w.d, r=w.r, n_h=w.n_h, d_h=w.d_h, dtype=w.act_dtype, stream=stream)
 
     def score_select(self, stream=None):
         w = self.w

@@ -27,7 +27,8 @@ def declared_functions():
 def test_header_declares_the_five_calls():
     fns = declared_functions()
     for f in ("lsa_project", "lsa_score_select", "lsa_union_compact", "lsa_topk", "lsa_gather",
-              "lsa_topk_workspace_size", "lsa_last_error", "lsa_version"):
+              "lsa_topk_workspace_size", "lsa_pack_weights_size", "lsa_pack_weights", "lsa_project_packed",
+              "lsa_last_error", "lsa_version"):
         assert f in fns
 
 
@@ -104,6 +105,26 @@ def test_project_validation(lsa):
     _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.project, [lay], **{**base, "dtype": "fp8"})
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.project, [{**lay, "q_out": lay["c_out"]}], **base, match="alias")
     _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.project, [lay], **{**base, "n_h": 3, "d_h": 5})
+
+
+def test_packed_projection_validation(lsa):
+    assert lsa.pack_weights_size(2048, 4096) == 128 * 128 * 1024
+    assert lsa.pack_weights_size(64, 4096) == 4 * 128 * 1024
+    assert lsa.pack_weights_size(65, 4096) == 5 * 128 * 1024   # rows padded to a multiple of 16
+    assert lsa.pack_weights_size(64, 4010) == 0                 # K not a multiple of 32
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.pack_weights, FAKE, 64, 4010, FAKE, out_bytes=1 << 30, stream=0)
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.pack_weights, FAKE, 64, 4096, FAKE, out_bytes=1000, stream=0,
+            match="needs")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.pack_weights, FAKE + 2, 64, 4096, FAKE, out_bytes=1 << 30, stream=0,
+            match="aligned")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.pack_weights, None, 64, 4096, FAKE, out_bytes=1 << 30, stream=0)
+    lay = dict(h=FAKE, w_dq=FAKE, w_iuq=FAKE, w_w=FAKE, c_out=FAKE + 4096, q_out=FAKE + 8192, w_out=FAKE + 16384)
+    base = dict(B=8, d=4096, r=2048, n_h=64, d_h=128, stream=0)
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.project_packed, [lay], **{**base, "B": 33}, match="B must")
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.project_packed, [lay], **{**base, "r": 2016}, match="multiple")
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.project_packed, [lay], **{**base, "n_h": 3, "d_h": 5})
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.project_packed, [{**lay, "w_w": FAKE + 8}], **base, match="aligned")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.project_packed, [{**lay, "w_out": lay["c_out"]}], **base, match="alias")
 
 
 def test_union_topk_gather_validation(lsa):

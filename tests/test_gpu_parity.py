@@ -75,6 +75,41 @@ def test_repeat_is_deterministic(torch_cuda):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("rows,K", [(37, 96), (64, 4096), (16, 32)])
+def test_pack_weights_layout(rows, K, torch_cuda):
+    """lsa_pack_weights against the layout its header defines, written out with numpy."""
+    from sparse_kv_retrieval_amd import lsa
+    P.say(f"[parity] pack layout {rows}x{K}")
+    rng = np.random.default_rng(rows * 7 + K)
+    w = rng.integers(0, 1 << 16, (rows, K), dtype=np.uint64).astype(np.uint16)
+    wd = torch_cuda.from_numpy(w.view(np.int16)).cuda()
+    out = torch_cuda.empty(lsa.pack_weights_size(rows, K), dtype=torch_cuda.uint8, device="cuda")
+    lsa.pack_weights(wd, rows, K, out)
+    got = out.cpu().numpy().view(np.uint16)
+    nrb, nch = (rows + 15) // 16, K // 32
+    pad = np.zeros((nrb * 16, K), np.uint16)
+    pad[:rows] = w
+    # block (rb, ch), unit l = 16*kg + m: row 16rb + m, columns 32ch + 8kg .. + 7
+    want = pad.reshape(nrb, 16, nch, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.gpu
+def test_unpacked_projection_parity(torch_cuda):
+    """The same path with plain out x in bf16 weights (lsa_project instead of lsa_project_packed)."""
+    from sparse_kv_retrieval_amd.pipeline import Pipeline
+    w = SMALL["three_layer_mixed"]
+    P.say("[parity] unpacked projection")
+    inp = synth.make(w)
+    p = Pipeline(inp, "cuda", with_scores=True, guard=True, packed=False)
+    assert not p.packed
+    p.run()
+    torch_cuda.cuda.synchronize()
+    assert p.check_guards() == []
+    P.full_check(p, inp)
+
+
+@pytest.mark.gpu
 def test_graph_replay_matches_eager(torch_cuda):
     """The whole path captured in one HIP graph: every replay equals the eager run bit for bit."""
     from sparse_kv_retrieval_amd.pipeline import Pipeline
