@@ -2,8 +2,9 @@
 
 `Pipeline(inputs)` copies a seeded input set (from `synth.make`) into HBM and
 allocates every output and the top-k workspace once. `run()` then enqueues the
-five library calls on the current stream, with no allocation and no host
-synchronisation:
+five library calls, with no allocation and no host synchronisation, on the
+current stream (the gather on a second stream that forks after the union and
+joins at the end):
 
   lsa_project        memory-indexer and native query/gates for every layer (one call, 2L layers);
                      with bf16 weights, lsa_project_packed on weights packed once at set-up
@@ -37,7 +38,7 @@ CANARY = 0x5A
 
 class Pipeline:
     def __init__(self, inp, device="cuda", *, with_scores=False, with_topk_scores=True, gather_capacity=None,
-                 guard=False, packed=True):
+                 guard=False, packed=True, overlap=True):
         w = inp.workload
         self.w = w
         self.inp = inp
@@ -45,6 +46,10 @@ class Pipeline:
         self.device = dev
         self._guarded = []
         self.guard = guard
+        self.overlap = overlap
+        self._side = torch.cuda.Stream(device=dev)  # default priority
+        self._fork = torch.cuda.Event()
+        self._join = torch.cuda.Event()
         B, L = w.B, w.L
         self.rows = int(inp.key_offsets[-1])
         self.words = int(inp.mask_word_offsets[-1])
@@ -164,11 +169,22 @@ class Pipeline:
                    out=self.gathered, out_capacity_rows=self.gather_capacity, stream=stream)
 
     def run(self, stream=None):
-        self.project(stream)
-        self.score_select(stream)
-        self.union_compact(stream)
-        self.topk(stream)
-        self.gather(stream)
+        """One pass of the path. Top-k and gather both read only the union list, so the
+        gather runs on a second stream, forked after union_compact and joined at the end."""
+        main = torch.cuda.current_stream() if stream is None else stream
+        self.project(main)
+        self.score_select(main)
+        self.union_compact(main)
+        if self.pool is None or not self.overlap:
+            self.topk(main)
+            self.gather(main)
+            return
+        self._fork.record(main)
+        self._side.wait_event(self._fork)
+        self.gather(self._side)
+        self.topk(main)
+        self._join.record(self._side)
+        main.wait_event(self._join)
 
     def capture(self):
         """Record one run() into a HIP graph and return it (replay with .replay()).

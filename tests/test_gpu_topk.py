@@ -1,0 +1,105 @@
+"""lsa_topk on hand-made scores, through the C-ABI (marked gpu).
+
+With one head, gate 1, query e_0 and bf16 keys, the native score of entry s is
+y_s = ReLU(K_s[0]) exactly, so the expected top-k is the oracle's (-y, s) order
+on known values. The cases reach every branch of the select: the
+sample-threshold filter, its fall-backs (too few entries above the estimate,
+too many) and the in-register and streaming radix selects.
+"""
+import numpy as np
+import pytest
+
+from sparse_kv_retrieval_amd import synth
+from tests import parity as P
+
+
+def _bf16_exact(v):
+    """Values rounded to bf16 (round to nearest even), returned as (bits, exact float64 values)."""
+    bits = synth.f32_to_bf16_bits(np.asarray(v, np.float32))
+    return bits, synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _run(torch, y_target, k, M_list=None):
+    from oracle import lsa_oracle as O
+    from sparse_kv_retrieval_amd import lsa
+    M = len(y_target)
+    d_h = 32
+    bits, y = _bf16_exact(y_target)
+    keys = np.zeros((M, d_h), np.uint16)
+    keys[:, 0] = bits
+    y = np.maximum(y, 0.0)                         # the ReLU
+    n = M if M_list is None else M_list
+    idx = np.arange(n, dtype=np.int32)             # the union list: the first n entries
+    dev = "cuda"
+    t_keys = torch.from_numpy(keys.view(np.int16)).to(dev)
+    q = torch.zeros(1, 1, d_h, dtype=torch.float32, device=dev)
+    q[0, 0, 0] = 1.0
+    w = torch.ones(1, 1, dtype=torch.float32, device=dev)
+    ko_h = np.array([0, M], np.int64)
+    ko = torch.from_numpy(ko_h).to(dev)
+    t_idx = torch.from_numpy(np.concatenate([idx, np.zeros(M - n, np.int32)])).to(dev)
+    cnt = torch.tensor([n], dtype=torch.int32, device=dev)
+    out = torch.full((1, k), -7, dtype=torch.int32, device=dev)
+    outs = torch.zeros((1, k), dtype=torch.float32, device=dev)
+    tcount = torch.zeros((1, 1), dtype=torch.int32, device=dev)
+    ws = torch.empty(lsa.topk_workspace_size(1, 1, M, k), dtype=torch.uint8, device=dev)
+    lsa.topk([dict(q=q, w=w, keys=t_keys, key_scale=None, topk_idx_out=out, topk_score_out=outs)], B=1,
+             key_offsets=ko, key_offsets_host=ko_h, idx=t_idx, count=cnt, n_h=1, d_h=d_h, key_dtype="bf16", k=k,
+             topk_count_out=tcount, workspace=ws)
+    torch.cuda.synchronize()
+    want = O.topk(y[:n], idx.astype(np.int64), k)
+    m = min(k, n)
+    got = out.cpu().numpy()[0]
+    assert int(tcount.cpu()[0, 0]) == m
+    assert np.array_equal(got[:m], want), f"first difference at {np.flatnonzero(got[:m] != want)[:5]}"
+    assert np.all(got[m:] == -1)
+    assert np.array_equal(outs.cpu().numpy()[0][:m], y[got[:m]].astype(np.float32))
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    return t
+
+
+@pytest.mark.gpu
+def test_topk_sample_misses_the_top(torch):
+    """The highest scores sit only at positions the sample never reads: the filter keeps too few, fall back."""
+    P.say("[topk] sample misses the top")
+    M, k = 8192, 2048
+    y = np.full(M, 1.0)
+    y[1::2] = 64.0 + (np.arange(M // 2) % 64)      # odd positions high; the sample reads even positions
+    _run(torch, y, k)
+
+
+@pytest.mark.gpu
+def test_topk_all_equal(torch):
+    """Every score ties: the filter keeps everything (more than it can hold), fall back; lowest indices win."""
+    P.say("[topk] all equal")
+    _run(torch, np.full(20000, 3.0), 2048)
+
+
+@pytest.mark.gpu
+def test_topk_heavy_ties(torch):
+    """Sixteen distinct scores over 50,000 entries: the k-th key is shared by thousands of entries."""
+    P.say("[topk] heavy ties")
+    rng = np.random.default_rng(5)
+    _run(torch, rng.integers(0, 16, 50000).astype(np.float64), 2048)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M", [8192, 50000, 90000, 200000])
+def test_topk_random(M, torch):
+    """Random scores (many exact ties in bf16): the filtered path, and the long lists past the register path."""
+    P.say(f"[topk] random M={M}")
+    rng = np.random.default_rng(M)
+    _run(torch, rng.standard_normal(M) * 4.0, 2048)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("n,k", [(5000, 2048), (2048, 2048), (1, 32), (7000, 7000), (30000, 3072)])
+def test_topk_shapes(n, k, torch):
+    """Lists shorter than, equal to and longer than k, and the largest k the filter takes."""
+    P.say(f"[topk] n={n} k={k}")
+    rng = np.random.default_rng(n + k)
+    _run(torch, rng.standard_normal(n + 100) * 4.0, k, M_list=n)
