@@ -234,6 +234,28 @@ lsa_status lsa_topk(const lsa_topk_layer* layers /* host [L] */, int32_t L, int3
                     int32_t* topk_count_out /* dev [L, B] */, void* workspace /* dev */,
                     size_t workspace_bytes, hipStream_t stream);
 
+/* The two stages of lsa_topk as separate calls, so that other work can be
+ * ordered between them (the scoring streams the subset's keys from HBM; the
+ * selection runs one workgroup per (layer, sequence) and is latency-bound).
+ * lsa_topk_score writes the subset scores into the workspace and reads only
+ * q, w, keys and key_scale of each layer. lsa_topk_select reads them back and
+ * writes topk_idx_out, topk_score_out and topk_count_out. Run them in that
+ * order with the same lists, counts and workspace (on one stream, or with the
+ * selection ordered after the scoring). lsa_topk is the two in sequence. */
+lsa_status lsa_topk_score(const lsa_topk_layer* layers /* host [L] */, int32_t L, int32_t B,
+                          const int64_t* key_offsets /* dev [B+1] */,
+                          const int64_t* key_offsets_host /* host [B+1] */,
+                          const int32_t* idx /* dev [rows] */, const int32_t* count /* dev [B] */,
+                          int32_t n_h, int32_t d_h, lsa_dtype key_dtype, void* workspace /* dev */,
+                          size_t workspace_bytes, hipStream_t stream);
+
+lsa_status lsa_topk_select(const lsa_topk_layer* layers /* host [L] */, int32_t L, int32_t B,
+                           const int64_t* key_offsets /* dev [B+1] */,
+                           const int64_t* key_offsets_host /* host [B+1] */,
+                           const int32_t* idx /* dev [rows] */, const int32_t* count /* dev [B] */,
+                           int32_t k, int32_t* topk_count_out /* dev [L, B] */, void* workspace /* dev */,
+                           size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * lsa_gather: load the selected entries' compressed-KV rows into a compact
  * device buffer ([HYPER] 方法: the subset C^MemComp is loaded into GPU memory).

@@ -103,6 +103,66 @@ lsa_status check_key_bytes(int32_t B, const int64_t* key_offsets_host, int32_t d
   return LSA_OK;
 }
 
+// The two stages of the top-k share their checks. Scoring needs the queries,
+// keys and key dtype; selection needs k and the outputs; both need the lists
+// and the workspace.
+lsa_status topk_stages(const lsa_topk_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
+                       const int64_t* key_offsets_host, const int32_t* idx, const int32_t* count, int32_t n_h,
+                       int32_t d_h, lsa_dtype key_dtype, int32_t k, int32_t* topk_count_out, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, bool do_score, bool do_select) {
+  if (!layers) return fail(LSA_ERR_INVALID_ARG, "layers is NULL");
+  if (L < 1 || L > LSA_MAX_LAYERS) return fail(LSA_ERR_INVALID_ARG, "L must be in [1, %d] (got %d)", LSA_MAX_LAYERS, L);
+  if (B < 1 || B > LSA_TOPK_MAX_B) return fail(LSA_ERR_UNSUPPORTED, "B must be in [1, %d] (got %d)", LSA_TOPK_MAX_B, B);
+  if (!key_offsets) return fail(LSA_ERR_INVALID_ARG, "key_offsets is NULL");
+  lsa_status s;
+  if ((s = check_offsets(key_offsets_host, B, "key_offsets")) != LSA_OK) return s;
+  int kind = KEY_BF16;
+  if (do_score) {
+    if ((s = check_heads(n_h, d_h)) != LSA_OK) return s;
+    if ((s = key_kind_of(key_dtype, &kind)) != LSA_OK) return s;
+    if ((s = check_key_bytes(B, key_offsets_host, d_h, kind)) != LSA_OK) return s;
+  }
+  if (do_select) {
+    if (k < 1 || k > 65536) return fail(LSA_ERR_UNSUPPORTED, "k must be in [1, 65536] (got %d)", k);
+    if (!topk_count_out) return fail(LSA_ERR_INVALID_ARG, "topk_count_out must be set");
+  }
+  if (!idx || !count) return fail(LSA_ERR_INVALID_ARG, "idx and count must be set");
+  const int64_t rows = key_offsets_host[B];
+  for (int32_t b = 0; b < B; ++b)
+    if (key_offsets_host[b + 1] - key_offsets_host[b] > INT32_MAX) return fail(LSA_ERR_UNSUPPORTED, "sequence too long");
+  const size_t need = lsa_topk_workspace_size(L, B, rows, do_select ? k : 1);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(LSA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  TopkScoreArgs sa{};
+  TopkSelectArgs ta{};
+  for (int l = 0; l < L; ++l) {
+    const lsa_topk_layer& p = layers[l];
+    if (do_score) {
+      if (!p.q || !p.w || !p.keys) return fail(LSA_ERR_INVALID_ARG, "layer %d: q, w and keys must be set", l);
+      if (kind == KEY_FP8 && !p.key_scale) return fail(LSA_ERR_INVALID_ARG, "layer %d: fp8 keys need key_scale", l);
+      if (kind != KEY_FP8 && p.key_scale) return fail(LSA_ERR_INVALID_ARG, "layer %d: key_scale is only for fp8 keys", l);
+      if (!aligned16(p.q) || !aligned16(p.keys)) return fail(LSA_ERR_INVALID_ARG, "layer %d: q and keys must be 16-byte aligned", l);
+    }
+    if (do_select && !p.topk_idx_out) return fail(LSA_ERR_INVALID_ARG, "layer %d: topk_idx_out must be set", l);
+    sa.q[l] = p.q; sa.w[l] = p.w; sa.keys[l] = p.keys; sa.scale[l] = p.key_scale;
+    ta.out_idx[l] = p.topk_idx_out; ta.out_score[l] = p.topk_score_out;
+  }
+  sa.ys = (float*)workspace; sa.idx = idx; sa.count = count; sa.key_off = key_offsets; sa.rows_total = rows;
+  sa.B = B; sa.L = L; sa.n_h = n_h;
+  ta.ys = (const float*)workspace; ta.idx = idx; ta.count = count; ta.key_off = key_offsets;
+  ta.out_count = topk_count_out; ta.rows_total = rows; ta.B = B; ta.k = k;
+  hipError_t e;
+  if (do_score && rows > 0) {
+    int64_t tiles = 0;
+    for (int32_t b = 0; b < B; ++b) tiles += (key_offsets_host[b + 1] - key_offsets_host[b] + 31) / 32;
+    const int64_t pairs = std::max<int64_t>(1, std::min<int64_t>(tiles * L, (int64_t)cu_count() * env_int("LSA_TOPK_PAIRS_PER_CU", 4)));
+    if ((e = launch_topk_score(sa, kind, d_h, (int)pairs, env_int("LSA_TOPK_DEPTH", 0), stream)) != hipSuccess)
+      return hip_fail("lsa_topk score launch", e);
+  }
+  if (do_select && (e = launch_topk_select(ta, L, stream)) != hipSuccess) return hip_fail("lsa_topk select launch", e);
+  return LSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -255,49 +315,22 @@ lsa_status lsa_topk(const lsa_topk_layer* layers, int32_t L, int32_t B, const in
                     const int64_t* key_offsets_host, const int32_t* idx, const int32_t* count, int32_t n_h, int32_t d_h,
                     lsa_dtype key_dtype, int32_t k, int32_t* topk_count_out, void* workspace, size_t workspace_bytes,
                     hipStream_t stream) {
-  if (!layers) return fail(LSA_ERR_INVALID_ARG, "layers is NULL");
-  if (L < 1 || L > LSA_MAX_LAYERS) return fail(LSA_ERR_INVALID_ARG, "L must be in [1, %d] (got %d)", LSA_MAX_LAYERS, L);
-  if (B < 1 || B > LSA_TOPK_MAX_B) return fail(LSA_ERR_UNSUPPORTED, "B must be in [1, %d] (got %d)", LSA_TOPK_MAX_B, B);
-  if (!key_offsets) return fail(LSA_ERR_INVALID_ARG, "key_offsets is NULL");
-  lsa_status s;
-  if ((s = check_offsets(key_offsets_host, B, "key_offsets")) != LSA_OK) return s;
-  if ((s = check_heads(n_h, d_h)) != LSA_OK) return s;
-  int kind;
-  if ((s = key_kind_of(key_dtype, &kind)) != LSA_OK) return s;
-  if ((s = check_key_bytes(B, key_offsets_host, d_h, kind)) != LSA_OK) return s;
-  if (k < 1 || k > 65536) return fail(LSA_ERR_UNSUPPORTED, "k must be in [1, 65536] (got %d)", k);
-  if (!idx || !count || !topk_count_out) return fail(LSA_ERR_INVALID_ARG, "idx, count and topk_count_out must be set");
-  const int64_t rows = key_offsets_host[B];
-  for (int32_t b = 0; b < B; ++b)
-    if (key_offsets_host[b + 1] - key_offsets_host[b] > INT32_MAX) return fail(LSA_ERR_UNSUPPORTED, "sequence too long");
-  const size_t need = lsa_topk_workspace_size(L, B, rows, k);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(LSA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
-  TopkScoreArgs sa{};
-  TopkSelectArgs ta{};
-  for (int l = 0; l < L; ++l) {
-    const lsa_topk_layer& p = layers[l];
-    if (!p.q || !p.w || !p.keys || !p.topk_idx_out) return fail(LSA_ERR_INVALID_ARG, "layer %d: q, w, keys and topk_idx_out must be set", l);
-    if (kind == KEY_FP8 && !p.key_scale) return fail(LSA_ERR_INVALID_ARG, "layer %d: fp8 keys need key_scale", l);
-    if (kind != KEY_FP8 && p.key_scale) return fail(LSA_ERR_INVALID_ARG, "layer %d: key_scale is only for fp8 keys", l);
-    if (!aligned16(p.q) || !aligned16(p.keys)) return fail(LSA_ERR_INVALID_ARG, "layer %d: q and keys must be 16-byte aligned", l);
-    sa.q[l] = p.q; sa.w[l] = p.w; sa.keys[l] = p.keys; sa.scale[l] = p.key_scale;
-    ta.out_idx[l] = p.topk_idx_out; ta.out_score[l] = p.topk_score_out;
-  }
-  sa.ys = (float*)workspace; sa.idx = idx; sa.count = count; sa.key_off = key_offsets; sa.rows_total = rows;
-  sa.B = B; sa.L = L; sa.n_h = n_h;
-  ta.ys = (const float*)workspace; ta.idx = idx; ta.count = count; ta.key_off = key_offsets;
-  ta.out_count = topk_count_out; ta.rows_total = rows; ta.B = B; ta.k = k;
-  hipError_t e;
-  if (rows > 0) {
-    int64_t tiles = 0;
-    for (int32_t b = 0; b < B; ++b) tiles += (key_offsets_host[b + 1] - key_offsets_host[b] + 31) / 32;
-    const int64_t pairs = std::max<int64_t>(1, std::min<int64_t>(tiles * L, (int64_t)cu_count() * env_int("LSA_TOPK_PAIRS_PER_CU", 4)));
-    if ((e = launch_topk_score(sa, kind, d_h, (int)pairs, env_int("LSA_TOPK_DEPTH", 0), stream)) != hipSuccess)
-      return hip_fail("lsa_topk score launch", e);
-  }
-  if ((e = launch_topk_select(ta, L, stream)) != hipSuccess) return hip_fail("lsa_topk select launch", e);
-  return LSA_OK;
+  return topk_stages(layers, L, B, key_offsets, key_offsets_host, idx, count, n_h, d_h, key_dtype, k, topk_count_out,
+                     workspace, workspace_bytes, stream, true, true);
+}
+
+lsa_status lsa_topk_score(const lsa_topk_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
+                          const int64_t* key_offsets_host, const int32_t* idx, const int32_t* count, int32_t n_h,
+                          int32_t d_h, lsa_dtype key_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return topk_stages(layers, L, B, key_offsets, key_offsets_host, idx, count, n_h, d_h, key_dtype, 1, nullptr,
+                     workspace, workspace_bytes, stream, true, false);
+}
+
+lsa_status lsa_topk_select(const lsa_topk_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
+                           const int64_t* key_offsets_host, const int32_t* idx, const int32_t* count, int32_t k,
+                           int32_t* topk_count_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return topk_stages(layers, L, B, key_offsets, key_offsets_host, idx, count, 1, 32, LSA_BF16, k, topk_count_out,
+                     workspace, workspace_bytes, stream, false, true);
 }
 
 lsa_status lsa_gather(const void* pool, int64_t row_bytes, int32_t B, const int64_t* pool_row_offsets,

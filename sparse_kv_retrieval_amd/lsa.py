@@ -70,11 +70,16 @@ _union_compact = _sig("lsa_union_compact", _i32, [ctypes.POINTER(_vp), _i32, _i3
 _topk_ws = _sig("lsa_topk_workspace_size", _sz, [_i32, _i32, _i64, _i32])
 _topk = _sig("lsa_topk", _i32, [ctypes.POINTER(TopkLayer), _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                  _i32, _vp, _vp, _sz, _vp])
+_topk_score = _sig("lsa_topk_score", _i32, [ctypes.POINTER(TopkLayer), _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32,
+                                             _i32, _vp, _sz, _vp])
+_topk_select = _sig("lsa_topk_select", _i32, [ctypes.POINTER(TopkLayer), _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
+                                               _vp, _sz, _vp])
 _gather = _sig("lsa_gather", _i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp])
 _last_error = _sig("lsa_last_error", ctypes.c_char_p, [])
 _version = _sig("lsa_version", _i32, [])
 
-EXPORTED = ("lsa_project", "lsa_pack_weights_size", "lsa_pack_weights", "lsa_project_packed", "lsa_score_select", "lsa_union_compact", "lsa_topk_workspace_size", "lsa_topk",
+EXPORTED = ("lsa_project", "lsa_pack_weights_size", "lsa_pack_weights", "lsa_project_packed", "lsa_score_select",
+            "lsa_topk_score", "lsa_topk_select", "lsa_union_compact", "lsa_topk_workspace_size", "lsa_topk",
             "lsa_gather", "lsa_last_error", "lsa_version")
 
 
@@ -182,6 +187,33 @@ def topk(layers, *, B, key_offsets, key_offsets_host, idx, count, n_h, d_h, key_
     _check("lsa_topk", _topk(arr, len(layers), B, _p(key_offsets), kop, _p(idx), _p(count), n_h, d_h,
                              DTYPES.get(key_dtype, key_dtype), k, _p(topk_count_out), _p(workspace), nbytes,
                              _stream(stream)))
+
+
+def _topk_layers(layers):
+    return (TopkLayer * len(layers))(*[TopkLayer(_p(x.get("q")), _p(x.get("w")), _p(x.get("keys")),
+                                                 _p(x.get("key_scale")), _p(x.get("topk_idx_out")),
+                                                 _p(x.get("topk_score_out"))) for x in layers])
+
+
+def topk_score(layers, *, B, key_offsets, key_offsets_host, idx, count, n_h, d_h, key_dtype, workspace,
+               stream=None):
+    """lsa_topk_score: the subset scores into the workspace. `layers`: dicts with q, w, keys, key_scale."""
+    ko, kop = _host64(key_offsets_host)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("lsa_topk_score", _topk_score(_topk_layers(layers), len(layers), B, _p(key_offsets), kop, _p(idx),
+                                         _p(count), n_h, d_h, DTYPES.get(key_dtype, key_dtype), _p(workspace),
+                                         nbytes, _stream(stream)))
+
+
+def topk_select(layers, *, B, key_offsets, key_offsets_host, idx, count, k, topk_count_out, workspace,
+                stream=None):
+    """lsa_topk_select: the top-k from the scores in the workspace. `layers`: dicts with topk_idx_out
+    and topk_score_out (optional)."""
+    ko, kop = _host64(key_offsets_host)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("lsa_topk_select", _topk_select(_topk_layers(layers), len(layers), B, _p(key_offsets), kop, _p(idx),
+                                           _p(count), k, _p(topk_count_out), _p(workspace), nbytes,
+                                           _stream(stream)))
 
 
 def gather(pool, *, row_bytes, B, pool_row_offsets, pool_row_offsets_host, idx, idx_offsets, count, out,

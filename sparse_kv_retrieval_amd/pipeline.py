@@ -3,14 +3,15 @@
 `Pipeline(inputs)` copies a seeded input set (from `synth.make`) into HBM and
 allocates every output and the top-k workspace once. `run()` then enqueues the
 five library calls, with no allocation and no host synchronisation, on the
-current stream (the gather on a second stream that forks after the union and
-joins at the end):
+current stream (the gather on a second stream that forks after the top-k
+scoring and joins at the end):
 
   lsa_project        memory-indexer and native query/gates for every layer (one call, 2L layers);
                      with bf16 weights, lsa_project_packed on weights packed once at set-up
   lsa_score_select   masks (and optional sigmoid scores) for every (layer, sequence)
   lsa_union_compact  OR over the layers -> ascending index list + count per sequence
   lsa_topk           native top-k inside the union, per (layer, sequence)
+                     (run() calls its two stages, lsa_topk_score and lsa_topk_select)
   lsa_gather         the union rows of the compressed-KV pool -> packed compact buffer
 
 This module only wires buffers. All arithmetic happens in the HIP kernels.
@@ -151,14 +152,29 @@ class Pipeline:
                           mask_word_offsets=self.mwo, mask_word_offsets_host=self.mwo_h, idx_out=self.idx,
                           count_out=self.count, union_mask_out=self.union_mask, stream=stream)
 
-    def topk(self, stream=None):
+    def _topk_layers(self):
         w, L = self.w, self.w.L
-        layers = [dict(q=self.q[L + l], w=self.g[L + l], keys=self.keys[l], key_scale=self.scale[l],
-                       topk_idx_out=self.topk_idx[l],
-                       topk_score_out=None if self.topk_score is None else self.topk_score[l]) for l in range(L)]
-        lsa.topk(layers, B=w.B, key_offsets=self.key_off, key_offsets_host=self.key_off_h, idx=self.idx,
-                 count=self.count, n_h=w.n_h, d_h=w.d_h, key_dtype=w.key_dtype, k=w.k,
+        return [dict(q=self.q[L + l], w=self.g[L + l], keys=self.keys[l], key_scale=self.scale[l],
+                     topk_idx_out=self.topk_idx[l],
+                     topk_score_out=None if self.topk_score is None else self.topk_score[l]) for l in range(L)]
+
+    def topk(self, stream=None):
+        w = self.w
+        lsa.topk(self._topk_layers(), B=w.B, key_offsets=self.key_off, key_offsets_host=self.key_off_h,
+                 idx=self.idx, count=self.count, n_h=w.n_h, d_h=w.d_h, key_dtype=w.key_dtype, k=w.k,
                  topk_count_out=self.topk_count, workspace=self.workspace, stream=stream)
+
+    def topk_score_stage(self, stream=None):
+        w = self.w
+        lsa.topk_score(self._topk_layers(), B=w.B, key_offsets=self.key_off, key_offsets_host=self.key_off_h,
+                       idx=self.idx, count=self.count, n_h=w.n_h, d_h=w.d_h, key_dtype=w.key_dtype,
+                       workspace=self.workspace, stream=stream)
+
+    def topk_select_stage(self, stream=None):
+        w = self.w
+        lsa.topk_select(self._topk_layers(), B=w.B, key_offsets=self.key_off, key_offsets_host=self.key_off_h,
+                        idx=self.idx, count=self.count, k=w.k, topk_count_out=self.topk_count,
+                        workspace=self.workspace, stream=stream)
 
     def gather(self, stream=None):
         if self.pool is None:
@@ -169,8 +185,10 @@ class Pipeline:
                    out=self.gathered, out_capacity_rows=self.gather_capacity, stream=stream)
 
     def run(self, stream=None):
-        """One pass of the path. Top-k and gather both read only the union list, so the
-        gather runs on a second stream, forked after union_compact and joined at the end."""
+        """One pass of the path. The gather reads only the union list. It runs on a second
+        stream, forked after the top-k scoring (which, like the gather, streams from HBM)
+        so that it overlaps the top-k selection (one workgroup per list, latency-bound),
+        and joined at the end."""
         main = torch.cuda.current_stream() if stream is None else stream
         self.project(main)
         self.score_select(main)
@@ -179,10 +197,11 @@ class Pipeline:
             self.topk(main)
             self.gather(main)
             return
+        self.topk_score_stage(main)
         self._fork.record(main)
         self._side.wait_event(self._fork)
         self.gather(self._side)
-        self.topk(main)
+        self.topk_select_stage(main)
         self._join.record(self._side)
         main.wait_event(self._join)
 

@@ -28,6 +28,7 @@ def test_header_declares_the_five_calls():
     fns = declared_functions()
     for f in ("lsa_project", "lsa_score_select", "lsa_union_compact", "lsa_topk", "lsa_gather",
               "lsa_topk_workspace_size", "lsa_pack_weights_size", "lsa_pack_weights", "lsa_project_packed",
+              "lsa_topk_score", "lsa_topk_select",
               "lsa_last_error", "lsa_version"):
         assert f in fns
 
@@ -149,6 +150,21 @@ def test_union_topk_gather_validation(lsa):
     _expect(lsa, lsa.ERR_WORKSPACE, lsa.topk, [tl], **tb, workspace=_WS(), match="workspace")
     _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.topk, [tl], **{**tb, "k": 0}, workspace=_WS())
     assert lsa.topk_workspace_size(3, 2, 30, 2048) == 3 * 30 * 4
+    # the two stages of the top-k check what each reads
+    class _WSBig(_WS):  # a workspace stand-in that is large enough
+        def numel(self):
+            return 1 << 20
+    sb = {k_: v for k_, v in tb.items() if k_ not in ("k", "topk_count_out")}
+    _expect(lsa, lsa.ERR_WORKSPACE, lsa.topk_score, [tl], **sb, workspace=_WS(), match="workspace")
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.topk_score, [tl], **{**sb, "d_h": 96}, workspace=_WS(), match="d_h")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.topk_score, [{**tl, "keys": None}], **sb, workspace=_WSBig(),
+            match="must be set")
+    xb = {k_: v for k_, v in tb.items() if k_ not in ("n_h", "d_h", "key_dtype")}
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.topk_select, [tl], **{**xb, "k": 0}, workspace=_WS())
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.topk_select, [{**tl, "topk_idx_out": None}], **xb, workspace=_WSBig(),
+            match="topk_idx_out")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.topk_select, [tl], **{**xb, "topk_count_out": None}, workspace=_WS())
+    _expect(lsa, lsa.ERR_WORKSPACE, lsa.topk_select, [tl], **xb, workspace=_WS(), match="workspace")
     gb = dict(row_bytes=1024, B=2, pool_row_offsets=FAKE, pool_row_offsets_host=ko, idx=FAKE, idx_offsets=FAKE,
               count=FAKE, out=FAKE, out_capacity_rows=30, stream=0)
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.gather, FAKE, **{**gb, "row_bytes": 1000}, match="multiple of 16")
