@@ -34,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_select_traffic_three_layer_b8.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_select_traffic_{}.txt")  # per workload
 # what the score_select kernel is built from: a change to any of these invalidates the measured traffic
 SCORE_SOURCES = ["csrc/score.hip", "csrc/scorer.hpp", "csrc/common.hpp", "csrc/kernels.hpp", "build.py"]
 
@@ -53,10 +53,11 @@ def score_source_hash() -> str:
 
 def read_traffic(workload: str):
     """HBM bytes per score_select launch from the committed PMC summary, if it was taken on these sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILE.format(workload)
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith(("#", " ", "|", "`")):
                 k, v = line.split(":", 1)
