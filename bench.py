@@ -36,7 +36,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_select_traffic_{}.txt")  # per workload
 # what the score_select kernel is built from: a change to any of these invalidates the measured traffic
-SCORE_SOURCES = ["csrc/score.hip", "csrc/scorer.hpp", "csrc/common.hpp", "csrc/kernels.hpp", "build.py"]
+SCORE_SOURCES = ["csrc/score.hip", "csrc/score_stream.hip", "csrc/cursor.hpp", "csrc/scorer.hpp", "csrc/common.hpp",
+                 "csrc/kernels.hpp", "build.py"]
 
 
 def log(*a):
@@ -207,7 +208,8 @@ def main():
                    "total_entries_per_layer": rows, "key_dtype": w.key_dtype, "n_h": w.n_h, "d_h": w.d_h,
                    "d": w.d, "r": w.r, "k": w.k, "threshold": w.threshold, "pool_row_bytes": w.pool_dim * 2},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "kernel": "score_select_kernel",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "score_stream_kernel" if w.key_dtype in ("bf16", "fp8") else "score_select_kernel",
                      "bytes_per_launch": ab["bytes_per_launch"], "per_entry_bytes": ab["per_entry_bytes"],
                      "avg_launch_us": stage_ms["score_select"] * 1e3},
         "stages_us": {k: v * 1e3 for k, v in stage_ms.items()},

@@ -11,7 +11,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["score.hip", "union.hip", "topk.hip", "gather.hip", "project.hip", "lsa_api.hip"]
+SOURCES = ["score.hip", "score_stream.hip", "union.hip", "topk.hip", "gather.hip", "project.hip", "lsa_api.hip"]
 OUT = os.path.join(HERE, "liblsa.so")
 
 BUILD_DIR = os.path.join(HERE, "_build")
@@ -22,6 +22,7 @@ HIPCC_FLAGS = [
     # MFMA results in ordinary VGPRs: the epilogues read them without v_accvgpr_read copies
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
+SOURCE_FLAGS: dict = {}  # per-source additions to HIPCC_FLAGS
 _NOISE = "is not a recognized feature for this target"
 
 
@@ -45,7 +46,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include")]
     objs = [os.path.join(BUILD_DIR, s.replace(".hip", ".o")) for s in SOURCES]
-    _run([[hipcc, *HIPCC_FLAGS, *inc, "-c", os.path.join(HERE, "csrc", s), "-o", o]
+    _run([[hipcc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(s, []), *inc, "-c", os.path.join(HERE, "csrc", s), "-o", o]
           for s, o in zip(SOURCES, objs)], verbose)
     tmp = OUT + ".tmp"
     _run([[hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]], verbose)

@@ -20,9 +20,11 @@ struct ScoreArgs {
   int64_t word_base;       // mwo[0]
   int64_t words_per_layer; // mwo[B] - mwo[0]
   int64_t total_words;     // L * words_per_layer
-  int32_t B, n_h;
+  int32_t B, n_h, L;
   float thr;               // logit threshold
   int32_t group;           // pairs per interleave group (grid size is a multiple)
+  // one-wave-per-tile kernel: a block's waves take chunks of chunk_words mask words
+  int32_t chunk_words;
 };
 
 struct TopkScoreArgs {
@@ -85,6 +87,9 @@ struct ProjArgs {
 };
 
 hipError_t launch_score_select(const ScoreArgs& a, int key_kind, int d_h, int pairs, int depth, hipStream_t st);
+// one wave per tile, keys loaded straight into LDS (bf16 and fp8 keys)
+bool score_stream_supported(int key_kind, int d_h);
+hipError_t launch_score_stream(const ScoreArgs& a, int key_kind, int d_h, int waves, int ring, hipStream_t st);
 hipError_t launch_topk_score(const TopkScoreArgs& a, int key_kind, int d_h, int grid, int depth, hipStream_t st);
 hipError_t launch_topk_select(const TopkSelectArgs& a, int L, hipStream_t st);
 hipError_t launch_union_compact(const UnionArgs& a, int B, int64_t max_words, hipStream_t st);

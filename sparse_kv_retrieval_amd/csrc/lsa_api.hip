@@ -272,8 +272,17 @@ lsa_status lsa_score_select(const lsa_score_layer* layers, int32_t L, int32_t B,
   a.word_base = mask_word_offsets_host[0];
   a.words_per_layer = mask_word_offsets_host[B] - mask_word_offsets_host[0];
   a.total_words = a.words_per_layer * L;
-  a.B = B; a.n_h = n_h; a.thr = (float)t;
+  a.B = B; a.n_h = n_h; a.L = L; a.thr = (float)t;
   if (a.total_words == 0) return LSA_OK;
+  if (score_stream_supported(kind, d_h) && env_int("LSA_SCORE_PAIRS", 0) == 0) {
+    // one block of 8 waves per CU, each block a contiguous run of mask words
+    // that its waves take in chunks of a few words
+    a.chunk_words = std::max(2, env_int("LSA_SCORE_CHUNK", 4));
+    const int64_t waves = std::min<int64_t>((a.total_words + 7) / 8, (int64_t)cu_count() * env_int("LSA_SCORE_BLOCKS_PER_CU", 1));
+    a.group = 1;
+    const hipError_t e = launch_score_stream(a, kind, d_h, (int)waves, env_int("LSA_SCORE_RING", 0), stream);
+    return e == hipSuccess ? LSA_OK : hip_fail("lsa_score_select launch", e);
+  }
   // One block per pair of waves. Groups of `group` pairs take interleaved words of a contiguous run.
   int64_t pairs = std::min<int64_t>(a.total_words, (int64_t)cu_count() * env_int("LSA_SCORE_PAIRS_PER_CU", 4));
   a.group = (int32_t)std::max<int64_t>(1, std::min<int64_t>(env_int("LSA_SCORE_GROUP", 1), pairs));

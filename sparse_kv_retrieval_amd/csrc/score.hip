@@ -11,6 +11,7 @@
 // mask word.
 #include "kernels.hpp"
 #include "scorer.hpp"
+#include "cursor.hpp"
 
 namespace lsa {
 
@@ -49,60 +50,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Sequence table lookups. For up to SEQ_TAB entries the key and word offsets
-// are copied to LDS once per block. A lookup is then an LDS read, which never
-// waits on the vector-memory counter that tracks the key DMAs.
-constexpr int SEQ_TAB = 256;
-
-struct SeqTab {
-  const int64_t* koff;  // LDS or global
-  const int64_t* mwo;
-};
-
-// Wave-uniform cursor over the mask words of one wave: (layer, sequence, word).
-// It advances one word at a time, so there is no division or search in the
-// steady state. A search runs only when the cursor is placed.
-struct WordCursor {
-  int l, b;
-  int64_t word;     // word index in the mask layout
-  int64_t seq_hi;   // first word after sequence b
-  int32_t e0;       // entry index (within sequence b) of the word's first bit
-  int32_t nb;       // sequence b's entry count (< 2^31, checked on the host)
-  int64_t row0;     // sequence b's first key row
-
-  __device__ __forceinline__ void load_seq(const SeqTab& t) {
-    const int64_t lo = uni(t.mwo[b]);
-    seq_hi = uni(t.mwo[b + 1]);
-    row0 = uni(t.koff[b]);
-    nb = uni((int32_t)(uni(t.koff[b + 1]) - row0));
-    e0 = uni((int32_t)((word - lo) * 64));
-  }
-  __device__ __forceinline__ void place(const ScoreArgs& a, const SeqTab& t, int64_t gw) {
-    l = uni((int32_t)(gw / a.words_per_layer));
-    word = uni(a.word_base + (gw - (int64_t)l * a.words_per_layer));
-    b = uni(upper_seq(t.mwo, a.B, word));
-    load_seq(t);
-  }
-  __device__ __forceinline__ void next(const ScoreArgs& a, const SeqTab& t) {
-    ++word;
-    e0 += 64;
-    if (word == seq_hi) {
-      if (word == a.word_base + a.words_per_layer) {
-        ++l;
-        word = a.word_base;
-        b = 0;
-      } else {
-        ++b;
-      }
-      while (uni(t.mwo[b + 1]) == uni(t.mwo[b])) ++b;  // skip empty sequences
-      load_seq(t);
-    }
-  }
-  __device__ __forceinline__ void advance(const ScoreArgs& a, const SeqTab& t, int g) {
-    for (int i = 0; i < g; ++i) next(a, t);
-  }
-};
-
 // Score + select: keys streamed HBM -> registers -> LDS -> MFMA, two waves per tile.
 //
 // A block is one pair of waves and owns a contiguous run of mask words. Each
@@ -140,9 +87,10 @@ struct TileIO {
 // if the entry exists), in mask word `word` of layer `l`.
 struct TileMeta {
   bool valid = false;
-  int64_t row = 0, word = 0;
-  int l = 0;
-  float scale = 1.0f;  // fp8 keys: the entry's scale
+  int64_t row = 0;
+  uint64_t* mw = nullptr;  // the tile's mask word
+  float* so = nullptr;     // the layer's sigmoid scores, or null
+  float scale = 1.0f;      // fp8 keys: the entry's scale
 };
 
 // Threshold, ballot and stores of one tile, given its full logit x (lane n of
@@ -151,10 +99,9 @@ struct TileMeta {
 __device__ __forceinline__ void finish_tile(const ScoreArgs& a, const TileMeta& m, float x, int odd,
                                             uint32_t& bits0, int lane, int g) {
   const uint32_t bits = (uint32_t)__ballot(m.valid && x >= a.thr);
-  float* so = a.score[m.l];
-  if (so != nullptr && g == 0 && m.valid) so[m.row] = 1.0f / (1.0f + __expf(-x));
+  if (m.so != nullptr && g == 0 && m.valid) m.so[m.row] = 1.0f / (1.0f + __expf(-x));
   if (odd) {
-    if (lane == 0) a.mask[m.l][m.word] = (uint64_t)bits0 | ((uint64_t)bits << 32);
+    if (lane == 0) *m.mw = (uint64_t)bits0 | ((uint64_t)bits << 32);
   } else {
     bits0 = bits;
   }
@@ -167,20 +114,10 @@ __global__ __launch_bounds__(128) void score_select_kernel(const ScoreArgs a) {
   static_assert(S_t::ROW_BYTES == IO::LRB, "LDS row layout");
   __shared__ __attribute__((aligned(16))) char stage[2][IO::LSUB];
   __shared__ float xpart[2][32];
-  __shared__ int64_t tab[2][SEQ_TAB + 1];
 
   const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
   const int h = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // which half of the heads
-  SeqTab t{a.key_off, a.mwo};
-  if (a.B < SEQ_TAB) {
-    for (int i = threadIdx.x; i <= a.B; i += 128) {
-      tab[0][i] = a.key_off[i];
-      tab[1][i] = a.mwo[i];
-    }
-    __syncthreads();
-    t.koff = tab[0];
-    t.mwo = tab[1];
-  }
+  const SeqTab t(a.key_off, a.mwo);
   // Pairs form groups of G. A group owns a contiguous run of mask words, and
   // its pairs take every G-th word of the run. The G pairs then stream
   // neighbouring tiles, which keeps DRAM accesses local, while each pair stays
@@ -229,14 +166,13 @@ __global__ __launch_bounds__(128) void score_select_kernel(const ScoreArgs a) {
 #define LSA_LOAD_TILE(SLOT, JJ, LIVE)                                                                 \
   do {                                                                                              \
     const bool live_ = (LIVE);                                                                      \
-    const int kl_ = live_ ? ic.l : 0;                                                               \
     const int32_t e_ = ic.e0 + ((JJ) & 1) * 32;                                                     \
     const int64_t row_ = ic.row0 + e_;                                                              \
     const uint32_t nr_ = live_ ? (uint32_t)uni(max(0, min(32, ic.nb - e_))) : 0u;                     \
-    const auto rk_ = buf_rsrc((const char*)a.keys[kl_] + row_ * IO::GRB, nr_ * IO::GRB);            \
+    const auto rk_ = buf_rsrc(ic.keys + row_ * IO::GRB, nr_ * IO::GRB);                             \
     _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i) R[SLOT][i] = buf_load16_nt(rk_, loff[i]);   \
     if constexpr (KT == KEY_FP8) {                                                                  \
-      const auto rs_ = buf_rsrc(a.scale[kl_] + row_, nr_ * 4);                                      \
+      const auto rs_ = buf_rsrc(ic.scale + row_, nr_ * 4);                                          \
       SC[SLOT] = __uint_as_float(buf_load4(rs_, n * 4));                                            \
     }                                                                                               \
     if (live_ && ((JJ) & 1)) ic.advance(a, t, G);                                                   \
@@ -316,8 +252,8 @@ __global__ __launch_bounds__(128) void score_select_kernel(const ScoreArgs a) {
         const int32_t se = cc.e0 + (j & 1) * 32 + n;
         m1.valid = se < cc.nb;
         m1.row = cc.row0 + se;
-        m1.word = cc.word;
-        m1.l = cc.l;
+        m1.mw = cc.mask + cc.word;
+        m1.so = cc.score;
         m1.scale = scale;
       }
       S.mma(acc);
@@ -360,6 +296,13 @@ struct TileCursor {
   int64_t base;       // first row of sequence b (also where its list starts)
   int32_t cnt;        // entries in b's list
   int32_t nrow;       // rows of sequence b
+  const char* keys;   // layer l's keys and fp8 scales (past the last layer: the last layer's, unused)
+  const float* scale;
+  __device__ __forceinline__ void load_layer(const TopkScoreArgs& a) {
+    const int ll = l < a.L ? l : a.L - 1;
+    keys = (const char*)a.keys[ll];
+    scale = a.scale[ll];
+  }
   __device__ __forceinline__ void load_seq(const TopkScoreArgs& a, const int32_t* tp) {
     nt = uni(tp[b + 1]) - uni(tp[b]);
     base = uni(a.key_off[b]);
@@ -373,6 +316,7 @@ struct TileCursor {
     b = uni(upper_seq(tp, a.B, tt));
     jt = tt - uni(tp[b]);
     load_seq(a, tp);
+    load_layer(a);
   }
   __device__ __forceinline__ void next(const TopkScoreArgs& a, const int32_t* tp) {
     if (++jt < nt) return;
@@ -381,6 +325,7 @@ struct TileCursor {
       if (++b == a.B) {
         b = 0;
         ++l;
+        load_layer(a);
       }
     } while (uni(tp[b + 1]) == uni(tp[b]));
     load_seq(a, tp);
@@ -442,13 +387,12 @@ __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) 
 #define LSA_LOAD_KEYS(SLOT, XSLOT, LIVE)                                                       \
   do {                                                                                         \
     const bool live_ = (LIVE);                                                                 \
-    const int kl_ = live_ ? ic.l : 0;                                                          \
-    const auto rk_ = buf_rsrc((const char*)a.keys[kl_] + ic.base * IO::GRB, (uint32_t)ic.nrow * IO::GRB); \
+    const auto rk_ = buf_rsrc(ic.keys + ic.base * IO::GRB, (uint32_t)ic.nrow * IO::GRB);          \
     _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i)                                        \
       R[SLOT][i] = buf_load16_nt(                                                              \
           rk_, live_ && loads ? (uint32_t)IX[XSLOT][i] * IO::GRB + lchunk[i] * 16 : BUF_OOB);   \
     if constexpr (KT == KEY_FP8) {                                                             \
-      const auto rs_ = buf_rsrc(a.scale[kl_] + ic.base, (uint32_t)ic.nrow * 4);                \
+      const auto rs_ = buf_rsrc(ic.scale + ic.base, (uint32_t)ic.nrow * 4);                    \
       SC[SLOT] = __uint_as_float(buf_load4(rs_, live_ ? (uint32_t)IXS[XSLOT] * 4 : BUF_OOB));  \
     }                                                                                          \
     if (live_) ic.next(a, tp);                                                                 \

@@ -131,14 +131,17 @@ struct Scorer {
   // max(int(x), 0) on the float's bits: exact for IEEE floats (every negative
   // value, -0 included, becomes +0) and free of NaN canonicalisation.
   // This lane's share of the head sum (its 16*NHB heads), before the lane swap.
+  // Two interleaved sums halve the dependent chain of FMAs.
   __device__ __forceinline__ float partial(const f32x16 (&acc)[NHB]) const {
-    float part = 0.0f;
+    float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
     for (int mb = 0; mb < NHB; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        part = fmaf(gate[mb][i], __int_as_float(max(__float_as_int(acc[mb][i]), 0)), part);
-    return part;
+      for (int i = 0; i < 16; i += 2) {
+        p0 = fmaf(gate[mb][i], __int_as_float(max(__float_as_int(acc[mb][i]), 0)), p0);
+        p1 = fmaf(gate[mb][i + 1], __int_as_float(max(__float_as_int(acc[mb][i + 1]), 0)), p1);
+      }
+    return p0 + p1;
   }
 
   __device__ __forceinline__ float logit(const f32x16 (&acc)[NHB]) const {
