@@ -56,6 +56,34 @@ def test_small_parity(case, torch_cuda):
           f"band_mismatch={st['mismatch_in_band']} max_dI={st['max_dI']:.2e}")
 
 
+# Launch variants of the score pass, chosen by environment knobs the library
+# reads at each call: the pair kernel (two waves per tile), and the
+# one-wave-per-tile kernel with other chunk sizes and LDS rings.
+SCORE_VARIANTS = {
+    "pairs": {"LSA_SCORE_PAIRS": "1"},
+    "chunk2": {"LSA_SCORE_CHUNK": "2"},
+    "chunk3_ring8": {"LSA_SCORE_CHUNK": "3", "LSA_SCORE_RING": "8"},
+    "chunk5": {"LSA_SCORE_CHUNK": "5"},
+}
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("variant", list(SCORE_VARIANTS))
+@pytest.mark.parametrize("case", ["three_layer_mixed", "fp8_two_seq", "ragged_small", "bf16_16heads_d64"])
+def test_score_variants(case, variant, torch_cuda, monkeypatch):
+    from sparse_kv_retrieval_amd.pipeline import Pipeline
+    for k, v in SCORE_VARIANTS[variant].items():
+        monkeypatch.setenv(k, v)
+    w = SMALL[case]
+    P.say(f"[variant] case={case} variant={variant}")
+    inp = synth.make(w)
+    p = Pipeline(inp, "cuda", with_scores=True, guard=True)
+    p.run()
+    torch_cuda.cuda.synchronize()
+    assert p.check_guards() == [], f"writes outside an output buffer: {p.check_guards()}"
+    P.full_check(p, inp)
+
+
 @pytest.mark.gpu
 def test_repeat_is_deterministic(torch_cuda):
     """Two runs give bit-identical masks, lists, top-k and gather."""
