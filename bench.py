@@ -115,6 +115,7 @@ def main():
     ap.add_argument("--workload", default="three_layer_b8")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-host-fetch", action="store_true", help="skip the cold-pool (pinned host) fetch measurement")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -182,6 +183,31 @@ def main():
     torch.cuda.synchronize()
     ms_per_step_graph = (time.perf_counter() - t0) * 1e3 / args.steps
 
+    host_fetch = None
+    if not args.no_host_fetch and inp.pool is not None:
+        # The load step from the cold pool: the same union rows read from a pinned
+        # host copy of the pool over the host link (lsa_fetch_host). Reported on
+        # its own; it is not part of the step above.
+        log("[bench] cold-pool fetch")
+        a = np.ascontiguousarray(inp.pool)
+        p.pool_host = torch.from_numpy(a.view(np.int16)).pin_memory()
+        for _ in range(2):
+            p.fetch_host()
+        torch.cuda.synchronize()
+        reps = 5
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            p.fetch_host()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fms = e0.elapsed_time(e1) / reps
+        rows_f = int(min(int(p.count.sum()), p.gather_capacity))
+        fbytes = rows_f * w.pool_dim * 2
+        host_fetch = {"rows": rows_f, "bytes_read": fbytes, "ms": fms, "GB_per_s": fbytes / (fms * 1e-3) / 1e9,
+                      "what": "union rows read from pinned host memory over the host link into HBM (lsa_fetch_host)"}
+        p.pool_host = None
+
     counts = p.count.cpu().numpy()
     rows = int(inp.key_offsets[-1])
     entries = int(np.sum(inp.lengths)) * w.L
@@ -217,6 +243,8 @@ def main():
         "ms_per_step_graph": ms_per_step_graph,
         "selection": {"union_fraction": float(counts.sum()) / rows, "union_per_seq_mean": float(counts.mean())},
     }
+    if host_fetch is not None:
+        out["host_fetch"] = host_fetch
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline")
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)

@@ -17,6 +17,8 @@
  *                                                    [BLOG] §2.2, §3.2
  *   lsa_gather         copy the selected compressed-KV rows into a compact buffer
  *                                                    [HYPER] 方法 (load C^MemComp)
+ *   lsa_fetch_host     the same copy from a pool in pinned host memory
+ *                                                    [HYPER] 方法, [BLOG] §3
  *
  * Conventions shared by every call:
  *  - Ownership: the caller allocates every buffer. Pointers marked "dev" are
@@ -279,6 +281,28 @@ lsa_status lsa_gather(const void* pool /* dev */, int64_t row_bytes, int32_t B,
                       const int32_t* count /* dev [B] */, void* out /* dev */,
                       const int64_t* out_row_offsets /* dev [B+1] or NULL */,
                       int64_t out_capacity_rows, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * lsa_fetch_host: the same row copy as lsa_gather, from a cold pool kept in
+ * host memory ([HYPER] 方法 and [BLOG] §3: the subset C^MemComp is loaded from
+ * the CPU-side pool into GPU memory). The device reads the selected rows
+ * straight from pinned host memory over the host link, with no staging copy,
+ * and writes them into `out` in device memory.
+ *
+ * Arguments and layout are those of lsa_gather, except:
+ *   - pool_host must point into pinned host memory the device can read
+ *     (allocated with hipHostMalloc or hipHostAlloc); pageable memory returns
+ *     LSA_ERR_INVALID_ARG. The caller keeps it alive until the stream has
+ *     passed the call.
+ * The copy is bit-exact. Its speed is that of the host link, not of HBM.
+ * ---------------------------------------------------------------------- */
+lsa_status lsa_fetch_host(const void* pool_host /* pinned host */, int64_t row_bytes, int32_t B,
+                          const int64_t* pool_row_offsets /* dev [B+1] */,
+                          const int64_t* pool_row_offsets_host /* host [B+1] */,
+                          const int32_t* idx /* dev */, const int64_t* idx_offsets /* dev [B] */,
+                          const int32_t* count /* dev [B] */, void* out /* dev */,
+                          const int64_t* out_row_offsets /* dev [B+1] or NULL */,
+                          int64_t out_capacity_rows, hipStream_t stream);
 
 /* Text describing the last non-OK status returned on the calling thread. */
 const char* lsa_last_error(void);

@@ -1,6 +1,9 @@
 // Load step: copy the selected compressed-KV rows into a compact buffer (the
 // hyper.ai digest of FlashMemory-DeepSeek-V4, "方法": C^MemComp is loaded into
-// GPU memory). This version copies HBM to HBM.
+// GPU memory). The pool is either in HBM (lsa_gather) or in pinned host
+// memory (lsa_fetch_host: the cold pool of the write-up, read over the host
+// link without a staging copy); the kernel is the same, with more rows in
+// flight per wave for the host link's longer latency.
 //
 // Each block computes, in LDS, where every sequence's rows land: a prefix sum
 // of min(count, capacity) in explicit mode, or of count in packed mode. For up
@@ -17,11 +20,13 @@
 namespace lsa {
 
 static constexpr int GA_THREADS = 256;
-static constexpr int GA_ROWS = 8;    // rows per wave per iteration
 static constexpr int GA_TAB = 1024;  // sequences whose offsets are cached in LDS
 
 // Dynamic LDS: pre[B+1], then (for B <= GA_TAB) t_pool[B], t_idx[B], t_out[B], all int64.
+// GA_ROWS rows per wave per iteration (at most 64: one lane resolves each).
+template <int GA_ROWS>
 __global__ __launch_bounds__(GA_THREADS) void gather_kernel(const GatherArgs a) {
+  static_assert(GA_ROWS >= 1 && GA_ROWS <= 64, "rows per wave");
   extern __shared__ int64_t dyn[];
   const bool cached = a.B <= GA_TAB;
   int64_t* pre = dyn;
@@ -101,9 +106,13 @@ __global__ __launch_bounds__(GA_THREADS) void gather_kernel(const GatherArgs a) 
   }
 }
 
-hipError_t launch_gather(const GatherArgs& a, int grid, hipStream_t st) {
+hipError_t launch_gather(const GatherArgs& a, int grid, int rows_per_wave, hipStream_t st) {
   const size_t lds = sizeof(int64_t) * ((size_t)a.B + 1 + (a.B <= GA_TAB ? 3 * (size_t)a.B : 0));
-  hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(GA_THREADS), lds, st, a);
+  switch (rows_per_wave) {
+    case 16: hipLaunchKernelGGL(gather_kernel<16>, dim3(grid), dim3(GA_THREADS), lds, st, a); break;
+    case 32: hipLaunchKernelGGL(gather_kernel<32>, dim3(grid), dim3(GA_THREADS), lds, st, a); break;
+    default: hipLaunchKernelGGL(gather_kernel<8>, dim3(grid), dim3(GA_THREADS), lds, st, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -93,7 +93,7 @@ hipError_t launch_score_stream(const ScoreArgs& a, int key_kind, int d_h, int wa
 hipError_t launch_topk_score(const TopkScoreArgs& a, int key_kind, int d_h, int grid, int depth, hipStream_t st);
 hipError_t launch_topk_select(const TopkSelectArgs& a, int L, hipStream_t st);
 hipError_t launch_union_compact(const UnionArgs& a, int B, int64_t max_words, hipStream_t st);
-hipError_t launch_gather(const GatherArgs& a, int grid, hipStream_t st);
+hipError_t launch_gather(const GatherArgs& a, int grid, int rows_per_wave, hipStream_t st);
 hipError_t launch_project(const ProjArgs& a, int L, bool f32, hipStream_t st);
 hipError_t launch_project_packed(const ProjArgs& a, int L, hipStream_t st);
 hipError_t launch_pack_weights(const void* w, int rows, int K, void* out, hipStream_t st);

@@ -342,10 +342,15 @@ lsa_status lsa_topk_select(const lsa_topk_layer* layers, int32_t L, int32_t B, c
                      workspace, workspace_bytes, stream, false, true);
 }
 
-lsa_status lsa_gather(const void* pool, int64_t row_bytes, int32_t B, const int64_t* pool_row_offsets,
-                      const int64_t* pool_row_offsets_host, const int32_t* idx, const int64_t* idx_offsets,
-                      const int32_t* count, void* out, const int64_t* out_row_offsets, int64_t out_capacity_rows,
-                      hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// Argument checks and launch shared by lsa_gather and lsa_fetch_host; `pool`
+// is the address the kernel reads through.
+lsa_status gather_call(const char* what, const void* pool, int64_t row_bytes, int32_t B,
+                       const int64_t* pool_row_offsets, const int64_t* pool_row_offsets_host, const int32_t* idx,
+                       const int64_t* idx_offsets, const int32_t* count, void* out, const int64_t* out_row_offsets,
+                       int64_t out_capacity_rows, int rows_per_wave, int waves_per_cu, hipStream_t stream) {
   if (B < 1 || B > LSA_TOPK_MAX_B) return fail(LSA_ERR_UNSUPPORTED, "B must be in [1, %d] (got %d)", LSA_TOPK_MAX_B, B);
   if (row_bytes <= 0 || row_bytes % 16) return fail(LSA_ERR_INVALID_ARG, "row_bytes must be a positive multiple of 16");
   if (!pool || !pool_row_offsets || !idx || !idx_offsets || !count || !out)
@@ -362,9 +367,43 @@ lsa_status lsa_gather(const void* pool, int64_t row_bytes, int32_t B, const int6
   GatherArgs a{};
   a.pool = (const char*)pool; a.pool_off = pool_row_offsets; a.idx = idx; a.idx_off = idx_offsets; a.count = count;
   a.out = (char*)out; a.out_off = out_row_offsets; a.out_capacity = out_capacity_rows; a.row_bytes = row_bytes; a.B = B;
-  const int64_t waves = std::min<int64_t>((bound + 7) / 8, (int64_t)cu_count() * 16);
-  const hipError_t e = launch_gather(a, (int)((waves + 3) / 4), stream);
-  return e == hipSuccess ? LSA_OK : hip_fail("lsa_gather launch", e);
+  const int64_t waves = std::min<int64_t>((bound + rows_per_wave - 1) / rows_per_wave, (int64_t)cu_count() * waves_per_cu);
+  const hipError_t e = launch_gather(a, (int)((waves + 3) / 4), rows_per_wave, stream);
+  return e == hipSuccess ? LSA_OK : hip_fail(what, e);
+}
+}  // namespace
+
+extern "C" {
+
+lsa_status lsa_gather(const void* pool, int64_t row_bytes, int32_t B, const int64_t* pool_row_offsets,
+                      const int64_t* pool_row_offsets_host, const int32_t* idx, const int64_t* idx_offsets,
+                      const int32_t* count, void* out, const int64_t* out_row_offsets, int64_t out_capacity_rows,
+                      hipStream_t stream) {
+  return gather_call("lsa_gather launch", pool, row_bytes, B, pool_row_offsets, pool_row_offsets_host, idx, idx_offsets,
+                     count, out, out_row_offsets, out_capacity_rows, 8, 16, stream);
+}
+
+lsa_status lsa_fetch_host(const void* pool_host, int64_t row_bytes, int32_t B, const int64_t* pool_row_offsets,
+                          const int64_t* pool_row_offsets_host, const int32_t* idx, const int64_t* idx_offsets,
+                          const int32_t* count, void* out, const int64_t* out_row_offsets, int64_t out_capacity_rows,
+                          hipStream_t stream) {
+  if (!pool_host) return fail(LSA_ERR_INVALID_ARG, "pool_host is NULL");
+  // The pool must be pinned host memory that the device can read (hipHostMalloc).
+  hipPointerAttribute_t attr{};
+  const hipError_t pe = hipPointerGetAttributes(&attr, pool_host);
+  if (pe != hipSuccess || attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) {
+    (void)hipGetLastError();  // leave no error behind for the caller's next HIP call
+    return fail(LSA_ERR_INVALID_ARG, "pool_host must be pinned host memory allocated with hipHostMalloc");
+  }
+  // the device's address for pool_host (the attributes may describe the whole allocation)
+  const char* dev_view = attr.hostPointer
+                             ? (const char*)attr.devicePointer + ((const char*)pool_host - (const char*)attr.hostPointer)
+                             : (const char*)attr.devicePointer;
+  int rows = env_int("LSA_FETCH_ROWS", 16);
+  if (rows != 8 && rows != 16 && rows != 32) rows = 16;
+  return gather_call("lsa_fetch_host launch", dev_view, row_bytes, B, pool_row_offsets, pool_row_offsets_host, idx,
+                     idx_offsets, count, out, out_row_offsets, out_capacity_rows, rows,
+                     std::max(1, env_int("LSA_FETCH_WAVES_PER_CU", 16)), stream);
 }
 
 }  // extern "C"

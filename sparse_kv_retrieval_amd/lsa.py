@@ -75,12 +75,13 @@ _topk_score = _sig("lsa_topk_score", _i32, [ctypes.POINTER(TopkLayer), _i32, _i3
 _topk_select = _sig("lsa_topk_select", _i32, [ctypes.POINTER(TopkLayer), _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
                                                _vp, _sz, _vp])
 _gather = _sig("lsa_gather", _i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp])
+_fetch_host = _sig("lsa_fetch_host", _i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp])
 _last_error = _sig("lsa_last_error", ctypes.c_char_p, [])
 _version = _sig("lsa_version", _i32, [])
 
 EXPORTED = ("lsa_project", "lsa_pack_weights_size", "lsa_pack_weights", "lsa_project_packed", "lsa_score_select",
             "lsa_topk_score", "lsa_topk_select", "lsa_union_compact", "lsa_topk_workspace_size", "lsa_topk",
-            "lsa_gather", "lsa_last_error", "lsa_version")
+            "lsa_gather", "lsa_fetch_host", "lsa_last_error", "lsa_version")
 
 
 def last_error() -> str:
@@ -222,3 +223,12 @@ def gather(pool, *, row_bytes, B, pool_row_offsets, pool_row_offsets_host, idx, 
     po, pop = _host64(pool_row_offsets_host)
     _check("lsa_gather", _gather(_p(pool), int(row_bytes), B, _p(pool_row_offsets), pop, _p(idx), _p(idx_offsets),
                                  _p(count), _p(out), _p(out_row_offsets), int(out_capacity_rows), _stream(stream)))
+
+
+def fetch_host(pool_host, *, row_bytes, B, pool_row_offsets, pool_row_offsets_host, idx, idx_offsets, count, out,
+               out_row_offsets=None, out_capacity_rows, stream=None):
+    """lsa_fetch_host: pool_host is a pinned CPU tensor (pin_memory=True); out is on the device."""
+    po, pop = _host64(pool_row_offsets_host)
+    _check("lsa_fetch_host", _fetch_host(_p(pool_host), int(row_bytes), B, _p(pool_row_offsets), pop, _p(idx),
+                                         _p(idx_offsets), _p(count), _p(out), _p(out_row_offsets),
+                                         int(out_capacity_rows), _stream(stream)))

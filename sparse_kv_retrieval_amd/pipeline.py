@@ -13,6 +13,8 @@ scoring and joins at the end):
   lsa_topk           native top-k inside the union, per (layer, sequence)
                      (run() calls its two stages, lsa_topk_score and lsa_topk_select)
   lsa_gather         the union rows of the compressed-KV pool -> packed compact buffer
+                     (with host_pool=True, lsa_fetch_host reads them from a copy of the
+                     pool in pinned host memory instead: the cold pool)
 
 This module only wires buffers. All arithmetic happens in the HIP kernels.
 """
@@ -39,7 +41,7 @@ CANARY = 0x5A
 
 class Pipeline:
     def __init__(self, inp, device="cuda", *, with_scores=False, with_topk_scores=True, gather_capacity=None,
-                 guard=False, packed=True, overlap=True):
+                 guard=False, packed=True, overlap=True, host_pool=False):
         w = inp.workload
         self.w = w
         self.inp = inp
@@ -81,6 +83,11 @@ class Pipeline:
         self.keys = [_dev(inp.keys[l], dev) for l in range(L)]
         self.scale = [None if inp.key_scale[l] is None else _dev(inp.key_scale[l], dev) for l in range(L)]
         self.pool = None if inp.pool is None else _dev(inp.pool, dev)
+        # the cold pool: the same rows in pinned host memory, read by lsa_fetch_host
+        self.pool_host = None
+        if host_pool and inp.pool is not None:
+            a = np.ascontiguousarray(inp.pool)
+            self.pool_host = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).pin_memory()
 
         f32, i32, i64, i16 = torch.float32, torch.int32, torch.int64, torch.int16
         out = self._out
@@ -184,6 +191,22 @@ class Pipeline:
                    pool_row_offsets_host=self.key_off_h, idx=self.idx, idx_offsets=self.key_off, count=self.count,
                    out=self.gathered, out_capacity_rows=self.gather_capacity, stream=stream)
 
+    def fetch_host(self, stream=None):
+        """The gather's rows, read from the pinned host copy of the pool (lsa_fetch_host)."""
+        if self.pool_host is None:
+            return
+        w = self.w
+        lsa.fetch_host(self.pool_host, row_bytes=w.pool_dim * 2, B=w.B, pool_row_offsets=self.key_off,
+                       pool_row_offsets_host=self.key_off_h, idx=self.idx, idx_offsets=self.key_off, count=self.count,
+                       out=self.gathered, out_capacity_rows=self.gather_capacity, stream=stream)
+
+    def load(self, stream=None):
+        """The load step: from the host pool when there is one, else from HBM."""
+        if self.pool_host is not None:
+            self.fetch_host(stream)
+        else:
+            self.gather(stream)
+
     def run(self, stream=None):
         """One pass of the path. The gather reads only the union list. It runs on a second
         stream, forked after the top-k scoring (which, like the gather, streams from HBM)
@@ -195,12 +218,12 @@ class Pipeline:
         self.union_compact(main)
         if self.pool is None or not self.overlap:
             self.topk(main)
-            self.gather(main)
+            self.load(main)
             return
         self.topk_score_stage(main)
         self._fork.record(main)
         self._side.wait_event(self._fork)
-        self.gather(self._side)
+        self.load(self._side)
         self.topk_select_stage(main)
         self._join.record(self._side)
         main.wait_event(self._join)

@@ -171,6 +171,8 @@ def test_union_topk_gather_validation(lsa):
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.gather, None, **gb)
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.gather, FAKE + 8, **gb, match="aligned")
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.gather, FAKE, **{**gb, "out_capacity_rows": -1})
+    # the host-pool fetch checks its pool before asking the runtime about it
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.fetch_host, None, **gb, match="NULL")
 
 
 def test_binding_has_no_oracle_import():
