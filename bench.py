@@ -12,7 +12,7 @@ Infinity Cache.
 Output: one JSON line. `value` is entries scored+selected per second over the
 whole step (sum over layers and sequences of N_b, divided by the step time).
 Whole steps are timed as Pipeline.run() calls, which launch the gather on a
-second stream so that it overlaps the top-k selection. `ms_per_step_graph` is
+second stream so that it overlaps both top-k stages. `ms_per_step_graph` is
 the same step replayed from a HIP graph, and `ms_per_step_sequential` the five
 calls one after another on one stream (with the per-stage events).
 `roofline` describes the dominant kernel (score_select), from HIP events on
@@ -161,7 +161,7 @@ def main():
                 for i, n in enumerate(names)}
 
     # Whole steps: run() as an application calls it (the gather on a second stream,
-    # overlapping the top-k selection), K steps between two synchronisations.
+    # overlapping the top-k stages), K steps between two synchronisations.
     for _ in range(args.warmup):
         p.run()
     log(f"[bench] timing {args.steps} whole steps")

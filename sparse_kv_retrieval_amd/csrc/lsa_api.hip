@@ -379,8 +379,11 @@ lsa_status lsa_gather(const void* pool, int64_t row_bytes, int32_t B, const int6
                       const int64_t* pool_row_offsets_host, const int32_t* idx, const int64_t* idx_offsets,
                       const int32_t* count, void* out, const int64_t* out_row_offsets, int64_t out_capacity_rows,
                       hipStream_t stream) {
+  int rows = env_int("LSA_GATHER_ROWS", 8);
+  if (rows != 8 && rows != 16 && rows != 32) rows = 8;
   return gather_call("lsa_gather launch", pool, row_bytes, B, pool_row_offsets, pool_row_offsets_host, idx, idx_offsets,
-                     count, out, out_row_offsets, out_capacity_rows, 8, 16, stream);
+                     count, out, out_row_offsets, out_capacity_rows, rows,
+                     std::max(1, env_int("LSA_GATHER_WAVES_PER_CU", 16)), stream);
 }
 
 lsa_status lsa_fetch_host(const void* pool_host, int64_t row_bytes, int32_t B, const int64_t* pool_row_offsets,

@@ -3,8 +3,8 @@
 `Pipeline(inputs)` copies a seeded input set (from `synth.make`) into HBM and
 allocates every output and the top-k workspace once. `run()` then enqueues the
 five library calls, with no allocation and no host synchronisation, on the
-current stream (the gather on a second stream that forks after the top-k
-scoring and joins at the end):
+current stream (the load step on a second stream that forks after the union
+and joins at the end):
 
   lsa_project        memory-indexer and native query/gates for every layer (one call, 2L layers);
                      with bf16 weights, lsa_project_packed on weights packed once at set-up
@@ -41,7 +41,7 @@ CANARY = 0x5A
 
 class Pipeline:
     def __init__(self, inp, device="cuda", *, with_scores=False, with_topk_scores=True, gather_capacity=None,
-                 guard=False, packed=True, overlap=True, host_pool=False):
+                 guard=False, packed=True, overlap=True, host_pool=False, early_fork=True):
         w = inp.workload
         self.w = w
         self.inp = inp
@@ -50,6 +50,7 @@ class Pipeline:
         self._guarded = []
         self.guard = guard
         self.overlap = overlap
+        self.early_fork = early_fork  # fork the load step before the top-k scoring (else after it)
         self._side = torch.cuda.Stream(device=dev)  # default priority
         self._fork = torch.cuda.Event()
         self._join = torch.cuda.Event()
@@ -208,10 +209,12 @@ class Pipeline:
             self.gather(stream)
 
     def run(self, stream=None):
-        """One pass of the path. The gather reads only the union list. It runs on a second
-        stream, forked after the top-k scoring (which, like the gather, streams from HBM)
-        so that it overlaps the top-k selection (one workgroup per list, latency-bound),
-        and joined at the end."""
+        """One pass of the path. The load step (gather, or the cold-pool fetch) needs only the
+        union list, so it runs on a second stream forked right after the union and compaction,
+        overlapping both top-k stages, and joins at the end. (Forking it after the top-k
+        scoring instead, so that it overlaps only the selection, is 14 us slower per step on
+        the three-layer workload: the scoring and the gather share HBM better than they
+        queue.)"""
         main = torch.cuda.current_stream() if stream is None else stream
         self.project(main)
         self.score_select(main)
@@ -220,10 +223,16 @@ class Pipeline:
             self.topk(main)
             self.load(main)
             return
-        self.topk_score_stage(main)
-        self._fork.record(main)
-        self._side.wait_event(self._fork)
-        self.load(self._side)
+        if self.early_fork:
+            self._fork.record(main)
+            self._side.wait_event(self._fork)
+            self.load(self._side)
+            self.topk_score_stage(main)
+        else:
+            self.topk_score_stage(main)
+            self._fork.record(main)
+            self._side.wait_event(self._fork)
+            self.load(self._side)
         self.topk_select_stage(main)
         self._join.record(self._side)
         main.wait_event(self._join)
