@@ -19,6 +19,9 @@
  *                                                    [HYPER] 方法 (load C^MemComp)
  *   lsa_fetch_host     the same copy from a pool in pinned host memory
  *                                                    [HYPER] 方法, [BLOG] §3
+ *   lsa_golden_labels  training targets: per-layer softmax top-p nucleus,
+ *                      cross-layer vote, union over the lookahead window
+ *                                                    [HYPER] 数据集, [BLOG] §4.1
  *
  * Conventions shared by every call:
  *  - Ownership: the caller allocates every buffer. Pointers marked "dev" are
@@ -57,6 +60,7 @@ extern "C" {
 #define LSA_MAX_LAYERS 8
 #define LSA_MAX_HEADS 64
 #define LSA_VERSION 1
+#define LSA_GOLDEN_MAX_ROW (1 << 28)  /* entries per (token, layer) logit row */
 
 typedef enum {
   LSA_F32 = 0,      /* IEEE binary32 */
@@ -303,6 +307,43 @@ lsa_status lsa_fetch_host(const void* pool_host /* pinned host */, int64_t row_b
                           const int32_t* count /* dev [B] */, void* out /* dev */,
                           const int64_t* out_row_offsets /* dev [B+1] or NULL */,
                           int64_t out_capacity_rows, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * lsa_golden_labels: golden-label mining, the training targets of the memory
+ * indexer ([HYPER] 数据集 (Dataset); [BLOG] §4.1 "Golden Label 怎么造"; the
+ * gist.science summary, §2.2). For each token i of a lookahead window of T
+ * tokens and each of L layers, the raw indexer logits y[i][l][s] over the
+ * token's n_valid[i] preceding compressed entries are turned into a softmax,
+ * and the top-p nucleus of that distribution is kept. An entry is golden for
+ * token i when at least `theta` layers keep it; the window's label set is the
+ * union of the tokens' golden sets. The pages use L = 21, p = 0.6, theta = 3.
+ *
+ * Nucleus: entries in descending logit order, equal logits by ascending entry
+ * index; an entry is kept while the mass of the entries before it is below
+ * top_p (so the entry that reaches top_p is kept, and the top entry always is).
+ *
+ *   logits          dev fp32 [T][L][row_stride]; row (i, l) holds token i's
+ *                   logits in its first n_valid[i] entries (finite values);
+ *                   the rest of the row is never read.
+ *   n_valid         dev int32 [T]; values are clamped to [0, row_stride].
+ *   top_p           in (0, 1].  theta >= 1 (theta > L gives an empty set).
+ *   row_mask_out    dev u64 [T * L][W], W = ceil(row_stride / 64): the nucleus
+ *                   of row (i, l) as bits (bit s % 64 of word s / 64); bits at
+ *                   or beyond n_valid[i] are 0.
+ *   nucleus_size_out  dev int32 [T * L] or NULL: kept entries per row.
+ *   token_golden_out  dev u64 [T][W] or NULL: token i's golden entries.
+ *   golden_out      dev u64 [W]: the window's label set.
+ * Probabilities are accumulated in fp64 from fp32 exponentials relative to the
+ * row maximum; an entry whose preceding mass is within about 1e-5 of top_p
+ * may fall either way. Requires 1 <= L <= 64, 1 <= row_stride <=
+ * LSA_GOLDEN_MAX_ROW; logits 4-byte and the mask buffers 8-byte aligned.
+ * ---------------------------------------------------------------------- */
+lsa_status lsa_golden_labels(const float* logits /* dev */, int64_t row_stride, int32_t T, int32_t L,
+                             const int32_t* n_valid /* dev [T] */, float top_p, int32_t theta,
+                             uint64_t* row_mask_out /* dev [T*L][W] */,
+                             int32_t* nucleus_size_out /* dev [T*L] or NULL */,
+                             uint64_t* token_golden_out /* dev [T][W] or NULL */,
+                             uint64_t* golden_out /* dev [W] */, hipStream_t stream);
 
 /* Text describing the last non-OK status returned on the calling thread. */
 const char* lsa_last_error(void);

@@ -86,6 +86,21 @@ struct ProjArgs {
   int32_t B, d, r, n_h, d_h;
 };
 
+// Golden-label mining (nucleus per (token, layer) row, then vote and union).
+struct GoldenArgs {
+  const float* logits;     // [T][L][row_stride]
+  const int32_t* n_valid;  // [T]
+  uint64_t* row_mask;      // [T * L][W]
+  int32_t* nucleus_size;   // [T * L] or null
+  uint64_t* token_golden;  // [T][W] or null
+  uint64_t* golden;        // [W]
+  int64_t row_stride;
+  int64_t W;               // ceil(row_stride / 64)
+  int32_t T, L;
+  float p;
+  int32_t theta;           // 1..127
+};
+
 hipError_t launch_score_select(const ScoreArgs& a, int key_kind, int d_h, int pairs, int depth, hipStream_t st);
 // one wave per tile, keys loaded straight into LDS (bf16 and fp8 keys)
 bool score_stream_supported(int key_kind, int d_h);
@@ -96,6 +111,7 @@ hipError_t launch_union_compact(const UnionArgs& a, int B, int64_t max_words, hi
 hipError_t launch_gather(const GatherArgs& a, int grid, int rows_per_wave, hipStream_t st);
 hipError_t launch_project(const ProjArgs& a, int L, bool f32, hipStream_t st);
 hipError_t launch_project_packed(const ProjArgs& a, int L, hipStream_t st);
+hipError_t launch_golden(const GoldenArgs& a, hipStream_t st);
 hipError_t launch_pack_weights(const void* w, int rows, int K, void* out, hipStream_t st);
 
 // ------------------------------------------------------------ block helpers

@@ -409,4 +409,28 @@ lsa_status lsa_fetch_host(const void* pool_host, int64_t row_bytes, int32_t B, c
                      std::max(1, env_int("LSA_FETCH_WAVES_PER_CU", 16)), stream);
 }
 
+lsa_status lsa_golden_labels(const float* logits, int64_t row_stride, int32_t T, int32_t L, const int32_t* n_valid,
+                             float top_p, int32_t theta, uint64_t* row_mask_out, int32_t* nucleus_size_out,
+                             uint64_t* token_golden_out, uint64_t* golden_out, hipStream_t stream) {
+  if (!logits || !n_valid || !row_mask_out || !golden_out)
+    return fail(LSA_ERR_INVALID_ARG, "logits, n_valid, row_mask_out and golden_out must be set");
+  if (T < 1 || L < 1 || L > 64) return fail(LSA_ERR_INVALID_ARG, "need T >= 1 and 1 <= L <= 64 (got T=%d L=%d)", T, L);
+  if ((int64_t)T * L > INT32_MAX) return fail(LSA_ERR_UNSUPPORTED, "T * L must fit in int32");
+  if (row_stride < 1 || row_stride > LSA_GOLDEN_MAX_ROW)
+    return fail(LSA_ERR_UNSUPPORTED, "row_stride must be in [1, %d] (got %lld)", LSA_GOLDEN_MAX_ROW,
+                (long long)row_stride);
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return fail(LSA_ERR_INVALID_ARG, "top_p must be in (0, 1]");
+  if (theta < 1) return fail(LSA_ERR_INVALID_ARG, "theta must be >= 1 (got %d)", theta);
+  if ((reinterpret_cast<uintptr_t>(logits) & 3u) || (reinterpret_cast<uintptr_t>(row_mask_out) & 7u) ||
+      (reinterpret_cast<uintptr_t>(golden_out) & 7u) || (reinterpret_cast<uintptr_t>(token_golden_out) & 7u))
+    return fail(LSA_ERR_INVALID_ARG, "logits must be 4-byte and mask buffers 8-byte aligned");
+  GoldenArgs a{};
+  a.logits = logits; a.n_valid = n_valid; a.row_mask = row_mask_out; a.nucleus_size = nucleus_size_out;
+  a.token_golden = token_golden_out; a.golden = golden_out;
+  a.row_stride = row_stride; a.W = (row_stride + 63) / 64; a.T = T; a.L = L; a.p = top_p;
+  a.theta = theta > 127 ? 127 : theta;  // more votes than layers: nothing is golden either way
+  const hipError_t e = launch_golden(a, stream);
+  return e == hipSuccess ? LSA_OK : hip_fail("lsa_golden_labels launch", e);
+}
+
 }  // extern "C"

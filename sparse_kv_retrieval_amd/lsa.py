@@ -76,12 +76,13 @@ _topk_select = _sig("lsa_topk_select", _i32, [ctypes.POINTER(TopkLayer), _i32, _
                                                _vp, _sz, _vp])
 _gather = _sig("lsa_gather", _i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp])
 _fetch_host = _sig("lsa_fetch_host", _i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp])
+_golden = _sig("lsa_golden_labels", _i32, [_vp, _i64, _i32, _i32, _vp, _f32, _i32, _vp, _vp, _vp, _vp, _vp])
 _last_error = _sig("lsa_last_error", ctypes.c_char_p, [])
 _version = _sig("lsa_version", _i32, [])
 
 EXPORTED = ("lsa_project", "lsa_pack_weights_size", "lsa_pack_weights", "lsa_project_packed", "lsa_score_select",
             "lsa_topk_score", "lsa_topk_select", "lsa_union_compact", "lsa_topk_workspace_size", "lsa_topk",
-            "lsa_gather", "lsa_fetch_host", "lsa_last_error", "lsa_version")
+            "lsa_gather", "lsa_fetch_host", "lsa_golden_labels", "lsa_last_error", "lsa_version")
 
 
 def last_error() -> str:
@@ -232,3 +233,12 @@ def fetch_host(pool_host, *, row_bytes, B, pool_row_offsets, pool_row_offsets_ho
     _check("lsa_fetch_host", _fetch_host(_p(pool_host), int(row_bytes), B, _p(pool_row_offsets), pop, _p(idx),
                                          _p(idx_offsets), _p(count), _p(out), _p(out_row_offsets),
                                          int(out_capacity_rows), _stream(stream)))
+
+
+def golden_labels(logits, *, row_stride, T, L, n_valid, top_p, theta, row_mask, golden, nucleus_size=None,
+                  token_golden=None, stream=None):
+    """lsa_golden_labels: logits [T, L, row_stride] fp32 and n_valid [T] int32 on the device; the mask
+    outputs are int64 tensors of ceil(row_stride / 64) words per row."""
+    _check("lsa_golden_labels", _golden(_p(logits), int(row_stride), int(T), int(L), _p(n_valid), float(top_p),
+                                        int(theta), _p(row_mask), _p(nucleus_size), _p(token_golden), _p(golden),
+                                        _stream(stream)))

@@ -175,6 +175,23 @@ def test_union_topk_gather_validation(lsa):
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.fetch_host, None, **gb, match="NULL")
 
 
+def test_golden_labels_validation(lsa):
+    gb = dict(row_stride=1000, T=4, L=21, n_valid=FAKE, top_p=0.6, theta=3, row_mask=FAKE, golden=FAKE, stream=0)
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, None, **gb, match="must be set")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "golden": None}, match="must be set")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "n_valid": None}, match="must be set")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "L": 65}, match="L <= 64")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "T": 0})
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "top_p": 0.0}, match="top_p")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "top_p": 1.5}, match="top_p")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "top_p": float("nan")}, match="top_p")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "theta": 0}, match="theta")
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.golden_labels, FAKE, **{**gb, "row_stride": 0}, match="row_stride")
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.golden_labels, FAKE, **{**gb, "row_stride": (1 << 28) + 1})
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE + 2, **gb, match="aligned")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "row_mask": FAKE + 4}, match="aligned")
+
+
 def test_binding_has_no_oracle_import():
     """The product path (binding, pipeline, library sources) never refers to the oracle."""
     pkg = os.path.join(ROOT, "sparse_kv_retrieval_amd")
@@ -183,4 +200,4 @@ def test_binding_has_no_oracle_import():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 txt = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", txt, re.M), f
-                assert "lsa_oracle" not in txt, f
+                assert "lsa_oracle" not in txt and "golden_oracle" not in txt, f

@@ -1,0 +1,181 @@
+"""lsa_golden_labels against the golden-label oracle (marked gpu).
+
+Small windows: every (token, layer) nucleus is compared with the oracle's
+nucleus entry by entry, up to the entries whose preceding probability mass lies
+within EPS of top_p (the oracle's nucleus_bounds); the window's label set is
+compared with the oracle's golden_bounds the same way. The per-token golden
+sets and the union are also recomputed exactly (bit for bit) from the GPU's
+own row masks, so the vote and the union are integer checks.
+
+Full size (64 tokens x 21 layers x 125K entries): every row mask is checked
+against the definition of a nucleus (kept logits above dropped ones, ties by
+index; the kept mass reaches top_p and the last kept entry starts below it, up
+to EPS), sampled rows against the oracle, and the vote and union exactly.
+
+EPS: the library accumulates fp64 sums of fp32 exponentials exp2((y - M)
+log2 e) with M the row maximum. Each term carries a relative error of a few
+units in 2^-24 from the product's rounding, times |y - M| log2 e, plus the
+exponential's own ulp; for the logits here (|y - M| < 40 wherever the mass is
+not negligible) that is below 4e-6 of the term, so any partial sum divided by
+the total is within 1e-5 of its exact value.
+"""
+import numpy as np
+import pytest
+
+from oracle import golden_oracle as G
+from sparse_kv_retrieval_amd import synth_golden as SG
+from tests import parity as P
+
+EPS = 1e-5
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available()
+    return torch
+
+
+def run_gpu(torch, inp, p=None, theta=None):
+    from sparse_kv_retrieval_amd import lsa
+    w = inp.workload
+    p = w.p if p is None else p
+    theta = w.theta if theta is None else theta
+    dev = torch.device("cuda")
+    logits = torch.from_numpy(inp.logits).to(dev)
+    nv = torch.from_numpy(inp.n_valid).to(dev)
+    W, rows = w.words, w.T * w.L
+    # outputs start as garbage so that an unwritten word shows
+    row_mask = torch.full((rows, W), -1, dtype=torch.int64, device=dev)
+    sizes = torch.full((rows,), -7, dtype=torch.int32, device=dev)
+    tok = torch.full((w.T, W), -1, dtype=torch.int64, device=dev)
+    golden = torch.full((W,), -1, dtype=torch.int64, device=dev)
+    lsa.golden_labels(logits, row_stride=w.row_stride, T=w.T, L=w.L, n_valid=nv, top_p=p, theta=theta,
+                      row_mask=row_mask, golden=golden, nucleus_size=sizes, token_golden=tok)
+    torch.cuda.synchronize()
+    return (row_mask.cpu().numpy().view(np.uint64), sizes.cpu().numpy(), tok.cpu().numpy().view(np.uint64),
+            golden.cpu().numpy().view(np.uint64))
+
+
+def bits(words, n):
+    """Bits of uint64 words as bools: (first n, the rest)."""
+    b = np.unpackbits(np.ascontiguousarray(words).view(np.uint8), bitorder="little").astype(bool)
+    return b[:n], b[n:]
+
+
+def check_vote_union(inp, row_mask, tok, golden, theta):
+    """Token sets and union recomputed from the GPU's own row masks: bit-exact."""
+    w = inp.workload
+    S = w.row_stride
+    m = np.unpackbits(row_mask.reshape(w.T, w.L, -1).view(np.uint8), axis=-1, bitorder="little")[..., :S]
+    votes = m.astype(np.int32).sum(axis=1)
+    tg = votes >= theta
+    got_t = np.unpackbits(tok.view(np.uint8), axis=-1, bitorder="little")[:, :S].astype(bool)
+    assert np.array_equal(got_t, tg), "token golden sets differ from the vote over the row masks"
+    got_g, tail = bits(golden, S)
+    assert np.array_equal(got_g, tg.any(axis=0)), "window union differs from the OR of the token sets"
+    assert not tail.any()
+    return got_g
+
+
+def check_nucleus_property(y, m, p, eps):
+    """m is a top-p nucleus of y: definition-level check, any size."""
+    n = y.size
+    if n == 0:
+        assert not m.any()
+        return
+    assert m.any(), "the top entry is always kept"
+    y64 = y.astype(np.float64)
+    P_ = np.exp(y64 - y64.max())
+    P_ /= P_.sum()
+    kmin = y[m].min()
+    if (~m).any():
+        dmax = y[~m].max()
+        assert kmin >= dmax, f"dropped logit {dmax} above kept {kmin}"
+        if kmin == dmax:
+            idx = np.arange(n)
+            assert idx[m & (y == kmin)].max() < idx[~m & (y == kmin)].min(), "ties not by ascending index"
+        assert P_[m].sum() >= p - eps, f"kept mass {P_[m].sum()} short of {p}"
+    plast = float(np.exp(np.float64(kmin) - y64.max()) / np.exp(y64 - y64.max()).sum())
+    assert P_[m].sum() - plast < p + eps, "the last kept entry starts at or above p"
+
+
+SMALL = ["golden_small", "golden_ragged", "golden_ties", "golden_flat", "golden_narrow"]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", SMALL)
+def test_golden_small(case, torch_cuda):
+    w = SG.WORKLOADS[case]
+    P.say(f"[golden] case={case} T={w.T} L={w.L} stride={w.row_stride} p={w.p} theta={w.theta}")
+    inp = SG.make(w)
+    row_mask, sizes, tok, golden = run_gpu(torch_cuda, inp)
+    band = 0
+    for i in range(w.T):
+        n = int(inp.n_valid[i])
+        for l in range(w.L):
+            r = i * w.L + l
+            m, tail = bits(row_mask[r], n)
+            assert not tail.any(), f"bits at or beyond n_valid set in row ({i}, {l})"
+            assert sizes[r] == m.sum(), (i, l, sizes[r], m.sum())
+            si, so = G.nucleus_bounds(inp.logits[i, l, :n], w.p, EPS)
+            assert not (si & ~m).any(), f"row ({i},{l}) drops {np.flatnonzero(si & ~m)[:8]}"
+            assert not (so & m).any(), f"row ({i},{l}) keeps {np.flatnonzero(so & m)[:8]}"
+            band += int((~si & ~so).sum())
+            check_nucleus_property(inp.logits[i, l, :n], m, w.p, EPS)
+    g = check_vote_union(inp, row_mask, tok, golden, w.theta)
+    sg, sn = G.golden_bounds(inp.logits, inp.n_valid, w.p, w.theta, EPS)
+    N = sg.size
+    assert not (sg & ~g[:N]).any() and not (sn & g[:N]).any()
+    assert not g[N:].any()
+    P.say(f"[golden] {case}: golden {int(g.sum())}, entries within the band {band}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("p,theta", [(1.0, 1), (1e-6, 1), (0.9, 2), (0.6, 5), (0.6, 6), (0.3, 200)])
+def test_golden_parameters(p, theta, torch_cuda):
+    w = SG.WORKLOADS["golden_small"]
+    P.say(f"[golden] p={p} theta={theta}")
+    inp = SG.make(w)
+    row_mask, sizes, tok, golden = run_gpu(torch_cuda, inp, p=p, theta=theta)
+    for i in range(w.T):
+        n = int(inp.n_valid[i])
+        for l in range(w.L):
+            m, _ = bits(row_mask[i * w.L + l], n)
+            si, so = G.nucleus_bounds(inp.logits[i, l, :n], p, EPS)
+            assert not (si & ~m).any() and not (so & m).any(), (i, l)
+            if p == 1e-6:
+                assert m.sum() == 1 and np.argmax(inp.logits[i, l, :n]) == np.flatnonzero(m)[0]
+    g = check_vote_union(inp, row_mask, tok, golden, theta)
+    sg, sn = G.golden_bounds(inp.logits, inp.n_valid, p, theta, EPS)
+    assert not (sg & ~g[:sg.size]).any() and not (sn & g[:sg.size]).any()
+    if theta > w.L:
+        assert not g.any()
+
+
+@pytest.mark.gpu
+def test_golden_full_size(torch_cuda):
+    w = SG.WORKLOADS["golden_t64_l21_n125k"]
+    P.say("[golden] golden_t64_l21_n125k: generating")
+    inp = SG.make(w)
+    P.say("[golden] golden_t64_l21_n125k: running")
+    row_mask, sizes, tok, golden = run_gpu(torch_cuda, inp)
+    P.say("[golden] checking every row against the nucleus definition")
+    for i in range(w.T):
+        n = int(inp.n_valid[i])
+        for l in range(w.L):
+            r = i * w.L + l
+            m, tail = bits(row_mask[r], n)
+            assert not tail.any()
+            assert sizes[r] == m.sum()
+            check_nucleus_property(inp.logits[i, l, :n], m, w.p, EPS)
+    rng = np.random.default_rng(7)
+    for r in rng.choice(w.T * w.L, size=16, replace=False):
+        i, l = divmod(int(r), w.L)
+        n = int(inp.n_valid[i])
+        m, _ = bits(row_mask[r], n)
+        si, so = G.nucleus_bounds(inp.logits[i, l, :n], w.p, EPS)
+        assert not (si & ~m).any() and not (so & m).any(), (i, l)
+    g = check_vote_union(inp, row_mask, tok, golden, w.theta)
+    P.say(f"[golden] full size: window label set {int(g.sum())} entries, nucleus sizes "
+          f"{int(sizes.min())}..{int(sizes.max())}")
