@@ -14,21 +14,29 @@
 // uint32 image of the crossing entry's logit) and an index cut such that an
 // entry is kept iff key > T, or key == T and index <= cut.
 //
-// Kernel 1 (one 1024-thread block per (token, layer) row):
-//   pass A  streams the row from HBM once: a running block maximum M and a
-//           4096-bin histogram of the masses exp(y - M) over the top 12 key
-//           bits (fp64 LDS atomics, rescaled whenever M grows);
-//   scan    finds the crossing bin b1 of the cumulative mass (descending keys)
-//           at p * Z, Z the histogram total;
-//   pass B  streams the row again: entries above b1 are written as kept into
-//           the row's bit mask, entries in b1 go to an LDS candidate list;
-//   levels  two 10-bit levels over the candidates find T exactly, the count of
-//           entries equal to T that are kept follows from their common mass,
-//           and if that is not all of them a 3 x 10-bit count select over
-//           their indices finds the cut;
-//   fix-up  kept candidates are OR-ed into the mask words.
-// If the crossing bin holds more candidates than the LDS list, every level
-// reads the row instead of the list and a final pass rewrites the mask.
+// Kernel 1, one 512-thread block per (token, layer) row, three blocks per CU.
+//
+// Pass F reads the row from HBM once. Each lane keeps online softmax
+// statistics of its entries (its maximum m and sum s of exp(y - m), in fp64),
+// and the block keeps in LDS a list of every entry whose key is at or above a
+// filter key tau. The first filter is the smallest of the waves' 4th largest
+// lane maxima over the first block chunk; whenever the list passes half its
+// capacity, a count histogram of it by value raises tau so that about a
+// quarter of the capacity stays, and the list is compacted. At the end the list holds every entry with key >=
+// tau, M and Z follow from the lanes' statistics, and if the list's mass at
+// or above tau reaches p * Z the nucleus lies inside it: a radix select by
+// mass over the list finds T (levels of 9, 9, 9 and 5 bits, fp64 weights),
+// the number of entries equal to T that are kept follows from their common
+// mass, and a count select over their indices finds the cut when not all of
+// them are. The row's mask is cleared and the kept entries' bits are set.
+//
+// Fallback, when the list overflowed or holds too little mass: a second read
+// builds a 4096-bin fp64 mass histogram over the top 12 key bits (LDS
+// atomics) and finds the crossing bin b1; a third read writes the mask bits of
+// the entries above b1 and lists the entries of b1; levels of 9, 9 and 2 bits
+// over that list (or over the row, if it does not fit) find T, and the kept entries
+// of b1 are OR-ed into the mask (or, when b1 did not fit, a last read rewrites
+// the whole mask).
 //
 // Kernel 2 (vote and union): per (token, mask word), a bit-sliced count of the
 // layers' mask bits, compared with theta, and OR-ed over the window's tokens.
@@ -38,27 +46,41 @@ namespace lsa {
 
 namespace {
 
-constexpr int GT = 1024;          // threads per nucleus block
+constexpr int GT = 512;           // threads per nucleus block
 constexpr int GW = GT / 64;       // waves per nucleus block
-constexpr int GLL = 16;           // dword loads per lane per wave chunk
-constexpr int GWC = 64 * GLL;     // entries per wave chunk: 16 mask words
+constexpr int GLL = 8;            // dword loads per lane per wave chunk
+constexpr int GWC = 64 * GLL;     // entries per wave chunk: 8 mask words
 constexpr int GBC = GWC * GW;     // entries per block chunk
-constexpr int NB1 = 4096;         // level-1 bins: key bits 31..20
-constexpr int NBL = 1024;         // later levels: 10 bits, one bin per thread
-constexpr int GCAP = 4096;        // candidates held in LDS
+constexpr int NB1 = 4096;         // fallback level-1 bins: key bits 31..20
+constexpr int LB = 9;             // radix level width: one digit per thread
+constexpr int NBL = 1 << LB;
+constexpr int GCAP = 3072;        // entries held in the LDS list
+constexpr int BOOT = 4;           // the first filter is the block minimum of each wave's BOOT-th largest lane maximum
+constexpr int KEEP = GCAP / 4;    // a compaction keeps the list's KEEP largest keys
+constexpr int EPOCH = 8;          // block chunks between two looks at the list's size
 constexpr uint32_t NONE = 0xFFFFFFFFu;
 constexpr float LOG2E = 1.4426950408889634f;
 
 struct GoldenSmem {
-  double bins[NB1];    // level-1 masses; levels 2-3 use the first NBL
-  uint32_t cnt[NBL];   // per-digit counts of levels 2-3 and of the index select
-  uint32_t ckey[GCAP];
-  uint32_t cidx[GCAP];
+  union {
+    double bins[NB1];   // fallback level-1 masses (not live at the same time as the list)
+    struct {
+      uint32_t ckey[GCAP];  // the list
+      uint32_t cidx[GCAP];
+      struct {              // fast path: the entries of the crossing bucket, as listed and by rank
+        uint32_t key[GT], idx[GT], rkey[GT], ridx[GT];
+        double w[GT], rw[GT];
+        uint32_t n;
+      } cb;
+    };
+  };
+  double lw[NBL];       // radix level weights
+  uint32_t lc[NBL];     // radix level counts
   double wsum[GW];
-  uint32_t usum[GW];
-  float wmax[2][GW];
+  float wmax[GW], wmin[GW];
   double res_A;
-  uint32_t res_digit, res_cnt, ncand, kept;
+  uint32_t res_digit, res_cnt, ncand, kept, tau;
+  uint32_t want[2];     // epoch e + 1 in want[e & 1]: the list passed half its capacity during epoch e
   int32_t last;
 };
 
@@ -67,8 +89,12 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float(u);
 }
 
-// Unnormalised probability of a logit relative to the row maximum M.
-__device__ __forceinline__ float rel_mass(float y, float M) { return __builtin_amdgcn_exp2f((y - M) * LOG2E); }
+// The smallest logit whose key is at or above the filter key tau (key 0: all).
+// For finite y, key(y) >= tau iff y >= filter_value(tau).
+__device__ __forceinline__ float filter_value(uint32_t tau) { return tau ? key_value(tau) : -INFINITY; }
+
+// Unnormalised probability of a logit relative to a reference m >= y.
+__device__ __forceinline__ float rel_mass(float y, float m) { return __builtin_amdgcn_exp2f((y - m) * LOG2E); }
 
 __device__ __forceinline__ uint32_t below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -106,28 +132,13 @@ __device__ __forceinline__ void block_scan_f64(double v, GoldenSmem& sm, double&
   total = tot;
 }
 
-// The same for uint32 counts (exact).
-__device__ __forceinline__ void block_scan_u32(uint32_t v, GoldenSmem& sm, uint32_t& excl, uint32_t& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sm.usum[w] = x;
-  __syncthreads();
-  uint32_t off = 0, tot = 0;
-  for (int i = 0; i < GW; ++i) {
-    off += i < w ? sm.usum[i] : 0u;
-    tot += sm.usum[i];
-  }
-  __syncthreads();
-  excl = off + x - v;
-  total = tot;
+__device__ __forceinline__ double block_sum_f64(double v, GoldenSmem& sm) {
+  double ex, in, tot;
+  block_scan_f64(v, sm, ex, in, tot);
+  return tot;
 }
 
-// Where the level's items come from: the LDS candidate list, or the whole row.
+// Where a radix level's items come from: the LDS list, or the whole row.
 struct FromList {
   const GoldenSmem* sm;
   uint32_t n;
@@ -154,37 +165,42 @@ struct FromRow {
   }
 };
 
-// One 10-bit mass level: among items whose key >> (sh + 10) equals pre, the
-// digit (key >> sh) & 1023 where the cumulative mass, taken in descending key
-// order on top of A (the mass of every key above the prefix), reaches target.
-// Returns the digit, the mass above it and its count. When rounding leaves the
-// sum short of the target, the lowest non-empty digit is taken.
-template <class Src>
-__device__ void mass_level(GoldenSmem& sm, const Src& src, uint32_t pre, int sh, float M, double target, double& A,
-                           uint32_t& digit, uint32_t& count) {
+// One radix level. For each item, item(key, idx, rk, wt) says whether it takes
+// part and gives its radix value rk and weight wt. Among the items whose rk
+// has the prefix pre above bit sh + wb, the wb-bit digit at bit sh where the
+// cumulative weight, taken from the largest digit down on top of A, reaches
+// target. Returns the digit, A plus the weight above it, and its item count.
+// When rounding leaves the sum short, the lowest digit holding items is taken.
+template <class Src, class Item>
+__device__ void radix_level(GoldenSmem& sm, const Src& src, const Item& item, uint32_t pre, int sh, int wb,
+                            double target, double& A, uint32_t& digit, uint32_t& count) {
   const int t = threadIdx.x;
-  __syncthreads();  // earlier readers of bins / cnt are done
-  sm.bins[t] = 0.0;
-  sm.cnt[t] = 0;
+  const uint32_t nd = 1u << wb, dmask = nd - 1;
+  __syncthreads();  // earlier readers of lw / lc are done
+  sm.lw[t] = 0.0;
+  sm.lc[t] = 0;
   if (t == 0) {
     sm.res_digit = NONE;
     sm.last = -1;
   }
   __syncthreads();
-  src.each([&](uint32_t key, uint32_t) {
-    if ((key >> (sh + 10)) == pre) {
-      const uint32_t d = (key >> sh) & (NBL - 1);
-      lds_add(&sm.bins[d], (double)rel_mass(key_value(key), M));
-      lds_inc(&sm.cnt[d]);
+  src.each([&](uint32_t key, uint32_t idx) {
+    uint32_t rk;
+    double wt;
+    if (item(key, idx, rk, wt) && (uint32_t)((uint64_t)rk >> (sh + wb)) == pre) {
+      const uint32_t d = (rk >> sh) & dmask;
+      lds_add(&sm.lw[d], wt);
+      lds_inc(&sm.lc[d]);
     }
   });
   __syncthreads();
-  const uint32_t d = NBL - 1 - t;  // thread order = descending digit
-  const double m = sm.bins[d];
-  const uint32_t c = sm.cnt[d];
+  const bool on = (uint32_t)t < nd;
+  const uint32_t d = on ? nd - 1 - t : 0;  // thread order = descending digit
+  const double m = on ? sm.lw[d] : 0.0;
+  const uint32_t c = on ? sm.lc[d] : 0u;
   double ex, in, tot;
   block_scan_f64(m, sm, ex, in, tot);
-  if (A + ex < target && A + in >= target) {
+  if (c > 0 && A + ex < target && A + in >= target) {
     sm.res_digit = d;
     sm.res_A = A + ex;
     sm.res_cnt = c;
@@ -196,43 +212,58 @@ __device__ void mass_level(GoldenSmem& sm, const Src& src, uint32_t pre, int sh,
     A = sm.res_A;
     count = sm.res_cnt;
   } else if (sm.last >= 0) {
-    const uint32_t dl = NBL - 1 - (uint32_t)sm.last;
+    const uint32_t dl = nd - 1 - (uint32_t)sm.last;
     digit = dl;
-    A = A + (tot - sm.bins[dl]);
-    count = sm.cnt[dl];
-  } else {  // no item under the prefix (not reached: the prefix always holds the crossing entry)
+    A = A + (tot - sm.lw[dl]);
+    count = sm.lc[dl];
+  } else {  // no item under the prefix (not reached: the prefix always holds an item)
     digit = 0;
     count = 0;
   }
 }
 
-// The rank-th smallest index (rank >= 1) among items with key == T, by three
-// 10-bit count levels over the index bits 29..0.
-template <class Src>
-__device__ uint32_t index_select(GoldenSmem& sm, const Src& src, uint32_t T, uint32_t rank) {
-  const int t = threadIdx.x;
-  uint32_t pre = 0;
-  for (int sh = 20; sh >= 0; sh -= 10) {
-    __syncthreads();
-    sm.cnt[t] = 0;
-    if (t == 0) sm.res_digit = NONE;
-    __syncthreads();
-    src.each([&](uint32_t key, uint32_t idx) {
-      if (key == T && (idx >> (sh + 10)) == pre) lds_inc(&sm.cnt[(idx >> sh) & (NBL - 1)]);
-    });
-    __syncthreads();
-    const uint32_t c = sm.cnt[t];
-    uint32_t ex, tot;
-    block_scan_u32(c, sm, ex, tot);
-    if (ex < rank && ex + c >= rank) {
-      sm.res_digit = t;
-      sm.res_cnt = ex;
-    }
-    __syncthreads();
-    pre = (pre << 10) | sm.res_digit;
-    rank -= sm.res_cnt;
+// Radix select over the low `bits` bits of radix values whose higher bits are
+// pre (levels of up to LB bits): the largest value v whose cumulative weight
+// (items with rk >= v, on top of A) reaches target. A becomes A plus the
+// weight of the items above v; cnt is the number of items equal to v.
+template <class Src, class Item>
+__device__ uint32_t radix_select(GoldenSmem& sm, const Src& src, const Item& item, double target, double& A,
+                                 uint32_t& cnt, uint32_t pre = 0, int bits = 32) {
+  uint32_t v = pre;
+  while (bits > 0) {
+    const int wb = bits < LB ? bits : LB;
+    bits -= wb;
+    uint32_t d;
+    radix_level(sm, src, item, v, bits, wb, target, A, d, cnt);
+    v = (v << wb) | d;
   }
-  return pre;
+  return v;
+}
+
+// Index cut among the nT entries whose key is T, given A, the mass of every
+// entry above T: they share one mass w, and the j-th of them (by ascending
+// index) is kept while A + (j - 1) w < target, so c = ceil((target - A) / w)
+// of them are, at least one. Returns the largest kept index (all of them:
+// 0x7FFFFFFF).
+template <class Src>
+__device__ uint32_t tie_cut(GoldenSmem& sm, const Src& src, uint32_t T, uint32_t nT, double A, double target,
+                            float M) {
+  const double w = (double)rel_mass(key_value(T), M);
+  const double q = (target - A) / w;
+  uint32_t c = nT;
+  if (q < (double)nT) c = q <= 1.0 ? 1u : (uint32_t)ceil(q);
+  if (c >= nT) return 0x7FFFFFFFu;
+  double A2 = 0.0;
+  uint32_t cc;
+  const uint32_t r = radix_select(
+      sm, src,
+      [T](uint32_t key, uint32_t idx, uint32_t& rk, double& wt) {
+        rk = ~idx;  // largest first = ascending index
+        wt = 1.0;
+        return key == T;
+      },
+      (double)c, A2, cc);
+  return ~r;
 }
 
 // The loads of one wave chunk: lane j of load k reads entry base + 64k + j, so
@@ -267,7 +298,118 @@ __device__ __forceinline__ void stream_row(const __amdgpu_buffer_rsrc_t rs, uint
   }
 }
 
-__global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(8, 8)))
+// The same with two chunks in flight while one is processed (pass F, which
+// has the registers for it); first(v) is called once on the first chunk.
+template <class P, class F>
+__device__ __forceinline__ void stream_row3(const __amdgpu_buffer_rsrc_t rs, uint32_t wv, uint32_t lane, uint32_t nit,
+                                            P&& first, F&& body) {
+  float va[GLL], vb[GLL], vc[GLL];
+  auto off = [&](uint32_t it) { return ((it * GW + wv) * GWC + lane) * 4u; };
+  load_chunk(rs, off(0), va);
+  load_chunk(rs, off(1), vb);
+  first(va);  // sees the first chunk while the second is in flight
+  for (uint32_t it = 0;; it += 3) {
+    load_chunk(rs, off(it + 2), vc);
+    body(va, (it * GW + wv) * GWC);
+    if (it + 1 >= nit) break;
+    load_chunk(rs, off(it + 3), va);
+    body(vb, ((it + 1) * GW + wv) * GWC);
+    if (it + 2 >= nit) break;
+    load_chunk(rs, off(it + 4), vb);
+    body(vc, ((it + 2) * GW + wv) * GWC);
+    if (it + 3 >= nit) break;
+  }
+}
+
+// Appends (key, idx) to the LDS list for the lanes where `pass` holds (one LDS
+// atomic per wave). Positions at or beyond GCAP are counted but not stored.
+__device__ __forceinline__ void list_push(GoldenSmem& sm, bool pass, uint32_t key, uint32_t idx, uint32_t lane) {
+  const uint64_t pm = __ballot(pass);
+  if (pm) {
+    uint32_t c0 = 0;
+    if (lane == 0)
+      c0 = __hip_atomic_fetch_add(&sm.ncand, (uint32_t)__popcll(pm), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    c0 = __shfl(c0, 0);
+    if (pass) {
+      const uint32_t pos = c0 + below(pm);
+      if (pos < GCAP) {
+        sm.ckey[pos] = key;
+        sm.cidx[pos] = idx;
+      }
+    }
+  }
+}
+
+// Raises the filter so that about KEEP of the list's entries stay, and drops
+// the rest: a count histogram of the list by distance below its largest value,
+// the bucket where the count from the top reaches KEEP, and the smallest value
+// in that bucket becomes the filter. Buckets are monotone in the value, so
+// exactly the buckets up to that one stay (at least KEEP entries). Every
+// thread calls it with the same nc, KEEP <= nc <= GCAP.
+__device__ __attribute__((noinline)) void compact_list(GoldenSmem& sm, uint32_t nc, uint32_t lane) {
+  const int t = threadIdx.x, wv = t >> 6;
+  float hi = -INFINITY, lo = INFINITY;
+  for (uint32_t j = t; j < nc; j += GT) {
+    const float yv = key_value(sm.ckey[j]);
+    hi = fmaxf(hi, yv);
+    lo = fminf(lo, yv);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    hi = fmaxf(hi, __shfl_xor(hi, o));
+    lo = fminf(lo, __shfl_xor(lo, o));
+  }
+  if (lane == 0) {
+    sm.wmax[wv] = hi;
+    sm.wmin[wv] = lo;
+  }
+  sm.lc[t] = 0;
+  if (t == 0) sm.res_digit = NONE;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < GW; ++j) {
+    hi = fmaxf(hi, sm.wmax[j]);
+    lo = fminf(lo, sm.wmin[j]);
+  }
+  const float sc = hi > lo ? (float)(NBL - 1) / (hi - lo) : 0.f;
+  auto bucket = [hi, sc](float yv) { return (uint32_t)fminf((hi - yv) * sc, (float)(NBL - 1)); };
+  for (uint32_t j = t; j < nc; j += GT) lds_inc(&sm.lc[bucket(key_value(sm.ckey[j]))]);
+  __syncthreads();
+  double ex, in, tot;
+  block_scan_f64((double)sm.lc[t], sm, ex, in, tot);  // counts: exact in fp64
+  if (ex < (double)KEEP && in >= (double)KEEP) sm.res_digit = t;
+  __syncthreads();
+  const uint32_t db = sm.res_digit;
+  float bmin = INFINITY;
+  for (uint32_t j = t; j < nc; j += GT) {
+    const float yv = key_value(sm.ckey[j]);
+    if (bucket(yv) == db) bmin = fminf(bmin, yv);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) bmin = fminf(bmin, __shfl_xor(bmin, o));
+  if (lane == 0) sm.wmin[wv] = bmin;
+  uint32_t k[GCAP / GT], x[GCAP / GT];
+#pragma unroll
+  for (int j = 0; j < GCAP / GT; ++j) {
+    const uint32_t p = t + j * GT;
+    k[j] = p < nc ? sm.ckey[p] : 0u;
+    x[j] = p < nc ? sm.cidx[p] : 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < GW; ++j) bmin = fminf(bmin, sm.wmin[j]);
+  const uint32_t tnew = order_key(bmin);
+  if (t == 0) {
+    sm.ncand = 0;
+    sm.tau = max(sm.tau, tnew);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < GCAP / GT; ++j) list_push(sm, t + j * GT < nc && k[j] >= tnew, k[j], x[j], lane);
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(6, 6)))
 void nucleus_kernel(const GoldenArgs a) {
   __shared__ GoldenSmem sm;
   const int t = threadIdx.x;
@@ -289,191 +431,385 @@ void nucleus_kernel(const GoldenArgs a) {
     if (a.nucleus_size && t == 0) a.nucleus_size[row] = 0;
     return;
   }
+  const uint32_t nit = (n + GBC - 1) / GBC;
 
-  // ---- pass A: maximum and level-1 mass histogram, one read of the row
-#pragma unroll
-  for (int j = 0; j < NB1 / GT; ++j) sm.bins[t * (NB1 / GT) + j] = 0.0;
+  // ---- pass F: lane softmax statistics and the filtered list, one read of the row
   if (t == 0) {
     sm.ncand = 0;
     sm.kept = 0;
+    sm.tau = 0;
+    sm.want[0] = sm.want[1] = 0;
   }
-  const uint32_t nit = (n + GBC - 1) / GBC;
-  float M = -INFINITY;
-  uint32_t par = 0;
-  stream_row(rs, wv, lane, nit, [&](float (&v)[GLL], uint32_t base) {
-    const bool full = base + GWC <= n;
-    float m = -INFINITY;
+  __syncthreads();
+  float ml = -INFINITY;  // this lane's maximum and sum of exp(y - ml)
+  double sl = 0.0;
+  bool ovf = false;  // block-uniform
+  uint32_t epoch = 0, cie = 0;
+  float tauf = -INFINITY;
+  auto first = [&](float (&v)[GLL]) {
+    // First filter: every wave's BOOT-th largest lane maximum over the first block
+    // chunk, and the smallest of those. At least BOOT entries per wave pass it.
+    float x = -INFINITY, kth = -INFINITY;
 #pragma unroll
     for (int k = 0; k < GLL; ++k)
-      if (full || base + 64u * k + lane < n) m = fmaxf(m, v[k]);
+      if (wv * GWC + 64u * k + lane < n) x = fmaxf(x, v[k]);
+    for (int r = 0; r < BOOT; ++r) {
+      float m = x;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if (lane == 0) sm.wmax[par][wv] = m;
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      kth = m;
+      const uint64_t at = __ballot(x == m);
+      if (lane == (uint32_t)__builtin_ctzll(at)) x = -INFINITY;
+    }
+    if (lane == 0) sm.wmax[wv] = kth;
     __syncthreads();
-    float Mn = M;
+    float f = INFINITY;
 #pragma unroll
-    for (int j = 0; j < GW; ++j) Mn = fmaxf(Mn, sm.wmax[par][j]);
-    par ^= 1;
-    if (Mn > M) {  // the same decision in every thread
-      if (M != -INFINITY) {
-        const double f = (double)rel_mass(M, Mn);
+    for (int j = 0; j < GW; ++j) f = fminf(f, sm.wmax[j]);
+    if (t == 0) sm.tau = f == -INFINITY ? 0u : order_key(f);
+    tauf = f;  // filter_value(order_key(f)) == f for finite f; -inf: everything passes
+  };
+  stream_row3(rs, wv, lane, nit, first, [&](float (&v)[GLL], uint32_t base) {
+    const bool full = base + GWC <= n;
+    float cm = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < NB1 / GT; ++j) sm.bins[t * (NB1 / GT) + j] *= f;
+    for (int k = 0; k < GLL; ++k)
+      if (full || base + 64u * k + lane < n) cm = fmaxf(cm, v[k]);
+    if (cm > ml) {
+      sl *= (double)rel_mass(ml, cm);  // 0 while ml is still -inf
+      ml = cm;
+    }
+    if (ml != -INFINITY) {
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < GLL; k += 2) {
+        if (full || base + 64u * k + lane < n) ps0 += rel_mass(v[k], ml);
+        if (full || base + 64u * (k + 1) + lane < n) ps1 += rel_mass(v[k + 1], ml);
       }
-      M = Mn;
-      __syncthreads();
+      sl += (double)ps0 + (double)ps1;
     }
-    if (full) {
-#pragma unroll
-      for (int k = 0; k < GLL; ++k) lds_add(&sm.bins[order_key(v[k]) >> 20], (double)rel_mass(v[k], M));
-    } else {
-#pragma unroll
-      for (int k = 0; k < GLL; ++k)
-        if (base + 64u * k + lane < n) lds_add(&sm.bins[order_key(v[k]) >> 20], (double)rel_mass(v[k], M));
-    }
-  });
-  __syncthreads();
-
-  // ---- level 1: crossing bin of the cumulative mass at p * Z
-  double A, target;
-  uint32_t b1;
-  {
-    double l[NB1 / GT], s = 0.0;  // this thread's bins, descending
-#pragma unroll
-    for (int j = 0; j < NB1 / GT; ++j) {
-      s += sm.bins[NB1 - 1 - (NB1 / GT) * t - j];
-      l[j] = s;
-    }
-    double ex, in, Z;
-    block_scan_f64(s, sm, ex, in, Z);
-    target = (double)a.p * Z;
-    if (t == 0) sm.res_digit = NONE;
-    __syncthreads();
-    if (ex < target && in >= target) {
-      // first of this thread's bins (descending) whose running sum reaches the
-      // target; if rounding leaves it short, the last bin that holds mass
-      int jj = -1, jm = 0;
-      double above = ex, above_m = ex, prev = 0.0;
-#pragma unroll
-      for (int j = 0; j < NB1 / GT; ++j) {
-        if (jj < 0 && ex + l[j] >= target) {
-          jj = j;
-          above = ex + prev;
-        }
-        if (l[j] > prev) {
-          jm = j;
-          above_m = ex + prev;
-        }
-        prev = l[j];
-      }
-      if (jj < 0) {
-        jj = jm;
-        above = above_m;
-      }
-      sm.res_digit = NB1 - 1 - (NB1 / GT) * t - jj;
-      sm.res_A = above;
-    }
-    __syncthreads();
-    b1 = sm.res_digit;
-    A = sm.res_A;
-  }
-
-  // ---- pass B: mask words for decided entries, candidates of bin b1
-  uint32_t kept = 0;
-  stream_row(rs, wv, lane, nit, [&](float (&v)[GLL], uint32_t base) {
-    uint64_t mine = 0;
+    // entries at or above the filter go to the list: one LDS atomic per chunk
+    bool va[GLL];
+    uint64_t pm[GLL];
+    uint32_t tot = 0;
 #pragma unroll
     for (int k = 0; k < GLL; ++k) {
-      const uint32_t e = base + 64u * k + lane;
-      const uint32_t key = order_key(v[k]);
-      const bool valid = e < n;
-      const uint64_t kw = __ballot(valid && (key >> 20) > b1);
-      const uint64_t cm = __ballot(valid && (key >> 20) == b1);
-      kept += (uint32_t)__popcll(kw);
-      mine = lane == (uint32_t)k ? kw : mine;
-      if (cm) {
-        uint32_t c0 = 0;
-        if (lane == 0)
-          c0 = __hip_atomic_fetch_add(&sm.ncand, (uint32_t)__popcll(cm), __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_WORKGROUP);
-        c0 = __shfl(c0, 0);
-        if (valid && (key >> 20) == b1) {
-          const uint32_t pos = c0 + below(cm);
-          if (pos < GCAP) {
-            sm.ckey[pos] = key;
-            sm.cidx[pos] = e;
-          }
+      va[k] = (full || base + 64u * k + lane < n) && v[k] >= tauf;
+      pm[k] = __ballot(va[k]);
+      tot += (uint32_t)__popcll(pm[k]);
+    }
+    if (tot) {
+      uint32_t c0 = 0;
+      if (lane == 0) {
+        c0 = __hip_atomic_fetch_add(&sm.ncand, tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (c0 + tot > GCAP / 2) sm.want[epoch & 1] = epoch + 1;
+      }
+      uint32_t pos = __builtin_amdgcn_readfirstlane(c0);
+#pragma unroll
+      for (int k = 0; k < GLL; ++k) {
+        const uint32_t p = pos + below(pm[k]);
+        if (va[k] && p < GCAP) {
+          sm.ckey[p] = order_key(v[k]);
+          sm.cidx[p] = base + 64u * k + lane;
+        }
+        pos += (uint32_t)__popcll(pm[k]);
+      }
+    }
+    if (++cie == EPOCH) {
+      // Every wave has ended the epoch's pushes at this barrier, so want[epoch & 1]
+      // is final and all read the same value; the next epoch writes the other slot.
+      cie = 0;
+      __syncthreads();
+      const bool look = sm.want[epoch & 1] == epoch + 1;
+      ++epoch;
+      if (look) {  // no wave pushes until every wave has left this branch
+        const uint32_t nc = sm.ncand;
+        __syncthreads();
+        if (nc > GCAP) {
+          ovf = true;
+          tauf = INFINITY;  // nothing passes any more: the fallback path takes the row
+        } else {
+          compact_list(sm, nc, lane);
+          tauf = filter_value(sm.tau);
         }
       }
     }
-    const uint32_t wi = (base >> 6) + lane;
-    if (lane < GLL && wi < nw) words[wi] = mine;
   });
-  if (lane == 0) __hip_atomic_fetch_add(&sm.kept, kept, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  // The mask stores are complete before any wave's fix-up atomic below. A
-  // workgroup-scope release is enough (waves of one block share the L2 that
-  // both go to); an agent-scope fence would write back the whole L2.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
-  const uint32_t nc = sm.ncand;
+  if (sm.ncand > GCAP) ovf = true;
 
-  // ---- levels 2 and 3, then the tie count and the index cut
-  uint32_t T, ncut = 0x7FFFFFFFu;
-  auto resolve = [&](const auto& src) {
-    uint32_t d2, c2, d3, nT;
-    mass_level(sm, src, b1, 10, M, target, A, d2, c2);
-    mass_level(sm, src, (b1 << 10) | d2, 0, M, target, A, d3, nT);
-    T = (b1 << 20) | (d2 << 10) | d3;
-    const double wT = (double)rel_mass(key_value(T), M);
-    const double q = (target - A) / wT;
-    uint32_t c = nT;
-    if (q < (double)nT) c = q <= 1.0 ? 1u : (uint32_t)ceil(q);
-    if (c < nT) ncut = index_select(sm, src, T, c);
-  };
-  if (nc <= GCAP) {
-    const FromList src{&sm, nc};
-    resolve(src);
-    uint32_t fixed = 0;
+  // ---- M and Z from the lanes' statistics
+  float wm = ml;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o));
+  if (lane == 0) sm.wmax[wv] = wm;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < GW; ++j) M = fmaxf(M, sm.wmax[j]);
+  const double Z = block_sum_f64(ml == -INFINITY ? 0.0 : sl * (double)rel_mass(ml, M), sm);
+  const double target = (double)a.p * Z;
+  uint32_t kept = 0;
+
+  bool done = false;
+  if (!ovf) {
+    const uint32_t nc = sm.ncand, tau = sm.tau;
+    // Buckets by distance below M over the list's range [lo, M]:
+    // d(y) = min(NBL - 1, (M - y) sc), so ascending d is descending y.
+    float lo = filter_value(tau);
+    if (tau == 0) {  // the list holds the whole (short) row: its own minimum
+      lo = INFINITY;
+      for (uint32_t j = t; j < nc; j += GT) lo = fminf(lo, key_value(sm.ckey[j]));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) lo = fminf(lo, __shfl_xor(lo, o));
+      if (lane == 0) sm.wmax[wv] = lo;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < GW; ++j) lo = fminf(lo, sm.wmax[j]);
+    }
+    const float sc = M > lo ? (float)(NBL - 1) / (M - lo) : 0.f;
+    auto bucket = [M, sc](float yv) { return (uint32_t)fminf((M - yv) * sc, (float)(NBL - 1)); };
+    sm.lw[t] = 0.0;
+    sm.lc[t] = 0;
+    if (t == 0) {
+      sm.res_digit = NONE;
+      sm.last = -1;
+      sm.cb.n = 0;
+    }
+    __syncthreads();
     for (uint32_t j = t; j < nc; j += GT) {
-      const uint32_t key = sm.ckey[j], idx = sm.cidx[j];
-      if (key > T || (key == T && idx <= ncut)) {
-        __hip_atomic_fetch_or(&words[idx >> 6], (uint64_t)1 << (idx & 63), __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_WORKGROUP);
-        ++fixed;
+      const uint32_t key = sm.ckey[j];
+      if (key >= tau) {
+        const float yv = key_value(key);
+        const uint32_t d = bucket(yv);
+        lds_add(&sm.lw[d], (double)rel_mass(yv, M));
+        lds_inc(&sm.lc[d]);
       }
     }
-    if (fixed) __hip_atomic_fetch_add(&sm.kept, fixed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  } else {
-    const FromRow src{rs, n};
-    resolve(src);
-    // rewrite every word; each word is stored by the same lane that stored it in pass B
     __syncthreads();
-    if (t == 0) sm.kept = 0;
+    double A, ex, in, tot;
+    const uint32_t c = sm.lc[t];
+    block_scan_f64(sm.lw[t], sm, ex, in, tot);  // tot: the list's mass at or above tau
+    if (c > 0 && ex < target && in >= target) {
+      sm.res_digit = t;
+      sm.res_A = ex;
+      sm.res_cnt = c;
+    }
+    if (c > 0) atomicMax(&sm.last, t);
     __syncthreads();
-    kept = 0;
+    if (tot > target * (1.0 + 1e-9)) {
+      // the nucleus lies inside the list: the crossing bucket db
+      uint32_t db, cnt;
+      if (sm.res_digit != NONE) {
+        db = sm.res_digit;
+        A = sm.res_A;
+        cnt = sm.res_cnt;
+      } else {  // rounding left the sum short: the last bucket that holds entries
+        db = (uint32_t)sm.last;
+        A = tot - sm.lw[db];
+        cnt = sm.lc[db];
+      }
+      uint32_t T, ncut;
+      if (cnt <= (uint32_t)GT) {
+        // exact order inside the bucket: rank by (key descending, index ascending)
+        for (uint32_t j = t; j < nc; j += GT) {
+          const uint32_t key = sm.ckey[j];
+          if (key >= tau && bucket(key_value(key)) == db) {
+            const uint32_t q = atomicAdd(&sm.cb.n, 1u);
+            sm.cb.key[q] = key;
+            sm.cb.idx[q] = sm.cidx[j];
+            sm.cb.w[q] = (double)rel_mass(key_value(key), M);
+          }
+        }
+        __syncthreads();
+        if ((uint32_t)t < cnt) {
+          const uint32_t kt = sm.cb.key[t], it2 = sm.cb.idx[t];
+          uint32_t r = 0;
+          for (uint32_t j = 0; j < cnt; ++j) {
+            const uint32_t kj = sm.cb.key[j];
+            r += (kj > kt || (kj == kt && sm.cb.idx[j] < it2)) ? 1u : 0u;
+          }
+          sm.cb.rkey[r] = kt;
+          sm.cb.ridx[r] = it2;
+          sm.cb.rw[r] = sm.cb.w[t];
+        }
+        __syncthreads();
+        // kept while the mass before it is below the target; rank 0 always is
+        block_scan_f64((uint32_t)t < cnt ? sm.cb.rw[t] : 0.0, sm, ex, in, tot);
+        const bool keep = (uint32_t)t < cnt && (t == 0 || A + ex < target);
+        const bool next = (uint32_t)t + 1 < cnt && A + in < target;
+        if (keep && !next) {
+          sm.res_digit = sm.cb.rkey[t];
+          sm.res_cnt = sm.cb.ridx[t];
+        }
+        __syncthreads();
+        T = sm.res_digit;
+        ncut = sm.res_cnt;
+      } else {
+        // a crowded bucket: radix select by mass over its entries
+        const FromList src{&sm, nc};
+        uint32_t nT;
+        T = radix_select(
+            sm, src,
+            [tau, M, db, &bucket](uint32_t key, uint32_t, uint32_t& rk, double& wt) {
+              rk = key;
+              const float yv = key_value(key);
+              wt = (double)rel_mass(yv, M);
+              return key >= tau && bucket(yv) == db;
+            },
+            target, A, nT);
+        ncut = tie_cut(sm, src, T, nT, A, target, M);
+      }
+      for (uint32_t j = t; j < nw; j += GT) words[j] = 0;
+      // the cleared words are stored before any wave's bit below (one L2 for the block)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+      for (uint32_t j = t; j < nc; j += GT) {
+        const uint32_t key = sm.ckey[j], idx = sm.cidx[j];
+        if (key > T || (key == T && idx <= ncut)) {
+          __hip_atomic_fetch_or(&words[idx >> 6], (uint64_t)1 << (idx & 63), __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_WORKGROUP);
+          ++kept;
+        }
+      }
+      done = true;
+    }
+  }
+
+  if (!done) {
+    // ---- fallback: level-1 mass histogram (second read; M is known now)
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NB1 / GT; ++j) sm.bins[t * (NB1 / GT) + j] = 0.0;
+    if (t == 0) sm.ncand = 0;
+    __syncthreads();
+    stream_row(rs, wv, lane, nit, [&](float (&v)[GLL], uint32_t base) {
+      if (base + GWC <= n) {
+#pragma unroll
+        for (int k = 0; k < GLL; ++k) lds_add(&sm.bins[order_key(v[k]) >> 20], (double)rel_mass(v[k], M));
+      } else {
+#pragma unroll
+        for (int k = 0; k < GLL; ++k)
+          if (base + 64u * k + lane < n) lds_add(&sm.bins[order_key(v[k]) >> 20], (double)rel_mass(v[k], M));
+      }
+    });
+    __syncthreads();
+
+    // crossing bin b1 of the cumulative mass at p * Zh, Zh the histogram total
+    double A, tgt;
+    uint32_t b1;
+    {
+      double l[NB1 / GT], s = 0.0;  // this thread's bins, descending
+#pragma unroll
+      for (int j = 0; j < NB1 / GT; ++j) {
+        s += sm.bins[NB1 - 1 - (NB1 / GT) * t - j];
+        l[j] = s;
+      }
+      double ex, in, Zh;
+      block_scan_f64(s, sm, ex, in, Zh);
+      tgt = (double)a.p * Zh;
+      if (t == 0) sm.res_digit = NONE;
+      __syncthreads();
+      if (ex < tgt && in >= tgt) {
+        // first of this thread's bins whose running sum reaches the target;
+        // if rounding leaves it short, the last bin that holds mass
+        int jj = -1, jm = 0;
+        double above = ex, above_m = ex, prev = 0.0;
+#pragma unroll
+        for (int j = 0; j < NB1 / GT; ++j) {
+          if (jj < 0 && ex + l[j] >= tgt) {
+            jj = j;
+            above = ex + prev;
+          }
+          if (l[j] > prev) {
+            jm = j;
+            above_m = ex + prev;
+          }
+          prev = l[j];
+        }
+        if (jj < 0) {
+          jj = jm;
+          above = above_m;
+        }
+        sm.res_digit = NB1 - 1 - (NB1 / GT) * t - jj;
+        sm.res_A = above;
+      }
+      __syncthreads();
+      b1 = sm.res_digit;
+      A = sm.res_A;
+    }
+
+    // mask words for the entries outside b1, list of the entries in b1 (third read)
     stream_row(rs, wv, lane, nit, [&](float (&v)[GLL], uint32_t base) {
       uint64_t mine = 0;
 #pragma unroll
       for (int k = 0; k < GLL; ++k) {
         const uint32_t e = base + 64u * k + lane;
         const uint32_t key = order_key(v[k]);
-        const uint64_t kw = __ballot(e < n && (key > T || (key == T && e <= ncut)));
-        kept += (uint32_t)__popcll(kw);
+        const bool valid = e < n;
+        const uint64_t kw = __ballot(valid && (key >> 20) > b1);
+        if (lane == 0) kept += (uint32_t)__popcll(kw);  // counted once per wave
         mine = lane == (uint32_t)k ? kw : mine;
+        list_push(sm, valid && (key >> 20) == b1, key, e, lane);
       }
       const uint32_t wi = (base >> 6) + lane;
       if (lane < GLL && wi < nw) words[wi] = mine;
     });
-    if (lane == 0) __hip_atomic_fetch_add(&sm.kept, kept, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // the mask stores are complete before any wave's fix-up atomic below
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    const uint32_t nc = sm.ncand;
+
+    auto mass_item = [M](uint32_t key, uint32_t, uint32_t& rk, double& wt) {
+      rk = key;
+      wt = (double)rel_mass(key_value(key), M);
+      return true;
+    };
+    uint32_t T, ncut;
+    auto resolve = [&](const auto& src) {
+      uint32_t nT;
+      T = radix_select(sm, src, mass_item, tgt, A, nT, b1, 20);
+      ncut = tie_cut(sm, src, T, nT, A, tgt, M);
+    };
+    if (nc <= GCAP) {
+      resolve(FromList{&sm, nc});
+      for (uint32_t j = t; j < nc; j += GT) {
+        const uint32_t key = sm.ckey[j], idx = sm.cidx[j];
+        if (key > T || (key == T && idx <= ncut)) {
+          __hip_atomic_fetch_or(&words[idx >> 6], (uint64_t)1 << (idx & 63), __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_WORKGROUP);
+          ++kept;
+        }
+      }
+    } else {
+      resolve(FromRow{rs, n});
+      // rewrite every word; each word is stored by the same lane that stored it above
+      kept = 0;
+      stream_row(rs, wv, lane, nit, [&](float (&v)[GLL], uint32_t base) {
+        uint64_t mine = 0;
+#pragma unroll
+        for (int k = 0; k < GLL; ++k) {
+          const uint32_t e = base + 64u * k + lane;
+          const uint32_t key = order_key(v[k]);
+          const uint64_t kw = __ballot(e < n && (key > T || (key == T && e <= ncut)));
+          if (lane == 0) kept += (uint32_t)__popcll(kw);
+          mine = lane == (uint32_t)k ? kw : mine;
+        }
+        const uint32_t wi = (base >> 6) + lane;
+        if (lane < GLL && wi < nw) words[wi] = mine;
+      });
+    }
   }
-  __syncthreads();
-  if (a.nucleus_size && t == 0) a.nucleus_size[row] = (int32_t)sm.kept;
+  if (a.nucleus_size) {
+    const double tot = block_sum_f64((double)kept, sm);
+    if (t == 0) a.nucleus_size[row] = (int32_t)tot;
+  }
 }
 
 // Per (token, word): count the L layers' bits in 7 bit planes, keep the bits
 // with count >= theta, store the token's word if asked, and OR the block's
 // tokens into the window's word.
-constexpr int VT = 1024;
+constexpr int VT = 256;
 constexpr int VTOK = VT / 64;  // tokens per block, one per wave
 
 __global__ __launch_bounds__(VT) void vote_union_kernel(const GoldenArgs a) {
@@ -485,13 +821,19 @@ __global__ __launch_bounds__(VT) void vote_union_kernel(const GoldenArgs a) {
   if (tok < a.T && w < a.W) {
     uint64_t c[7] = {0, 0, 0, 0, 0, 0, 0};
     const uint64_t* m = a.row_mask + (int64_t)tok * a.L * a.W + w;
-    for (int l = 0; l < a.L; ++l) {
-      uint64_t carry = m[(int64_t)l * a.W];
+    for (int l0 = 0; l0 < a.L; l0 += 8) {
+      uint64_t x[8];  // eight layers' loads in flight at once
 #pragma unroll
-      for (int b = 0; b < 7; ++b) {
-        const uint64_t nc = c[b] & carry;
-        c[b] ^= carry;
-        carry = nc;
+      for (int j = 0; j < 8; ++j) x[j] = l0 + j < a.L ? m[(int64_t)(l0 + j) * a.W] : 0ull;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint64_t carry = x[j];
+#pragma unroll
+        for (int b = 0; b < 7; ++b) {
+          const uint64_t nc = c[b] & carry;
+          c[b] ^= carry;
+          carry = nc;
+        }
       }
     }
     // count >= theta, most significant plane first
