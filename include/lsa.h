@@ -27,7 +27,8 @@
  *  - Ownership: the caller allocates every buffer. Pointers marked "dev" are
  *    device memory on the current HIP device; pointers marked "host" are host
  *    memory read during the call only. The library never allocates, frees or
- *    synchronises. Its only scratch space is the caller's top-k workspace.
+ *    synchronises. Its only scratch space is the caller's workspace (top-k and
+ *    golden labels).
  *  - Asynchrony: kernels are enqueued on `stream` and the call returns at once.
  *    Results are valid once the stream reaches that point. Calls are reentrant.
  *  - Errors: every argument is checked on the host before anything is enqueued.
@@ -333,17 +334,24 @@ lsa_status lsa_fetch_host(const void* pool_host /* pinned host */, int64_t row_b
  *   nucleus_size_out  dev int32 [T * L] or NULL: kept entries per row.
  *   token_golden_out  dev u64 [T][W] or NULL: token i's golden entries.
  *   golden_out      dev u64 [W]: the window's label set.
+ *   workspace       dev scratch of lsa_golden_workspace_size(T, L, row_stride)
+ *                   bytes, 16-byte aligned; its contents need no clearing and
+ *                   are not meaningful to the caller. Calls that share one
+ *                   workspace must be ordered on a stream.
  * Probabilities are accumulated in fp64 from fp32 exponentials relative to the
  * row maximum; an entry whose preceding mass is within about 1e-5 of top_p
  * may fall either way. Requires 1 <= L <= 64, 1 <= row_stride <=
  * LSA_GOLDEN_MAX_ROW; logits 4-byte and the mask buffers 8-byte aligned.
+ * A missing or short workspace returns LSA_ERR_WORKSPACE.
  * ---------------------------------------------------------------------- */
+size_t lsa_golden_workspace_size(int32_t T, int32_t L, int64_t row_stride);
 lsa_status lsa_golden_labels(const float* logits /* dev */, int64_t row_stride, int32_t T, int32_t L,
                              const int32_t* n_valid /* dev [T] */, float top_p, int32_t theta,
                              uint64_t* row_mask_out /* dev [T*L][W] */,
                              int32_t* nucleus_size_out /* dev [T*L] or NULL */,
                              uint64_t* token_golden_out /* dev [T][W] or NULL */,
-                             uint64_t* golden_out /* dev [W] */, hipStream_t stream);
+                             uint64_t* golden_out /* dev [W] */, void* workspace /* dev */,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /* Text describing the last non-OK status returned on the calling thread. */
 const char* lsa_last_error(void);

@@ -40,6 +40,8 @@
 //
 // Kernel 2 (vote and union): per (token, mask word), a bit-sliced count of the
 // layers' mask bits, compared with theta, and OR-ed over the window's tokens.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace lsa {
@@ -54,12 +56,23 @@ constexpr int GBC = GWC * GW;     // entries per block chunk
 constexpr int NB1 = 4096;         // fallback level-1 bins: key bits 31..20
 constexpr int LB = 9;             // radix level width: one digit per thread
 constexpr int NBL = 1 << LB;
-constexpr int GCAP = 3072;        // entries held in the LDS list
-constexpr int BOOT = 4;           // the first filter is the block minimum of each wave's BOOT-th largest lane maximum
-constexpr int KEEP = GCAP / 4;    // a compaction keeps the list's KEEP largest keys
-constexpr int EPOCH = 8;          // block chunks between two looks at the list's size
+constexpr int GCAP = 2048;        // entries held in the LDS list
+constexpr int BOOT = 2;           // first filter: the smallest of the waves' BOOT-th largest lane maxima
+constexpr int LW = GCAP / GW;     // list entries per wave in the segment kernel
+constexpr int SEG = 32768;        // entries per row segment (one block of the first kernel)
 constexpr uint32_t NONE = 0xFFFFFFFFu;
 constexpr float LOG2E = 1.4426950408889634f;
+
+// A segment's record in the workspace, followed by its list (key, index).
+struct SegHead {
+  double Z;         // sum of exp(y - M) over the segment
+  float M;          // the segment's largest logit (-inf: empty)
+  uint32_t tau;     // the list holds every entry of the segment whose key is >= tau
+  uint32_t count;   // entries in the list
+  uint32_t ovf;     // the list overflowed and is incomplete
+  uint32_t pad[2];
+};
+constexpr int SEG_BYTES = (int)sizeof(SegHead) + GCAP * 8;
 
 struct GoldenSmem {
   union {
@@ -78,9 +91,9 @@ struct GoldenSmem {
   uint32_t lc[NBL];     // radix level counts
   double wsum[GW];
   float wmax[GW], wmin[GW];
+  uint32_t wu[GW], wo[GW];
   double res_A;
   uint32_t res_digit, res_cnt, ncand, kept, tau;
-  uint32_t want[2];     // epoch e + 1 in want[e & 1]: the list passed half its capacity during epoch e
   int32_t last;
 };
 
@@ -92,6 +105,9 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 // The smallest logit whose key is at or above the filter key tau (key 0: all).
 // For finite y, key(y) >= tau iff y >= filter_value(tau).
 __device__ __forceinline__ float filter_value(uint32_t tau) { return tau ? key_value(tau) : -INFINITY; }
+
+// max of two finite floats (no NaN quieting: the inputs are finite logits)
+__device__ __forceinline__ float fmax_finite(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
 
 // Unnormalised probability of a logit relative to a reference m >= y.
 __device__ __forceinline__ float rel_mass(float y, float m) { return __builtin_amdgcn_exp2f((y - m) * LOG2E); }
@@ -138,6 +154,13 @@ __device__ __forceinline__ double block_sum_f64(double v, GoldenSmem& sm) {
   return tot;
 }
 
+// sm.last = max(sm.last, the largest thread index where `has` holds): one LDS
+// atomic per wave. Every thread of the block calls it.
+__device__ __forceinline__ void note_last(GoldenSmem& sm, bool has) {
+  const uint64_t m = __ballot(has);
+  if ((threadIdx.x & 63) == 0 && m) atomicMax(&sm.last, (int32_t)(threadIdx.x + 63 - __builtin_clzll(m)));
+}
+
 // Where a radix level's items come from: the LDS list, or the whole row.
 struct FromList {
   const GoldenSmem* sm;
@@ -160,6 +183,33 @@ struct FromRow {
       for (int u = 0; u < 4; ++u) {
         const uint32_t e = e0 + u * GT + threadIdx.x;
         if (e < n) f(order_key(v[u]), e);
+      }
+    }
+  }
+};
+
+// The segment lists of one row, read from the workspace: one wave per segment,
+// four entries per lane in flight. f runs in divergent lanes (no wave-wide ops).
+struct FromSegs {
+  const char* rec;
+  uint32_t nseg;
+  template <class F>
+  __device__ __forceinline__ void each(F&& f) const {
+    const uint32_t wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (uint32_t s = wv; s < nseg; s += GW) {
+      const SegHead* h = (const SegHead*)(rec + (int64_t)s * SEG_BYTES);
+      const uint32_t cnt = h->count;
+      const uint2* lst = (const uint2*)(h + 1);
+      for (uint32_t j0 = 0; j0 < cnt; j0 += 256) {
+        uint2 e[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t j = j0 + 64u * u + lane;
+          e[u] = j < cnt ? lst[j] : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (j0 + 64u * u + lane < cnt) f(e[u].x, e[u].y);
       }
     }
   }
@@ -205,7 +255,7 @@ __device__ void radix_level(GoldenSmem& sm, const Src& src, const Item& item, ui
     sm.res_A = A + ex;
     sm.res_cnt = c;
   }
-  if (c > 0) atomicMax(&sm.last, t);
+  note_last(sm, c > 0);
   __syncthreads();
   if (sm.res_digit != NONE) {
     digit = sm.res_digit;
@@ -340,115 +390,61 @@ __device__ __forceinline__ void list_push(GoldenSmem& sm, bool pass, uint32_t ke
   }
 }
 
-// Raises the filter so that about KEEP of the list's entries stay, and drops
-// the rest: a count histogram of the list by distance below its largest value,
-// the bucket where the count from the top reaches KEEP, and the smallest value
-// in that bucket becomes the filter. Buckets are monotone in the value, so
-// exactly the buckets up to that one stay (at least KEEP entries). Every
-// thread calls it with the same nc, KEEP <= nc <= GCAP.
-__device__ __attribute__((noinline)) void compact_list(GoldenSmem& sm, uint32_t nc, uint32_t lane) {
-  const int t = threadIdx.x, wv = t >> 6;
-  float hi = -INFINITY, lo = INFINITY;
-  for (uint32_t j = t; j < nc; j += GT) {
-    const float yv = key_value(sm.ckey[j]);
-    hi = fmaxf(hi, yv);
-    lo = fminf(lo, yv);
-  }
+// The R-th largest key (1 <= R <= m) among the m <= LW keys of a wave's list
+// region: bit by bit from the top, the largest v with count(key >= v) >= R.
+// Every lane of the wave calls it; no LDS writes.
+__device__ uint32_t wave_kth_key(const uint32_t* keys, uint32_t m, uint32_t R, uint32_t lane) {
+  uint32_t kk[LW / 64];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    hi = fmaxf(hi, __shfl_xor(hi, o));
-    lo = fminf(lo, __shfl_xor(lo, o));
+  for (int u = 0; u < LW / 64; ++u) {
+    const uint32_t j = 64u * u + lane;
+    kk[u] = j < m ? keys[j] : 0u;  // key 0 is below every candidate value tried
   }
-  if (lane == 0) {
-    sm.wmax[wv] = hi;
-    sm.wmin[wv] = lo;
-  }
-  sm.lc[t] = 0;
-  if (t == 0) sm.res_digit = NONE;
-  __syncthreads();
+  uint32_t v = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = v | (1u << b);
+    uint32_t cnt = 0;
 #pragma unroll
-  for (int j = 0; j < GW; ++j) {
-    hi = fmaxf(hi, sm.wmax[j]);
-    lo = fminf(lo, sm.wmin[j]);
+    for (int u = 0; u < LW / 64; ++u) cnt += (uint32_t)__popcll(__ballot(kk[u] >= c));
+    if (cnt >= R) v = c;
   }
-  const float sc = hi > lo ? (float)(NBL - 1) / (hi - lo) : 0.f;
-  auto bucket = [hi, sc](float yv) { return (uint32_t)fminf((hi - yv) * sc, (float)(NBL - 1)); };
-  for (uint32_t j = t; j < nc; j += GT) lds_inc(&sm.lc[bucket(key_value(sm.ckey[j]))]);
-  __syncthreads();
-  double ex, in, tot;
-  block_scan_f64((double)sm.lc[t], sm, ex, in, tot);  // counts: exact in fp64
-  if (ex < (double)KEEP && in >= (double)KEEP) sm.res_digit = t;
-  __syncthreads();
-  const uint32_t db = sm.res_digit;
-  float bmin = INFINITY;
-  for (uint32_t j = t; j < nc; j += GT) {
-    const float yv = key_value(sm.ckey[j]);
-    if (bucket(yv) == db) bmin = fminf(bmin, yv);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) bmin = fminf(bmin, __shfl_xor(bmin, o));
-  if (lane == 0) sm.wmin[wv] = bmin;
-  uint32_t k[GCAP / GT], x[GCAP / GT];
-#pragma unroll
-  for (int j = 0; j < GCAP / GT; ++j) {
-    const uint32_t p = t + j * GT;
-    k[j] = p < nc ? sm.ckey[p] : 0u;
-    x[j] = p < nc ? sm.cidx[p] : 0u;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < GW; ++j) bmin = fminf(bmin, sm.wmin[j]);
-  const uint32_t tnew = order_key(bmin);
-  if (t == 0) {
-    sm.ncand = 0;
-    sm.tau = max(sm.tau, tnew);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < GCAP / GT; ++j) list_push(sm, t + j * GT < nc && k[j] >= tnew, k[j], x[j], lane);
-  __syncthreads();
+  return v;
 }
 
+// Kernel 1: one block per segment of SEG entries of a (token, layer) row.
+// Each wave keeps its own part of the list (LW entries of LDS, a register
+// count, its own filter), so pushes need no atomics and no barriers.
 __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(6, 6)))
-void nucleus_kernel(const GoldenArgs a) {
+void segment_kernel(const GoldenArgs a) {
   __shared__ GoldenSmem sm;
   const int t = threadIdx.x;
   const uint32_t wv = uni((int32_t)(t >> 6));  // wave-uniform
   const uint32_t lane = t & 63;
-  const int row = blockIdx.x;
+  const int row = blockIdx.y, seg = blockIdx.x;
   const int tok = row / a.L;
   const int32_t nv = a.n_valid[tok];
-  const uint32_t n = (uint32_t)min((int64_t)max(nv, 0), a.row_stride);
-  const uint32_t nw = (n + 63) >> 6;
-  const float* y = a.logits + (int64_t)row * a.row_stride;
-  uint64_t* words = a.row_mask + (int64_t)row * a.W;
-  const auto rs = buf_rsrc(y, n * 4u);
-
-  if (row == 0)
-    for (int64_t j = t; j < a.W; j += GT) a.golden[j] = 0;  // the vote kernel ORs into it
-  for (uint32_t j = nw + t; j < (uint32_t)a.W; j += GT) words[j] = 0;
-  if (n == 0) {
-    if (a.nucleus_size && t == 0) a.nucleus_size[row] = 0;
+  const uint32_t nrow = (uint32_t)min((int64_t)max(nv, 0), a.row_stride);
+  const uint32_t s0 = (uint32_t)seg * SEG;
+  SegHead* h = (SegHead*)(a.ws + ((int64_t)row * a.S + seg) * SEG_BYTES);
+  uint2* lst = (uint2*)(h + 1);
+  if (s0 >= nrow) {
+    if (t == 0) *h = SegHead{0.0, -INFINITY, 0u, 0u, 0u, {0u, 0u}};
     return;
   }
+  const uint32_t n = min(nrow - s0, (uint32_t)SEG);  // entries of this segment
+  const auto rs = buf_rsrc(a.logits + (int64_t)row * a.row_stride + s0, n * 4u);
   const uint32_t nit = (n + GBC - 1) / GBC;
+  uint32_t* wkey = sm.ckey + wv * LW;
+  uint32_t* widx = sm.cidx + wv * LW;
 
-  // ---- pass F: lane softmax statistics and the filtered list, one read of the row
-  if (t == 0) {
-    sm.ncand = 0;
-    sm.kept = 0;
-    sm.tau = 0;
-    sm.want[0] = sm.want[1] = 0;
-  }
-  __syncthreads();
   float ml = -INFINITY;  // this lane's maximum and sum of exp(y - ml)
   double sl = 0.0;
-  bool ovf = false;  // block-uniform
-  uint32_t epoch = 0, cie = 0;
-  float tauf = -INFINITY;
+  uint32_t wc = 0;       // entries in this wave's list (wave-uniform)
+  bool wovf = false;     // this wave's list overflowed (wave-uniform)
+  float tauf = -INFINITY;  // this wave's filter: its list holds every entry it saw at or above it
   auto first = [&](float (&v)[GLL]) {
-    // First filter: every wave's BOOT-th largest lane maximum over the first block
-    // chunk, and the smallest of those. At least BOOT entries per wave pass it.
+    // First filter: every wave's BOOT-th largest lane maximum over its first
+    // chunk, and the smallest of those (one wave's sample alone can sit high).
     float x = -INFINITY, kth = -INFINITY;
 #pragma unroll
     for (int k = 0; k < GLL; ++k)
@@ -461,111 +457,221 @@ void nucleus_kernel(const GoldenArgs a) {
       const uint64_t at = __ballot(x == m);
       if (lane == (uint32_t)__builtin_ctzll(at)) x = -INFINITY;
     }
-    if (lane == 0) sm.wmax[wv] = kth;
+    if (lane == 0) sm.wmin[wv] = kth == -INFINITY ? INFINITY : kth;  // a wave without entries has no say
     __syncthreads();
     float f = INFINITY;
 #pragma unroll
-    for (int j = 0; j < GW; ++j) f = fminf(f, sm.wmax[j]);
-    if (t == 0) sm.tau = f == -INFINITY ? 0u : order_key(f);
-    tauf = f;  // filter_value(order_key(f)) == f for finite f; -inf: everything passes
+    for (int j = 0; j < GW; ++j) f = fminf(f, sm.wmin[j]);
+    tauf = f == INFINITY ? -INFINITY : f;
   };
-  stream_row3(rs, wv, lane, nit, first, [&](float (&v)[GLL], uint32_t base) {
-    const bool full = base + GWC <= n;
-    float cm = -INFINITY;
+  // One chunk: lane statistics and list pushes. FULL: every entry is inside the
+  // segment (all chunks but the last), so no per-entry bounds test.
+  auto chunk = [&](auto full_t, float (&v)[GLL], uint32_t base) {
+    constexpr bool FULL = decltype(full_t)::value;
+    bool ok[GLL];
 #pragma unroll
-    for (int k = 0; k < GLL; ++k)
-      if (full || base + 64u * k + lane < n) cm = fmaxf(cm, v[k]);
-    if (cm > ml) {
-      sl *= (double)rel_mass(ml, cm);  // 0 while ml is still -inf
-      ml = cm;
-    }
-    if (ml != -INFINITY) {
-      float ps0 = 0.f, ps1 = 0.f;
+    for (int k = 0; k < GLL; ++k) ok[k] = FULL || base + 64u * k + lane < n;
+    float cm = ml;
 #pragma unroll
-      for (int k = 0; k < GLL; k += 2) {
-        if (full || base + 64u * k + lane < n) ps0 += rel_mass(v[k], ml);
-        if (full || base + 64u * (k + 1) + lane < n) ps1 += rel_mass(v[k + 1], ml);
-      }
-      sl += (double)ps0 + (double)ps1;
+    for (int k = 0; k < GLL; ++k) cm = ok[k] ? fmax_finite(cm, v[k]) : cm;
+    // rescale the running sum when the maximum grows (the factor is 1 otherwise)
+    const float f = cm == ml ? 1.f : rel_mass(ml, cm);  // 0 while ml is still -inf
+    ml = cm;
+    float ps = 0.f;
+#pragma unroll
+    for (int k = 0; k < GLL; ++k) {
+      const float e = rel_mass(v[k], ml);
+      ps += FULL ? e : (ok[k] ? e : 0.f);
     }
-    // entries at or above the filter go to the list: one LDS atomic per chunk
-    bool va[GLL];
+    sl = sl * (double)f + (double)ps;
+    // entries at or above the filter go to the wave's list
     uint64_t pm[GLL];
     uint32_t tot = 0;
 #pragma unroll
     for (int k = 0; k < GLL; ++k) {
-      va[k] = (full || base + 64u * k + lane < n) && v[k] >= tauf;
-      pm[k] = __ballot(va[k]);
+      pm[k] = __ballot(ok[k] & (v[k] >= tauf));
       tot += (uint32_t)__popcll(pm[k]);
     }
     if (tot) {
-      uint32_t c0 = 0;
-      if (lane == 0) {
-        c0 = __hip_atomic_fetch_add(&sm.ncand, tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (c0 + tot > GCAP / 2) sm.want[epoch & 1] = epoch + 1;
-      }
-      uint32_t pos = __builtin_amdgcn_readfirstlane(c0);
+      uint32_t pos = wc;
 #pragma unroll
       for (int k = 0; k < GLL; ++k) {
         const uint32_t p = pos + below(pm[k]);
-        if (va[k] && p < GCAP) {
-          sm.ckey[p] = order_key(v[k]);
-          sm.cidx[p] = base + 64u * k + lane;
+        if (((pm[k] >> lane) & 1) && p < (uint32_t)LW) {
+          wkey[p] = order_key(v[k]);
+          widx[p] = s0 + base + 64u * k + lane;
         }
         pos += (uint32_t)__popcll(pm[k]);
       }
-    }
-    if (++cie == EPOCH) {
-      // Every wave has ended the epoch's pushes at this barrier, so want[epoch & 1]
-      // is final and all read the same value; the next epoch writes the other slot.
-      cie = 0;
-      __syncthreads();
-      const bool look = sm.want[epoch & 1] == epoch + 1;
-      ++epoch;
-      if (look) {  // no wave pushes until every wave has left this branch
-        const uint32_t nc = sm.ncand;
-        __syncthreads();
-        if (nc > GCAP) {
-          ovf = true;
-          tauf = INFINITY;  // nothing passes any more: the fallback path takes the row
-        } else {
-          compact_list(sm, nc, lane);
-          tauf = filter_value(sm.tau);
+      wc = pos;
+      if (wc > (uint32_t)LW) {  // entries were lost: the row takes the fallback
+        wovf = true;
+        tauf = INFINITY;
+      } else if (wc > (uint32_t)LW / 2) {
+        // keep the LW / 4 largest keys (and their ties) and raise the filter to the smallest of them
+        const uint32_t kv = wave_kth_key(wkey, wc, LW / 4, lane);
+        uint32_t kk[LW / 64], xx[LW / 64];
+#pragma unroll
+        for (int u = 0; u < LW / 64; ++u) {
+          const uint32_t j = 64u * u + lane;
+          kk[u] = j < wc ? wkey[j] : 0u;
+          xx[u] = j < wc ? widx[j] : 0u;
         }
+        uint32_t q = 0;
+#pragma unroll
+        for (int u = 0; u < LW / 64; ++u) {
+          const uint64_t km = __ballot(kk[u] >= kv);
+          if ((km >> lane) & 1) {
+            wkey[q + below(km)] = kk[u];
+            widx[q + below(km)] = xx[u];
+          }
+          q += (uint32_t)__popcll(km);
+        }
+        wc = q;
+        tauf = key_value(kv);
       }
     }
+  };
+  stream_row3(rs, wv, lane, nit, first, [&](float (&v)[GLL], uint32_t base) {
+    if (base + GWC <= n)
+      chunk(std::true_type{}, v, base);
+    else
+      chunk(std::false_type{}, v, base);
   });
-  __syncthreads();
-  if (sm.ncand > GCAP) ovf = true;
 
-  // ---- M and Z from the lanes' statistics
+  // ---- the segment's M, Z and common filter, then its record
   float wm = ml;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o));
-  if (lane == 0) sm.wmax[wv] = wm;
+  if (lane == 0) {
+    sm.wmax[wv] = wm;
+    sm.wu[wv] = tauf == -INFINITY ? 0u : (wovf ? 0xFFFFFFFFu : order_key(tauf));
+    sm.wo[wv] = wovf ? 1u : 0u;
+  }
   __syncthreads();
   float M = -INFINITY;
+  uint32_t tau = 0;
+  bool ovf = false;
 #pragma unroll
-  for (int j = 0; j < GW; ++j) M = fmaxf(M, sm.wmax[j]);
+  for (int j = 0; j < GW; ++j) {
+    M = fmaxf(M, sm.wmax[j]);
+    tau = max(tau, sm.wu[j]);
+    ovf = ovf || sm.wo[j];
+  }
   const double Z = block_sum_f64(ml == -INFINITY ? 0.0 : sl * (double)rel_mass(ml, M), sm);
-  const double target = (double)a.p * Z;
-  uint32_t kept = 0;
+  // every wave's list is complete at or above its own filter, so all are at or above tau
+  uint32_t kk[LW / 64], xx[LW / 64], mine = 0;
+  uint64_t km[LW / 64];
+#pragma unroll
+  for (int u = 0; u < LW / 64; ++u) {
+    const uint32_t j = 64u * u + lane;
+    kk[u] = j < wc ? wkey[j] : 0u;
+    xx[u] = j < wc ? widx[j] : 0u;
+    km[u] = __ballot(!ovf && j < wc && kk[u] >= tau);
+    mine += (uint32_t)__popcll(km[u]);
+  }
+  if (lane == 0) sm.wu[wv] = mine;
+  __syncthreads();
+  uint32_t off = 0, cnt = 0;
+#pragma unroll
+  for (int j = 0; j < GW; ++j) {
+    off += j < (int)wv ? sm.wu[j] : 0u;
+    cnt += sm.wu[j];
+  }
+#pragma unroll
+  for (int u = 0; u < LW / 64; ++u) {
+    if ((km[u] >> lane) & 1) lst[off + below(km[u])] = make_uint2(kk[u], xx[u]);
+    off += (uint32_t)__popcll(km[u]);
+  }
+  if (t == 0) *h = SegHead{Z, M, tau, cnt, ovf ? 1u : 0u, {0u, 0u}};
+}
 
+// Kernel 2: one block per (token, layer) row. Merges the row's segment records
+// and finds the nucleus, or takes the fallback.
+__global__ __launch_bounds__(GT) void resolve_kernel(const GoldenArgs a) {
+  __shared__ GoldenSmem sm;
+  const int t = threadIdx.x;
+  const uint32_t wv = uni((int32_t)(t >> 6));  // wave-uniform
+  const uint32_t lane = t & 63;
+  const int row = blockIdx.x;
+  const int tok = row / a.L;
+  const int32_t nv = a.n_valid[tok];
+  const uint32_t n = (uint32_t)min((int64_t)max(nv, 0), a.row_stride);
+  const uint32_t nw = (n + 63) >> 6;
+  const float* y = a.logits + (int64_t)row * a.row_stride;
+  uint64_t* words = a.row_mask + (int64_t)row * a.W;
+  const auto rs = buf_rsrc(y, n * 4u);
+  const uint32_t nit = (n + GBC - 1) / GBC;
+
+  if (row == 0)
+    for (int64_t j = t; j < a.W; j += GT) a.golden[j] = 0;  // the vote kernel ORs into it
+  for (uint32_t j = nw + t; j < (uint32_t)a.W; j += GT) words[j] = 0;
+  if (n == 0) {
+    if (a.nucleus_size && t == 0) a.nucleus_size[row] = 0;
+    return;
+  }
+
+  // ---- merge the segment records: M, Z, the common filter and the lists above it
+  const uint32_t nseg = (n + SEG - 1) / SEG;
+  const char* rec = a.ws + (int64_t)row * a.S * SEG_BYTES;
+  float hm = -INFINITY;
+  double hz = 0.0;
+  uint32_t ht = 0, hc = 0, ho = 0;
+  if ((uint32_t)t < nseg) {  // one record per thread (rows of up to GT segments)
+    const SegHead* h = (const SegHead*)(rec + (int64_t)t * SEG_BYTES);
+    hm = h->M;
+    hz = h->Z;
+    ht = h->tau;
+    hc = h->count;
+    ho = h->ovf;
+  }
+  {
+    float m = hm;
+    uint32_t tm = ht, o = ho;
+#pragma unroll
+    for (int x = 32; x > 0; x >>= 1) {
+      m = fmaxf(m, __shfl_xor(m, x));
+      tm = max(tm, (uint32_t)__shfl_xor((int)tm, x));
+      o |= (uint32_t)__shfl_xor((int)o, x);
+    }
+    if (lane == 0) {
+      sm.wmax[wv] = m;
+      sm.wu[wv] = tm;
+      sm.wo[wv] = o;
+    }
+  }
+  __syncthreads();
+  float M = -INFINITY;
+  uint32_t tau = 0;
+  bool ovf = nseg >= (uint32_t)GT;  // rows of GT or more segments take the fallback
+#pragma unroll
+  for (int j = 0; j < GW; ++j) {
+    M = fmaxf(M, sm.wmax[j]);
+    tau = max(tau, sm.wu[j]);
+    ovf = ovf || sm.wo[j];
+  }
+  double ex, in, tot;
+  block_scan_f64(hm == -INFINITY ? 0.0 : hz * (double)rel_mass(hm, M), sm, ex, in, tot);
+  const double Z = tot;
+  const double target = (double)a.p * Z;
+  if (t == 0) sm.tau = tau;
+  uint32_t kept = 0;
   bool done = false;
   if (!ovf) {
-    const uint32_t nc = sm.ncand, tau = sm.tau;
-    // Buckets by distance below M over the list's range [lo, M]:
+    // Every entry with key >= tau is in its segment's list (tau is at or above
+    // each segment's filter). Buckets by distance below M over [lo, M]:
     // d(y) = min(NBL - 1, (M - y) sc), so ascending d is descending y.
+    const FromSegs src{rec, nseg};
     float lo = filter_value(tau);
-    if (tau == 0) {  // the list holds the whole (short) row: its own minimum
+    if (tau == 0) {  // the lists hold the whole (short) row: its own minimum
       lo = INFINITY;
-      for (uint32_t j = t; j < nc; j += GT) lo = fminf(lo, key_value(sm.ckey[j]));
+      src.each([&](uint32_t key, uint32_t) { lo = fminf(lo, key_value(key)); });
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) lo = fminf(lo, __shfl_xor(lo, o));
-      if (lane == 0) sm.wmax[wv] = lo;
+      if (lane == 0) sm.wmin[wv] = lo;
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < GW; ++j) lo = fminf(lo, sm.wmax[j]);
+      for (int j = 0; j < GW; ++j) lo = fminf(lo, sm.wmin[j]);
     }
     const float sc = M > lo ? (float)(NBL - 1) / (M - lo) : 0.f;
     auto bucket = [M, sc](float yv) { return (uint32_t)fminf((M - yv) * sc, (float)(NBL - 1)); };
@@ -577,28 +683,27 @@ void nucleus_kernel(const GoldenArgs a) {
       sm.cb.n = 0;
     }
     __syncthreads();
-    for (uint32_t j = t; j < nc; j += GT) {
-      const uint32_t key = sm.ckey[j];
+    src.each([&](uint32_t key, uint32_t) {
       if (key >= tau) {
         const float yv = key_value(key);
         const uint32_t d = bucket(yv);
         lds_add(&sm.lw[d], (double)rel_mass(yv, M));
         lds_inc(&sm.lc[d]);
       }
-    }
+    });
     __syncthreads();
-    double A, ex, in, tot;
+    double A;
     const uint32_t c = sm.lc[t];
-    block_scan_f64(sm.lw[t], sm, ex, in, tot);  // tot: the list's mass at or above tau
+    block_scan_f64(sm.lw[t], sm, ex, in, tot);  // tot: the lists' mass at or above tau
     if (c > 0 && ex < target && in >= target) {
       sm.res_digit = t;
       sm.res_A = ex;
       sm.res_cnt = c;
     }
-    if (c > 0) atomicMax(&sm.last, t);
+    note_last(sm, c > 0);
     __syncthreads();
     if (tot > target * (1.0 + 1e-9)) {
-      // the nucleus lies inside the list: the crossing bucket db
+      // the nucleus lies inside the lists: the crossing bucket db
       uint32_t db, cnt;
       if (sm.res_digit != NONE) {
         db = sm.res_digit;
@@ -612,15 +717,14 @@ void nucleus_kernel(const GoldenArgs a) {
       uint32_t T, ncut;
       if (cnt <= (uint32_t)GT) {
         // exact order inside the bucket: rank by (key descending, index ascending)
-        for (uint32_t j = t; j < nc; j += GT) {
-          const uint32_t key = sm.ckey[j];
+        src.each([&](uint32_t key, uint32_t idx) {
           if (key >= tau && bucket(key_value(key)) == db) {
             const uint32_t q = atomicAdd(&sm.cb.n, 1u);
             sm.cb.key[q] = key;
-            sm.cb.idx[q] = sm.cidx[j];
+            sm.cb.idx[q] = idx;
             sm.cb.w[q] = (double)rel_mass(key_value(key), M);
           }
-        }
+        });
         __syncthreads();
         if ((uint32_t)t < cnt) {
           const uint32_t kt = sm.cb.key[t], it2 = sm.cb.idx[t];
@@ -647,7 +751,6 @@ void nucleus_kernel(const GoldenArgs a) {
         ncut = sm.res_cnt;
       } else {
         // a crowded bucket: radix select by mass over its entries
-        const FromList src{&sm, nc};
         uint32_t nT;
         T = radix_select(
             sm, src,
@@ -664,14 +767,13 @@ void nucleus_kernel(const GoldenArgs a) {
       // the cleared words are stored before any wave's bit below (one L2 for the block)
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __syncthreads();
-      for (uint32_t j = t; j < nc; j += GT) {
-        const uint32_t key = sm.ckey[j], idx = sm.cidx[j];
-        if (key > T || (key == T && idx <= ncut)) {
+      src.each([&](uint32_t key, uint32_t idx) {
+        if (key > T || (key == T && idx <= ncut)) {  // T >= tau: these are at or above the filter
           __hip_atomic_fetch_or(&words[idx >> 6], (uint64_t)1 << (idx & 63), __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_WORKGROUP);
           ++kept;
         }
-      }
+      });
       done = true;
     }
   }
@@ -862,10 +964,19 @@ __global__ __launch_bounds__(VT) void vote_union_kernel(const GoldenArgs a) {
 
 }  // namespace
 
-hipError_t launch_golden(const GoldenArgs& a, hipStream_t st) {
+size_t golden_workspace_bytes(int64_t rows, int64_t row_stride) {
+  return (size_t)rows * (size_t)((row_stride + SEG - 1) / SEG) * (size_t)SEG_BYTES;
+}
+
+hipError_t launch_golden(const GoldenArgs& a0, hipStream_t st) {
+  GoldenArgs a = a0;
+  a.S = (int32_t)((a.row_stride + SEG - 1) / SEG);
   const int rows = a.T * a.L;
-  hipLaunchKernelGGL(nucleus_kernel, dim3(rows), dim3(GT), 0, st, a);
+  hipLaunchKernelGGL(segment_kernel, dim3((unsigned)a.S, (unsigned)rows), dim3(GT), 0, st, a);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(resolve_kernel, dim3(rows), dim3(GT), 0, st, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 g((unsigned)((a.W + 63) / 64), (unsigned)((a.T + VTOK - 1) / VTOK));
   hipLaunchKernelGGL(vote_union_kernel, g, dim3(VT), 0, st, a);

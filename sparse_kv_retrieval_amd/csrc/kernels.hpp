@@ -94,11 +94,13 @@ struct GoldenArgs {
   int32_t* nucleus_size;   // [T * L] or null
   uint64_t* token_golden;  // [T][W] or null
   uint64_t* golden;        // [W]
+  char* ws;                // per-segment records, golden_workspace_bytes()
   int64_t row_stride;
   int64_t W;               // ceil(row_stride / 64)
   int32_t T, L;
   float p;
   int32_t theta;           // 1..127
+  int32_t S;               // segments per row (set by launch_golden)
 };
 
 hipError_t launch_score_select(const ScoreArgs& a, int key_kind, int d_h, int pairs, int depth, hipStream_t st);
@@ -111,6 +113,7 @@ hipError_t launch_union_compact(const UnionArgs& a, int B, int64_t max_words, hi
 hipError_t launch_gather(const GatherArgs& a, int grid, int rows_per_wave, hipStream_t st);
 hipError_t launch_project(const ProjArgs& a, int L, bool f32, hipStream_t st);
 hipError_t launch_project_packed(const ProjArgs& a, int L, hipStream_t st);
+size_t golden_workspace_bytes(int64_t rows, int64_t row_stride);
 hipError_t launch_golden(const GoldenArgs& a, hipStream_t st);
 hipError_t launch_pack_weights(const void* w, int rows, int K, void* out, hipStream_t st);
 

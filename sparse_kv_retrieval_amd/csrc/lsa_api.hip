@@ -409,9 +409,15 @@ lsa_status lsa_fetch_host(const void* pool_host, int64_t row_bytes, int32_t B, c
                      std::max(1, env_int("LSA_FETCH_WAVES_PER_CU", 16)), stream);
 }
 
+size_t lsa_golden_workspace_size(int32_t T, int32_t L, int64_t row_stride) {
+  if (T < 1 || L < 1 || row_stride < 1) return 0;
+  return golden_workspace_bytes((int64_t)T * L, row_stride);
+}
+
 lsa_status lsa_golden_labels(const float* logits, int64_t row_stride, int32_t T, int32_t L, const int32_t* n_valid,
                              float top_p, int32_t theta, uint64_t* row_mask_out, int32_t* nucleus_size_out,
-                             uint64_t* token_golden_out, uint64_t* golden_out, hipStream_t stream) {
+                             uint64_t* token_golden_out, uint64_t* golden_out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
   if (!logits || !n_valid || !row_mask_out || !golden_out)
     return fail(LSA_ERR_INVALID_ARG, "logits, n_valid, row_mask_out and golden_out must be set");
   if (T < 1 || L < 1 || L > 64) return fail(LSA_ERR_INVALID_ARG, "need T >= 1 and 1 <= L <= 64 (got T=%d L=%d)", T, L);
@@ -424,7 +430,12 @@ lsa_status lsa_golden_labels(const float* logits, int64_t row_stride, int32_t T,
   if ((reinterpret_cast<uintptr_t>(logits) & 3u) || (reinterpret_cast<uintptr_t>(row_mask_out) & 7u) ||
       (reinterpret_cast<uintptr_t>(golden_out) & 7u) || (reinterpret_cast<uintptr_t>(token_golden_out) & 7u))
     return fail(LSA_ERR_INVALID_ARG, "logits must be 4-byte and mask buffers 8-byte aligned");
+  const size_t need = golden_workspace_bytes((int64_t)T * L, row_stride);
+  if (!workspace || workspace_bytes < need)
+    return fail(LSA_ERR_WORKSPACE, "lsa_golden_labels needs a workspace of %zu bytes (got %zu)", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 15u) return fail(LSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   GoldenArgs a{};
+  a.ws = (char*)workspace;
   a.logits = logits; a.n_valid = n_valid; a.row_mask = row_mask_out; a.nucleus_size = nucleus_size_out;
   a.token_golden = token_golden_out; a.golden = golden_out;
   a.row_stride = row_stride; a.W = (row_stride + 63) / 64; a.T = T; a.L = L; a.p = top_p;

@@ -76,13 +76,16 @@ _topk_select = _sig("lsa_topk_select", _i32, [ctypes.POINTER(TopkLayer), _i32, _
                                                _vp, _sz, _vp])
 _gather = _sig("lsa_gather", _i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp])
 _fetch_host = _sig("lsa_fetch_host", _i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp])
-_golden = _sig("lsa_golden_labels", _i32, [_vp, _i64, _i32, _i32, _vp, _f32, _i32, _vp, _vp, _vp, _vp, _vp])
+_golden_ws = _sig("lsa_golden_workspace_size", _sz, [_i32, _i32, _i64])
+_golden = _sig("lsa_golden_labels", _i32, [_vp, _i64, _i32, _i32, _vp, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _sz,
+                                           _vp])
 _last_error = _sig("lsa_last_error", ctypes.c_char_p, [])
 _version = _sig("lsa_version", _i32, [])
 
 EXPORTED = ("lsa_project", "lsa_pack_weights_size", "lsa_pack_weights", "lsa_project_packed", "lsa_score_select",
             "lsa_topk_score", "lsa_topk_select", "lsa_union_compact", "lsa_topk_workspace_size", "lsa_topk",
-            "lsa_gather", "lsa_fetch_host", "lsa_golden_labels", "lsa_last_error", "lsa_version")
+            "lsa_gather", "lsa_fetch_host", "lsa_golden_workspace_size", "lsa_golden_labels", "lsa_last_error",
+            "lsa_version")
 
 
 def last_error() -> str:
@@ -119,6 +122,11 @@ def _stream(stream):
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    """Size in bytes of a tensor (0 for None)."""
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _check(fn, st):
@@ -235,10 +243,15 @@ def fetch_host(pool_host, *, row_bytes, B, pool_row_offsets, pool_row_offsets_ho
                                          int(out_capacity_rows), _stream(stream)))
 
 
-def golden_labels(logits, *, row_stride, T, L, n_valid, top_p, theta, row_mask, golden, nucleus_size=None,
-                  token_golden=None, stream=None):
+def golden_workspace_size(T, L, row_stride) -> int:
+    return int(_golden_ws(int(T), int(L), int(row_stride)))
+
+
+def golden_labels(logits, *, row_stride, T, L, n_valid, top_p, theta, row_mask, golden, workspace,
+                  nucleus_size=None, token_golden=None, stream=None):
     """lsa_golden_labels: logits [T, L, row_stride] fp32 and n_valid [T] int32 on the device; the mask
-    outputs are int64 tensors of ceil(row_stride / 64) words per row."""
+    outputs are int64 tensors of ceil(row_stride / 64) words per row; workspace is a device tensor of at
+    least golden_workspace_size(T, L, row_stride) bytes."""
     _check("lsa_golden_labels", _golden(_p(logits), int(row_stride), int(T), int(L), _p(n_valid), float(top_p),
                                         int(theta), _p(row_mask), _p(nucleus_size), _p(token_golden), _p(golden),
-                                        _stream(stream)))
+                                        _p(workspace), _nbytes(workspace), _stream(stream)))

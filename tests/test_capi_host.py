@@ -175,8 +175,33 @@ def test_union_topk_gather_validation(lsa):
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.fetch_host, None, **gb, match="NULL")
 
 
+class _Buf:
+    """A device-buffer stand-in of a given size (never dereferenced: validation fails first)."""
+    def __init__(self, nbytes, ptr=FAKE):
+        self.n, self.ptr = nbytes, ptr
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return 1
+
+    def data_ptr(self):
+        return self.ptr
+
+
 def test_golden_labels_validation(lsa):
-    gb = dict(row_stride=1000, T=4, L=21, n_valid=FAKE, top_p=0.6, theta=3, row_mask=FAKE, golden=FAKE, stream=0)
+    need = lsa.golden_workspace_size(4, 21, 1000)
+    assert need > 0 and lsa.golden_workspace_size(4, 21, 70000) > need
+    assert lsa.golden_workspace_size(0, 21, 1000) == 0
+    ws = _Buf(need)
+    gb = dict(row_stride=1000, T=4, L=21, n_valid=FAKE, top_p=0.6, theta=3, row_mask=FAKE, golden=FAKE,
+              workspace=ws, stream=0)
+    _expect(lsa, lsa.ERR_WORKSPACE, lsa.golden_labels, FAKE, **{**gb, "workspace": _Buf(need - 1)},
+            match="workspace")
+    _expect(lsa, lsa.ERR_WORKSPACE, lsa.golden_labels, FAKE, **{**gb, "workspace": None}, match="workspace")
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "workspace": _Buf(need, FAKE + 8)},
+            match="aligned")
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, None, **gb, match="must be set")
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "golden": None}, match="must be set")
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "n_valid": None}, match="must be set")
@@ -187,7 +212,8 @@ def test_golden_labels_validation(lsa):
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "top_p": float("nan")}, match="top_p")
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "theta": 0}, match="theta")
     _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.golden_labels, FAKE, **{**gb, "row_stride": 0}, match="row_stride")
-    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.golden_labels, FAKE, **{**gb, "row_stride": (1 << 28) + 1})
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.golden_labels, FAKE, **{**gb, "row_stride": (1 << 28) + 1,
+                                                                     "workspace": _Buf(1 << 40)})
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE + 2, **gb, match="aligned")
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "row_mask": FAKE + 4}, match="aligned")
 

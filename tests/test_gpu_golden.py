@@ -50,8 +50,9 @@ def run_gpu(torch, inp, p=None, theta=None):
     sizes = torch.full((rows,), -7, dtype=torch.int32, device=dev)
     tok = torch.full((w.T, W), -1, dtype=torch.int64, device=dev)
     golden = torch.full((W,), -1, dtype=torch.int64, device=dev)
+    ws = torch.full((lsa.golden_workspace_size(w.T, w.L, w.row_stride),), 0x5A, dtype=torch.uint8, device=dev)
     lsa.golden_labels(logits, row_stride=w.row_stride, T=w.T, L=w.L, n_valid=nv, top_p=p, theta=theta,
-                      row_mask=row_mask, golden=golden, nucleus_size=sizes, token_golden=tok)
+                      row_mask=row_mask, golden=golden, nucleus_size=sizes, token_golden=tok, workspace=ws)
     torch.cuda.synchronize()
     return (row_mask.cpu().numpy().view(np.uint64), sizes.cpu().numpy(), tok.cpu().numpy().view(np.uint64),
             golden.cpu().numpy().view(np.uint64))
