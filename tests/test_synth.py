@@ -1,11 +1,22 @@
-"""The seeded generator: determinism, layout and the planting structure."""
+"""The seeded generator: determinism, layout and the planting structure.
+
+The checks run on narrow copies of the workloads (d, r and n_h cut down): the
+layout and the planting rule do not depend on the width, and the full-width
+weights would dominate the CPU suite's time.
+"""
+import dataclasses
+
 import numpy as np
 
 from sparse_kv_retrieval_amd import synth
 
 
+def _narrow(w, **kw):
+    return dataclasses.replace(synth.scaled(w, **kw), d=512, r=256, n_h=8)
+
+
 def test_deterministic_and_layout():
-    w = synth.scaled(synth.WORKLOADS["ragged_b32"], N=(100, 0, 65, 1), name="t")
+    w = _narrow(synth.WORKLOADS["ragged_b32"], N=(100, 0, 65, 1), name="t")
     a, b = synth.make(w), synth.make(w)
     assert a.key_offsets.tolist() == [0, 100, 100, 165, 166]
     assert a.mask_word_offsets.tolist() == [0, 2, 2, 4, 5]
@@ -19,7 +30,7 @@ def test_deterministic_and_layout():
 
 
 def test_fp8_keys_and_scales():
-    w = synth.scaled(synth.WORKLOADS["fp8_1m"], N=300, B=2, name="t8")
+    w = _narrow(synth.WORKLOADS["fp8_1m"], N=300, B=2, name="t8")
     inp = synth.make(w, with_pool=False)
     assert inp.keys[0].dtype == np.uint8 and inp.key_scale[0].shape == (600,)
     assert np.all(inp.key_scale[0] > 0)
@@ -41,7 +52,7 @@ def test_tiny_is_plain_gaussian():
 
 
 def test_planted_fraction():
-    w = synth.scaled(synth.WORKLOADS["three_layer_b8"], N=2000, B=2, name="tp")
+    w = _narrow(synth.WORKLOADS["three_layer_b8"], N=2000, B=2, name="tp")
     inp = synth.make(w, with_pool=False)
     for l in range(w.L):
         assert inp.planted[l].sum() == 2 * round(0.05 * 2000)
