@@ -124,9 +124,12 @@ __device__ __forceinline__ void lds_inc(uint32_t* p) {
 }
 
 // Inclusive and exclusive block-wide prefix sums of one double per thread, in
-// thread order, and the block total. excl of thread t + 1 equals incl of
-// thread t bit for bit, so the running sums are exactly monotone.
-__device__ __forceinline__ void block_scan_f64(double v, GoldenSmem& sm, double& excl, double& incl, double& total) {
+// thread order, and the block total (NW waves; wsum is an NW-entry LDS table).
+// excl of thread t + 1 equals incl of thread t bit for bit, so the running
+// sums are exactly monotone.
+template <int NW>
+__device__ __forceinline__ void block_scan_f64_n(double v, double* wsum, double& excl, double& incl,
+                                                 double& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   double x = v;
 #pragma unroll
@@ -135,17 +138,21 @@ __device__ __forceinline__ void block_scan_f64(double v, GoldenSmem& sm, double&
     if (lane >= o) x += y;
   }
   const double prev = __shfl_up(x, 1);
-  if (lane == 63) sm.wsum[w] = x;
+  if (lane == 63) wsum[w] = x;
   __syncthreads();
   double off = 0.0, tot = 0.0;
-  for (int i = 0; i < GW; ++i) {
+  for (int i = 0; i < NW; ++i) {
     if (i == w) off = tot;
-    tot += sm.wsum[i];
+    tot += wsum[i];
   }
   __syncthreads();
   incl = off + x;
   excl = lane == 0 ? off : off + prev;
   total = tot;
+}
+
+__device__ __forceinline__ void block_scan_f64(double v, GoldenSmem& sm, double& excl, double& incl, double& total) {
+  block_scan_f64_n<GW>(v, sm.wsum, excl, incl, total);
 }
 
 __device__ __forceinline__ double block_sum_f64(double v, GoldenSmem& sm) {
@@ -411,12 +418,26 @@ __device__ uint32_t wave_kth_key(const uint32_t* keys, uint32_t m, uint32_t R, u
   return v;
 }
 
+// Per-row fallback flags, after the segment records in the workspace.
+__device__ __forceinline__ uint32_t* row_flags(const GoldenArgs& a) {
+  return (uint32_t*)(a.ws + (int64_t)a.T * a.L * a.S * SEG_BYTES);
+}
+__device__ __forceinline__ bool row_flag(const GoldenArgs& a, int row) { return row_flags(a)[row] != 0; }
+
 // Kernel 1: one block per segment of SEG entries of a (token, layer) row.
 // Each wave keeps its own part of the list (LW entries of LDS, a register
 // count, its own filter), so pushes need no atomics and no barriers.
+struct SegSmem {
+  uint32_t ckey[GCAP];
+  uint32_t cidx[GCAP];
+  double wsum[GW];
+  float wmax[GW], wmin[GW];
+  uint32_t wu[GW], wo[GW];
+};
+
 __global__ __launch_bounds__(GT) __attribute__((amdgpu_waves_per_eu(6, 6)))
 void segment_kernel(const GoldenArgs a) {
-  __shared__ GoldenSmem sm;
+  __shared__ SegSmem sm;
   const int t = threadIdx.x;
   const uint32_t wv = uni((int32_t)(t >> 6));  // wave-uniform
   const uint32_t lane = t & 63;
@@ -496,12 +517,14 @@ void segment_kernel(const GoldenArgs a) {
       uint32_t pos = wc;
 #pragma unroll
       for (int k = 0; k < GLL; ++k) {
-        const uint32_t p = pos + below(pm[k]);
-        if (((pm[k] >> lane) & 1) && p < (uint32_t)LW) {
-          wkey[p] = order_key(v[k]);
-          widx[p] = s0 + base + 64u * k + lane;
+        if (pm[k]) {  // most loads of a chunk have no entry above the filter
+          const uint32_t p = pos + below(pm[k]);
+          if (((pm[k] >> lane) & 1) && p < (uint32_t)LW) {
+            wkey[p] = order_key(v[k]);
+            widx[p] = s0 + base + 64u * k + lane;
+          }
+          pos += (uint32_t)__popcll(pm[k]);
         }
-        pos += (uint32_t)__popcll(pm[k]);
       }
       wc = pos;
       if (wc > (uint32_t)LW) {  // entries were lost: the row takes the fallback
@@ -558,7 +581,8 @@ void segment_kernel(const GoldenArgs a) {
     tau = max(tau, sm.wu[j]);
     ovf = ovf || sm.wo[j];
   }
-  const double Z = block_sum_f64(ml == -INFINITY ? 0.0 : sl * (double)rel_mass(ml, M), sm);
+  double ex, in, Z;
+  block_scan_f64_n<GW>(ml == -INFINITY ? 0.0 : sl * (double)rel_mass(ml, M), sm.wsum, ex, in, Z);
   // every wave's list is complete at or above its own filter, so all are at or above tau
   uint32_t kk[LW / 64], xx[LW / 64], mine = 0;
   uint64_t km[LW / 64];
@@ -586,10 +610,38 @@ void segment_kernel(const GoldenArgs a) {
   if (t == 0) *h = SegHead{Z, M, tau, cnt, ovf ? 1u : 0u, {0u, 0u}};
 }
 
-// Kernel 2: one block per (token, layer) row. Merges the row's segment records
-// and finds the nucleus, or takes the fallback.
-__global__ __launch_bounds__(GT) void resolve_kernel(const GoldenArgs a) {
-  __shared__ GoldenSmem sm;
+// Kernel 2: one 256-thread block per (token, layer) row. Merges the row's
+// segment records into an LDS list (every entry at or above the largest of the
+// segments' filters), finds the crossing bucket of the mass by distance below
+// M, ranks that bucket's entries exactly, and writes the row's mask. A row it
+// cannot finish that way (a list that overflowed or does not hold mass p, a
+// crowded bucket) is flagged for the fallback kernel.
+constexpr int RT = 256;           // threads per resolve block
+constexpr int RW = RT / 64;
+constexpr int NBR = RT;           // buckets: one per thread
+constexpr int MCAP = 2048;        // merged list entries held in LDS
+constexpr int CBR = 128;          // entries of the crossing bucket ranked in LDS
+
+struct ResolveSmem {
+  uint32_t key[MCAP], idx[MCAP];
+  double lw[NBR];
+  uint32_t lc[NBR];
+  uint32_t soff[RT + 1];
+  struct {
+    uint32_t key[CBR], idx[CBR], rkey[CBR], ridx[CBR];
+    double w[CBR], rw[CBR];
+    uint32_t n;
+  } cb;
+  double wsum[RW];
+  float wmax[RW];
+  uint32_t wu[RW], wo[RW];
+  double res_A;
+  uint32_t res_digit, res_cnt;
+  int32_t last;
+};
+
+__global__ __launch_bounds__(RT) void resolve_kernel(const GoldenArgs a) {
+  __shared__ ResolveSmem sm;
   const int t = threadIdx.x;
   const uint32_t wv = uni((int32_t)(t >> 6));  // wave-uniform
   const uint32_t lane = t & 63;
@@ -598,26 +650,27 @@ __global__ __launch_bounds__(GT) void resolve_kernel(const GoldenArgs a) {
   const int32_t nv = a.n_valid[tok];
   const uint32_t n = (uint32_t)min((int64_t)max(nv, 0), a.row_stride);
   const uint32_t nw = (n + 63) >> 6;
-  const float* y = a.logits + (int64_t)row * a.row_stride;
   uint64_t* words = a.row_mask + (int64_t)row * a.W;
-  const auto rs = buf_rsrc(y, n * 4u);
-  const uint32_t nit = (n + GBC - 1) / GBC;
+  uint32_t* flag = row_flags(a) + row;
 
   if (row == 0)
-    for (int64_t j = t; j < a.W; j += GT) a.golden[j] = 0;  // the vote kernel ORs into it
-  for (uint32_t j = nw + t; j < (uint32_t)a.W; j += GT) words[j] = 0;
+    for (int64_t j = t; j < a.W; j += RT) a.golden[j] = 0;  // the vote kernel ORs into it
+  for (uint32_t j = nw + t; j < (uint32_t)a.W; j += RT) words[j] = 0;
   if (n == 0) {
-    if (a.nucleus_size && t == 0) a.nucleus_size[row] = 0;
+    if (t == 0) {
+      *flag = 0;
+      if (a.nucleus_size) a.nucleus_size[row] = 0;
+    }
     return;
   }
 
-  // ---- merge the segment records: M, Z, the common filter and the lists above it
+  // ---- the segment records: M, Z, the common filter, the list offsets
   const uint32_t nseg = (n + SEG - 1) / SEG;
   const char* rec = a.ws + (int64_t)row * a.S * SEG_BYTES;
   float hm = -INFINITY;
   double hz = 0.0;
   uint32_t ht = 0, hc = 0, ho = 0;
-  if ((uint32_t)t < nseg) {  // one record per thread (rows of up to GT segments)
+  if ((uint32_t)t < nseg) {  // one record per thread; longer rows take the fallback
     const SegHead* h = (const SegHead*)(rec + (int64_t)t * SEG_BYTES);
     hm = h->M;
     hz = h->Z;
@@ -643,38 +696,61 @@ __global__ __launch_bounds__(GT) void resolve_kernel(const GoldenArgs a) {
   __syncthreads();
   float M = -INFINITY;
   uint32_t tau = 0;
-  bool ovf = nseg >= (uint32_t)GT;  // rows of GT or more segments take the fallback
+  bool fb = nseg >= (uint32_t)RT;
 #pragma unroll
-  for (int j = 0; j < GW; ++j) {
+  for (int j = 0; j < RW; ++j) {
     M = fmaxf(M, sm.wmax[j]);
     tau = max(tau, sm.wu[j]);
-    ovf = ovf || sm.wo[j];
+    fb = fb || sm.wo[j];
   }
   double ex, in, tot;
-  block_scan_f64(hm == -INFINITY ? 0.0 : hz * (double)rel_mass(hm, M), sm, ex, in, tot);
-  const double Z = tot;
-  const double target = (double)a.p * Z;
-  if (t == 0) sm.tau = tau;
+  block_scan_f64_n<RW>(hm == -INFINITY ? 0.0 : hz * (double)rel_mass(hm, M), sm.wsum, ex, in, tot);
+  const double target = (double)a.p * tot;
+  block_scan_f64_n<RW>((double)hc, sm.wsum, ex, in, tot);  // list counts: exact in fp64
+  if ((uint32_t)t <= nseg) sm.soff[t] = (uint32_t)ex;       // soff[nseg]: the total
+  const uint32_t total = (uint32_t)tot;
+  fb = fb || total > (uint32_t)MCAP;
   uint32_t kept = 0;
-  bool done = false;
-  if (!ovf) {
-    // Every entry with key >= tau is in its segment's list (tau is at or above
-    // each segment's filter). Buckets by distance below M over [lo, M]:
-    // d(y) = min(NBL - 1, (M - y) sc), so ascending d is descending y.
-    const FromSegs src{rec, nseg};
+  if (!fb) {
+    __syncthreads();
+    // gather the lists (every entry with key >= tau is in them: tau is at or
+    // above each segment's filter)
+    for (uint32_t g0 = 0; g0 < total; g0 += 4 * RT) {
+      uint2 e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t g = g0 + u * RT + t;
+        e[u] = make_uint2(0u, 0u);
+        if (g < total) {
+          uint32_t sg = 0;
+          while (sm.soff[sg + 1] <= g) ++sg;
+          e[u] = ((const uint2*)(rec + (int64_t)sg * SEG_BYTES + sizeof(SegHead)))[g - sm.soff[sg]];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t g = g0 + u * RT + t;
+        if (g < total) {
+          sm.key[g] = e[u].x;
+          sm.idx[g] = e[u].y;
+        }
+      }
+    }
+    // buckets by distance below M over [lo, M]: ascending d is descending y
     float lo = filter_value(tau);
     if (tau == 0) {  // the lists hold the whole (short) row: its own minimum
       lo = INFINITY;
-      src.each([&](uint32_t key, uint32_t) { lo = fminf(lo, key_value(key)); });
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) lo = fminf(lo, __shfl_xor(lo, o));
-      if (lane == 0) sm.wmin[wv] = lo;
+      for (uint32_t j = t; j < total; j += RT) lo = fminf(lo, key_value(sm.key[j]));
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < GW; ++j) lo = fminf(lo, sm.wmin[j]);
+      for (int o = 32; o > 0; o >>= 1) lo = fminf(lo, __shfl_xor(lo, o));
+      if (lane == 0) sm.wmax[wv] = lo;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < RW; ++j) lo = fminf(lo, sm.wmax[j]);
     }
-    const float sc = M > lo ? (float)(NBL - 1) / (M - lo) : 0.f;
-    auto bucket = [M, sc](float yv) { return (uint32_t)fminf((M - yv) * sc, (float)(NBL - 1)); };
+    const float sc = M > lo ? (float)(NBR - 1) / (M - lo) : 0.f;
+    auto bucket = [M, sc](float yv) { return (uint32_t)fminf((M - yv) * sc, (float)(NBR - 1)); };
     sm.lw[t] = 0.0;
     sm.lc[t] = 0;
     if (t == 0) {
@@ -683,28 +759,32 @@ __global__ __launch_bounds__(GT) void resolve_kernel(const GoldenArgs a) {
       sm.cb.n = 0;
     }
     __syncthreads();
-    src.each([&](uint32_t key, uint32_t) {
+    for (uint32_t j = t; j < total; j += RT) {
+      const uint32_t key = sm.key[j];
       if (key >= tau) {
         const float yv = key_value(key);
         const uint32_t d = bucket(yv);
         lds_add(&sm.lw[d], (double)rel_mass(yv, M));
         lds_inc(&sm.lc[d]);
       }
-    });
+    }
     __syncthreads();
-    double A;
     const uint32_t c = sm.lc[t];
-    block_scan_f64(sm.lw[t], sm, ex, in, tot);  // tot: the lists' mass at or above tau
+    block_scan_f64_n<RW>(sm.lw[t], sm.wsum, ex, in, tot);  // tot: the lists' mass at or above tau
     if (c > 0 && ex < target && in >= target) {
       sm.res_digit = t;
       sm.res_A = ex;
       sm.res_cnt = c;
     }
-    note_last(sm, c > 0);
+    {
+      const uint64_t m = __ballot(c > 0);
+      if (lane == 0 && m) atomicMax(&sm.last, (int32_t)(t + 63 - __builtin_clzll(m)));
+    }
     __syncthreads();
-    if (tot > target * (1.0 + 1e-9)) {
-      // the nucleus lies inside the lists: the crossing bucket db
-      uint32_t db, cnt;
+    fb = !(tot > target * (1.0 + 1e-9));  // the nucleus does not lie inside the lists
+    uint32_t db = 0, cnt = 0;
+    double A = 0.0;
+    if (!fb) {
       if (sm.res_digit != NONE) {
         db = sm.res_digit;
         A = sm.res_A;
@@ -714,71 +794,95 @@ __global__ __launch_bounds__(GT) void resolve_kernel(const GoldenArgs a) {
         A = tot - sm.lw[db];
         cnt = sm.lc[db];
       }
-      uint32_t T, ncut;
-      if (cnt <= (uint32_t)GT) {
-        // exact order inside the bucket: rank by (key descending, index ascending)
-        src.each([&](uint32_t key, uint32_t idx) {
-          if (key >= tau && bucket(key_value(key)) == db) {
-            const uint32_t q = atomicAdd(&sm.cb.n, 1u);
-            sm.cb.key[q] = key;
-            sm.cb.idx[q] = idx;
-            sm.cb.w[q] = (double)rel_mass(key_value(key), M);
-          }
-        });
-        __syncthreads();
-        if ((uint32_t)t < cnt) {
-          const uint32_t kt = sm.cb.key[t], it2 = sm.cb.idx[t];
-          uint32_t r = 0;
-          for (uint32_t j = 0; j < cnt; ++j) {
-            const uint32_t kj = sm.cb.key[j];
-            r += (kj > kt || (kj == kt && sm.cb.idx[j] < it2)) ? 1u : 0u;
-          }
-          sm.cb.rkey[r] = kt;
-          sm.cb.ridx[r] = it2;
-          sm.cb.rw[r] = sm.cb.w[t];
+      fb = cnt > (uint32_t)CBR;
+    }
+    if (!fb) {
+      // exact order inside the bucket: rank by (key descending, index ascending)
+      for (uint32_t j = t; j < total; j += RT) {
+        const uint32_t key = sm.key[j];
+        if (key >= tau && bucket(key_value(key)) == db) {
+          const uint32_t q = atomicAdd(&sm.cb.n, 1u);
+          sm.cb.key[q] = key;
+          sm.cb.idx[q] = sm.idx[j];
+          sm.cb.w[q] = (double)rel_mass(key_value(key), M);
         }
-        __syncthreads();
-        // kept while the mass before it is below the target; rank 0 always is
-        block_scan_f64((uint32_t)t < cnt ? sm.cb.rw[t] : 0.0, sm, ex, in, tot);
-        const bool keep = (uint32_t)t < cnt && (t == 0 || A + ex < target);
-        const bool next = (uint32_t)t + 1 < cnt && A + in < target;
-        if (keep && !next) {
-          sm.res_digit = sm.cb.rkey[t];
-          sm.res_cnt = sm.cb.ridx[t];
-        }
-        __syncthreads();
-        T = sm.res_digit;
-        ncut = sm.res_cnt;
-      } else {
-        // a crowded bucket: radix select by mass over its entries
-        uint32_t nT;
-        T = radix_select(
-            sm, src,
-            [tau, M, db, &bucket](uint32_t key, uint32_t, uint32_t& rk, double& wt) {
-              rk = key;
-              const float yv = key_value(key);
-              wt = (double)rel_mass(yv, M);
-              return key >= tau && bucket(yv) == db;
-            },
-            target, A, nT);
-        ncut = tie_cut(sm, src, T, nT, A, target, M);
       }
-      for (uint32_t j = t; j < nw; j += GT) words[j] = 0;
+      __syncthreads();
+      if ((uint32_t)t < cnt) {
+        const uint32_t kt = sm.cb.key[t], it2 = sm.cb.idx[t];
+        uint32_t r = 0;
+        for (uint32_t j = 0; j < cnt; ++j) {
+          const uint32_t kj = sm.cb.key[j];
+          r += (kj > kt || (kj == kt && sm.cb.idx[j] < it2)) ? 1u : 0u;
+        }
+        sm.cb.rkey[r] = kt;
+        sm.cb.ridx[r] = it2;
+        sm.cb.rw[r] = sm.cb.w[t];
+      }
+      __syncthreads();
+      // kept while the mass before it is below the target; rank 0 always is
+      block_scan_f64_n<RW>((uint32_t)t < cnt ? sm.cb.rw[t] : 0.0, sm.wsum, ex, in, tot);
+      const bool keep = (uint32_t)t < cnt && (t == 0 || A + ex < target);
+      const bool next = (uint32_t)t + 1 < cnt && A + in < target;
+      if (keep && !next) {
+        sm.res_digit = sm.cb.rkey[t];
+        sm.res_cnt = sm.cb.ridx[t];
+      }
+      __syncthreads();
+      const uint32_t T = sm.res_digit, ncut = sm.res_cnt;
+      for (uint32_t j = t; j < nw; j += RT) words[j] = 0;
       // the cleared words are stored before any wave's bit below (one L2 for the block)
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __syncthreads();
-      src.each([&](uint32_t key, uint32_t idx) {
+      for (uint32_t j = t; j < total; j += RT) {
+        const uint32_t key = sm.key[j], idx = sm.idx[j];
         if (key > T || (key == T && idx <= ncut)) {  // T >= tau: these are at or above the filter
           __hip_atomic_fetch_or(&words[idx >> 6], (uint64_t)1 << (idx & 63), __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_WORKGROUP);
           ++kept;
         }
-      });
-      done = true;
+      }
     }
   }
+  if (t == 0) *flag = fb ? 1u : 0u;
+  if (!fb && a.nucleus_size) {
+    block_scan_f64_n<RW>((double)kept, sm.wsum, ex, in, tot);
+    if (t == 0) a.nucleus_size[row] = (int32_t)tot;
+  }
+}
 
-  if (!done) {
+// Kernel 3: the fallback, one block per row; only rows the resolve kernel
+// flagged do any work. M comes from the segment records again.
+__global__ __launch_bounds__(GT) void fallback_kernel(const GoldenArgs a) {
+  __shared__ GoldenSmem sm;
+  const int t = threadIdx.x;
+  const uint32_t wv = uni((int32_t)(t >> 6));  // wave-uniform
+  const uint32_t lane = t & 63;
+  const int row = blockIdx.x;
+  const int tok = row / a.L;
+  const int32_t nv = a.n_valid[tok];
+  const uint32_t n = (uint32_t)min((int64_t)max(nv, 0), a.row_stride);
+  const uint32_t nw = (n + 63) >> 6;
+  const float* y = a.logits + (int64_t)row * a.row_stride;
+  uint64_t* words = a.row_mask + (int64_t)row * a.W;
+  const auto rs = buf_rsrc(y, n * 4u);
+  const uint32_t nit = (n + GBC - 1) / GBC;
+
+  if (n == 0 || !row_flag(a, row)) return;
+
+  // ---- the row maximum from the segment records
+  const uint32_t nseg = (n + SEG - 1) / SEG;
+  const char* rec = a.ws + (int64_t)row * a.S * SEG_BYTES;
+  float M = -INFINITY;
+  for (uint32_t s = t; s < nseg; s += GT) M = fmaxf(M, ((const SegHead*)(rec + (int64_t)s * SEG_BYTES))->M);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) sm.wmax[wv] = M;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < GW; ++j) M = fmaxf(M, sm.wmax[j]);
+  uint32_t kept = 0;
+  {
     // ---- fallback: level-1 mass histogram (second read; M is known now)
     __syncthreads();
 #pragma unroll
@@ -965,7 +1069,8 @@ __global__ __launch_bounds__(VT) void vote_union_kernel(const GoldenArgs a) {
 }  // namespace
 
 size_t golden_workspace_bytes(int64_t rows, int64_t row_stride) {
-  return (size_t)rows * (size_t)((row_stride + SEG - 1) / SEG) * (size_t)SEG_BYTES;
+  // segment records, then one fallback flag per row
+  return (size_t)rows * (size_t)((row_stride + SEG - 1) / SEG) * (size_t)SEG_BYTES + (size_t)rows * 4;
 }
 
 hipError_t launch_golden(const GoldenArgs& a0, hipStream_t st) {
@@ -975,7 +1080,10 @@ hipError_t launch_golden(const GoldenArgs& a0, hipStream_t st) {
   hipLaunchKernelGGL(segment_kernel, dim3((unsigned)a.S, (unsigned)rows), dim3(GT), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(resolve_kernel, dim3(rows), dim3(GT), 0, st, a);
+  hipLaunchKernelGGL(resolve_kernel, dim3(rows), dim3(RT), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fallback_kernel, dim3(rows), dim3(GT), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 g((unsigned)((a.W + 63) / 64), (unsigned)((a.T + VTOK - 1) / VTOK));
