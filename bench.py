@@ -18,6 +18,12 @@ calls one after another on one stream (with the per-stage events).
 `roofline` describes the dominant kernel (score_select), from HIP events on
 its stream. `cpu_baseline` is the CPU oracle on a bounded sample of the same
 workload.
+
+`golden_labels` reports the label-mining step (lsa_golden_labels) on its own
+workload, one lookahead window of 64 tokens x 21 layers x 125K entries: the
+window time from HIP events on its stream, the rate against the bytes it must
+move (the logits once, the masks written once) and HBM peak, and the oracle's
+rate on a few of the window's tokens. `--golden-only` runs just that part.
 """
 from __future__ import annotations
 
@@ -107,6 +113,101 @@ def cpu_baseline(inp, budget_s: float):
                       f"{el:.1f} s"}
 
 
+GOLDEN_WORKLOAD = "golden_t64_l21_n125k"
+GOLDEN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "golden_segment_traffic_{}.txt")
+GOLDEN_SOURCES = ["csrc/golden.hip", "csrc/common.hpp", "csrc/kernels.hpp", "build.py"]
+
+
+def golden_source_hash() -> str:
+    h = hashlib.sha256()
+    for s in GOLDEN_SOURCES:
+        with open(os.path.join(ROOT, "sparse_kv_retrieval_amd", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def golden_cpu_baseline(inp, budget_s: float) -> dict:
+    """The golden-label oracle as it stands, over whole tokens of the window (all layers) until about budget_s."""
+    from oracle import golden_oracle as G
+    w = inp.workload
+    t0 = time.perf_counter()
+    toks = 0
+    entries = 0
+    while time.perf_counter() - t0 < budget_s and toks < w.T:
+        n = int(inp.n_valid[toks])
+        G.votes(inp.logits[toks], n, w.p)
+        entries += n * w.L
+        toks += 1
+    el = time.perf_counter() - t0
+    return {"value": entries / el, "unit": "entries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{toks} of the {w.T} tokens x {w.L} layers (softmax, nucleus, vote per token), {el:.1f} s"}
+
+
+def golden_measure(steps: int, warmup: int, cpu_budget: float | None) -> dict:
+    """Golden-label mining for one lookahead window (lsa_golden_labels), timed with HIP events on its stream."""
+    import torch
+    from sparse_kv_retrieval_amd import lsa
+    from sparse_kv_retrieval_amd import synth_golden as SG
+    w = SG.WORKLOADS[GOLDEN_WORKLOAD]
+    log(f"[bench] golden labels: generating {w.name}")
+    inp = SG.make(w)
+    dev = torch.device("cuda")
+    logits = torch.from_numpy(inp.logits).to(dev)
+    nv = torch.from_numpy(inp.n_valid).to(dev)
+    rows, W = w.T * w.L, w.words
+    row_mask = torch.empty((rows, W), dtype=torch.int64, device=dev)
+    sizes = torch.empty(rows, dtype=torch.int32, device=dev)
+    golden = torch.empty(W, dtype=torch.int64, device=dev)
+    ws = torch.empty(lsa.golden_workspace_size(w.T, w.L, w.row_stride), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        lsa.golden_labels(logits, row_stride=w.row_stride, T=w.T, L=w.L, n_valid=nv, top_p=w.p, theta=w.theta,
+                          row_mask=row_mask, golden=golden, nucleus_size=sizes, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    entries = int(inp.n_valid.astype(np.int64).sum()) * w.L
+    # logits read once; row masks, nucleus sizes and the window's label set written once
+    alg = entries * 4 + rows * W * 8 + rows * 4 + W * 8
+    label = int(np.unpackbits(golden.cpu().numpy().view(np.uint8)).sum())
+    sz = sizes.cpu().numpy()
+    achieved = alg / (ms * 1e-3) / 1e9
+    out = {"workload": w.name, "T": w.T, "L": w.L, "entries_per_row": int(inp.n_valid.max()), "top_p": w.p,
+           "theta": w.theta, "us_per_window": ms * 1e3, "entries_per_s": entries / (ms * 1e-3),
+           "algorithmic_bytes": alg, "achieved_GBs": achieved, "peak_GBs": PEAK_HBM_GBS,
+           "frac": achieved / PEAK_HBM_GBS, "label_set": label,
+           "nucleus_size": {"min": int(sz.min()), "mean": float(sz.mean()), "max": int(sz.max())},
+           "what": "lsa_golden_labels over one window: every (token, layer) row's top-p nucleus, the layer vote "
+                   "per token and the union over the window (four kernels; logits read once)"}
+    traffic = None
+    path = GOLDEN_TRAFFIC_FILE.format(w.name)
+    if os.path.exists(path):
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith(("#", " ", "|", "`")):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_hash") == golden_source_hash() and kv.get("workload") == w.name:
+            traffic = int(kv["traffic_bytes_per_launch"])
+    out["segment_kernel_traffic"] = traffic
+    if cpu_budget:
+        log("[bench] golden labels: cpu baseline")
+        out["cpu_baseline"] = golden_cpu_baseline(inp, cpu_budget)
+    del logits, row_mask, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +217,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-host-fetch", action="store_true", help="skip the cold-pool (pinned host) fetch measurement")
+    ap.add_argument("--no-golden", action="store_true", help="skip the golden-label mining measurement")
+    ap.add_argument("--golden-only", action="store_true", help="only the golden-label mining measurement")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -126,6 +229,11 @@ def main():
     import torch
     from sparse_kv_retrieval_amd import synth
     from sparse_kv_retrieval_amd.pipeline import Pipeline
+
+    if args.golden_only:
+        g = golden_measure(args.steps, args.warmup, None if args.no_cpu_baseline else 3.0)
+        print(json.dumps({"golden_labels": g}), flush=True)
+        return
 
     w = synth.WORKLOADS[args.workload]
     log(f"[bench] generating {w.name}")
@@ -245,6 +353,10 @@ def main():
     }
     if host_fetch is not None:
         out["host_fetch"] = host_fetch
+    if not args.no_golden:
+        del p
+        torch.cuda.empty_cache()
+        out["golden_labels"] = golden_measure(args.steps, args.warmup, None if args.no_cpu_baseline else 3.0)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline")
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
