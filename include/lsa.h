@@ -22,13 +22,17 @@
  *   lsa_golden_labels  training targets: per-layer softmax top-p nucleus,
  *                      cross-layer vote, union over the lookahead window
  *                                                    [HYPER] 数据集, [BLOG] §4.1
+ *   lsa_train_step     one training step of an indexer layer: focal BCE of
+ *                      the score against golden labels, gradients of W^DQ,
+ *                      W^IUQ and W^w with the keys frozen
+ *                                                  [BLOG] §4 训练, [HYPER] 方法
  *
  * Conventions shared by every call:
  *  - Ownership: the caller allocates every buffer. Pointers marked "dev" are
  *    device memory on the current HIP device; pointers marked "host" are host
  *    memory read during the call only. The library never allocates, frees or
- *    synchronises. Its only scratch space is the caller's workspace (top-k and
- *    golden labels).
+ *    synchronises. Its only scratch space is the caller's workspace (top-k,
+ *    golden labels and the training step).
  *  - Asynchrony: kernels are enqueued on `stream` and the call returns at once.
  *    Results are valid once the stream reaches that point. Calls are reentrant.
  *  - Errors: every argument is checked on the host before anything is enqueued.
@@ -352,6 +356,57 @@ lsa_status lsa_golden_labels(const float* logits /* dev */, int64_t row_stride, 
                              uint64_t* token_golden_out /* dev [T][W] or NULL */,
                              uint64_t* golden_out /* dev [W] */, void* workspace /* dev */,
                              size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * lsa_train_step: one training step of a memory-indexer layer ([BLOG] §4
+ * "训练" (training); [HYPER] 方法 (Method); the gist.science summary names the
+ * same loss). The compressed index keys are frozen; the query side's
+ * projections are trained with a focal binary cross-entropy on the selection
+ * score against the golden labels.
+ *
+ *   c = h W^DQ, q = c W^IUQ viewed as [n_h, d_h], w = h W^w   (as lsa_project)
+ *   x_s = sum_j w_j ReLU(q_j . K_s),  p_s = sigmoid(x_s)       ([BLOG] §3.1)
+ *   loss = mean over every entry s of every sequence of
+ *          -alpha (1 - p_s)^gamma log p_s          if s is golden,
+ *          -(1 - alpha) p_s^gamma log(1 - p_s)     otherwise.
+ * Outputs are the loss and its gradients with respect to the three weight
+ * matrices, in the weights' own "out x in" layouts.
+ *
+ *   h, w_dq, w_iuq, w_w  dev bf16, the lsa_project layouts ([B, d], [r, d],
+ *                   [n_h*d_h, r], [n_h, d]); 16-byte aligned.
+ *   keys            dev bf16 [rows][d_h], the selection path's layout.
+ *   key_offsets, mask_word_offsets (dev and host copies): as lsa_score_select.
+ *   labels          dev u64 bit masks in the lsa_score_select mask layout: bit
+ *                   s % 64 of word mask_word_offsets[b] + s / 64 is 1 when entry s
+ *                   of sequence b is golden. Bits past N_b are ignored.
+ *   gamma >= 0, alpha in [0, 1]  the focal constants (2 and 0.25 usually).
+ *   loss_out        dev fp32 [1].
+ *   g_dq            dev fp32 [r, d];  g_iuq  dev fp32 [n_h*d_h, r];
+ *   g_w             dev fp32 [n_h, d]. Every element is written.
+ *   workspace       dev scratch of lsa_train_workspace_size(B,
+ *                   key_offsets_host, r) bytes, 16-byte aligned; it needs no
+ *                   clearing. Calls that share one workspace must be ordered.
+ * Precision: the projections as lsa_project with LSA_BF16; in the key scan q
+ * and the per-(entry, head) gradient coefficients enter bf16 MFMAs as hi + lo
+ * pairs (about 16 significant bits), with fp32 accumulation. The loss is summed
+ * in fp64 per block of 1024 entries. A score within rounding of 0 may fall on
+ * either side of the ReLU kink.
+ * Supported: n_h = 64, d_h = 128, 1 <= B <= 32, d and r positive multiples of
+ * 32, N_b < 2^23 entries per sequence. A sequence with no entries adds nothing;
+ * with no entries at all the loss and the gradients are 0.
+ * A missing or short workspace returns LSA_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------- */
+size_t lsa_train_workspace_size(int32_t B, const int64_t* key_offsets_host /* host [B+1] */, int32_t r);
+lsa_status lsa_train_step(const void* h /* dev */, const void* w_dq /* dev */, const void* w_iuq /* dev */,
+                          const void* w_w /* dev */, const void* keys /* dev */,
+                          const int64_t* key_offsets /* dev [B+1] */,
+                          const int64_t* key_offsets_host /* host [B+1] */, const uint64_t* labels /* dev */,
+                          const int64_t* mask_word_offsets /* dev [B+1] */,
+                          const int64_t* mask_word_offsets_host /* host [B+1] */, int32_t B, int32_t d, int32_t r,
+                          int32_t n_h, int32_t d_h, float gamma, float alpha, float* loss_out /* dev [1] */,
+                          float* g_dq /* dev [r, d] */, float* g_iuq /* dev [n_h*d_h, r] */,
+                          float* g_w /* dev [n_h, d] */, void* workspace /* dev */, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /* Text describing the last non-OK status returned on the calling thread. */
 const char* lsa_last_error(void);

@@ -11,7 +11,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["score.hip", "score_stream.hip", "union.hip", "topk.hip", "gather.hip", "project.hip", "golden.hip", "lsa_api.hip"]
+SOURCES = ["score.hip", "score_stream.hip", "union.hip", "topk.hip", "gather.hip", "project.hip", "golden.hip", "train.hip", "lsa_api.hip"]
 OUT = os.path.join(HERE, "liblsa.so")
 
 BUILD_DIR = os.path.join(HERE, "_build")

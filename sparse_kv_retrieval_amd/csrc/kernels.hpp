@@ -103,6 +103,31 @@ struct GoldenArgs {
   int32_t S;               // segments per row (set by launch_golden)
 };
 
+// Indexer training step (one layer; n_h = 64, d_h = 128 keys in bf16).
+struct TrainArgs {
+  const void* keys;        // bf16 [rows][128], sequence b at key_off[b]
+  const int64_t* key_off;  // [B+1]
+  const uint64_t* labels;  // label bits, region b at mwo[b]
+  const int64_t* mwo;      // [B+1]
+  const void* h;           // bf16 [B][d]
+  const void* w_iuq;       // bf16 [n_h*d_h][r]
+  const float* c;          // [B][r]
+  const float* q;          // [B][n_h][d_h]
+  const float* w;          // [B][n_h]
+  float* part;             // scan block partials
+  float* dq;               // [B][n_h*d_h]
+  float* dw;               // [B][n_h]
+  float* dc;               // [B][r]
+  float* dcp;              // dc partials [n_h*d_h / 64][B][r]
+  float* loss;             // [1]
+  float* g_dq;             // [r][d]
+  float* g_iuq;            // [n_h*d_h][r]
+  float* g_w;              // [n_h][d]
+  int64_t nblk;            // scan blocks
+  int32_t B, d, r;
+  float gamma, alpha, inv_total;
+};
+
 hipError_t launch_score_select(const ScoreArgs& a, int key_kind, int d_h, int pairs, int depth, hipStream_t st);
 // one wave per tile, keys loaded straight into LDS (bf16 and fp8 keys)
 bool score_stream_supported(int key_kind, int d_h);
@@ -114,6 +139,9 @@ hipError_t launch_gather(const GatherArgs& a, int grid, int rows_per_wave, hipSt
 hipError_t launch_project(const ProjArgs& a, int L, bool f32, hipStream_t st);
 hipError_t launch_project_packed(const ProjArgs& a, int L, hipStream_t st);
 size_t golden_workspace_bytes(int64_t rows, int64_t row_stride);
+int64_t train_scan_blocks(const int64_t* key_off_host, int B);
+size_t train_workspace_bytes(int B, int r, int64_t nblk);
+hipError_t launch_train(const TrainArgs& a, hipStream_t st);
 hipError_t launch_golden(const GoldenArgs& a, hipStream_t st);
 hipError_t launch_pack_weights(const void* w, int rows, int K, void* out, hipStream_t st);
 

@@ -444,4 +444,60 @@ lsa_status lsa_golden_labels(const float* logits, int64_t row_stride, int32_t T,
   return e == hipSuccess ? LSA_OK : hip_fail("lsa_golden_labels launch", e);
 }
 
+size_t lsa_train_workspace_size(int32_t B, const int64_t* key_offsets_host, int32_t r) {
+  if (B < 1 || !key_offsets_host || r < 1) return 0;
+  return train_workspace_bytes(B, r, train_scan_blocks(key_offsets_host, B));
+}
+
+lsa_status lsa_train_step(const void* h, const void* w_dq, const void* w_iuq, const void* w_w, const void* keys,
+                          const int64_t* key_offsets, const int64_t* key_offsets_host, const uint64_t* labels,
+                          const int64_t* mask_word_offsets, const int64_t* mask_word_offsets_host, int32_t B,
+                          int32_t d, int32_t r, int32_t n_h, int32_t d_h, float gamma, float alpha, float* loss_out,
+                          float* g_dq, float* g_iuq, float* g_w, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  if (!h || !w_dq || !w_iuq || !w_w || !keys || !labels || !loss_out || !g_dq || !g_iuq || !g_w)
+    return fail(LSA_ERR_INVALID_ARG, "h, the weights, keys, labels, loss_out and the gradients must be set");
+  if (B < 1 || B > 32) return fail(LSA_ERR_UNSUPPORTED, "B must be in [1, 32] (got %d)", B);
+  if (n_h != 64 || d_h != 128) return fail(LSA_ERR_UNSUPPORTED, "the training step needs n_h = 64, d_h = 128");
+  if (d < 32 || d % 32 || r < 32 || r % 32)
+    return fail(LSA_ERR_UNSUPPORTED, "d and r must be positive multiples of 32 (got d=%d r=%d)", d, r);
+  if (!(gamma >= 0.f && gamma < 1e6f) || !(alpha >= 0.f && alpha <= 1.f))
+    return fail(LSA_ERR_INVALID_ARG, "need gamma >= 0 and 0 <= alpha <= 1");
+  lsa_status s;
+  if ((s = check_seq_layout(B, key_offsets, key_offsets_host, mask_word_offsets, mask_word_offsets_host)) != LSA_OK)
+    return s;
+  for (int32_t b = 0; b < B; ++b)
+    if ((key_offsets_host[b + 1] - key_offsets_host[b]) * 256 >= ((int64_t)1 << 31))
+      return fail(LSA_ERR_UNSUPPORTED, "sequence %d is longer than the training scan addresses (2^23 entries)", b);
+  if (!aligned16(h) || !aligned16(w_dq) || !aligned16(w_iuq) || !aligned16(keys) || !aligned16(workspace))
+    return fail(LSA_ERR_INVALID_ARG, "h, w_dq, w_iuq, keys and workspace must be 16-byte aligned");
+  const int64_t nblk = train_scan_blocks(key_offsets_host, B);
+  const size_t need = train_workspace_bytes(B, r, nblk);
+  if (!workspace || workspace_bytes < need)
+    return fail(LSA_ERR_WORKSPACE, "lsa_train_step needs a workspace of %zu bytes (got %zu)", need, workspace_bytes);
+  const int64_t total = key_offsets_host[B] - key_offsets_host[0];
+  float* f = (float*)workspace;
+  float* c = f; f += (int64_t)B * r;
+  float* q = f; f += (int64_t)B * n_h * d_h;
+  float* w = f; f += (int64_t)B * n_h;
+  float* dq = f; f += (int64_t)B * n_h * d_h;
+  float* dw = f; f += (int64_t)B * n_h;
+  float* dc = f; f += (int64_t)B * r;
+  float* part = f; f += nblk * (n_h * d_h + n_h + 1);
+  float* dcp = f;
+  ProjArgs p{};
+  p.h[0] = h; p.w_dq[0] = w_dq; p.w_iuq[0] = w_iuq; p.w_w[0] = w_w;
+  p.c[0] = c; p.q[0] = q; p.w[0] = w;
+  p.B = B; p.d = d; p.r = r; p.n_h = n_h; p.d_h = d_h;
+  hipError_t e = launch_project(p, 1, false, stream);
+  if (e != hipSuccess) return hip_fail("lsa_train_step projection", e);
+  TrainArgs a{};
+  a.keys = keys; a.key_off = key_offsets; a.labels = labels; a.mwo = mask_word_offsets; a.h = h; a.w_iuq = w_iuq;
+  a.c = c; a.q = q; a.w = w; a.part = part; a.dq = dq; a.dw = dw; a.dc = dc; a.dcp = dcp; a.loss = loss_out;
+  a.g_dq = g_dq; a.g_iuq = g_iuq; a.g_w = g_w; a.nblk = nblk; a.B = B; a.d = d; a.r = r;
+  a.gamma = gamma; a.alpha = alpha; a.inv_total = total > 0 ? (float)(1.0 / (double)total) : 0.f;
+  e = launch_train(a, stream);
+  return e == hipSuccess ? LSA_OK : hip_fail("lsa_train_step launch", e);
+}
+
 }  // extern "C"

@@ -79,12 +79,16 @@ _fetch_host = _sig("lsa_fetch_host", _i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp,
 _golden_ws = _sig("lsa_golden_workspace_size", _sz, [_i32, _i32, _i64])
 _golden = _sig("lsa_golden_labels", _i32, [_vp, _i64, _i32, _i32, _vp, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _sz,
                                            _vp])
+_train_ws = _sig("lsa_train_workspace_size", _sz, [_i32, _vp, _i32])
+_train = _sig("lsa_train_step", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                       _i32, _f32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
 _last_error = _sig("lsa_last_error", ctypes.c_char_p, [])
 _version = _sig("lsa_version", _i32, [])
 
 EXPORTED = ("lsa_project", "lsa_pack_weights_size", "lsa_pack_weights", "lsa_project_packed", "lsa_score_select",
             "lsa_topk_score", "lsa_topk_select", "lsa_union_compact", "lsa_topk_workspace_size", "lsa_topk",
-            "lsa_gather", "lsa_fetch_host", "lsa_golden_workspace_size", "lsa_golden_labels", "lsa_last_error",
+            "lsa_gather", "lsa_fetch_host", "lsa_golden_workspace_size", "lsa_golden_labels", "lsa_train_workspace_size",
+            "lsa_train_step", "lsa_last_error",
             "lsa_version")
 
 
@@ -255,3 +259,22 @@ def golden_labels(logits, *, row_stride, T, L, n_valid, top_p, theta, row_mask, 
     _check("lsa_golden_labels", _golden(_p(logits), int(row_stride), int(T), int(L), _p(n_valid), float(top_p),
                                         int(theta), _p(row_mask), _p(nucleus_size), _p(token_golden), _p(golden),
                                         _p(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def train_workspace_size(B, key_offsets_host, r) -> int:
+    ko, kop = _host64(key_offsets_host)
+    return int(_train_ws(int(B), kop, int(r)))
+
+
+def train_step(*, h, w_dq, w_iuq, w_w, keys, key_offsets, key_offsets_host, labels, mask_word_offsets,
+               mask_word_offsets_host, B, d, r, n_h, d_h, gamma, alpha, loss, g_dq, g_iuq, g_w, workspace,
+               stream=None):
+    """lsa_train_step: h [B, d], w_dq [r, d], w_iuq [n_h*d_h, r], w_w [n_h, d] and keys [rows, d_h] as bf16
+    bits on the device; labels are the selection path's bit masks; loss [1] and the gradients (the
+    weights' shapes) are fp32 device tensors; workspace holds train_workspace_size(...) bytes."""
+    ko, kop = _host64(key_offsets_host)
+    mo, mop = _host64(mask_word_offsets_host)
+    _check("lsa_train_step", _train(_p(h), _p(w_dq), _p(w_iuq), _p(w_w), _p(keys), _p(key_offsets), kop, _p(labels),
+                                    _p(mask_word_offsets), mop, int(B), int(d), int(r), int(n_h), int(d_h),
+                                    float(gamma), float(alpha), _p(loss), _p(g_dq), _p(g_iuq), _p(g_w),
+                                    _p(workspace), _nbytes(workspace), _stream(stream)))

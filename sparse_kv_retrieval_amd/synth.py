@@ -78,6 +78,7 @@ class Workload:
     N: tuple = ()            # entries per sequence (fixed lengths)
     ragged_tokens: tuple = ()  # (lo, hi) log-uniform token range, N = tokens // 4
     planted: float = 0.0     # planted fraction per layer; 0 = plain N(0,1) keys, no spikes
+    random_init: bool = False  # indexer weights and h without the spikes (keys still planted)
     threshold: float = 0.5
     pool_dim: int = 512      # bf16 latent width of the compressed-KV pool rows
     seed: int = 0
@@ -87,7 +88,7 @@ class Workload:
         return self.planted > 0.0
 
 
-# The five workloads this build runs (entry counts assume 4:1 CSA compression).
+# The workloads this build runs (entry counts assume 4:1 CSA compression).
 WORKLOADS = {
     w.name: w
     for w in (
@@ -106,6 +107,10 @@ WORKLOADS = {
         Workload("ragged_b32", 4, B=32, L=3, d=4096, r=2048, n_h=64, d_h=128,
                  key_dtype="bf16", act_dtype="bf16", k=2048,
                  ragged_tokens=(16_384, 524_288), planted=0.05, seed=4),
+        # one indexer layer being trained from random initialisation against frozen planted keys
+        Workload("train_b8", 5, B=8, L=1, d=4096, r=2048, n_h=64, d_h=128,
+                 key_dtype="bf16", act_dtype="bf16", k=2048, N=(125_000,) * 8,
+                 planted=0.05, random_init=True, seed=5),
     )
 }
 
@@ -196,7 +201,7 @@ def _layer_weights(w: Workload, g: np.random.Generator, a, u) -> LayerWeights:
     wdq = g.standard_normal((r, d), dtype=np.float32) * np.float32(1.0 / math.sqrt(d))
     wiuq = g.standard_normal((nh * dh, r), dtype=np.float32) * np.float32(1.0 / math.sqrt(r))
     ww = g.standard_normal((nh, d), dtype=np.float32) * np.float32(1.0 / math.sqrt(d))
-    if w.structured:
+    if w.structured and not w.random_init:
         pol = np.where(np.arange(nh) < nh // 2, 1.0, -1.0)
         wdq[:, 0] = (C_SPIKE / KAPPA) * a
         alpha = Q_SPIKE / C_SPIKE
@@ -233,7 +238,7 @@ def make(w: Workload, *, with_pool: bool = True) -> Inputs:
         hl = np.empty((B, w.d), np.float32)
         for b in range(B):
             hl[b] = _rng(w, 4, l, b).standard_normal(w.d, dtype=np.float32)
-        if w.structured:
+        if w.structured and not w.random_init:
             hl[:, 0] = KAPPA
         hs.append(_store_act(w, hl))
 
@@ -279,3 +284,38 @@ def make(w: Workload, *, with_pool: bool = True) -> Inputs:
             pool[key_offsets[b]:key_offsets[b + 1]] = g.integers(
                 0, 1 << 16, size=(int(n[b]), w.pool_dim), dtype=np.uint16)
     return Inputs(w, n, key_offsets, mwo, hs, mem, nat, keys, scales, pool, planted)
+
+
+# ---------------------------------------------------------------- training labels
+def pack_mask_words(bits: np.ndarray, key_offsets: np.ndarray, mask_word_offsets: np.ndarray) -> np.ndarray:
+    """Lay out per-entry booleans [rows] as the selection path's u64 mask words.
+
+    Entry s of sequence b is bit s % 64 of word mask_word_offsets[b] + s // 64;
+    bits past N_b are 0."""
+    B = len(key_offsets) - 1
+    out = np.zeros(int(mask_word_offsets[-1]), np.uint64)
+    for b in range(B):
+        s0, s1 = int(key_offsets[b]), int(key_offsets[b + 1])
+        n = s1 - s0
+        if n == 0:
+            continue
+        padded = np.zeros(((n + 63) // 64) * 64, np.uint8)
+        padded[:n] = bits[s0:s1]
+        words = np.packbits(padded, bitorder="little").view(np.uint64)
+        out[int(mask_word_offsets[b]):int(mask_word_offsets[b + 1])] = words
+    return out
+
+
+def train_labels(inp: Inputs, layer: int = 0, flip: float = 0.02):
+    """Golden labels for a training step on one layer's keys.
+
+    The labels are the layer's planted entries (the keys the structured indexer
+    is built to favour), with a fraction `flip` of all entries toggled at random
+    so that both classes hold entries the current weights get wrong. Returns
+    (bool [rows], u64 mask words in the selection path's layout)."""
+    w = inp.workload
+    rows = int(inp.key_offsets[-1])
+    g = _rng(w, 7, layer)
+    lab = inp.planted[layer].copy() if inp.planted else np.zeros(rows, bool)
+    lab ^= g.random(rows) < flip
+    return lab, pack_mask_words(lab, inp.key_offsets, inp.mask_word_offsets)

@@ -218,6 +218,43 @@ def test_golden_labels_validation(lsa):
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.golden_labels, FAKE, **{**gb, "row_mask": FAKE + 4}, match="aligned")
 
 
+def test_train_step_validation(lsa):
+    ko = np.array([0, 1000, 1000, 3049], np.int64)
+    mo = np.array([0, 16, 16, 49], np.int64)
+    need = lsa.train_workspace_size(3, ko, 128)
+    assert need > 0 and lsa.train_workspace_size(3, np.array([0, 1000, 1000, 300000]), 128) > need
+    assert lsa.train_workspace_size(0, ko, 128) == 0
+    tb = dict(h=FAKE, w_dq=FAKE, w_iuq=FAKE, w_w=FAKE, keys=FAKE, key_offsets=FAKE, key_offsets_host=ko,
+              labels=FAKE, mask_word_offsets=FAKE, mask_word_offsets_host=mo, B=3, d=256, r=128, n_h=64, d_h=128,
+              gamma=2.0, alpha=0.25, loss=FAKE, g_dq=FAKE, g_iuq=FAKE, g_w=FAKE, workspace=_Buf(need), stream=0)
+
+    def bad(st, match=None, **kw):
+        _expect(lsa, st, lsa.train_step, **{**tb, **kw}, match=match)
+
+    bad(lsa.ERR_WORKSPACE, "workspace", workspace=_Buf(need - 1))
+    bad(lsa.ERR_WORKSPACE, "workspace", workspace=None)
+    bad(lsa.ERR_INVALID_ARG, "aligned", workspace=_Buf(need, FAKE + 8))
+    for name in ("h", "w_dq", "w_iuq", "w_w", "keys", "labels", "loss", "g_dq", "g_iuq", "g_w"):
+        bad(lsa.ERR_INVALID_ARG, "must be set", **{name: None})
+    bad(lsa.ERR_INVALID_ARG, "aligned", h=FAKE + 2)
+    bad(lsa.ERR_INVALID_ARG, "aligned", keys=FAKE + 8)
+    bad(lsa.ERR_UNSUPPORTED, "B must be", B=0)
+    bad(lsa.ERR_UNSUPPORTED, "B must be", B=33)
+    bad(lsa.ERR_UNSUPPORTED, "n_h = 64", n_h=32)
+    bad(lsa.ERR_UNSUPPORTED, "n_h = 64", d_h=64)
+    bad(lsa.ERR_UNSUPPORTED, "multiples of 32", d=250)
+    bad(lsa.ERR_UNSUPPORTED, "multiples of 32", r=0)
+    bad(lsa.ERR_INVALID_ARG, "gamma", gamma=-1.0)
+    bad(lsa.ERR_INVALID_ARG, "gamma", gamma=float("nan"))
+    bad(lsa.ERR_INVALID_ARG, "alpha", alpha=1.5)
+    bad(lsa.ERR_INVALID_ARG, "ceil", mask_word_offsets_host=np.array([0, 15, 15, 48], np.int64))
+    bad(lsa.ERR_INVALID_ARG, "decreasing", key_offsets_host=np.array([0, 1000, 999, 3049], np.int64))
+    long_ko = np.array([0, 1 << 23, 1 << 23, 1 << 23], np.int64)
+    long_mo = np.array([0, (1 << 23) // 64] * 1 + [(1 << 23) // 64] * 2, np.int64)
+    bad(lsa.ERR_UNSUPPORTED, "longer", key_offsets_host=long_ko, mask_word_offsets_host=long_mo,
+        workspace=_Buf(1 << 40))
+
+
 def test_binding_has_no_oracle_import():
     """The product path (binding, pipeline, library sources) never refers to the oracle."""
     pkg = os.path.join(ROOT, "sparse_kv_retrieval_amd")
@@ -226,4 +263,4 @@ def test_binding_has_no_oracle_import():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 txt = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", txt, re.M), f
-                assert "lsa_oracle" not in txt and "golden_oracle" not in txt, f
+                assert "lsa_oracle" not in txt and "golden_oracle" not in txt and "train_oracle" not in txt, f
