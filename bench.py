@@ -24,6 +24,11 @@ workload, one lookahead window of 64 tokens x 21 layers x 125K entries: the
 window time from HIP events on its stream, the rate against the bytes it must
 move (the logits once, the masks written once) and HBM peak, and the oracle's
 rate on a few of the window's tokens. `--golden-only` runs just that part.
+
+`train_step` reports one training step of an indexer layer (lsa_train_step)
+on 8 sequences x 125K entries with d = 4096, r = 2048: the step time from HIP
+events, the rate against the bytes the step must move, and the oracle's rate
+on a few of the sequences. `--train-only` runs just that part.
 """
 from __future__ import annotations
 
@@ -208,6 +213,92 @@ def golden_measure(steps: int, warmup: int, cpu_budget: float | None) -> dict:
     return out
 
 
+TRAIN_WORKLOAD = "train_b8"
+
+
+def train_bytes(w, entries: int) -> dict:
+    """Bytes one training step must move: the keys and labels once; h and the three weight matrices for
+    the projections, W^IUQ a second time for dc = dq W^IUQ (dq exists only after the key scan); the three
+    gradients written once."""
+    d, r, m, nh = w.d, w.r, w.n_h * w.d_h, w.n_h
+    keys = entries * w.d_h * 2 + entries // 8
+    weights = w.B * d * 2 + r * d * 2 + 2 * m * r * 2 + nh * d * 2
+    grads = (r * d + m * r + nh * d) * 4
+    return {"keys_and_labels": keys, "activations_and_weights": weights, "gradients": grads,
+            "total": keys + weights + grads}
+
+
+def train_measure(steps: int, warmup: int, cpu_budget: float | None) -> dict:
+    """One indexer-layer training step (lsa_train_step) on its own workload, timed with HIP events."""
+    import torch
+    from sparse_kv_retrieval_amd import lsa
+    from sparse_kv_retrieval_amd import synth
+    w = synth.WORKLOADS[TRAIN_WORKLOAD]
+    log(f"[bench] training step: generating {w.name}")
+    inp = synth.make(w, with_pool=False)
+    lab, words = synth.train_labels(inp, 0, 0.02)
+    dev = torch.device("cuda")
+
+    def u16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    mw = inp.mem_w[0]
+    args = dict(h=u16(inp.h[0]), w_dq=u16(mw.w_dq), w_iuq=u16(mw.w_iuq), w_w=u16(mw.w_w), keys=u16(inp.keys[0]),
+                key_offsets=torch.from_numpy(inp.key_offsets).to(dev), key_offsets_host=inp.key_offsets,
+                labels=torch.from_numpy(words.view(np.int64)).to(dev),
+                mask_word_offsets=torch.from_numpy(inp.mask_word_offsets).to(dev),
+                mask_word_offsets_host=inp.mask_word_offsets, B=w.B, d=w.d, r=w.r, n_h=w.n_h, d_h=w.d_h,
+                gamma=2.0, alpha=0.25, loss=torch.empty(1, dtype=torch.float32, device=dev),
+                g_dq=torch.empty((w.r, w.d), dtype=torch.float32, device=dev),
+                g_iuq=torch.empty((w.n_h * w.d_h, w.r), dtype=torch.float32, device=dev),
+                g_w=torch.empty((w.n_h, w.d), dtype=torch.float32, device=dev),
+                workspace=torch.empty(lsa.train_workspace_size(w.B, inp.key_offsets, w.r), dtype=torch.uint8,
+                                      device=dev))
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        lsa.train_step(**args, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        lsa.train_step(**args, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    entries = int(inp.key_offsets[-1])
+    tb = train_bytes(w, entries)
+    achieved = tb["total"] / (ms * 1e-3) / 1e9
+    out = {"workload": w.name, "B": w.B, "N_per_seq": int(inp.lengths.max()), "d": w.d, "r": w.r, "n_h": w.n_h,
+           "d_h": w.d_h, "gamma": 2.0, "alpha": 0.25, "us_per_step": ms * 1e3, "entries_per_s": entries / (ms * 1e-3),
+           "loss": float(args["loss"].item()), "algorithmic_bytes": tb, "achieved_GBs": achieved,
+           "peak_GBs": PEAK_HBM_GBS, "frac": achieved / PEAK_HBM_GBS,
+           "what": "lsa_train_step: projections, one fused MFMA pass over the frozen keys (scores, focal loss, "
+                   "dq and dw), the gradient reduction and the three rank-B gradient products"}
+    if cpu_budget:
+        log("[bench] training step: cpu baseline")
+        from oracle import lsa_oracle as O
+        from oracle import train_oracle as TO
+        n_seq = 0
+        t0 = time.perf_counter()
+        H = O.decode_act(inp.h[0], "bf16")
+        Ws = [O.decode_act(m, "bf16") for m in (mw.w_dq, mw.w_iuq, mw.w_w)]
+        done = 0
+        while n_seq < w.B and time.perf_counter() - t0 < cpu_budget:
+            s0, s1 = int(inp.key_offsets[n_seq]), int(inp.key_offsets[n_seq + 1])
+            TO.train_step(H[n_seq:n_seq + 1], *Ws, [O.decode_keys(inp.keys[0][s0:s1], "bf16")], [lab[s0:s1]],
+                          w.n_h, w.d_h)
+            done += s1 - s0
+            n_seq += 1
+        el = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": done / el, "unit": "entries/s", "cores": torch.get_num_threads(),
+                               "kind": "oracle",
+                               "sample": f"{n_seq} of the {w.B} sequences, each as a one-sequence step "
+                                         f"(float64 numpy, decoding included), {el:.1f} s"}
+    del args
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +310,8 @@ def main():
     ap.add_argument("--no-host-fetch", action="store_true", help="skip the cold-pool (pinned host) fetch measurement")
     ap.add_argument("--no-golden", action="store_true", help="skip the golden-label mining measurement")
     ap.add_argument("--golden-only", action="store_true", help="only the golden-label mining measurement")
+    ap.add_argument("--no-train", action="store_true", help="skip the training-step measurement")
+    ap.add_argument("--train-only", action="store_true", help="only the training-step measurement")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -233,6 +326,10 @@ def main():
     if args.golden_only:
         g = golden_measure(args.steps, args.warmup, None if args.no_cpu_baseline else 3.0)
         print(json.dumps({"golden_labels": g}), flush=True)
+        return
+    if args.train_only:
+        t = train_measure(args.steps, args.warmup, None if args.no_cpu_baseline else 3.0)
+        print(json.dumps({"train_step": t}), flush=True)
         return
 
     w = synth.WORKLOADS[args.workload]
@@ -357,6 +454,8 @@ def main():
         del p
         torch.cuda.empty_cache()
         out["golden_labels"] = golden_measure(args.steps, args.warmup, None if args.no_cpu_baseline else 3.0)
+    if not args.no_train:
+        out["train_step"] = train_measure(args.steps, args.warmup, None if args.no_cpu_baseline else 3.0)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline")
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)

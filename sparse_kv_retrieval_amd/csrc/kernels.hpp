@@ -104,6 +104,7 @@ struct GoldenArgs {
 };
 
 // Indexer training step (one layer; n_h = 64, d_h = 128 keys in bf16).
+constexpr int kTrainDcSlices = 64;  // row slices of W^IUQ in dc = dq W^IUQ (partials [slices][B][r])
 struct TrainArgs {
   const void* keys;        // bf16 [rows][128], sequence b at key_off[b]
   const int64_t* key_off;  // [B+1]
@@ -118,7 +119,7 @@ struct TrainArgs {
   float* dq;               // [B][n_h*d_h]
   float* dw;               // [B][n_h]
   float* dc;               // [B][r]
-  float* dcp;              // dc partials [n_h*d_h / 64][B][r]
+  float* dcp;              // dc partials [kTrainDcSlices][B][r], 16-byte aligned
   float* loss;             // [1]
   float* g_dq;             // [r][d]
   float* g_iuq;            // [n_h*d_h][r]

@@ -483,8 +483,8 @@ lsa_status lsa_train_step(const void* h, const void* w_dq, const void* w_iuq, co
   float* dq = f; f += (int64_t)B * n_h * d_h;
   float* dw = f; f += (int64_t)B * n_h;
   float* dc = f; f += (int64_t)B * r;
-  float* part = f; f += nblk * (n_h * d_h + n_h + 1);
-  float* dcp = f;
+  float* dcp = f; f += (int64_t)kTrainDcSlices * B * r;  // dc partials, 16-byte aligned
+  float* part = f;
   ProjArgs p{};
   p.h[0] = h; p.w_dq[0] = w_dq; p.w_iuq[0] = w_iuq; p.w_w[0] = w_w;
   p.c[0] = c; p.q[0] = q; p.w[0] = w;

@@ -18,10 +18,14 @@
 //                      (q split hi + lo), x_s, the loss, g_s = dloss/dx_s, and
 //                      the contraction dq_j += sum_s g_s w_j [S_sj > 0] K_s on
 //                      MFMA (coefficients split hi + lo), dw_j += sum_s g_s
-//                      ReLU(S_sj). Per-block partial sums go to the workspace.
-//   train_reduce_kernel  sums a sequence's block partials: dq, dw, the loss.
-//   train_dc_kernel    dc = dq W^IUQ (bf16 weights), per row block, and
-//   sum kernel         the row blocks' partials added.
+//                      ReLU(S_sj). The focal terms are evaluated once per entry
+//                      in each wave and shared through LDS. Per-block partial
+//                      sums go to the workspace.
+//   train_reduce_kernel  sums a sequence's block partials: dq, dw; one block sums
+//                      the loss over every block.
+//   train_dc_kernel    dc = dq W^IUQ (bf16 weights) in row slices of 128, each
+//                      block one slice x 512 columns, and
+//   train_sum_kernel   the slices' partials added.
 //   train_outer_kernel rank-B products for the three gradients:
 //                      g_iuq = dq^T c, g_dq = dc^T h, g_w = dw^T h.
 #include "kernels.hpp"
@@ -37,42 +41,53 @@ constexpr int TE = 32;             // entries per tile
 constexpr int TPB = 32;            // tiles per scan block
 constexpr int BE = TE * TPB;       // entries per scan block
 constexpr int PW = TNH * TDH + TNH + 1;  // floats per block partial: dq, dw, loss
-constexpr float TLOG2E = 1.4426950408889634f;
+
+// The transposed tile holds, for each key dim d, the tile's 32 entries in "slot" order: entry
+// e = 16 mb + 4 kg + i sits in slot 8 kg + 4 mb + i, so that the gradient MFMA's k-group kg is
+// exactly the entries whose head dots lane (head, kg) holds after the score MFMA. Row d is 64
+// bytes (4 chunks of 8 slots); chunk c is stored at c ^ swz(d), which keeps both the paired
+// writes and the MFMA reads free of LDS bank conflicts beyond two-way.
+__device__ __forceinline__ int tt_swz(int d) { return ((d >> 2) ^ (d >> 4)) & 3; }
+__device__ __forceinline__ int tt_slot(int e) { return 8 * ((e >> 2) & 3) + 4 * (e >> 4) + (e & 3); }
 
 struct TrainScanSmem {
-  uint4 kt[TE * 16];               // tile row-major: chunk c of entry e at e*16 + (c ^ (e & 15))
-  uint32_t ktt[TDH * TE / 2];      // tile transposed: entry e of dim d at byte d*64 + ((e/8) ^ ((d/2)&3))*16 + (e%8)*2
-  float xpart[4][TE];
-  uint32_t coef[4][2][16][TE / 2]; // per wave: hi and lo bf16 of d loss / d S, [head][entry]
+  uint4 kt[2][TE * 16];            // row-major tiles: chunk c of entry e at e*16 + (c ^ (e & 15))
+  uint4 ktt[2][TDH * TE / 8];      // transposed tiles (above)
+  float4 xpart[2][TE];             // per entry: the four waves' partial logits
+  float gs[4][TE];                 // per wave: d loss / d x of the tile's entries
   double lsum[4];
 };
 
-__device__ __forceinline__ float t_log_sigmoid(float x) {  // log(1 / (1 + exp(-x))), stable for both signs
-  return fminf(x, 0.f) - log1pf(__expf(-fabsf(x)));
-}
-
-// Focal loss term and its derivative in the logit x (fp32), label y.
+// Focal loss term and its derivative in the logit x (fp32), label y. With L = log(1 + e^-|x|),
+// log p = min(x, 0) - L and log(1 - p) = min(-x, 0) - L; powers are exponentials of gamma times those.
 __device__ __forceinline__ void focal(float x, bool y, float gamma, float alpha, float& loss, float& grad) {
-  const float lp = t_log_sigmoid(x), lq = t_log_sigmoid(-x);  // log p, log(1 - p)
+  const float L = log1pf(__expf(-fabsf(x)));
+  const float lp = fminf(x, 0.f) - L, lq = fminf(-x, 0.f) - L;  // log p, log(1 - p)
   const float p = __expf(lp), q = __expf(lq);
+  const float pw = __expf(gamma * (y ? lq : lp));                 // (1-p)^gamma or p^gamma
   if (y) {
-    const float qg = gamma == 0.f ? 1.f : powf(q, gamma);
-    loss = -alpha * qg * lp;
-    grad = alpha * qg * (gamma * p * lp - q);
+    loss = -alpha * pw * lp;
+    grad = alpha * pw * (gamma * p * lp - q);
   } else {
-    const float pg = gamma == 0.f ? 1.f : powf(p, gamma);
-    loss = -(1.f - alpha) * pg * lq;
-    grad = (1.f - alpha) * pg * (p - gamma * q * lq);
+    loss = -(1.f - alpha) * pw * lq;
+    grad = (1.f - alpha) * pw * (p - gamma * q * lq);
   }
 }
-
-__device__ __forceinline__ uint32_t pack_bf16x2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
 
 // First scan block of sequence b (blocks are laid out sequence by sequence).
 __device__ __forceinline__ int64_t first_block(const int64_t* __restrict__ off, int b) {
   int64_t s = 0;
   for (int i = 0; i < b; ++i) s += (off[i + 1] - off[i] + BE - 1) / BE;
   return s;
+}
+
+template <int N>
+__device__ __forceinline__ float ror(float v) {  // lane i of each row of 16 gets lane (i + N) % 16
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 | N, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ uint32_t ror_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 | N, 0xF, 0xF, false);
 }
 
 __global__ __launch_bounds__(TT) void train_scan_kernel(const TrainArgs a) {
@@ -112,35 +127,36 @@ __global__ __launch_bounds__(TT) void train_scan_kernel(const TrainArgs a) {
   float dwl = 0.f;
   double ll = 0.0;
 
-  // tile loads: thread t holds chunks 2c, 2c+1 (16 bf16) of entry t / 8
-  const int le = t >> 3, lc = (t & 7) * 2;
+  // tile loads: thread t holds chunks 2g, 2g+1 (key dims 16g .. 16g+15) of entry le
+  const int le = t >> 3, g = t & 7;
+  const int odd = le & 1;
+  const uint32_t psel = odd ? 0x03020706u : 0x05040100u;  // pair (partner, own) high halves / own, partner low
+  // paired transposed writes: dword j of this thread goes to row d = 16 g + 2 (j ^ (g & 1)) + odd
+  const int slot = tt_slot(le & ~1);
   auto load_tile = [&](int tile, u32x4& v0, u32x4& v1) {
-    const uint32_t off = (uint32_t)((e_begin + (int64_t)tile * TE + le) * (TDH * 2) + lc * 16);
+    const uint32_t off = (uint32_t)((e_begin + (int64_t)tile * TE + le) * (TDH * 2) + g * 32);
     v0 = buf_load16(rs, off);
     v1 = buf_load16(rs, off + 16);
   };
-  u32x4 n0, n1;
-  load_tile(0, n0, n1);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const u32x4 c0 = n0, c1 = n1;
-    if (tile + 1 < ntiles) load_tile(tile + 1, n0, n1);
-    const int64_t s0 = e_begin + (int64_t)tile * TE;  // first entry of the tile (a multiple of 32)
-    // ---- stage the tile: row-major (swizzled) and transposed
-    sm.kt[le * 16 + (lc ^ (le & 15))] = __builtin_bit_cast(uint4, c0);
-    sm.kt[le * 16 + ((lc + 1) ^ (le & 15))] = __builtin_bit_cast(uint4, c1);
-    {
-      uint16_t* tt = (uint16_t*)sm.ktt;
+  auto stage = [&](int buf, const u32x4& c0, const u32x4& c1) {
+    sm.kt[buf][le * 16 + ((2 * g) ^ (le & 15))] = __builtin_bit_cast(uint4, c0);
+    sm.kt[buf][le * 16 + ((2 * g + 1) ^ (le & 15))] = __builtin_bit_cast(uint4, c1);
+    char* tt = (char*)sm.ktt[buf];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t w32 = j < 4 ? c0[j] : c1[j - 4];
-#pragma unroll
-        for (int hlf = 0; hlf < 2; ++hlf) {
-          const int d = lc * 8 + 2 * j + hlf;
-          tt[(d * 64 + (((le >> 3) ^ ((d >> 1) & 3)) * 16) + (le & 7) * 2) / 2] = (uint16_t)(w32 >> (16 * hlf));
-        }
-      }
+    for (int j = 0; j < 8; ++j) {
+      const int jj = j ^ (g & 1);
+      const u32x4& c = j < 4 ? c0 : c1;
+      const uint32_t own = (g & 1) ? c[(j ^ 1) & 3] : c[j & 3];
+      // the partner (entry le ^ 1, same dims, same jj) is lane ^ 8, in the same row of 16 lanes
+      const uint32_t part = ror_u<8>(own);
+      const uint32_t v = __builtin_amdgcn_perm(part, own, psel);
+      const int d = 16 * g + 2 * jj + odd;
+      *(uint32_t*)(tt + d * 64 + (((slot >> 3) ^ tt_swz(d)) << 4) + (slot & 7) * 2) = v;
     }
-    __syncthreads();
+  };
+  auto step = [&](int tile, int buf) {
+    const int64_t s0 = e_begin + (int64_t)tile * TE;  // first entry of the tile (a multiple of 32)
+    __syncthreads();  // the tile is in LDS
     // ---- head dots of 32 entries x this wave's 16 heads
     f32x4 S[2];
 #pragma unroll
@@ -149,67 +165,84 @@ __global__ __launch_bounds__(TT) void train_scan_kernel(const TrainArgs a) {
       const int e = 16 * mb + hl;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 A = __builtin_bit_cast(bf16x8, sm.kt[e * 16 + ((4 * ks + kg) ^ (e & 15))]);
+        const bf16x8 A = __builtin_bit_cast(bf16x8, sm.kt[buf][e * 16 + ((4 * ks + kg) ^ (e & 15))]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qh[ks], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, ql[ks], acc, 0, 0, 0);
       }
       S[mb] = acc;  // S[mb][i]: entry 16mb + 4kg + i, head 16wq + hl
     }
-    // partial x over this wave's heads, summed over the 16 lanes of each group
+    // ---- partial logits over this wave's heads: sums over the 16 lanes of a row
+    float xs[8];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int v = 0; v < 8; ++v) {
+      float x = wh * fmaxf(S[v >> 2][v & 3], 0.f);
+      x += ror<8>(x);
+      x += ror<4>(x);
+      x += ror<2>(x);
+      x += ror<1>(x);
+      xs[v] = x;
+    }
+    if (hl < 8) {  // lane hl writes value hl: entry 16 (hl / 4) + 4 kg + hl % 4
+      float x = xs[0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = wh * fmaxf(S[mb][i], 0.f);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
-        if (hl == 0) sm.xpart[wq][16 * mb + 4 * kg + i] = v;
-      }
+      for (int v = 1; v < 8; ++v) x = hl == v ? xs[v] : x;
+      ((float*)&sm.xpart[buf][16 * (hl >> 2) + 4 * kg + (hl & 3)])[wq] = x;
+    }
     __syncthreads();
-    // ---- loss, d loss / d x, the gate gradient and the coefficients d loss / d S
-    const uint32_t lw = (uint32_t)(lab[s0 >> 6] >> (s0 & 63));  // the tile's 32 labels
+    // ---- loss and d loss / d x: entry e = lane % 32, once per wave (lanes 32..63 repeat it)
+    {
+      const int e = lane & 31;
+      const float4 xp = sm.xpart[buf][e];
+      const float x = (xp.x + xp.y) + (xp.z + xp.w);
+      const bool valid = s0 + e < n_b;
+      const uint32_t lw = (uint32_t)(lab[s0 >> 6] >> (s0 & 63));  // the tile's 32 labels
+      float fl, fg;
+      focal(x, (lw >> e) & 1, a.gamma, a.alpha, fl, fg);
+      if (lane < 32) sm.gs[wq][e] = valid ? fg * a.inv_total : 0.f;
+      if (wq == 0 && lane < 32 && valid) ll += (double)fl;
+    }
+    __builtin_amdgcn_wave_barrier();  // gs is written and read by this wave only: LDS keeps the wave's order
+    // ---- the gate gradient and the coefficients d loss / d S = g_s w_j [S_sj > 0], in registers:
+    // lane (head hl, kg) holds entries 16 mb + 4 kg + i, which are slots 8 kg + 4 mb + i
+    float cf[8];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      uint32_t hi2[2] = {0, 0}, lo2[2] = {0, 0};
+      const float4 g4 = *(const float4*)&sm.gs[wq][16 * mb + 4 * kg];
+      const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int e = 16 * mb + 4 * kg + i;
-        const float x = sm.xpart[0][e] + sm.xpart[1][e] + sm.xpart[2][e] + sm.xpart[3][e];
-        const bool valid = s0 + e < n_b;
-        float fl, fg;
-        focal(x, (lw >> e) & 1, a.gamma, a.alpha, fl, fg);
-        const float g = valid ? fg * a.inv_total : 0.f;
-        if (valid && wq == 0 && hl == 0) ll += (double)fl;
-        dwl += g * fmaxf(S[mb][i], 0.f);
-        const float cf = S[mb][i] > 0.f ? g * wh : 0.f;
-        const uint32_t h16 = bf16_rne_bits(cf);
-        const uint32_t l16 = bf16_rne_bits(cf - bf16_bits_to_f32(h16));
-        if (i & 1) {
-          hi2[i >> 1] |= h16 << 16;
-          lo2[i >> 1] |= l16 << 16;
-        } else {
-          hi2[i >> 1] = h16;
-          lo2[i >> 1] = l16;
-        }
+        dwl += gv[i] * fmaxf(S[mb][i], 0.f);
+        cf[4 * mb + i] = S[mb][i] > 0.f ? gv[i] * wh : 0.f;
       }
-      const int wi = (16 * mb + 4 * kg) / 2;
-      *(uint2*)&sm.coef[wq][0][hl][wi] = make_uint2(hi2[0], hi2[1]);
-      *(uint2*)&sm.coef[wq][1][hl][wi] = make_uint2(lo2[0], lo2[1]);
     }
-    // ---- dq for this wave's heads: coef^T (16 heads x 32 entries) x K (32 entries x 128)
-    __builtin_amdgcn_wave_barrier();  // coef is written and read by this wave only: LDS keeps the wave's order
-    {
-      const bf16x8 Ah = __builtin_bit_cast(bf16x8, *(const uint4*)&sm.coef[wq][0][hl][4 * kg]);
-      const bf16x8 Al = __builtin_bit_cast(bf16x8, *(const uint4*)&sm.coef[wq][1][hl][4 * kg]);
+    bf16x8 Ah, Al;
+    split8(cf, Ah, Al);
+    // ---- dq for this wave's heads: coef (16 heads x 32 slots) x K^T (32 slots x 128 dims)
+    const char* tt = (const char*)sm.ktt[buf];
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const int d = 16 * nb + hl;
-        const bf16x8 Bk = __builtin_bit_cast(bf16x8, *(const uint4*)((const char*)sm.ktt + d * 64 + ((kg ^ ((d >> 1) & 3)) * 16)));
-        accb[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, Bk, accb[nb], 0, 0, 0);
-        accb[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, Bk, accb[nb], 0, 0, 0);
-      }
+    for (int nb = 0; nb < 8; ++nb) {
+      const int d = 16 * nb + hl;
+      const bf16x8 Bk = __builtin_bit_cast(bf16x8, *(const uint4*)(tt + d * 64 + ((kg ^ tt_swz(d)) << 4)));
+      accb[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, Bk, accb[nb], 0, 0, 0);
+      accb[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, Bk, accb[nb], 0, 0, 0);
     }
-    __syncthreads();  // the next tile overwrites kt and ktt
+  };
+
+  // two tiles in flight; the LDS tiles alternate, so one barrier before the score MFMAs and one
+  // before the loss are enough (a wave writes buffer x only after every wave has passed the
+  // barriers of the tile that read it last)
+  u32x4 ra0, ra1, rb0, rb1;
+  load_tile(0, ra0, ra1);
+  if (ntiles > 1) load_tile(1, rb0, rb1);
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    stage(0, ra0, ra1);
+    if (tile + 2 < ntiles) load_tile(tile + 2, ra0, ra1);
+    step(tile, 0);
+    if (tile + 1 < ntiles) {
+      stage(1, rb0, rb1);
+      if (tile + 3 < ntiles) load_tile(tile + 3, rb0, rb1);
+      step(tile + 1, 1);
+    }
   }
 
   // ---- this block's partial sums
@@ -228,39 +261,60 @@ __global__ __launch_bounds__(TT) void train_scan_kernel(const TrainArgs a) {
   if (t == 0) part[TNH * TDH + TNH] = (float)(sm.lsum[0] + sm.lsum[1] + sm.lsum[2] + sm.lsum[3]);
 }
 
-// dq[b], dw[b] = sums of sequence b's block partials; the loss from every block.
+// dq[b], dw[b] = sums of sequence b's block partials (blocks x < NRJ, y = b); the loss from every block
+// (block x = NRJ of row y = 0).
+constexpr int NRJ = (PW - 1 + 255) / 256;
 __global__ __launch_bounds__(256) void train_reduce_kernel(const TrainArgs a) {
   const int b = blockIdx.y;
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= PW) return;
-  if (j == PW - 1) {  // the loss: every block of every sequence, once
-    if (b == 0) {
-      double s = 0.0;
-      for (int64_t k = 0; k < a.nblk; ++k) s += (double)a.part[k * PW + PW - 1];
-      a.loss[0] = (float)(s * (double)a.inv_total);
+  if (blockIdx.x == NRJ) {
+    if (b != 0) return;
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int64_t k = threadIdx.x; k < a.nblk; k += 256) s += (double)a.part[k * PW + PW - 1];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+      __syncthreads();
     }
+    if (threadIdx.x == 0) a.loss[0] = (float)(red[0] * (double)a.inv_total);
     return;
   }
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= PW - 1) return;
   const int64_t k0 = first_block(a.key_off, b);
   const int64_t k1 = k0 + (a.key_off[b + 1] - a.key_off[b] + BE - 1) / BE;
-  float s = 0.f;
-  for (int64_t k = k0; k < k1; ++k) s += a.part[k * PW + j];
+  const float* p = a.part + j;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int64_t k = k0;
+  for (; k + 4 <= k1; k += 4) {
+    s0 += p[k * PW];
+    s1 += p[(k + 1) * PW];
+    s2 += p[(k + 2) * PW];
+    s3 += p[(k + 3) * PW];
+  }
+  for (; k < k1; ++k) s0 += p[k * PW];
+  const float s = (s0 + s1) + (s2 + s3);
   if (j < TNH * TDH)
     a.dq[(int64_t)b * TNH * TDH + j] = s;
   else
     a.dw[(int64_t)b * TNH + (j - TNH * TDH)] = s;
 }
 
-// Partial dc over 64 rows o of W^IUQ: dcp[blk][b][k] = sum_o dq[b][o] W[o][k].
-// Thread t owns columns 8t..8t+7 of a 2048-column chunk (blockIdx.y).
-constexpr int DCR = 64;
+// Partial dc = dq W^IUQ over a slice of DCR rows o of the w_iuq buffer: dcp[slice][b][k] =
+// sum_{o in slice} dq[b][o] W[o][k]. Block: one slice x 512 columns; wave w takes rows o = w, w+4, ...
+// of the slice, lane l columns 8l..8l+7; the four waves' sums meet in LDS.
+constexpr int DCR = TNH * TDH / kTrainDcSlices;
+constexpr int DCC = 512;
 __global__ __launch_bounds__(256) void train_dc_kernel(const TrainArgs a) {
-  __shared__ float dqs[DCR][32];
+  __shared__ float dqs[DCR][33];
+  __shared__ float4 red[3][4][DCC / 4];
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
   const int o0 = blockIdx.x * DCR;
-  const int k = blockIdx.y * 2048 + threadIdx.x * 8;
-  for (int i = threadIdx.x; i < DCR * a.B; i += 256) dqs[i % DCR][i / DCR] = a.dq[(int64_t)(i / DCR) * TNH * TDH + o0 + i % DCR];
+  const int k = blockIdx.y * DCC + lane * 8;
+  for (int i = t; i < DCR * a.B; i += 256) dqs[i % DCR][i / DCR] = a.dq[(int64_t)(i / DCR) * TNH * TDH + o0 + i % DCR];
   __syncthreads();
-  if (k >= a.r) return;
+  const bool col_ok = k < a.r;
   const uint16_t* W = (const uint16_t*)a.w_iuq;
   for (int b0 = 0; b0 < a.B; b0 += 8) {
     float acc[8][8];
@@ -268,27 +322,55 @@ __global__ __launch_bounds__(256) void train_dc_kernel(const TrainArgs a) {
     for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[u][c] = 0.f;
-    for (int o = 0; o < DCR; ++o) {
-      const uint4 raw = *(const uint4*)(W + (int64_t)(o0 + o) * a.r + k);
-      float wv[8];
-      const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+    if (col_ok) {
+#pragma unroll 4
+      for (int o = wv; o < DCR; o += 4) {
+        const uint4 raw = *(const uint4*)(W + (int64_t)(o0 + o) * a.r + k);
+        float wv8[8];
+        const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        wv[2 * c] = bf16_bits_to_f32(rw[c] & 0xFFFFu);
-        wv[2 * c + 1] = bf16_bits_to_f32(rw[c] >> 16);
-      }
+        for (int c = 0; c < 4; ++c) {
+          wv8[2 * c] = bf16_bits_to_f32(rw[c] & 0xFFFFu);
+          wv8[2 * c + 1] = bf16_bits_to_f32(rw[c] >> 16);
+        }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float dv = b0 + u < a.B ? dqs[o][b0 + u] : 0.f;
+        for (int u = 0; u < 8; ++u) {
+          const float dv = b0 + u < a.B ? dqs[o][b0 + u] : 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[u][c] = fmaf(dv, wv[c], acc[u][c]);
+          for (int c = 0; c < 8; ++c) acc[u][c] = fmaf(dv, wv8[c], acc[u][c]);
+        }
       }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (b0 + u < a.B)
+    for (int hf = 0; hf < 2; ++hf) {  // sequences b0 + 4hf .. b0 + 4hf + 3
+      if (wv > 0)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) a.dcp[((int64_t)blockIdx.x * a.B + b0 + u) * a.r + k + c] = acc[u][c];
+        for (int u = 0; u < 4; ++u) {
+          red[wv - 1][u][2 * lane] = make_float4(acc[4 * hf + u][0], acc[4 * hf + u][1], acc[4 * hf + u][2],
+                                                 acc[4 * hf + u][3]);
+          red[wv - 1][u][2 * lane + 1] = make_float4(acc[4 * hf + u][4], acc[4 * hf + u][5], acc[4 * hf + u][6],
+                                                     acc[4 * hf + u][7]);
+        }
+      __syncthreads();
+      if (wv == 0 && col_ok)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (b0 + 4 * hf + u >= a.B) break;
+          float o8[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) o8[c] = acc[4 * hf + u][c];
+#pragma unroll
+          for (int w2 = 0; w2 < 3; ++w2) {
+            const float4 x0 = red[w2][u][2 * lane], x1 = red[w2][u][2 * lane + 1];
+            o8[0] += x0.x; o8[1] += x0.y; o8[2] += x0.z; o8[3] += x0.w;
+            o8[4] += x1.x; o8[5] += x1.y; o8[6] += x1.z; o8[7] += x1.w;
+          }
+          float4* dst = (float4*)(a.dcp + ((int64_t)blockIdx.x * a.B + b0 + 4 * hf + u) * a.r + k);
+          dst[0] = make_float4(o8[0], o8[1], o8[2], o8[3]);
+          dst[1] = make_float4(o8[4], o8[5], o8[6], o8[7]);
+        }
+      __syncthreads();  // red is reused
+    }
   }
 }
 
@@ -297,9 +379,16 @@ __global__ __launch_bounds__(256) void train_sum_kernel(const float* __restrict_
                                                       float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  float s = 0.f;
-  for (int p = 0; p < nparts; ++p) s += in[(int64_t)p * n + i];
-  out[i] = s;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int p = 0;
+  for (; p + 4 <= nparts; p += 4) {
+    s0 += in[(int64_t)p * n + i];
+    s1 += in[(int64_t)(p + 1) * n + i];
+    s2 += in[(int64_t)(p + 2) * n + i];
+    s3 += in[(int64_t)(p + 3) * n + i];
+  }
+  for (; p < nparts; ++p) s0 += in[(int64_t)p * n + i];
+  out[i] = (s0 + s1) + (s2 + s3);
 }
 
 // out[i][j] = sum_b u[b][i] v[b][j] (u fp32 with row stride I, v fp32 or bf16 with row stride J).
@@ -307,33 +396,37 @@ __global__ __launch_bounds__(256) void train_sum_kernel(const float* __restrict_
 template <bool VBF16>
 __global__ __launch_bounds__(256) void train_outer_kernel(const float* __restrict__ u, const void* __restrict__ v,
                                                         int B, int64_t I, int64_t J, float* __restrict__ out) {
-  __shared__ float us[32][32];  // [b][i]
+  __shared__ float4 us[32][8];  // [b][i / 4]
   const int64_t i0 = (int64_t)blockIdx.y * 32;
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (int x = threadIdx.x; x < 32 * 32; x += 256) {  // rows b >= B are zero: garbage times zero may be NaN
+  for (int x = threadIdx.x; x < 32 * B; x += 256) {
     const int bb = x / 32, ii = x % 32;
-    us[bb][ii] = bb < B && i0 + ii < I ? u[(int64_t)bb * I + i0 + ii] : 0.f;
+    ((float*)us[bb])[ii] = i0 + ii < I ? u[(int64_t)bb * I + i0 + ii] : 0.f;
   }
   __syncthreads();
   if (j >= J) return;
-  float vb[32];
+  float s[32];
 #pragma unroll
-  for (int bb = 0; bb < 32; ++bb) {
-    float x = 0.f;
-    if (bb < B) {
-      if constexpr (VBF16)
-        x = bf16_bits_to_f32(((const uint16_t*)v)[(int64_t)bb * J + j]);
-      else
-        x = ((const float*)v)[(int64_t)bb * J + j];
+  for (int ii = 0; ii < 32; ++ii) s[ii] = 0.f;
+  for (int bb = 0; bb < B; ++bb) {
+    float x;
+    if constexpr (VBF16)
+      x = bf16_bits_to_f32(((const uint16_t*)v)[(int64_t)bb * J + j]);
+    else
+      x = ((const float*)v)[(int64_t)bb * J + j];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 c = us[bb][q];
+      s[4 * q] = fmaf(c.x, x, s[4 * q]);
+      s[4 * q + 1] = fmaf(c.y, x, s[4 * q + 1]);
+      s[4 * q + 2] = fmaf(c.z, x, s[4 * q + 2]);
+      s[4 * q + 3] = fmaf(c.w, x, s[4 * q + 3]);
     }
-    vb[bb] = x;
   }
-  for (int ii = 0; ii < 32 && i0 + ii < I; ++ii) {
-    float s = 0.f;
+  const int nrow = (int)min((int64_t)32, I - i0);
 #pragma unroll
-    for (int bb = 0; bb < 32; ++bb) s = fmaf(us[bb][ii], vb[bb], s);
-    out[(i0 + ii) * J + j] = s;
-  }
+  for (int ii = 0; ii < 32; ++ii)
+    if (ii < nrow) out[(i0 + ii) * J + j] = s[ii];
 }
 
 }  // namespace
@@ -346,7 +439,7 @@ int64_t train_scan_blocks(const int64_t* key_off_host, int B) {
 
 size_t train_workspace_bytes(int B, int r, int64_t nblk) {
   const int64_t f = (int64_t)B * r * 2 + (int64_t)B * TNH * TDH * 2 + (int64_t)B * TNH * 2 + nblk * PW +
-                    (int64_t)(TNH * TDH / DCR) * B * r;
+                    (int64_t)kTrainDcSlices * B * r;
   return (size_t)f * 4 + 256;
 }
 
@@ -356,10 +449,10 @@ hipError_t launch_train(const TrainArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(train_scan_kernel, dim3((unsigned)a.nblk), dim3(TT), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(train_reduce_kernel, dim3((PW + 255) / 256, a.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(train_reduce_kernel, dim3(NRJ + 1, a.B), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int nrb = TNH * TDH / DCR;
-  hipLaunchKernelGGL(train_dc_kernel, dim3(nrb, (a.r + 2047) / 2048), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(train_dc_kernel, dim3(nrb, (a.r + DCC - 1) / DCC), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t ndc = (int64_t)a.B * a.r;
   hipLaunchKernelGGL(train_sum_kernel, dim3((unsigned)((ndc + 255) / 256)), dim3(256), 0, st, a.dcp, nrb, ndc, a.dc);
