@@ -389,7 +389,8 @@ lsa_status lsa_golden_labels(const float* logits /* dev */, int64_t row_stride, 
  * Precision: the projections as lsa_project with LSA_BF16; in the key scan q
  * and the per-(entry, head) gradient coefficients enter bf16 MFMAs as hi + lo
  * pairs (about 16 significant bits), with fp32 accumulation. The loss is summed
- * in fp64 per block of 1024 entries. A score within rounding of 0 may fall on
+ * in fp64 per scan block (a run of at least 256 entries of one sequence). A
+ * score within rounding of 0 may fall on
  * either side of the ReLU kink.
  * Supported: n_h = 64, d_h = 128, 1 <= B <= 32, d and r positive multiples of
  * 32, N_b < 2^23 entries per sequence. A sequence with no entries adds nothing;

@@ -125,6 +125,7 @@ struct TrainArgs {
   float* g_iuq;            // [n_h*d_h][r]
   float* g_w;              // [n_h][d]
   int64_t nblk;            // scan blocks
+  int32_t tpb;             // 32-entry tiles per scan block
   int32_t B, d, r;
   float gamma, alpha, inv_total;
 };
@@ -140,7 +141,7 @@ hipError_t launch_gather(const GatherArgs& a, int grid, int rows_per_wave, hipSt
 hipError_t launch_project(const ProjArgs& a, int L, bool f32, hipStream_t st);
 hipError_t launch_project_packed(const ProjArgs& a, int L, hipStream_t st);
 size_t golden_workspace_bytes(int64_t rows, int64_t row_stride);
-int64_t train_scan_blocks(const int64_t* key_off_host, int B);
+int64_t train_scan_blocks(const int64_t* key_off_host, int B, int* tiles_per_block);
 size_t train_workspace_bytes(int B, int r, int64_t nblk);
 hipError_t launch_train(const TrainArgs& a, hipStream_t st);
 hipError_t launch_golden(const GoldenArgs& a, hipStream_t st);

@@ -446,7 +446,7 @@ lsa_status lsa_golden_labels(const float* logits, int64_t row_stride, int32_t T,
 
 size_t lsa_train_workspace_size(int32_t B, const int64_t* key_offsets_host, int32_t r) {
   if (B < 1 || !key_offsets_host || r < 1) return 0;
-  return train_workspace_bytes(B, r, train_scan_blocks(key_offsets_host, B));
+  return train_workspace_bytes(B, r, train_scan_blocks(key_offsets_host, B, nullptr));
 }
 
 lsa_status lsa_train_step(const void* h, const void* w_dq, const void* w_iuq, const void* w_w, const void* keys,
@@ -471,7 +471,8 @@ lsa_status lsa_train_step(const void* h, const void* w_dq, const void* w_iuq, co
       return fail(LSA_ERR_UNSUPPORTED, "sequence %d is longer than the training scan addresses (2^23 entries)", b);
   if (!aligned16(h) || !aligned16(w_dq) || !aligned16(w_iuq) || !aligned16(keys) || !aligned16(workspace))
     return fail(LSA_ERR_INVALID_ARG, "h, w_dq, w_iuq, keys and workspace must be 16-byte aligned");
-  const int64_t nblk = train_scan_blocks(key_offsets_host, B);
+  int tpb = 0;
+  const int64_t nblk = train_scan_blocks(key_offsets_host, B, &tpb);
   const size_t need = train_workspace_bytes(B, r, nblk);
   if (!workspace || workspace_bytes < need)
     return fail(LSA_ERR_WORKSPACE, "lsa_train_step needs a workspace of %zu bytes (got %zu)", need, workspace_bytes);
@@ -494,7 +495,7 @@ lsa_status lsa_train_step(const void* h, const void* w_dq, const void* w_iuq, co
   TrainArgs a{};
   a.keys = keys; a.key_off = key_offsets; a.labels = labels; a.mwo = mask_word_offsets; a.h = h; a.w_iuq = w_iuq;
   a.c = c; a.q = q; a.w = w; a.part = part; a.dq = dq; a.dw = dw; a.dc = dc; a.dcp = dcp; a.loss = loss_out;
-  a.g_dq = g_dq; a.g_iuq = g_iuq; a.g_w = g_w; a.nblk = nblk; a.B = B; a.d = d; a.r = r;
+  a.g_dq = g_dq; a.g_iuq = g_iuq; a.g_w = g_w; a.nblk = nblk; a.tpb = tpb; a.B = B; a.d = d; a.r = r;
   a.gamma = gamma; a.alpha = alpha; a.inv_total = total > 0 ? (float)(1.0 / (double)total) : 0.f;
   e = launch_train(a, stream);
   return e == hipSuccess ? LSA_OK : hip_fail("lsa_train_step launch", e);

@@ -12,7 +12,9 @@
 //
 // Kernels, after the projection kernels give c, q and w:
 //   train_scan_kernel  one pass over the keys (4 waves per block, 16 heads per
-//                      wave, tiles of 32 entries staged in LDS twice: row-major
+//                      wave; the grid is sized to one round of resident blocks,
+//                      each a run of tiles of one sequence; tiles of 32 entries
+//                      staged in LDS twice: row-major
 //                      for the score MFMAs and transposed for the gradient
 //                      MFMAs). Per tile: the head dots S = K q^T on bf16 MFMA
 //                      (q split hi + lo), x_s, the loss, g_s = dloss/dx_s, and
@@ -28,6 +30,8 @@
 //   train_sum_kernel   the slices' partials added.
 //   train_outer_kernel rank-B products for the three gradients:
 //                      g_iuq = dq^T c, g_dq = dc^T h, g_w = dw^T h.
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace lsa {
@@ -38,8 +42,8 @@ constexpr int TT = 256;            // scan block: 4 waves
 constexpr int TNH = 64;            // heads (16 per wave)
 constexpr int TDH = 128;           // head dim = key dim
 constexpr int TE = 32;             // entries per tile
-constexpr int TPB = 32;            // tiles per scan block
-constexpr int BE = TE * TPB;       // entries per scan block
+constexpr int SCAN_BLOCKS = 768;   // target grid: three resident blocks on each of 256 CUs, one round
+constexpr int MIN_TPB = 8;         // at least this many tiles per scan block
 constexpr int PW = TNH * TDH + TNH + 1;  // floats per block partial: dq, dw, loss
 
 // The transposed tile holds, for each key dim d, the tile's 32 entries in "slot" order: entry
@@ -60,8 +64,15 @@ struct TrainScanSmem {
 
 // Focal loss term and its derivative in the logit x (fp32), label y. With L = log(1 + e^-|x|),
 // log p = min(x, 0) - L and log(1 - p) = min(-x, 0) - L; powers are exponentials of gamma times those.
+// log(1 + e) for e in [0, 1]: log(u) e / (u - 1) with u = 1 + e rounded, which cancels the rounding of u
+// (Goldberg's form), so a hardware logarithm keeps a few-ulp relative error even for tiny e.
+__device__ __forceinline__ float t_log1p(float e) {
+  const float u = 1.f + e;
+  return u == 1.f ? e : __logf(u) * __fdividef(e, u - 1.f);
+}
+
 __device__ __forceinline__ void focal(float x, bool y, float gamma, float alpha, float& loss, float& grad) {
-  const float L = log1pf(__expf(-fabsf(x)));
+  const float L = t_log1p(__expf(-fabsf(x)));
   const float lp = fminf(x, 0.f) - L, lq = fminf(-x, 0.f) - L;  // log p, log(1 - p)
   const float p = __expf(lp), q = __expf(lq);
   const float pw = __expf(gamma * (y ? lq : lp));                 // (1-p)^gamma or p^gamma
@@ -74,10 +85,31 @@ __device__ __forceinline__ void focal(float x, bool y, float gamma, float alpha,
   }
 }
 
+// bf16 hi + lo split of 8 fp32 values (x ~= hi + lo, about 16 significant bits), two at a time with
+// the hardware's round-to-nearest-even conversion; hi + lo pack as MFMA operands.
+typedef __bf16 tbf16x2 __attribute__((ext_vector_type(2)));
+typedef float tf32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((tf32x2){a, b}, tbf16x2));
+}
+__device__ __forceinline__ void tsplit8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t hp = cvt_bf16x2(x[2 * i], x[2 * i + 1]);
+    const float r0 = x[2 * i] - __uint_as_float(hp << 16);
+    const float r1 = x[2 * i + 1] - __uint_as_float(hp & 0xFFFF0000u);
+    h[i] = hp;
+    l[i] = cvt_bf16x2(r0, r1);
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
 // First scan block of sequence b (blocks are laid out sequence by sequence).
-__device__ __forceinline__ int64_t first_block(const int64_t* __restrict__ off, int b) {
+__device__ __forceinline__ int64_t first_block(const int64_t* __restrict__ off, int b, int64_t be) {
   int64_t s = 0;
-  for (int i = 0; i < b; ++i) s += (off[i + 1] - off[i] + BE - 1) / BE;
+  for (int i = 0; i < b; ++i) s += (off[i + 1] - off[i] + be - 1) / be;
   return s;
 }
 
@@ -95,17 +127,18 @@ __global__ __launch_bounds__(TT) void train_scan_kernel(const TrainArgs a) {
   const int t = threadIdx.x, lane = t & 63;
   const int wq = __builtin_amdgcn_readfirstlane(t >> 6);
   const int hl = lane & 15, kg = lane >> 4;
-  // this block's sequence and entry range
+  // this block's sequence and entry range (blocks of a.tpb tiles, sequence by sequence)
+  const int64_t be = (int64_t)a.tpb * TE;
   int b = 0;
   int64_t blk0 = 0;
   for (;; ++b) {
-    const int64_t nb = (a.key_off[b + 1] - a.key_off[b] + BE - 1) / BE;
+    const int64_t nb = (a.key_off[b + 1] - a.key_off[b] + be - 1) / be;
     if ((int64_t)blockIdx.x < blk0 + nb) break;
     blk0 += nb;
   }
   const int64_t n_b = a.key_off[b + 1] - a.key_off[b];
-  const int64_t e_begin = ((int64_t)blockIdx.x - blk0) * BE;
-  const int ntiles = (int)min((int64_t)TPB, (n_b - e_begin + TE - 1) / TE);
+  const int64_t e_begin = ((int64_t)blockIdx.x - blk0) * be;
+  const int ntiles = (int)min((int64_t)a.tpb, (n_b - e_begin + TE - 1) / TE);
   const auto rs = buf_rsrc((const char*)a.keys + a.key_off[b] * (TDH * 2), (uint32_t)(n_b * (TDH * 2)));
   const uint64_t* lab = a.labels + a.mwo[b];
 
@@ -216,7 +249,7 @@ __global__ __launch_bounds__(TT) void train_scan_kernel(const TrainArgs a) {
       }
     }
     bf16x8 Ah, Al;
-    split8(cf, Ah, Al);
+    tsplit8(cf, Ah, Al);
     // ---- dq for this wave's heads: coef (16 heads x 32 slots) x K^T (32 slots x 128 dims)
     const char* tt = (const char*)sm.ktt[buf];
 #pragma unroll
@@ -282,8 +315,9 @@ __global__ __launch_bounds__(256) void train_reduce_kernel(const TrainArgs a) {
   }
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= PW - 1) return;
-  const int64_t k0 = first_block(a.key_off, b);
-  const int64_t k1 = k0 + (a.key_off[b + 1] - a.key_off[b] + BE - 1) / BE;
+  const int64_t be = (int64_t)a.tpb * TE;
+  const int64_t k0 = first_block(a.key_off, b, be);
+  const int64_t k1 = k0 + (a.key_off[b + 1] - a.key_off[b] + be - 1) / be;
   const float* p = a.part + j;
   float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
   int64_t k = k0;
@@ -431,9 +465,13 @@ __global__ __launch_bounds__(256) void train_outer_kernel(const float* __restric
 
 }  // namespace
 
-int64_t train_scan_blocks(const int64_t* key_off_host, int B) {
+int64_t train_scan_blocks(const int64_t* key_off_host, int B, int* tpb_out) {
+  int64_t tiles = 0;
+  for (int b = 0; b < B; ++b) tiles += (key_off_host[b + 1] - key_off_host[b] + TE - 1) / TE;
+  const int64_t tpb = std::max<int64_t>(MIN_TPB, (tiles + SCAN_BLOCKS - 1) / SCAN_BLOCKS);
   int64_t s = 0;
-  for (int b = 0; b < B; ++b) s += (key_off_host[b + 1] - key_off_host[b] + BE - 1) / BE;
+  for (int b = 0; b < B; ++b) s += (key_off_host[b + 1] - key_off_host[b] + tpb * TE - 1) / (tpb * TE);
+  if (tpb_out) *tpb_out = (int)tpb;
   return s;
 }
 
