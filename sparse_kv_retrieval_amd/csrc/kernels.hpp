@@ -115,7 +115,7 @@ struct TrainArgs {
   const float* c;          // [B][r]
   const float* q;          // [B][n_h][d_h]
   const float* w;          // [B][n_h]
-  float* part;             // scan block partials
+  float* part;             // scan block partials: dq' (the gate factored out) and the loss
   float* dq;               // [B][n_h*d_h]
   float* dw;               // [B][n_h]
   float* dc;               // [B][r]
@@ -143,6 +143,11 @@ hipError_t launch_project_packed(const ProjArgs& a, int L, hipStream_t st);
 size_t golden_workspace_bytes(int64_t rows, int64_t row_stride);
 int64_t train_scan_blocks(const int64_t* key_off_host, int B, int* tiles_per_block);
 size_t train_workspace_bytes(int B, int r, int64_t nblk);
+struct TrainWs {
+  float *c, *q, *w, *dq, *dw, *dc, *dcp, *part;
+  size_t bytes;
+};
+TrainWs train_carve(void* ws, int B, int r, int64_t nblk);
 hipError_t launch_train(const TrainArgs& a, hipStream_t st);
 hipError_t launch_golden(const GoldenArgs& a, hipStream_t st);
 hipError_t launch_pack_weights(const void* w, int rows, int K, void* out, hipStream_t st);

@@ -477,24 +477,17 @@ lsa_status lsa_train_step(const void* h, const void* w_dq, const void* w_iuq, co
   if (!workspace || workspace_bytes < need)
     return fail(LSA_ERR_WORKSPACE, "lsa_train_step needs a workspace of %zu bytes (got %zu)", need, workspace_bytes);
   const int64_t total = key_offsets_host[B] - key_offsets_host[0];
-  float* f = (float*)workspace;
-  float* c = f; f += (int64_t)B * r;
-  float* q = f; f += (int64_t)B * n_h * d_h;
-  float* w = f; f += (int64_t)B * n_h;
-  float* dq = f; f += (int64_t)B * n_h * d_h;
-  float* dw = f; f += (int64_t)B * n_h;
-  float* dc = f; f += (int64_t)B * r;
-  float* dcp = f; f += (int64_t)kTrainDcSlices * B * r;  // dc partials, 16-byte aligned
-  float* part = f;
+  const TrainWs ws = train_carve(workspace, B, r, nblk);
   ProjArgs p{};
   p.h[0] = h; p.w_dq[0] = w_dq; p.w_iuq[0] = w_iuq; p.w_w[0] = w_w;
-  p.c[0] = c; p.q[0] = q; p.w[0] = w;
+  p.c[0] = ws.c; p.q[0] = ws.q; p.w[0] = ws.w;
   p.B = B; p.d = d; p.r = r; p.n_h = n_h; p.d_h = d_h;
   hipError_t e = launch_project(p, 1, false, stream);
   if (e != hipSuccess) return hip_fail("lsa_train_step projection", e);
   TrainArgs a{};
   a.keys = keys; a.key_off = key_offsets; a.labels = labels; a.mwo = mask_word_offsets; a.h = h; a.w_iuq = w_iuq;
-  a.c = c; a.q = q; a.w = w; a.part = part; a.dq = dq; a.dw = dw; a.dc = dc; a.dcp = dcp; a.loss = loss_out;
+  a.c = ws.c; a.q = ws.q; a.w = ws.w; a.part = ws.part; a.dq = ws.dq; a.dw = ws.dw; a.dc = ws.dc; a.dcp = ws.dcp;
+  a.loss = loss_out;
   a.g_dq = g_dq; a.g_iuq = g_iuq; a.g_w = g_w; a.nblk = nblk; a.tpb = tpb; a.B = B; a.d = d; a.r = r;
   a.gamma = gamma; a.alpha = alpha; a.inv_total = total > 0 ? (float)(1.0 / (double)total) : 0.f;
   e = launch_train(a, stream);

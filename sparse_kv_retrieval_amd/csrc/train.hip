@@ -18,13 +18,16 @@
 //                      for the score MFMAs and transposed for the gradient
 //                      MFMAs). Per tile: the head dots S = K q^T on bf16 MFMA
 //                      (q split hi + lo), x_s, the loss, g_s = dloss/dx_s, and
-//                      the contraction dq_j += sum_s g_s w_j [S_sj > 0] K_s on
-//                      MFMA (coefficients split hi + lo), dw_j += sum_s g_s
-//                      ReLU(S_sj). The focal terms are evaluated once per entry
-//                      in each wave and shared through LDS. Per-block partial
-//                      sums go to the workspace.
-//   train_reduce_kernel  sums a sequence's block partials: dq, dw; one block sums
-//                      the loss over every block.
+//                      the contraction dq_j = sum_s g_s w_j [S_sj > 0] K_s on
+//                      MFMA. The gate is factored out: the MFMA sums
+//                      dq'_j = sum_s g_s [S_sj > 0] K_s with g_s split hi + lo
+//                      once per entry, and dq_j = w_j dq'_j, dw_j = sum_s g_s
+//                      ReLU(S_sj) = q_j . dq'_j follow after the scan. The focal
+//                      terms are evaluated once per entry in each wave and
+//                      shared through LDS. Per-block partial sums go to the
+//                      workspace.
+//   train_reduce_kernel  sums a sequence's block partials into dq' and forms dq
+//                      and dw; one block sums the loss over every block.
 //   train_dc_kernel    dc = dq W^IUQ (bf16 weights) in row slices of 128, each
 //                      block one slice x 512 columns, and
 //   train_sum_kernel   the slices' partials added.
@@ -44,7 +47,7 @@ constexpr int TDH = 128;           // head dim = key dim
 constexpr int TE = 32;             // entries per tile
 constexpr int SCAN_BLOCKS = 768;   // target grid: three resident blocks on each of 256 CUs, one round
 constexpr int MIN_TPB = 8;         // at least this many tiles per scan block
-constexpr int PW = TNH * TDH + TNH + 1;  // floats per block partial: dq, dw, loss
+constexpr int PW = TNH * TDH + 1;  // floats per block partial: dq' (below) and the loss
 
 // The transposed tile holds, for each key dim d, the tile's 32 entries in "slot" order: entry
 // e = 16 mb + 4 kg + i sits in slot 8 kg + 4 mb + i, so that the gradient MFMA's k-group kg is
@@ -58,7 +61,7 @@ struct TrainScanSmem {
   uint4 kt[2][TE * 16];            // row-major tiles: chunk c of entry e at e*16 + (c ^ (e & 15))
   uint4 ktt[2][TDH * TE / 8];      // transposed tiles (above)
   float4 xpart[2][TE];             // per entry: the four waves' partial logits
-  float gs[4][TE];                 // per wave: d loss / d x of the tile's entries
+  uint16_t gh[4][TE], gl[4][TE];   // per wave: d loss / d x of the tile's entries as bf16 hi + lo
   double lsum[4];
 };
 
@@ -85,27 +88,12 @@ __device__ __forceinline__ void focal(float x, bool y, float gamma, float alpha,
   }
 }
 
-// bf16 hi + lo split of 8 fp32 values (x ~= hi + lo, about 16 significant bits), two at a time with
-// the hardware's round-to-nearest-even conversion; hi + lo pack as MFMA operands.
+// Two fp32 values to packed bf16 with the hardware's round-to-nearest-even conversion.
 typedef __bf16 tbf16x2 __attribute__((ext_vector_type(2)));
 typedef float tf32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((tf32x2){a, b}, tbf16x2));
 }
-__device__ __forceinline__ void tsplit8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
-  u32x4 h, l;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t hp = cvt_bf16x2(x[2 * i], x[2 * i + 1]);
-    const float r0 = x[2 * i] - __uint_as_float(hp << 16);
-    const float r1 = x[2 * i + 1] - __uint_as_float(hp & 0xFFFF0000u);
-    h[i] = hp;
-    l[i] = cvt_bf16x2(r0, r1);
-  }
-  hi = __builtin_bit_cast(bf16x8, h);
-  lo = __builtin_bit_cast(bf16x8, l);
-}
-
 // First scan block of sequence b (blocks are laid out sequence by sequence).
 __device__ __forceinline__ int64_t first_block(const int64_t* __restrict__ off, int b, int64_t be) {
   int64_t s = 0;
@@ -157,7 +145,6 @@ __global__ __launch_bounds__(TT) void train_scan_kernel(const TrainArgs a) {
   f32x4 accb[8];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) accb[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float dwl = 0.f;
   double ll = 0.0;
 
   // tile loads: thread t holds chunks 2g, 2g+1 (key dims 16g .. 16g+15) of entry le
@@ -222,7 +209,7 @@ __global__ __launch_bounds__(TT) void train_scan_kernel(const TrainArgs a) {
       ((float*)&sm.xpart[buf][16 * (hl >> 2) + 4 * kg + (hl & 3)])[wq] = x;
     }
     __syncthreads();
-    // ---- loss and d loss / d x: entry e = lane % 32, once per wave (lanes 32..63 repeat it)
+    // ---- loss and g_s = d loss / d x_s: entry e = lane % 32, once per wave (lanes 32..63 repeat it)
     {
       const int e = lane & 31;
       const float4 xp = sm.xpart[buf][e];
@@ -231,26 +218,32 @@ __global__ __launch_bounds__(TT) void train_scan_kernel(const TrainArgs a) {
       const uint32_t lw = (uint32_t)(lab[s0 >> 6] >> (s0 & 63));  // the tile's 32 labels
       float fl, fg;
       focal(x, (lw >> e) & 1, a.gamma, a.alpha, fl, fg);
-      if (lane < 32) sm.gs[wq][e] = valid ? fg * a.inv_total : 0.f;
+      const float gv = valid ? fg * a.inv_total : 0.f;
+      const uint32_t gp = cvt_bf16x2(gv, gv - __uint_as_float(cvt_bf16x2(gv, 0.f) << 16));
+      if (lane < 32) {
+        sm.gh[wq][e] = (uint16_t)gp;
+        sm.gl[wq][e] = (uint16_t)(gp >> 16);
+      }
       if (wq == 0 && lane < 32 && valid) ll += (double)fl;
     }
-    __builtin_amdgcn_wave_barrier();  // gs is written and read by this wave only: LDS keeps the wave's order
-    // ---- the gate gradient and the coefficients d loss / d S = g_s w_j [S_sj > 0], in registers:
-    // lane (head hl, kg) holds entries 16 mb + 4 kg + i, which are slots 8 kg + 4 mb + i
-    float cf[8];
+    __builtin_amdgcn_wave_barrier();  // gh, gl are written and read by this wave only: LDS keeps the wave's order
+    // ---- the coefficients g_s [S_sj > 0] as bf16 hi + lo, in registers: lane (head hl, kg) holds
+    // entries 16 mb + 4 kg + i, which are slots 8 kg + 4 mb + i. The gate w_j is applied after the
+    // scan (dq_j = w_j dq'_j), and dw_j = sum_s g_s ReLU(S_sj) = q_j . dq'_j follows from the same sum.
+    u32x4 ch, cl;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const float4 g4 = *(const float4*)&sm.gs[wq][16 * mb + 4 * kg];
-      const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
+      const uint2 h2 = *(const uint2*)&sm.gh[wq][16 * mb + 4 * kg];
+      const uint2 l2 = *(const uint2*)&sm.gl[wq][16 * mb + 4 * kg];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dwl += gv[i] * fmaxf(S[mb][i], 0.f);
-        cf[4 * mb + i] = S[mb][i] > 0.f ? gv[i] * wh : 0.f;
+      for (int p = 0; p < 2; ++p) {
+        const uint32_t m = (S[mb][2 * p] > 0.f ? 0x0000FFFFu : 0u) | (S[mb][2 * p + 1] > 0.f ? 0xFFFF0000u : 0u);
+        ch[2 * mb + p] = (p ? h2.y : h2.x) & m;
+        cl[2 * mb + p] = (p ? l2.y : l2.x) & m;
       }
     }
-    bf16x8 Ah, Al;
-    tsplit8(cf, Ah, Al);
-    // ---- dq for this wave's heads: coef (16 heads x 32 slots) x K^T (32 slots x 128 dims)
+    const bf16x8 Ah = __builtin_bit_cast(bf16x8, ch), Al = __builtin_bit_cast(bf16x8, cl);
+    // ---- dq' for this wave's heads: coefficients (16 heads x 32 slots) x K^T (32 slots x 128 dims)
     const char* tt = (const char*)sm.ktt[buf];
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
@@ -284,37 +277,35 @@ __global__ __launch_bounds__(TT) void train_scan_kernel(const TrainArgs a) {
   for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) part[(16 * wq + 4 * kg + i) * TDH + 16 * nb + hl] = accb[nb][i];
-  dwl += __shfl_xor(dwl, 16);
-  dwl += __shfl_xor(dwl, 32);
-  if (kg == 0) part[TNH * TDH + 16 * wq + hl] = dwl;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) ll += __shfl_xor(ll, o);
   if (lane == 0) sm.lsum[wq] = ll;
   __syncthreads();
-  if (t == 0) part[TNH * TDH + TNH] = (float)(sm.lsum[0] + sm.lsum[1] + sm.lsum[2] + sm.lsum[3]);
+  if (t == 0) part[TNH * TDH] = (float)(sm.lsum[0] + sm.lsum[1] + sm.lsum[2] + sm.lsum[3]);
 }
 
-// dq[b], dw[b] = sums of sequence b's block partials (blocks x < NRJ, y = b); the loss from every block
-// (block x = NRJ of row y = 0).
-constexpr int NRJ = (PW - 1 + 255) / 256;
+// dq'[b] = the sum of sequence b's block partials (blocks x < NRJ, y = b; block x covers heads 2x and
+// 2x + 1); then dq_j = w_j dq'_j and dw_j = q_j . dq'_j. Block x = NRJ of row y = 0 sums the loss.
+constexpr int NRJ = TNH * TDH / 256;
 __global__ __launch_bounds__(256) void train_reduce_kernel(const TrainArgs a) {
   const int b = blockIdx.y;
+  const int t = threadIdx.x;
   if (blockIdx.x == NRJ) {
     if (b != 0) return;
     __shared__ double red[256];
     double s = 0.0;
-    for (int64_t k = threadIdx.x; k < a.nblk; k += 256) s += (double)a.part[k * PW + PW - 1];
-    red[threadIdx.x] = s;
+    for (int64_t k = t; k < a.nblk; k += 256) s += (double)a.part[k * PW + PW - 1];
+    red[t] = s;
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
-      if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+      if (t < o) red[t] += red[t + o];
       __syncthreads();
     }
-    if (threadIdx.x == 0) a.loss[0] = (float)(red[0] * (double)a.inv_total);
+    if (t == 0) a.loss[0] = (float)(red[0] * (double)a.inv_total);
     return;
   }
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= PW - 1) return;
+  __shared__ float wsum[4];
+  const int j = blockIdx.x * 256 + t;  // head j / TDH, dim j % TDH
   const int64_t be = (int64_t)a.tpb * TE;
   const int64_t k0 = first_block(a.key_off, b, be);
   const int64_t k1 = k0 + (a.key_off[b + 1] - a.key_off[b] + be - 1) / be;
@@ -329,10 +320,14 @@ __global__ __launch_bounds__(256) void train_reduce_kernel(const TrainArgs a) {
   }
   for (; k < k1; ++k) s0 += p[k * PW];
   const float s = (s0 + s1) + (s2 + s3);
-  if (j < TNH * TDH)
-    a.dq[(int64_t)b * TNH * TDH + j] = s;
-  else
-    a.dw[(int64_t)b * TNH + (j - TNH * TDH)] = s;
+  const int head = j / TDH;
+  a.dq[(int64_t)b * TNH * TDH + j] = a.w[(int64_t)b * TNH + head] * s;
+  float v = a.q[(int64_t)b * TNH * TDH + j] * s;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((t & 63) == 0) wsum[t >> 6] = v;
+  __syncthreads();
+  if (t == 0 || t == 128) a.dw[(int64_t)b * TNH + head] = wsum[t >> 6] + wsum[(t >> 6) + 1];
 }
 
 // Partial dc = dq W^IUQ over a slice of DCR rows o of the w_iuq buffer: dcp[slice][b][k] =
@@ -475,11 +470,28 @@ int64_t train_scan_blocks(const int64_t* key_off_host, int B, int* tpb_out) {
   return s;
 }
 
-size_t train_workspace_bytes(int B, int r, int64_t nblk) {
-  const int64_t f = (int64_t)B * r * 2 + (int64_t)B * TNH * TDH * 2 + (int64_t)B * TNH * 2 + nblk * PW +
-                    (int64_t)kTrainDcSlices * B * r;
-  return (size_t)f * 4 + 256;
+// Workspace: c [B][r], q [B][n_h d_h], w [B][n_h], dq, dw, dc, the dc partials, then the scan
+// blocks' partials (PW floats each, odd, so they come last).
+TrainWs train_carve(void* ws, int B, int r, int64_t nblk) {
+  TrainWs o{};
+  size_t off = 0;  // in floats
+  auto take = [&](float*& p, int64_t n) {
+    p = ws ? (float*)ws + off : nullptr;
+    off += (size_t)n;
+  };
+  take(o.c, (int64_t)B * r);
+  take(o.q, (int64_t)B * TNH * TDH);
+  take(o.w, (int64_t)B * TNH);
+  take(o.dq, (int64_t)B * TNH * TDH);
+  take(o.dw, (int64_t)B * TNH);
+  take(o.dc, (int64_t)B * r);
+  take(o.dcp, (int64_t)kTrainDcSlices * B * r);
+  take(o.part, nblk * PW);
+  o.bytes = off * sizeof(float);
+  return o;
 }
+
+size_t train_workspace_bytes(int B, int r, int64_t nblk) { return train_carve(nullptr, B, r, nblk).bytes + 256; }
 
 hipError_t launch_train(const TrainArgs& a, hipStream_t st) {
   hipError_t e;
