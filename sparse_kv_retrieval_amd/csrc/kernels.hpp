@@ -140,6 +140,9 @@ hipError_t launch_union_compact(const UnionArgs& a, int B, int64_t max_words, hi
 hipError_t launch_gather(const GatherArgs& a, int grid, int rows_per_wave, hipStream_t st);
 hipError_t launch_project(const ProjArgs& a, int L, bool f32, hipStream_t st);
 hipError_t launch_project_packed(const ProjArgs& a, int L, hipStream_t st);
+// One bf16 layer with each reduction split over two blocks that add into zeroed outputs (a grid of
+// twice the blocks, for a single layer on a large device).
+hipError_t launch_project_split2(const ProjArgs& a, hipStream_t st);
 size_t golden_workspace_bytes(int64_t rows, int64_t row_stride);
 int64_t train_scan_blocks(const int64_t* key_off_host, int B, int* tiles_per_block);
 size_t train_workspace_bytes(int B, int r, int64_t nblk);
@@ -148,6 +151,7 @@ struct TrainWs {
   size_t bytes;
 };
 TrainWs train_carve(void* ws, int B, int r, int64_t nblk);
+hipError_t launch_train_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_train(const TrainArgs& a, hipStream_t st);
 hipError_t launch_golden(const GoldenArgs& a, hipStream_t st);
 hipError_t launch_pack_weights(const void* w, int rows, int K, void* out, hipStream_t st);

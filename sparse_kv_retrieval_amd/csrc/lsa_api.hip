@@ -482,7 +482,9 @@ lsa_status lsa_train_step(const void* h, const void* w_dq, const void* w_iuq, co
   p.h[0] = h; p.w_dq[0] = w_dq; p.w_iuq[0] = w_iuq; p.w_w[0] = w_w;
   p.c[0] = ws.c; p.q[0] = ws.q; p.w[0] = ws.w;
   p.B = B; p.d = d; p.r = r; p.n_h = n_h; p.d_h = d_h;
-  hipError_t e = launch_project(p, 1, false, stream);
+  // c, q, w are contiguous in the workspace; the split projection adds into them
+  hipError_t e = launch_train_zero(ws.c, (int64_t)B * (r + n_h * d_h + n_h), stream);
+  if (e == hipSuccess) e = launch_project_split2(p, stream);
   if (e != hipSuccess) return hip_fail("lsa_train_step projection", e);
   TrainArgs a{};
   a.keys = keys; a.key_off = key_offsets; a.labels = labels; a.mwo = mask_word_offsets; a.h = h; a.w_iuq = w_iuq;

@@ -66,8 +66,13 @@ __global__ __launch_bounds__(PJ_THREADS) void project_kernel(const ProjArgs a) {
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) acc[mb][cb] = f32x4{0, 0, 0, 0};
 
+  // the reduction is split over the block's four waves and over gridDim.z blocks; with more than one
+  // block per output (gridDim.z == 2), both add into outputs the caller has zeroed, and 0 + a + b
+  // rounds the same in either order
+  const int ks = gridDim.z;
   const int chunks = K / KCH;
-  const int c0 = wv * chunks / 4, c1 = (wv + 1) * chunks / 4;
+  const int part = (int)blockIdx.z * 4 + wv;
+  const int c0 = part * chunks / (4 * ks), c1 = (part + 1) * chunks / (4 * ks);
 
   // one reduction chunk: k0 is this lane's first k
   auto b_frag_bf16 = [&](int cb, int k0) -> bf16x8 {
@@ -190,13 +195,12 @@ __global__ __launch_bounds__(PJ_THREADS) void project_kernel(const ProjArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int row = rb + 16 * mb + 4 * kg + i;
         if (row >= rows) continue;
-        if (UP) {
-          a.q[l][(int64_t)seq * rows + row] = s[i];
-        } else if (row < a.r) {
-          a.c[l][(int64_t)seq * a.r + row] = s[i];
-        } else {
-          a.w[l][(int64_t)seq * a.n_h + (row - a.r)] = s[i];
-        }
+        float* dst = UP ? &a.q[l][(int64_t)seq * rows + row]
+                        : row < a.r ? &a.c[l][(int64_t)seq * a.r + row] : &a.w[l][(int64_t)seq * a.n_h + (row - a.r)];
+        if (ks > 1)
+          unsafeAtomicAdd(dst, s[i]);
+        else
+          *dst = s[i];
       }
     }
   }
@@ -355,9 +359,9 @@ __global__ __launch_bounds__(64 * W) void project_packed_kernel(const ProjArgs a
 }
 
 template <bool F32, bool UP, int MB, int NBMAX>
-static hipError_t launch_stage(const ProjArgs& a, int L, int nb, hipStream_t st) {
+static hipError_t launch_stage(const ProjArgs& a, int L, int nb, hipStream_t st, int ks = 1) {
   const int rows = UP ? a.n_h * a.d_h : a.r + a.n_h;
-  const dim3 grid((rows + 16 * MB - 1) / (16 * MB), L);
+  const dim3 grid((rows + 16 * MB - 1) / (16 * MB), L, ks);
 #define LSA_PJ(NB_) hipLaunchKernelGGL((project_kernel<F32, UP, NB_, MB>), grid, dim3(PJ_THREADS), 0, st, a)
   if (nb <= 1) LSA_PJ(1);
   else if (nb <= 2) LSA_PJ(2);
@@ -433,6 +437,14 @@ hipError_t launch_project(const ProjArgs& a, int L, bool f32, hipStream_t st) {
   // the up stage reuses each hi/lo split of c across 4 row groups while the B operand stays small
   if (nb_up <= 4) return launch_stage<false, true, 4, 4>(a, L, nb_up, st);
   return launch_stage<false, true, 1, 16>(a, L, nb_up, st);
+}
+
+hipError_t launch_project_split2(const ProjArgs& a, hipStream_t st) {
+  hipError_t e;
+  const int nb_down = (a.B + 15) / 16, nb_up = (a.B + 7) / 8;
+  if ((e = launch_stage<false, false, 1, 16>(a, 1, nb_down, st, 2)) != hipSuccess) return e;
+  if (nb_up <= 4) return launch_stage<false, true, 4, 4>(a, 1, nb_up, st, 2);
+  return launch_stage<false, true, 1, 16>(a, 1, nb_up, st, 2);
 }
 
 }  // namespace lsa

@@ -26,12 +26,13 @@
 //                      terms are evaluated once per entry in each wave and
 //                      shared through LDS. Per-block partial sums go to the
 //                      workspace.
-//   train_reduce_kernel  sums a sequence's block partials into dq' and forms dq
-//                      and dw; one block sums the loss over every block.
+//   train_reduce_kernel  sums a sequence's block partials into dq' (one block per
+//                      head and sequence) and forms dq and dw; one block sums
+//                      the loss over every block.
 //   train_dc_kernel    dc = dq W^IUQ (bf16 weights) in row slices of 128, each
-//                      block one slice x 512 columns, and
+//                      block one slice x 256 columns, and
 //   train_sum_kernel   the slices' partials added.
-//   train_outer_kernel rank-B products for the three gradients:
+//   train_outer_kernel rank-B products for the three gradients (16-byte stores):
 //                      g_iuq = dq^T c, g_dq = dc^T h, g_w = dw^T h.
 #include <algorithm>
 
@@ -284,122 +285,114 @@ __global__ __launch_bounds__(TT) void train_scan_kernel(const TrainArgs a) {
   if (t == 0) part[TNH * TDH] = (float)(sm.lsum[0] + sm.lsum[1] + sm.lsum[2] + sm.lsum[3]);
 }
 
-// dq'[b] = the sum of sequence b's block partials (blocks x < NRJ, y = b; block x covers heads 2x and
-// 2x + 1); then dq_j = w_j dq'_j and dw_j = q_j . dq'_j. Block x = NRJ of row y = 0 sums the loss.
-constexpr int NRJ = TNH * TDH / 256;
-__global__ __launch_bounds__(256) void train_reduce_kernel(const TrainArgs a) {
+// dq'[b] = the sum of sequence b's block partials; then dq_j = w_j dq'_j and dw_j = q_j . dq'_j.
+// Block (head x, sequence y): 512 threads, thread t sums dim t % 128 of the head over a quarter of the
+// blocks (t / 128), the quarters meet in LDS. Block x = TNH of row y = 0 sums the loss.
+__global__ __launch_bounds__(512) void train_reduce_kernel(const TrainArgs a) {
   const int b = blockIdx.y;
   const int t = threadIdx.x;
-  if (blockIdx.x == NRJ) {
+  if (blockIdx.x == TNH) {
     if (b != 0) return;
-    __shared__ double red[256];
+    __shared__ double red[512];
     double s = 0.0;
-    for (int64_t k = t; k < a.nblk; k += 256) s += (double)a.part[k * PW + PW - 1];
+    for (int64_t k = t; k < a.nblk; k += 512) s += (double)a.part[k * PW + PW - 1];
     red[t] = s;
     __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
+    for (int o = 256; o > 0; o >>= 1) {
       if (t < o) red[t] += red[t + o];
       __syncthreads();
     }
     if (t == 0) a.loss[0] = (float)(red[0] * (double)a.inv_total);
     return;
   }
-  __shared__ float wsum[4];
-  const int j = blockIdx.x * 256 + t;  // head j / TDH, dim j % TDH
+  __shared__ float qs[4][TDH];
+  __shared__ float wsum[2];
+  const int head = blockIdx.x, dim = t & (TDH - 1), quarter = t >> 7;
+  const int j = head * TDH + dim;
   const int64_t be = (int64_t)a.tpb * TE;
   const int64_t k0 = first_block(a.key_off, b, be);
-  const int64_t k1 = k0 + (a.key_off[b + 1] - a.key_off[b] + be - 1) / be;
+  const int64_t nk = (a.key_off[b + 1] - a.key_off[b] + be - 1) / be;
   const float* p = a.part + j;
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-  int64_t k = k0;
-  for (; k + 4 <= k1; k += 4) {
-    s0 += p[k * PW];
-    s1 += p[(k + 1) * PW];
-    s2 += p[(k + 2) * PW];
-    s3 += p[(k + 3) * PW];
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int64_t k = k0 + quarter * nk / 4;
+  const int64_t k1 = k0 + (quarter + 1) * nk / 4;
+  for (; k + 8 <= k1; k += 8)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += p[(k + u) * PW];
+  for (; k < k1; ++k) acc[0] += p[k * PW];
+  qs[quarter][dim] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  __syncthreads();
+  float v = 0.f;
+  if (t < TDH) {
+    const float s = (qs[0][dim] + qs[1][dim]) + (qs[2][dim] + qs[3][dim]);
+    a.dq[(int64_t)b * TNH * TDH + j] = a.w[(int64_t)b * TNH + head] * s;
+    v = a.q[(int64_t)b * TNH * TDH + j] * s;
   }
-  for (; k < k1; ++k) s0 += p[k * PW];
-  const float s = (s0 + s1) + (s2 + s3);
-  const int head = j / TDH;
-  a.dq[(int64_t)b * TNH * TDH + j] = a.w[(int64_t)b * TNH + head] * s;
-  float v = a.q[(int64_t)b * TNH * TDH + j] * s;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  if ((t & 63) == 0) wsum[t >> 6] = v;
+  if (t < TDH && (t & 63) == 0) wsum[t >> 6] = v;
   __syncthreads();
-  if (t == 0 || t == 128) a.dw[(int64_t)b * TNH + head] = wsum[t >> 6] + wsum[(t >> 6) + 1];
+  if (t == 0) a.dw[(int64_t)b * TNH + head] = wsum[0] + wsum[1];
 }
 
 // Partial dc = dq W^IUQ over a slice of DCR rows o of the w_iuq buffer: dcp[slice][b][k] =
-// sum_{o in slice} dq[b][o] W[o][k]. Block: one slice x 512 columns; wave w takes rows o = w, w+4, ...
-// of the slice, lane l columns 8l..8l+7; the four waves' sums meet in LDS.
+// sum_{o in slice} dq[b][o] W[o][k]. Block: one slice x DCC columns; wave w takes rows o = w, w+4, ...
+// of the slice, lane l columns 4l..4l+3, with 16 rows' loads in flight; the four waves' sums meet in LDS.
 constexpr int DCR = TNH * TDH / kTrainDcSlices;
-constexpr int DCC = 512;
+constexpr int DCC = 256;
 __global__ __launch_bounds__(256) void train_dc_kernel(const TrainArgs a) {
   __shared__ float dqs[DCR][33];
-  __shared__ float4 red[3][4][DCC / 4];
+  __shared__ float4 red[3][8][DCC / 4];
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
   const int o0 = blockIdx.x * DCR;
-  const int k = blockIdx.y * DCC + lane * 8;
+  const int k = blockIdx.y * DCC + lane * 4;
   for (int i = t; i < DCR * a.B; i += 256) dqs[i % DCR][i / DCR] = a.dq[(int64_t)(i / DCR) * TNH * TDH + o0 + i % DCR];
   __syncthreads();
   const bool col_ok = k < a.r;
   const uint16_t* W = (const uint16_t*)a.w_iuq;
   for (int b0 = 0; b0 < a.B; b0 += 8) {
-    float acc[8][8];
+    float acc[8][4];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[u][c] = 0.f;
+      for (int c = 0; c < 4; ++c) acc[u][c] = 0.f;
     if (col_ok) {
-#pragma unroll 4
-      for (int o = wv; o < DCR; o += 4) {
-        const uint4 raw = *(const uint4*)(W + (int64_t)(o0 + o) * a.r + k);
-        float wv8[8];
-        const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+      constexpr int RU = 16;  // rows of this wave with loads in flight together
+      for (int o1 = wv; o1 < DCR; o1 += 4 * RU) {
+        uint2 raw[RU];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          wv8[2 * c] = bf16_bits_to_f32(rw[c] & 0xFFFFu);
-          wv8[2 * c + 1] = bf16_bits_to_f32(rw[c] >> 16);
-        }
+        for (int u = 0; u < RU; ++u) raw[u] = *(const uint2*)(W + (int64_t)(o0 + o1 + 4 * u) * a.r + k);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float dv = b0 + u < a.B ? dqs[o][b0 + u] : 0.f;
+        for (int ru = 0; ru < RU; ++ru) {
+          const int o = o1 + 4 * ru;
+          const float w4[4] = {bf16_bits_to_f32(raw[ru].x & 0xFFFFu), bf16_bits_to_f32(raw[ru].x >> 16),
+                               bf16_bits_to_f32(raw[ru].y & 0xFFFFu), bf16_bits_to_f32(raw[ru].y >> 16)};
 #pragma unroll
-          for (int c = 0; c < 8; ++c) acc[u][c] = fmaf(dv, wv8[c], acc[u][c]);
+          for (int u = 0; u < 8; ++u) {
+            const float dv = b0 + u < a.B ? dqs[o][b0 + u] : 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[u][c] = fmaf(dv, w4[c], acc[u][c]);
+          }
         }
       }
     }
+    if (wv > 0)
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {  // sequences b0 + 4hf .. b0 + 4hf + 3
-      if (wv > 0)
+      for (int u = 0; u < 8; ++u) red[wv - 1][u][lane] = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+    __syncthreads();
+    if (wv == 0 && col_ok)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          red[wv - 1][u][2 * lane] = make_float4(acc[4 * hf + u][0], acc[4 * hf + u][1], acc[4 * hf + u][2],
-                                                 acc[4 * hf + u][3]);
-          red[wv - 1][u][2 * lane + 1] = make_float4(acc[4 * hf + u][4], acc[4 * hf + u][5], acc[4 * hf + u][6],
-                                                     acc[4 * hf + u][7]);
+      for (int u = 0; u < 8; ++u) {
+        if (b0 + u >= a.B) break;
+        float4 o4 = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+#pragma unroll
+        for (int w2 = 0; w2 < 3; ++w2) {
+          const float4 x = red[w2][u][lane];
+          o4.x += x.x; o4.y += x.y; o4.z += x.z; o4.w += x.w;
         }
-      __syncthreads();
-      if (wv == 0 && col_ok)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (b0 + 4 * hf + u >= a.B) break;
-          float o8[8];
-#pragma unroll
-          for (int c = 0; c < 8; ++c) o8[c] = acc[4 * hf + u][c];
-#pragma unroll
-          for (int w2 = 0; w2 < 3; ++w2) {
-            const float4 x0 = red[w2][u][2 * lane], x1 = red[w2][u][2 * lane + 1];
-            o8[0] += x0.x; o8[1] += x0.y; o8[2] += x0.z; o8[3] += x0.w;
-            o8[4] += x1.x; o8[5] += x1.y; o8[6] += x1.z; o8[7] += x1.w;
-          }
-          float4* dst = (float4*)(a.dcp + ((int64_t)blockIdx.x * a.B + b0 + 4 * hf + u) * a.r + k);
-          dst[0] = make_float4(o8[0], o8[1], o8[2], o8[3]);
-          dst[1] = make_float4(o8[4], o8[5], o8[6], o8[7]);
-        }
-      __syncthreads();  // red is reused
-    }
+        *(float4*)(a.dcp + ((int64_t)blockIdx.x * a.B + b0 + u) * a.r + k) = o4;
+      }
+    __syncthreads();  // red is reused by the next group of 8 sequences
   }
 }
 
@@ -408,57 +401,79 @@ __global__ __launch_bounds__(256) void train_sum_kernel(const float* __restrict_
                                                       float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  float acc[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) acc[u] = 0.f;
   int p = 0;
-  for (; p + 4 <= nparts; p += 4) {
-    s0 += in[(int64_t)p * n + i];
-    s1 += in[(int64_t)(p + 1) * n + i];
-    s2 += in[(int64_t)(p + 2) * n + i];
-    s3 += in[(int64_t)(p + 3) * n + i];
-  }
-  for (; p < nparts; ++p) s0 += in[(int64_t)p * n + i];
-  out[i] = (s0 + s1) + (s2 + s3);
+  for (; p + 16 <= nparts; p += 16)
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc[u] += in[(int64_t)(p + u) * n + i];
+  for (; p < nparts; ++p) acc[0] += in[(int64_t)p * n + i];
+#pragma unroll
+  for (int w = 8; w > 0; w >>= 1)
+#pragma unroll
+    for (int u = 0; u < w; ++u) acc[u] += acc[u + w];
+  out[i] = acc[0];
 }
 
-// out[i][j] = sum_b u[b][i] v[b][j] (u fp32 with row stride I, v fp32 or bf16 with row stride J).
-// Block: 32 rows i x 256 columns j, one column per thread.
+// out[i][j] = sum_b u[b][i] v[b][j] (u fp32 with row stride I, v fp32 or bf16 with row stride J, J a
+// multiple of 4). Block: 16 rows i x 1024 columns j, four consecutive columns per thread (16-byte stores).
 template <bool VBF16>
 __global__ __launch_bounds__(256) void train_outer_kernel(const float* __restrict__ u, const void* __restrict__ v,
                                                         int B, int64_t I, int64_t J, float* __restrict__ out) {
-  __shared__ float4 us[32][8];  // [b][i / 4]
-  const int64_t i0 = (int64_t)blockIdx.y * 32;
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (int x = threadIdx.x; x < 32 * B; x += 256) {
-    const int bb = x / 32, ii = x % 32;
+  __shared__ float4 us[32][4];  // [b][i / 4]
+  const int64_t i0 = (int64_t)blockIdx.y * 16;
+  const int64_t j = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  for (int x = threadIdx.x; x < 16 * B; x += 256) {
+    const int bb = x / 16, ii = x % 16;
     ((float*)us[bb])[ii] = i0 + ii < I ? u[(int64_t)bb * I + i0 + ii] : 0.f;
   }
   __syncthreads();
   if (j >= J) return;
-  float s[32];
+  float s[16][4];
 #pragma unroll
-  for (int ii = 0; ii < 32; ++ii) s[ii] = 0.f;
+  for (int ii = 0; ii < 16; ++ii)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s[ii][c] = 0.f;
   for (int bb = 0; bb < B; ++bb) {
-    float x;
-    if constexpr (VBF16)
-      x = bf16_bits_to_f32(((const uint16_t*)v)[(int64_t)bb * J + j]);
-    else
-      x = ((const float*)v)[(int64_t)bb * J + j];
+    float x[4];
+    if constexpr (VBF16) {
+      const uint2 raw = *(const uint2*)((const uint16_t*)v + (int64_t)bb * J + j);
+      x[0] = bf16_bits_to_f32(raw.x & 0xFFFFu);
+      x[1] = bf16_bits_to_f32(raw.x >> 16);
+      x[2] = bf16_bits_to_f32(raw.y & 0xFFFFu);
+      x[3] = bf16_bits_to_f32(raw.y >> 16);
+    } else {
+      const float4 f = *(const float4*)((const float*)v + (int64_t)bb * J + j);
+      x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+    }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float4 c = us[bb][q];
-      s[4 * q] = fmaf(c.x, x, s[4 * q]);
-      s[4 * q + 1] = fmaf(c.y, x, s[4 * q + 1]);
-      s[4 * q + 2] = fmaf(c.z, x, s[4 * q + 2]);
-      s[4 * q + 3] = fmaf(c.w, x, s[4 * q + 3]);
+    for (int q = 0; q < 4; ++q) {
+      const float4 cu = us[bb][q];
+      const float cv[4] = {cu.x, cu.y, cu.z, cu.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) s[4 * q + r][c] = fmaf(cv[r], x[c], s[4 * q + r][c]);
     }
   }
-  const int nrow = (int)min((int64_t)32, I - i0);
+  const int nrow = (int)min((int64_t)16, I - i0);
 #pragma unroll
-  for (int ii = 0; ii < 32; ++ii)
-    if (ii < nrow) out[(i0 + ii) * J + j] = s[ii];
+  for (int ii = 0; ii < 16; ++ii)
+    if (ii < nrow) *(float4*)(out + (i0 + ii) * J + j) = make_float4(s[ii][0], s[ii][1], s[ii][2], s[ii][3]);
+}
+
+__global__ __launch_bounds__(256) void train_zero_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
 }
 
 }  // namespace
+
+hipError_t launch_train_zero(float* p, int64_t n, hipStream_t st) {
+  if (n > 0) hipLaunchKernelGGL(train_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
 
 int64_t train_scan_blocks(const int64_t* key_off_host, int B, int* tpb_out) {
   int64_t tiles = 0;
@@ -499,7 +514,7 @@ hipError_t launch_train(const TrainArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(train_scan_kernel, dim3((unsigned)a.nblk), dim3(TT), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(train_reduce_kernel, dim3(NRJ + 1, a.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(train_reduce_kernel, dim3(TNH + 1, a.B), dim3(512), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int nrb = TNH * TDH / DCR;
   hipLaunchKernelGGL(train_dc_kernel, dim3(nrb, (a.r + DCC - 1) / DCC), dim3(256), 0, st, a);
@@ -508,13 +523,13 @@ hipError_t launch_train(const TrainArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(train_sum_kernel, dim3((unsigned)((ndc + 255) / 256)), dim3(256), 0, st, a.dcp, nrb, ndc, a.dc);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // g_iuq = dq^T c, g_dq = dc^T h, g_w = dw^T h
-  hipLaunchKernelGGL(train_outer_kernel<false>, dim3((a.r + 255) / 256, (TNH * TDH + 31) / 32), dim3(256), 0, st,
+  hipLaunchKernelGGL(train_outer_kernel<false>, dim3((a.r + 1023) / 1024, (TNH * TDH + 15) / 16), dim3(256), 0, st,
                      a.dq, (const void*)a.c, a.B, (int64_t)TNH * TDH, (int64_t)a.r, a.g_iuq);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(train_outer_kernel<true>, dim3((a.d + 255) / 256, (a.r + 31) / 32), dim3(256), 0, st, a.dc,
+  hipLaunchKernelGGL(train_outer_kernel<true>, dim3((a.d + 1023) / 1024, (a.r + 15) / 16), dim3(256), 0, st, a.dc,
                      a.h, a.B, (int64_t)a.r, (int64_t)a.d, a.g_dq);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(train_outer_kernel<true>, dim3((a.d + 255) / 256, (TNH + 31) / 32), dim3(256), 0, st, a.dw,
+  hipLaunchKernelGGL(train_outer_kernel<true>, dim3((a.d + 1023) / 1024, (TNH + 15) / 16), dim3(256), 0, st, a.dw,
                      a.h, a.B, (int64_t)TNH, (int64_t)a.d, a.g_w);
   return hipGetLastError();
 }
