@@ -214,6 +214,31 @@ def golden_measure(steps: int, warmup: int, cpu_budget: float | None) -> dict:
 
 
 TRAIN_WORKLOAD = "train_b8"
+TRAIN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "train_scan_traffic_{}.txt")
+TRAIN_SOURCES = ["csrc/train.hip", "csrc/common.hpp", "csrc/kernels.hpp", "build.py"]
+
+
+def train_source_hash() -> str:
+    h = hashlib.sha256()
+    for s in TRAIN_SOURCES:
+        with open(os.path.join(ROOT, "sparse_kv_retrieval_amd", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_kv_traffic(path: str, workload: str, source_hash: str):
+    """traffic_bytes_per_launch from a committed summary, or None when it is missing or stale."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(("#", " ", "|", "`")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_hash") == source_hash and kv.get("workload") == workload:
+        return int(kv["traffic_bytes_per_launch"])
+    return None
 
 
 def train_bytes(w, entries: int) -> dict:
@@ -268,12 +293,15 @@ def train_measure(steps: int, warmup: int, cpu_budget: float | None) -> dict:
     entries = int(inp.key_offsets[-1])
     tb = train_bytes(w, entries)
     achieved = tb["total"] / (ms * 1e-3) / 1e9
+    scan_bytes = entries * w.d_h * 2 + entries // 8  # the scan kernel: keys and labels once
     out = {"workload": w.name, "B": w.B, "N_per_seq": int(inp.lengths.max()), "d": w.d, "r": w.r, "n_h": w.n_h,
            "d_h": w.d_h, "gamma": 2.0, "alpha": 0.25, "us_per_step": ms * 1e3, "entries_per_s": entries / (ms * 1e-3),
            "loss": float(args["loss"].item()), "algorithmic_bytes": tb, "achieved_GBs": achieved,
            "peak_GBs": PEAK_HBM_GBS, "frac": achieved / PEAK_HBM_GBS,
            "what": "lsa_train_step: projections, one fused MFMA pass over the frozen keys (scores, focal loss, "
-                   "dq and dw), the gradient reduction and the three rank-B gradient products"}
+                   "dq and dw), the gradient reduction and the three rank-B gradient products",
+           "scan_kernel": {"algorithmic_bytes": scan_bytes,
+                           "traffic": read_kv_traffic(TRAIN_TRAFFIC_FILE.format(w.name), w.name, train_source_hash())}}
     if cpu_budget:
         log("[bench] training step: cpu baseline")
         from oracle import lsa_oracle as O
