@@ -72,7 +72,7 @@ struct TrainScanSmem {
 // (Goldberg's form), so a hardware logarithm keeps a few-ulp relative error even for tiny e.
 __device__ __forceinline__ float t_log1p(float e) {
   const float u = 1.f + e;
-  return u == 1.f ? e : __logf(u) * __fdividef(e, u - 1.f);
+  return u == 1.f ? e : __logf(u) * (e * __builtin_amdgcn_rcpf(u - 1.f));
 }
 
 __device__ __forceinline__ void focal(float x, bool y, float gamma, float alpha, float& loss, float& grad) {
@@ -104,11 +104,11 @@ __device__ __forceinline__ int64_t first_block(const int64_t* __restrict__ off, 
 
 template <int N>
 __device__ __forceinline__ float ror(float v) {  // lane i of each row of 16 gets lane (i + N) % 16
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 | N, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 | N, 0xF, 0xF, false));
 }
 template <int N>
 __device__ __forceinline__ uint32_t ror_u(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 | N, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x120 | N, 0xF, 0xF, false);
 }
 
 __global__ __launch_bounds__(TT) void train_scan_kernel(const TrainArgs a) {
@@ -151,6 +151,7 @@ __global__ __launch_bounds__(TT) void train_scan_kernel(const TrainArgs a) {
   // tile loads: thread t holds chunks 2g, 2g+1 (key dims 16g .. 16g+15) of entry le
   const int le = t >> 3, g = t & 7;
   const int odd = le & 1;
+  const bool godd = (g & 1) != 0;
   const uint32_t psel = odd ? 0x03020706u : 0x05040100u;  // pair (partner, own) high halves / own, partner low
   // paired transposed writes: dword j of this thread goes to row d = 16 g + 2 (j ^ (g & 1)) + odd
   const int slot = tt_slot(le & ~1);
@@ -166,8 +167,9 @@ __global__ __launch_bounds__(TT) void train_scan_kernel(const TrainArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int jj = j ^ (g & 1);
-      const u32x4& c = j < 4 ? c0 : c1;
-      const uint32_t own = (g & 1) ? c[(j ^ 1) & 3] : c[j & 3];
+      const u32x4 c = j < 4 ? c0 : c1;
+      const uint32_t a0 = c[j & 3], a1 = c[(j ^ 1) & 3];  // compile-time lanes of the vector
+      const uint32_t own = godd ? a1 : a0;
       // the partner (entry le ^ 1, same dims, same jj) is lane ^ 8, in the same row of 16 lanes
       const uint32_t part = ror_u<8>(own);
       const uint32_t v = __builtin_amdgcn_perm(part, own, psel);
