@@ -104,7 +104,7 @@ __device__ __forceinline__ int64_t first_block(const int64_t* __restrict__ off, 
 
 template <int N>
 __device__ __forceinline__ float ror(float v) {  // lane i of each row of 16 gets lane (i + N) % 16
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 | N, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 | N, 0xF, 0xF, true));
 }
 template <int N>
 __device__ __forceinline__ uint32_t ror_u(uint32_t v) {
