@@ -420,11 +420,22 @@ __global__ __launch_bounds__(256) void train_sum_kernel(const float* __restrict_
 
 // out[i][j] = sum_b u[b][i] v[b][j] (u fp32 with row stride I, v fp32 or bf16 with row stride J, J a
 // multiple of 4). Block: 16 rows i x 1024 columns j, four consecutive columns per thread (16-byte stores).
+// One launch can hold two such products: blocks y < ny0 form the first (u, I, out), the others the
+// second (u1, I1, out1), over the same v.
 template <bool VBF16>
 __global__ __launch_bounds__(256) void train_outer_kernel(const float* __restrict__ u, const void* __restrict__ v,
-                                                        int B, int64_t I, int64_t J, float* __restrict__ out) {
+                                                        int B, int64_t I, int64_t J, float* __restrict__ out,
+                                                        int ny0, const float* __restrict__ u1, int64_t I1,
+                                                        float* __restrict__ out1) {
   __shared__ float4 us[32][4];  // [b][i / 4]
-  const int64_t i0 = (int64_t)blockIdx.y * 16;
+  int by = blockIdx.y;
+  if (by >= ny0) {
+    by -= ny0;
+    u = u1;
+    I = I1;
+    out = out1;
+  }
+  const int64_t i0 = (int64_t)by * 16;
   const int64_t j = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   for (int x = threadIdx.x; x < 16 * B; x += 256) {
     const int bb = x / 16, ii = x % 16;
@@ -524,15 +535,15 @@ hipError_t launch_train(const TrainArgs& a, hipStream_t st) {
   const int64_t ndc = (int64_t)a.B * a.r;
   hipLaunchKernelGGL(train_sum_kernel, dim3((unsigned)((ndc + 255) / 256)), dim3(256), 0, st, a.dcp, nrb, ndc, a.dc);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // g_iuq = dq^T c, g_dq = dc^T h, g_w = dw^T h
-  hipLaunchKernelGGL(train_outer_kernel<false>, dim3((a.r + 1023) / 1024, (TNH * TDH + 15) / 16), dim3(256), 0, st,
-                     a.dq, (const void*)a.c, a.B, (int64_t)TNH * TDH, (int64_t)a.r, a.g_iuq);
+  // g_iuq = dq^T c; then g_dq = dc^T h and g_w = dw^T h in one launch
+  const int ny_iuq = (TNH * TDH + 15) / 16;
+  hipLaunchKernelGGL(train_outer_kernel<false>, dim3((a.r + 1023) / 1024, ny_iuq), dim3(256), 0, st, a.dq,
+                     (const void*)a.c, a.B, (int64_t)TNH * TDH, (int64_t)a.r, a.g_iuq, ny_iuq, (const float*)nullptr,
+                     (int64_t)0, (float*)nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(train_outer_kernel<true>, dim3((a.d + 1023) / 1024, (a.r + 15) / 16), dim3(256), 0, st, a.dc,
-                     a.h, a.B, (int64_t)a.r, (int64_t)a.d, a.g_dq);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(train_outer_kernel<true>, dim3((a.d + 1023) / 1024, (TNH + 15) / 16), dim3(256), 0, st, a.dw,
-                     a.h, a.B, (int64_t)TNH, (int64_t)a.d, a.g_w);
+  const int ny_dq = (a.r + 15) / 16, ny_w = (TNH + 15) / 16;
+  hipLaunchKernelGGL(train_outer_kernel<true>, dim3((a.d + 1023) / 1024, ny_dq + ny_w), dim3(256), 0, st, a.dc, a.h,
+                     a.B, (int64_t)a.r, (int64_t)a.d, a.g_dq, ny_dq, (const float*)a.dw, (int64_t)TNH, a.g_w);
   return hipGetLastError();
 }
 
