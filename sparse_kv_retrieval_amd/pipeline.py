@@ -214,7 +214,9 @@ class Pipeline:
         overlapping both top-k stages, and joins at the end. (Forking it after the top-k
         scoring instead, so that it overlaps only the selection, is 14 us slower per step on
         the three-layer workload: the scoring and the gather share HBM better than they
-        queue.)"""
+        queue. Projecting the native indexer on the second stream while the memory indexer
+        scores is 6 us slower per step: score_select is the HBM-bound stage and loses more
+        than the projection gains.)"""
         main = torch.cuda.current_stream() if stream is None else stream
         self.project(main)
         self.score_select(main)
