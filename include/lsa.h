@@ -97,7 +97,8 @@ typedef enum {
  * w_out [B, n_h]. c_out is both an output and the input of the second stage,
  * so it must not alias the other buffers.
  * Supported shapes: 1 <= B <= 128; d and r multiples of 32 (of 4 for LSA_F32);
- * n_h * d_h a multiple of 16; 1 <= n_h <= LSA_MAX_HEADS.
+ * n_h * d_h a multiple of 16; 1 <= n_h <= LSA_MAX_HEADS. h, w_dq, w_iuq, w_w
+ * and c_out must be 16-byte aligned.
  * Accumulation is fp32. With LSA_BF16, c enters the second product as
  * bf16 hi + lo, which keeps about 16 significant bits.
  * ---------------------------------------------------------------------- */
@@ -376,13 +377,14 @@ lsa_status lsa_golden_labels(const float* logits /* dev */, int64_t row_stride, 
  *                   [n_h*d_h, r], [n_h, d]); 16-byte aligned.
  *   keys            dev bf16 [rows][d_h], the selection path's layout.
  *   key_offsets, mask_word_offsets (dev and host copies): as lsa_score_select.
- *   labels          dev u64 bit masks in the lsa_score_select mask layout: bit
+ *   labels          dev u64 bit masks (8-byte aligned) in the lsa_score_select mask layout: bit
  *                   s % 64 of word mask_word_offsets[b] + s / 64 is 1 when entry s
  *                   of sequence b is golden. Bits past N_b are ignored.
  *   gamma >= 0, alpha in [0, 1]  the focal constants (2 and 0.25 usually).
  *   loss_out        dev fp32 [1].
  *   g_dq            dev fp32 [r, d];  g_iuq  dev fp32 [n_h*d_h, r];
- *   g_w             dev fp32 [n_h, d]. Every element is written.
+ *   g_w             dev fp32 [n_h, d]. Every element is written. The gradients
+ *                   must be 16-byte aligned.
  *   workspace       dev scratch of lsa_train_workspace_size(B,
  *                   key_offsets_host, r) bytes, 16-byte aligned; it needs no
  *                   clearing. Calls that share one workspace must be ordered.

@@ -187,8 +187,8 @@ lsa_status lsa_project(const lsa_proj_layer* layers, int32_t L, int32_t B, int32
     const lsa_proj_layer& p = layers[l];
     if (!p.h || !p.w_dq || !p.w_iuq || !p.w_w || !p.c_out || !p.q_out || !p.w_out)
       return fail(LSA_ERR_INVALID_ARG, "layer %d: a pointer is NULL", l);
-    if (!aligned16(p.h) || !aligned16(p.w_dq) || !aligned16(p.w_iuq) || !aligned16(p.c_out))
-      return fail(LSA_ERR_INVALID_ARG, "layer %d: h, w_dq, w_iuq and c_out must be 16-byte aligned", l);
+    if (!aligned16(p.h) || !aligned16(p.w_dq) || !aligned16(p.w_iuq) || !aligned16(p.w_w) || !aligned16(p.c_out))
+      return fail(LSA_ERR_INVALID_ARG, "layer %d: h, w_dq, w_iuq, w_w and c_out must be 16-byte aligned", l);
     if ((const void*)p.c_out == (const void*)p.q_out || (const void*)p.c_out == (const void*)p.w_out)
       return fail(LSA_ERR_INVALID_ARG, "layer %d: c_out aliases another output", l);
     a.h[l] = p.h; a.w_dq[l] = p.w_dq; a.w_iuq[l] = p.w_iuq; a.w_w[l] = p.w_w;
@@ -469,8 +469,13 @@ lsa_status lsa_train_step(const void* h, const void* w_dq, const void* w_iuq, co
   for (int32_t b = 0; b < B; ++b)
     if ((key_offsets_host[b + 1] - key_offsets_host[b]) * 256 >= ((int64_t)1 << 31))
       return fail(LSA_ERR_UNSUPPORTED, "sequence %d is longer than the training scan addresses (2^23 entries)", b);
-  if (!aligned16(h) || !aligned16(w_dq) || !aligned16(w_iuq) || !aligned16(keys) || !aligned16(workspace))
-    return fail(LSA_ERR_INVALID_ARG, "h, w_dq, w_iuq, keys and workspace must be 16-byte aligned");
+  if (!aligned16(h) || !aligned16(w_dq) || !aligned16(w_iuq) || !aligned16(w_w) || !aligned16(keys) ||
+      !aligned16(workspace))
+    return fail(LSA_ERR_INVALID_ARG, "h, w_dq, w_iuq, w_w, keys and workspace must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(labels) & 7u) || (reinterpret_cast<uintptr_t>(g_dq) & 15u) ||
+      (reinterpret_cast<uintptr_t>(g_iuq) & 15u) || (reinterpret_cast<uintptr_t>(g_w) & 15u) ||
+      (reinterpret_cast<uintptr_t>(loss_out) & 3u))
+    return fail(LSA_ERR_INVALID_ARG, "labels must be 8-byte aligned, the gradients 16-byte and loss_out 4-byte aligned");
   int tpb = 0;
   const int64_t nblk = train_scan_blocks(key_offsets_host, B, &tpb);
   const size_t need = train_workspace_bytes(B, r, nblk);

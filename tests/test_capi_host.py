@@ -106,6 +106,7 @@ def test_project_validation(lsa):
     _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.project, [lay], **{**base, "dtype": "fp8"})
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.project, [{**lay, "q_out": lay["c_out"]}], **base, match="alias")
     _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.project, [lay], **{**base, "n_h": 3, "d_h": 5})
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.project, [{**lay, "w_w": FAKE + 8}], **base, match="aligned")
 
 
 def test_packed_projection_validation(lsa):
@@ -238,6 +239,9 @@ def test_train_step_validation(lsa):
         bad(lsa.ERR_INVALID_ARG, "must be set", **{name: None})
     bad(lsa.ERR_INVALID_ARG, "aligned", h=FAKE + 2)
     bad(lsa.ERR_INVALID_ARG, "aligned", keys=FAKE + 8)
+    bad(lsa.ERR_INVALID_ARG, "aligned", w_w=FAKE + 8)
+    bad(lsa.ERR_INVALID_ARG, "aligned", labels=FAKE + 4)
+    bad(lsa.ERR_INVALID_ARG, "aligned", g_iuq=FAKE + 4)
     bad(lsa.ERR_UNSUPPORTED, "B must be", B=0)
     bad(lsa.ERR_UNSUPPORTED, "B must be", B=33)
     bad(lsa.ERR_UNSUPPORTED, "n_h = 64", n_h=32)
