@@ -200,3 +200,50 @@ def test_train_full_size(torch_cuda):
     got = run_gpu(torch_cuda, inp, words, 2.0, 0.25)
     say("  gpu done")
     compare(got, run_oracle(inp, lab, 2.0, 0.25), kink_allowance(inp, lab, 2.0, 0.25), "full")
+
+
+def test_train_deterministic_and_workspace_independent(torch_cuda):
+    """Two calls give the same bits, whatever the workspace held before (the split projection adds two
+    partial sums into zeroed outputs, which rounds the same in either order)."""
+    from sparse_kv_retrieval_amd import lsa
+    w = _workload((5000, 1234), name="train_det", seed=24)
+    say("train_deterministic")
+    inp = S.make(w, with_pool=False)
+    lab, words = S.train_labels(inp, 0, 0.05)
+    first = run_gpu(torch_cuda, inp, words, 2.0, 0.25)
+    # a workspace full of 0xFF bytes (NaN patterns) instead of 0x7F
+    orig_full = torch_cuda.full
+
+    def full_ff(size, value, **kw):
+        if kw.get("dtype") == torch_cuda.uint8:
+            value = 0xFF
+        return orig_full(size, value, **kw)
+
+    torch_cuda.full = full_ff
+    try:
+        second = run_gpu(torch_cuda, inp, words, 2.0, 0.25)
+    finally:
+        torch_cuda.full = orig_full
+    assert first[0] == second[0]
+    for a, b in zip(first[1:], second[1:]):
+        assert np.array_equal(a, b)
+    assert lsa.train_workspace_size(w.B, inp.key_offsets, w.r) > 0
+
+
+@pytest.mark.parametrize("kind", ["all_golden", "no_golden", "saturated"])
+def test_train_label_and_logit_extremes(torch_cuda, kind):
+    """Every entry golden, none golden, and logits in the hundreds (h scaled by 8: the sigmoid
+    saturates, the focal weights vanish for the easy entries)."""
+    w = _workload((2100, 300), name="train_" + kind, seed=25)
+    say(f"train_extremes {kind}")
+    inp = S.make(w, with_pool=False)
+    lab, _ = S.train_labels(inp, 0, 0.05)
+    if kind == "all_golden":
+        lab = np.ones_like(lab)
+    elif kind == "no_golden":
+        lab = np.zeros_like(lab)
+    else:
+        inp.h[0] = S.f32_to_bf16_bits(S.bf16_bits_to_f32(inp.h[0]) * np.float32(8.0))
+    words = S.pack_mask_words(lab, inp.key_offsets, inp.mask_word_offsets)
+    compare(run_gpu(torch_cuda, inp, words, 2.0, 0.25), run_oracle(inp, lab, 2.0, 0.25),
+            kink_allowance(inp, lab, 2.0, 0.25), kind)
