@@ -82,6 +82,21 @@ def read_traffic(workload: str):
         return None
 
 
+def read_kv_traffic(path: str, workload: str, source_hash: str):
+    """traffic_bytes_per_launch from a committed summary, or None when it is missing or stale."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(("#", " ", "|", "`")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_hash") == source_hash and kv.get("workload") == workload:
+        return int(kv["traffic_bytes_per_launch"])
+    return None
+
+
 def algorithmic_bytes(w, lengths) -> dict:
     """Bytes the score+select pass must move: every key once, its fp8 scale, one mask bit, plus q and w once per (b, l)."""
     esz = {"f32": 4, "bf16": 2, "fp8": 1}[w.key_dtype]
@@ -193,17 +208,7 @@ def golden_measure(steps: int, warmup: int, cpu_budget: float | None) -> dict:
            "nucleus_size": {"min": int(sz.min()), "mean": float(sz.mean()), "max": int(sz.max())},
            "what": "lsa_golden_labels over one window: every (token, layer) row's top-p nucleus, the layer vote "
                    "per token and the union over the window (four kernels; logits read once)"}
-    traffic = None
-    path = GOLDEN_TRAFFIC_FILE.format(w.name)
-    if os.path.exists(path):
-        kv = {}
-        with open(path) as f:
-            for line in f:
-                if ":" in line and not line.startswith(("#", " ", "|", "`")):
-                    k, v = line.split(":", 1)
-                    kv[k.strip()] = v.strip()
-        if kv.get("source_hash") == golden_source_hash() and kv.get("workload") == w.name:
-            traffic = int(kv["traffic_bytes_per_launch"])
+    traffic = read_kv_traffic(GOLDEN_TRAFFIC_FILE.format(w.name), w.name, golden_source_hash())
     out["segment_kernel_traffic"] = traffic
     if cpu_budget:
         log("[bench] golden labels: cpu baseline")
@@ -224,21 +229,6 @@ def train_source_hash() -> str:
         with open(os.path.join(ROOT, "sparse_kv_retrieval_amd", s), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
-
-
-def read_kv_traffic(path: str, workload: str, source_hash: str):
-    """traffic_bytes_per_launch from a committed summary, or None when it is missing or stale."""
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    with open(path) as f:
-        for line in f:
-            if ":" in line and not line.startswith(("#", " ", "|", "`")):
-                k, v = line.split(":", 1)
-                kv[k.strip()] = v.strip()
-    if kv.get("source_hash") == source_hash and kv.get("workload") == workload:
-        return int(kv["traffic_bytes_per_launch"])
-    return None
 
 
 def train_bytes(w, entries: int) -> dict:
