@@ -45,7 +45,7 @@ def _workload(N, d=256, r=128, name="train_small", seed=21):
     return dataclasses.replace(S.scaled(base, N=N, name=name), d=d, r=r, L=1, seed=seed)
 
 
-def run_gpu(torch, inp, words, gamma, alpha, layer=0):
+def run_gpu(torch, inp, words, gamma, alpha, layer=0, ws_fill=0x7F):
     from sparse_kv_retrieval_amd import lsa
     w = inp.workload
     dev = torch.device("cuda")
@@ -64,7 +64,7 @@ def run_gpu(torch, inp, words, gamma, alpha, layer=0):
     g_dq = torch.full((w.r, w.d), float("nan"), dtype=torch.float32, device=dev)
     g_iuq = torch.full((w.n_h * w.d_h, w.r), float("nan"), dtype=torch.float32, device=dev)
     g_w = torch.full((w.n_h, w.d), float("nan"), dtype=torch.float32, device=dev)
-    ws = torch.full((lsa.train_workspace_size(w.B, inp.key_offsets, w.r),), 0x7F, dtype=torch.uint8, device=dev)
+    ws = torch.full((lsa.train_workspace_size(w.B, inp.key_offsets, w.r),), ws_fill, dtype=torch.uint8, device=dev)
     lsa.train_step(h=u16(inp.h[layer]), w_dq=u16(mw.w_dq), w_iuq=u16(mw.w_iuq), w_w=u16(mw.w_w), keys=keys,
                    key_offsets=ko, key_offsets_host=inp.key_offsets, labels=labels, mask_word_offsets=mo,
                    mask_word_offsets_host=inp.mask_word_offsets, B=w.B, d=w.d, r=w.r, n_h=w.n_h, d_h=w.d_h,
@@ -211,19 +211,7 @@ def test_train_deterministic_and_workspace_independent(torch_cuda):
     inp = S.make(w, with_pool=False)
     lab, words = S.train_labels(inp, 0, 0.05)
     first = run_gpu(torch_cuda, inp, words, 2.0, 0.25)
-    # a workspace full of 0xFF bytes (NaN patterns) instead of 0x7F
-    orig_full = torch_cuda.full
-
-    def full_ff(size, value, **kw):
-        if kw.get("dtype") == torch_cuda.uint8:
-            value = 0xFF
-        return orig_full(size, value, **kw)
-
-    torch_cuda.full = full_ff
-    try:
-        second = run_gpu(torch_cuda, inp, words, 2.0, 0.25)
-    finally:
-        torch_cuda.full = orig_full
+    second = run_gpu(torch_cuda, inp, words, 2.0, 0.25, ws_fill=0xFF)  # NaN patterns instead of 0x7F bytes
     assert first[0] == second[0]
     for a, b in zip(first[1:], second[1:]):
         assert np.array_equal(a, b)
