@@ -6,26 +6,26 @@
 // query side's projections are trained, with binary cross-entropy made focal
 // (the gist.science summary states the same loss). The score is the
 // selection path's: I_s = sigmoid(x_s), x_s = sum_j w_j ReLU(q_j . K_s),
-// q = (h W^DQ) W^IUQ, w = h W^w ([BLOG] §3.1). Focal form with p = I_s:
-// -alpha (1-p)^gamma log p for a golden entry, -(1-alpha) p^gamma log(1-p)
-// otherwise; the loss is the mean over the batch's entries.
+// q = (h W^DQ) W^IUQ, w = h W^w (the write-up's §3.1). Focal form with
+// p = I_s: -alpha (1-p)^gamma log p for a golden entry, -(1-alpha) p^gamma
+// log(1-p) otherwise; the loss is the mean over the batch's entries.
 //
-// Kernels, after the projection kernels give c, q and w:
-//   train_scan_kernel  one pass over the keys (4 waves per block, 16 heads per
-//                      wave; the grid is sized to one round of resident blocks,
-//                      each a run of tiles of one sequence; tiles of 32 entries
-//                      staged in LDS twice: row-major
-//                      for the score MFMAs and transposed for the gradient
-//                      MFMAs). Per tile: the head dots S = K q^T on bf16 MFMA
-//                      (q split hi + lo), x_s, the loss, g_s = dloss/dx_s, and
-//                      the contraction dq_j = sum_s g_s w_j [S_sj > 0] K_s on
-//                      MFMA. The gate is factored out: the MFMA sums
-//                      dq'_j = sum_s g_s [S_sj > 0] K_s with g_s split hi + lo
-//                      once per entry, and dq_j = w_j dq'_j, dw_j = sum_s g_s
-//                      ReLU(S_sj) = q_j . dq'_j follow after the scan. The focal
-//                      terms are evaluated once per entry in each wave and
-//                      shared through LDS. Per-block partial sums go to the
-//                      workspace.
+// Kernels, after a zero fill of c, q, w and the two projection stages (each
+// reduction split over two blocks that add into the zeroed outputs):
+//   train_scan_kernel  one pass over the keys. 4 waves per block, 16 heads per
+//                      wave; the grid is one round of resident blocks, each a
+//                      run of 32-entry tiles of one sequence. Each tile is
+//                      staged in LDS twice (double-buffered): row-major for the
+//                      score MFMAs, transposed for the gradient MFMAs. Per
+//                      tile: the head dots S = K q^T on bf16 MFMA (q split
+//                      hi + lo), x_s, the loss and g_s = d loss / d x_s, and
+//                      the gradient contraction on MFMA with the gate factored
+//                      out: dq'_j = sum_s g_s [S_sj > 0] K_s, with g_s split
+//                      hi + lo once per entry. dq_j = w_j dq'_j and
+//                      dw_j = sum_s g_s ReLU(S_sj) = q_j . dq'_j follow after
+//                      the scan. The focal terms are evaluated once per entry
+//                      in each wave and shared through LDS. Per-block partial
+//                      sums (dq' and the loss) go to the workspace.
 //   train_reduce_kernel  sums a sequence's block partials into dq' (one block per
 //                      head and sequence) and forms dq and dw; one block sums
 //                      the loss over every block.
@@ -33,7 +33,8 @@
 //                      block one slice x 256 columns, and
 //   train_sum_kernel   the slices' partials added.
 //   train_outer_kernel rank-B products for the three gradients (16-byte stores):
-//                      g_iuq = dq^T c, g_dq = dc^T h, g_w = dw^T h.
+//                      g_iuq = dq^T c; g_dq = dc^T h and g_w = dw^T h in one
+//                      launch.
 #include <algorithm>
 
 #include "kernels.hpp"
@@ -66,8 +67,6 @@ struct TrainScanSmem {
   double lsum[4];
 };
 
-// Focal loss term and its derivative in the logit x (fp32), label y. With L = log(1 + e^-|x|),
-// log p = min(x, 0) - L and log(1 - p) = min(-x, 0) - L; powers are exponentials of gamma times those.
 // log(1 + e) for e in [0, 1]: log(u) e / (u - 1) with u = 1 + e rounded, which cancels the rounding of u
 // (Goldberg's form), so a hardware logarithm keeps a few-ulp relative error even for tiny e.
 __device__ __forceinline__ float t_log1p(float e) {
@@ -75,6 +74,8 @@ __device__ __forceinline__ float t_log1p(float e) {
   return u == 1.f ? e : __logf(u) * (e * __builtin_amdgcn_rcpf(u - 1.f));
 }
 
+// Focal loss term and its derivative in the logit x (fp32), label y. With L = log(1 + e^-|x|),
+// log p = min(x, 0) - L and log(1 - p) = min(-x, 0) - L; powers are exponentials of gamma times those.
 __device__ __forceinline__ void focal(float x, bool y, float gamma, float alpha, float& loss, float& grad) {
   const float L = t_log1p(__expf(-fabsf(x)));
   const float lp = fminf(x, 0.f) - L, lq = fminf(-x, 0.f) - L;  // log p, log(1 - p)
@@ -339,7 +340,8 @@ __global__ __launch_bounds__(512) void train_reduce_kernel(const TrainArgs a) {
 
 // Partial dc = dq W^IUQ over a slice of DCR rows o of the w_iuq buffer: dcp[slice][b][k] =
 // sum_{o in slice} dq[b][o] W[o][k]. Block: one slice x DCC columns; wave w takes rows o = w, w+4, ...
-// of the slice, lane l columns 4l..4l+3, with 16 rows' loads in flight; the four waves' sums meet in LDS.
+// of the slice, lane l columns 4l..4l+3, with 16 rows' loads in flight at a time; the four waves' sums
+// meet in LDS.
 constexpr int DCR = TNH * TDH / kTrainDcSlices;
 constexpr int DCC = 256;
 __global__ __launch_bounds__(256) void train_dc_kernel(const TrainArgs a) {
