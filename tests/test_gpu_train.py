@@ -45,7 +45,7 @@ def _workload(N, d=256, r=128, name="train_small", seed=21):
     return dataclasses.replace(S.scaled(base, N=N, name=name), d=d, r=r, L=1, seed=seed)
 
 
-def run_gpu(torch, inp, words, gamma, alpha, layer=0, ws_fill=0x7F):
+def run_gpu(torch, inp, words, gamma, alpha, layer=0, ws_fill=0x7F, labels_dev=None):
     from sparse_kv_retrieval_amd import lsa
     w = inp.workload
     dev = torch.device("cuda")
@@ -56,8 +56,12 @@ def run_gpu(torch, inp, words, gamma, alpha, layer=0, ws_fill=0x7F):
     mw = inp.mem_w[layer]
     ko = torch.from_numpy(inp.key_offsets).to(dev)
     mo = torch.from_numpy(inp.mask_word_offsets).to(dev)
-    labels = torch.from_numpy(words.view(np.int64)).to(dev) if words.size else torch.zeros(1, dtype=torch.int64,
-                                                                                           device=dev)
+    if labels_dev is not None:
+        labels = labels_dev
+    elif words.size:
+        labels = torch.from_numpy(words.view(np.int64)).to(dev)
+    else:
+        labels = torch.zeros(1, dtype=torch.int64, device=dev)
     keys = u16(inp.keys[layer]) if inp.keys[layer].size else torch.zeros(8, dtype=torch.int16, device=dev)
     # outputs start as garbage so that an unwritten element shows
     loss = torch.full((1,), float("nan"), dtype=torch.float32, device=dev)
@@ -235,3 +239,33 @@ def test_train_label_and_logit_extremes(torch_cuda, kind):
     words = S.pack_mask_words(lab, inp.key_offsets, inp.mask_word_offsets)
     compare(run_gpu(torch_cuda, inp, words, 2.0, 0.25), run_oracle(inp, lab, 2.0, 0.25),
             kink_allowance(inp, lab, 2.0, 0.25), kind)
+
+
+def test_train_on_mined_labels(torch_cuda):
+    """Labels straight from golden-label mining: lsa_golden_labels writes the window's label set in the
+    same bit layout that lsa_train_step reads, so the mined words feed the training step on the device.
+    The oracle side mines its own labels (the golden-label oracle) and trains on those."""
+    from oracle import golden_oracle as G
+    from sparse_kv_retrieval_amd import lsa
+    from sparse_kv_retrieval_amd import synth_golden as SG
+    dev = torch_cuda.device("cuda")
+    gw = SG.WORKLOADS["golden_small"]
+    gi = SG.make(gw)
+    W = gw.words
+    golden = torch_cuda.full((W,), -1, dtype=torch_cuda.int64, device=dev)
+    lsa.golden_labels(torch_cuda.from_numpy(gi.logits).to(dev), row_stride=gw.row_stride, T=gw.T, L=gw.L,
+                      n_valid=torch_cuda.from_numpy(gi.n_valid).to(dev), top_p=gw.p, theta=gw.theta,
+                      row_mask=torch_cuda.empty((gw.T * gw.L, W), dtype=torch_cuda.int64, device=dev), golden=golden,
+                      workspace=torch_cuda.empty(lsa.golden_workspace_size(gw.T, gw.L, gw.row_stride),
+                                                 dtype=torch_cuda.uint8, device=dev))
+    torch_cuda.cuda.synchronize()
+    lab = G.golden_labels(gi.logits, gi.n_valid, gw.p, gw.theta)       # the oracle's own label set
+    N = lab.size
+    mined = np.unpackbits(golden.cpu().numpy().view(np.uint8), bitorder="little").astype(bool)[:N]
+    assert np.array_equal(mined, lab), "mined label set differs from the oracle's on this window"
+    w = _workload((N,), name="train_mined", seed=26)
+    say(f"train_on_mined_labels: N={N}, {int(lab.sum())} golden")
+    inp = S.make(w, with_pool=False)
+    assert int(inp.mask_word_offsets[-1]) == (N + 63) // 64 <= W
+    got = run_gpu(torch_cuda, inp, np.zeros(0, np.uint64), 2.0, 0.25, labels_dev=golden[:(N + 63) // 64])
+    compare(got, run_oracle(inp, lab, 2.0, 0.25), kink_allowance(inp, lab, 2.0, 0.25), "mined")
