@@ -25,6 +25,28 @@ def mat(a):
     return [[frac(v) for v in row] for row in a]
 
 
+def e4m3fn(byte: int) -> Fraction:
+    """Exact value of one OCP FP8 E4M3 ("fn") byte, from its bit fields.
+
+    Sign bit 7; exponent field bits 6..3 (bias 7); mantissa field bits 2..0.
+    A zero exponent field is a subnormal, mantissa/8 * 2^-6. S.1111.111 is NaN
+    and is refused here (keys are finite).
+    """
+    sign = -1 if byte & 0x80 else 1
+    ef, mf = (byte >> 3) & 0xF, byte & 0x7
+    if ef == 0xF and mf == 0x7:
+        raise ValueError("NaN byte")
+    if ef == 0:
+        return sign * Fraction(mf, 8) * Fraction(1, 64)
+    mag = Fraction(8 + mf, 8)
+    return sign * (mag * 2 ** (ef - 7) if ef >= 7 else mag / 2 ** (7 - ef))
+
+
+def fp8_keys(key_bytes, scales):
+    """Exact keys of e4m3fn rows with one float32 scale per row: K_s = scale_s * value(byte)."""
+    return [[frac(sc) * e4m3fn(int(b)) for b in row] for row, sc in zip(key_bytes, scales)]
+
+
 def project(h_row, W_dq, W_iuq, W_w, n_h, d_h):
     """Exact c, q, w for one hidden state.
 

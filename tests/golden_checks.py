@@ -123,5 +123,72 @@ def check_votes_union(G):
     assert g.size == 20
 
 
+def _bounds_by_definition(y, p, eps):
+    """sure_in / sure_out of one row, from a plain loop: entries in (-y, s) order, each with the
+    exact-order running mass before it; the first entry is always kept."""
+    y = [float(v) for v in y]
+    P = _probs(np.array(y)) if y else np.zeros(0)
+    order = sorted(range(len(y)), key=lambda s: (-y[s], s))
+    sure_in, sure_out = np.zeros(len(y), bool), np.zeros(len(y), bool)
+    before = 0.0
+    for rank, s in enumerate(order):
+        sure_in[s] = rank == 0 or before < p - eps
+        sure_out[s] = rank > 0 and before >= p + eps
+        before += P[s]
+    return sure_in, sure_out
+
+
+def check_bounds_at_zero_eps(G):
+    """With no tolerance the bounds are the nucleus and its complement, and the window bounds
+    are the label set and its complement."""
+    rng = np.random.default_rng(21)
+    for n in (1, 2, 7, 50, 333):
+        y = np.round(rng.normal(0, 2, n) * 2) / 2
+        for p in (0.05, 0.6, 0.97):
+            si, so = G.nucleus_bounds(y, p, 0.0)
+            nuc = G.nucleus(y, p)
+            assert np.array_equal(si, nuc) and np.array_equal(so, ~nuc), (n, p)
+    T, L, N = 3, 4, 40
+    logits = np.round(rng.normal(0, 2, (T, L, N)) * 2) / 2
+    nv = [30, 35, 40]
+    for th in (1, 2, 3, 5):
+        sg, sn = G.golden_bounds(logits, nv, 0.6, th, 0.0)
+        gl = G.golden_labels(logits, nv, 0.6, th)
+        assert np.array_equal(sg, gl) and np.array_equal(sn, ~gl), th
+
+
+def check_bounds_definition(G):
+    """With a tolerance, against the definition written as loops: per row, the entries surely in
+    or out of the nucleus; per window, an entry is surely golden when some token has at least
+    theta layers that surely keep it, and surely not when no token has theta layers that may."""
+    rng = np.random.default_rng(22)
+    for trial in range(30):
+        n = int(rng.integers(1, 12))
+        y = np.round(rng.normal(0, 1.2, n) * 2) / 2
+        for p in (0.05, 0.3, 0.6, 0.9):
+            for eps in (0.02, 0.1):
+                si, so = G.nucleus_bounds(y, p, eps)
+                wi, wo = _bounds_by_definition(y, p, eps)
+                assert np.array_equal(si, wi) and np.array_equal(so, wo), (trial, p, eps, y)
+                nuc = G.nucleus(y, p)
+                assert not (si & ~nuc).any() and not (so & nuc).any()
+    T, L, N = 4, 5, 9
+    logits = np.round(rng.normal(0, 1.2, (T, L, N)) * 2) / 2
+    nv = [6, 7, 9, 9]
+    for th in (1, 2, 3):
+        for eps in (0.03, 0.1):
+            sg, sn = G.golden_bounds(logits, nv, 0.6, th, eps)
+            want_g, maybe = np.zeros(N, bool), np.zeros(N, bool)
+            for i in range(T):
+                lo, hi = np.zeros(N, int), np.zeros(N, int)
+                for l in range(L):
+                    wi, wo = _bounds_by_definition(logits[i, l, :nv[i]], 0.6, eps)
+                    lo[:nv[i]] += wi
+                    hi[:nv[i]] += ~wo
+                want_g |= lo >= th
+                maybe |= hi >= th
+            assert np.array_equal(sg, want_g) and np.array_equal(sn, ~maybe), (th, eps)
+
+
 ALL = [check_hand_nucleus, check_hand_window, check_nucleus_brute_force, check_nucleus_closed_forms,
-       check_votes_union]
+       check_votes_union, check_bounds_at_zero_eps, check_bounds_definition]

@@ -164,13 +164,17 @@ def check_brute_force(O, seeds=range(6)):
             Ww = O.decode_act(ww, "f32" if ww.dtype == np.float32 else "bf16")
             K = O.decode_keys(keys, kdt, sc)
             c, q, w = O.project(H, Wdq, Wiuq, Ww, n_h, d_h)
+            # exact keys straight from the stored values: the fp8 bytes and scales are decoded
+            # by the brute-force module's own field decoder, not by the oracle
+            Kb = brute.fp8_keys(keys, sc) if kdt == "fp8" else brute.mat(keys.astype(np.float64) if kdt == "f32"
+                                                                         else synth.bf16_bits_to_f32(keys))
+            assert np.array_equal(K, np.array([[float(v) for v in row] for row in Kb], np.float64).reshape(K.shape))
             # exact path (math layout = transposes of the stored buffers)
             hb = [brute.frac(v) for v in H[0]]
             cb, qb, wb = brute.project(hb, brute.mat(Wdq.T), brute.mat(Wiuq.T), brute.mat(Ww.T), n_h, d_h)
             assert np.allclose(c[0], [float(v) for v in cb], rtol=1e-12, atol=1e-12)
             assert np.allclose(q[0].ravel(), [float(v) for row in qb for v in row], rtol=1e-11, atol=1e-11)
             assert np.allclose(w[0], [float(v) for v in wb], rtol=1e-12, atol=1e-12)
-            Kb = brute.mat(K)
             # exact logits from the exact q, w
             xb = [brute.logit(qb, wb, key) for key in Kb]
             x = O.logits(q[0], w[0], K)
@@ -295,8 +299,64 @@ def check_same_query_topk(O):
     assert np.array_equal(out, np.sort(best))
 
 
+# ------------------------------------------------------------- fp8 scale
+def load_json(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def check_fp8_scale_hand(O):
+    """e4m3fn bytes times their per-entry scale, against values decoded by hand."""
+    g = load_json("fp8_keys_hand.json")
+    for case in (g, g["square"]):
+        got = O.decode_keys(np.array(case["bytes"], np.uint8), "fp8", np.array(case["scales"], np.float32))
+        assert np.array_equal(got, np.array(case["keys"], np.float64)), (got, case["keys"])
+
+
+# ------------------------------------------------------- whole-path wiring
+def hand_inputs(key_dtype="f32", k=2):
+    """The run_path_hand.json example as a synthetic-input object (one sequence, two layers)."""
+    g = load_json("run_path_hand.json")
+    w = synth.Workload("hand_path", 99, B=1, L=2, d=2, r=1, n_h=2, d_h=2, key_dtype=key_dtype, act_dtype="f32",
+                       k=k, N=(8,), pool_dim=4)
+    f32 = lambda a: np.array(a, np.float32)
+    lw = lambda e: synth.LayerWeights(w_dq=f32(e["w_dq"]), w_iuq=f32(e["w_iuq"]), w_w=f32(e["w_w"]))
+    if key_dtype == "fp8":
+        keys = [np.array(b, np.uint8) for b in g["fp8"]["bytes"]]
+        scales = [f32(s) for s in g["fp8"]["scales"]]
+    else:
+        keys = [f32(k_) for k_ in g["keys"]]
+        scales = [None, None]
+    pool = (np.arange(8 * 4, dtype=np.uint16).reshape(8, 4) * np.uint16(37) + np.uint16(0x3F00))
+    return g, synth.Inputs(workload=w, lengths=np.array([8], np.int64), key_offsets=np.array([0, 8], np.int64),
+                           mask_word_offsets=np.array([0, 1], np.int64), h=[f32(g["h"][0:1]), f32(g["h"][1:2])],
+                           mem_w=[lw(e) for e in g["mem"]], nat_w=[lw(e) for e in g["nat"]], keys=keys,
+                           key_scale=scales, pool=pool)
+
+
+def check_run_path_hand(O):
+    """The whole path on the hand example: which weights and which layer's keys feed each step."""
+    for kdt in ("f32", "fp8"):
+        for k in ("2", "5", "8"):
+            g, inp = hand_inputs(kdt, int(k))
+            r = O.run_path(inp)[0]
+            for l in range(2):
+                assert np.array_equal(r["c"][l], g["mem"][l]["c"]), (kdt, l, r["c"][l])
+                assert np.array_equal(r["q"][l], np.array(g["mem"][l]["q"], np.float64)), (kdt, l)
+                assert np.array_equal(r["w"][l], g["mem"][l]["w"]), (kdt, l)
+                assert np.array_equal(r["x"][l], g["x"][l]), (kdt, l, r["x"][l])
+                assert O.compact(r["mask"][l]).tolist() == g["selected"][l], (kdt, l)
+                assert np.array_equal(r["qn"][l], np.array(g["nat"][l]["q"], np.float64)), (kdt, l)
+                assert np.array_equal(r["wn"][l], g["nat"][l]["w"]), (kdt, l)
+                assert np.array_equal(r["y"][l], g["y"][l]), (kdt, l, r["y"][l])
+                assert r["topk"][l].tolist() == g["topk"][k][l], (kdt, k, l, r["topk"][l])
+            assert r["idx"].tolist() == g["union"], (kdt, r["idx"])
+            assert np.array_equal(r["gathered"], inp.pool[g["union"]])
+
+
 ALL_CHECKS = [
     check_hand_scores, check_hand_topk, check_hand_projection, check_sigmoid_closed_forms,
     check_threshold, check_bf16_decode, check_e4m3fn, check_brute_force, check_special_cases,
     check_union_compact, check_topk_properties, check_gather, check_same_query_topk,
+    check_fp8_scale_hand, check_run_path_hand,
 ]

@@ -102,8 +102,63 @@ def _mut_intersection(m):
     m.golden_labels = golden_labels
 
 
+def _bounds_with(inside, outside, top=True):
+    def nucleus_bounds(y, p, eps):
+        y = np.asarray(y, np.float64)
+        si, so = np.zeros(y.size, bool), np.zeros(y.size, bool)
+        if y.size == 0:
+            return si, so
+        e = np.exp(y - y.max())
+        P = e / e.sum()
+        order = np.lexsort((np.arange(y.size), -y))
+        before = np.concatenate(([0.0], np.cumsum(P[order])[:-1]))
+        si[order[inside(before, p, eps)]] = True
+        so[order[outside(before, p, eps)]] = True
+        if top:
+            si[order[0]], so[order[0]] = True, False
+        return si, so
+    return nucleus_bounds
+
+
+def _mut_bounds_eps_sign(m):  # the band on the wrong side: decides entries it should leave open
+    m.nucleus_bounds = _bounds_with(lambda b, p, e: b < p + e, lambda b, p, e: b >= p - e)
+
+
+def _mut_bounds_no_top(m):  # forgets that the most probable entry is always kept
+    m.nucleus_bounds = _bounds_with(lambda b, p, e: b < p - e, lambda b, p, e: b >= p + e, top=False)
+
+
+def _golden_bounds_with(hi_from_sure_in=False, strict=False):
+    def golden_bounds(logits, n_valid, p, theta, eps):
+        logits = np.asarray(logits)
+        T, L = logits.shape[0], logits.shape[1]
+        N = int(max(n_valid))
+        sure_g, maybe_g = np.zeros(N, bool), np.zeros(N, bool)
+        for i in range(T):
+            n = int(n_valid[i])
+            lo, hi = np.zeros(n, np.int64), np.zeros(n, np.int64)
+            for l in range(L):
+                si, so = m_ref.nucleus_bounds(logits[i, l, :n], p, eps)
+                lo += si
+                hi += si if hi_from_sure_in else ~so
+            sure_g[:n] |= (lo > theta) if strict else (lo >= theta)
+            maybe_g[:n] |= hi >= theta
+        return sure_g, ~maybe_g
+    m_ref = G
+    return golden_bounds
+
+
+def _mut_golden_bounds_maybe_from_sure(m):  # "may be golden" counted from the sure votes only
+    m.golden_bounds = _golden_bounds_with(hi_from_sure_in=True)
+
+
+def _mut_golden_bounds_strict(m):
+    m.golden_bounds = _golden_bounds_with(strict=True)
+
+
 MUTATIONS = [_mut_stop_before_crossing, _mut_one_past, _mut_ties_high_index, _mut_ascending, _mut_unnormalised,
-             _mut_strict_vote, _mut_whole_row, _mut_intersection]
+             _mut_strict_vote, _mut_whole_row, _mut_intersection, _mut_bounds_eps_sign, _mut_bounds_no_top,
+             _mut_golden_bounds_maybe_from_sure, _mut_golden_bounds_strict]
 
 
 @pytest.mark.parametrize("mut", MUTATIONS, ids=lambda f: f.__name__)

@@ -3,7 +3,7 @@
 The mistakes are planted on the CPU in a throw-away copy of the oracle module.
 The real oracle is never modified.
 """
-import copy
+import inspect
 import types
 
 import numpy as np
@@ -119,11 +119,49 @@ def _mut_gather_offset(m):
     m.gather = lambda pool, idx: np.asarray(pool)[np.minimum(np.asarray(idx) + 1, len(pool) - 1)]
 
 
+def _from_source(m, fn_name, old, new):
+    """Re-define one oracle function in the copy from its source with `old` replaced by `new`."""
+    src = inspect.getsource(getattr(O, fn_name))
+    assert old in src, (fn_name, old)
+    exec(compile(src.replace(old, new), f"<mutant {fn_name}>", "exec"), m.__dict__)
+
+
+def _mut_fp8_divide_scale(m):
+    _from_source(m, "decode_keys", "e4m3fn_to_f64(keys) * np.asarray(scale", "e4m3fn_to_f64(keys) / np.asarray(scale")
+
+
+def _mut_fp8_scale_wrong_axis(m):
+    _from_source(m, "decode_keys", "[:, None]", "[None, :]")
+
+
+def _mut_fp8_scale_ignored(m):
+    _from_source(m, "decode_keys", "* np.asarray(scale, np.float32).astype(np.float64)[:, None]", "")
+
+
+def _mut_path_mem_query_topk(m):
+    _from_source(m, "run_path", "nw = inp.nat_w[l]", "nw = inp.mem_w[l]")
+
+
+def _mut_path_other_layer_keys(m):
+    _from_source(m, "run_path", 'per["K"][l][idx]', 'per["K"][(l + 1) % L][idx]')
+
+
+def _mut_path_topk_over_own_selection(m):
+    _from_source(m, "run_path", "tk[l] = topk(y, idx, w.k)",
+                 "tk[l] = topk(y[per['mask'][l][idx]], idx[per['mask'][l][idx]], w.k)")
+
+
+def _mut_path_first_layer_h(m):
+    _from_source(m, "run_path", "decode_act(inp.h[l][b:b + 1]", "decode_act(inp.h[0][b:b + 1]")
+
+
 MUTANTS = [_mut_no_relu, _mut_relu_after_gate, _mut_sum_then_relu, _mut_strict_threshold,
            _mut_threshold_sign, _mut_union_and, _mut_topk_tie_high, _mut_topk_score_order,
            _mut_topk_smallest, _mut_proj_no_transpose_q, _mut_proj_gate_from_c, _mut_bf16_low_half,
            _mut_e4m3_bias8, _mut_e4m3_no_subnormal, _mut_sigmoid_sign, _mut_compact_descending,
-           _mut_gather_offset]
+           _mut_gather_offset, _mut_fp8_divide_scale, _mut_fp8_scale_wrong_axis, _mut_fp8_scale_ignored,
+           _mut_path_mem_query_topk, _mut_path_other_layer_keys, _mut_path_topk_over_own_selection,
+           _mut_path_first_layer_h]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__)
@@ -137,3 +175,4 @@ def test_pins_catch_planted_mistake(mutate):
         except (AssertionError, ValueError, IndexError):
             caught.append(check.__name__)
     assert caught, f"no pin catches {mutate.__name__}"
+    print(mutate.__name__, "caught by", caught)
