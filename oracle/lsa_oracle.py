@@ -40,6 +40,10 @@ design notes.
   R7  The compacted list is in ascending entry order.
   R8  For fp8 keys, K_s = scale_s * e4m3fn(K8_s). Scales are positive, so the
       scale commutes with the ReLU.
+  R9  At every decode step after a trigger, the native indexer's own query for
+      that step (its projections of the step's hidden state) ranks the entries
+      of the subset loaded at the trigger, with that layer's keys ([BLOG] §3.2
+      second level; [HYPER] 方法). The subset is an input of the step.
 """
 from __future__ import annotations
 
@@ -239,4 +243,32 @@ def run_path(inp, *, sequences=None, layers=None, want_scores=True):
         if inp.pool is not None:
             per["gathered"] = gather(inp.pool[s0:s1], idx)
         out[b] = per
+    return out
+
+
+def step_topk(inp, h_step, lists, *, layers=None):
+    """The native top-k of one decode step over the resident subset (R9).
+
+    `h_step[l]` holds the step's hidden states [B, d] (stored values) for
+    layer l, and `lists[b]` the subset of sequence b (ascending entry indices,
+    loaded at the trigger). For every sequence b and layer l: q', w' are the
+    native indexer's projections of the step's h ([BLOG] §3.1 forms with the
+    native weights), y_s = sum_j w'_j ReLU(q'_j . K^l_s) for s in the subset,
+    and the k best by (-y, s), ascending. Returns {(b, l): (topk, y)}.
+    """
+    w = inp.workload
+    out = {}
+    lays = range(w.L) if layers is None else layers
+    for b in range(w.B):
+        s0, s1 = int(inp.key_offsets[b]), int(inp.key_offsets[b + 1])
+        idx = np.asarray(lists[b], dtype=np.int64)
+        for l in lays:
+            nw = inp.nat_w[l]
+            hl = decode_act(h_step[l][b:b + 1], w.act_dtype)
+            _, qn, wn = project(hl, decode_act(nw.w_dq, w.act_dtype), decode_act(nw.w_iuq, w.act_dtype),
+                                decode_act(nw.w_w, w.act_dtype), w.n_h, w.d_h)
+            sc = None if inp.key_scale[l] is None else inp.key_scale[l][s0:s1][idx]
+            K = decode_keys(inp.keys[l][s0:s1][idx], w.key_dtype, sc)
+            y = logits(qn[0], wn[0], K) if idx.size else np.zeros(0)
+            out[(b, l)] = (topk(y, idx, w.k), y)
     return out

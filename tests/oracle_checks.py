@@ -354,9 +354,23 @@ def check_run_path_hand(O):
             assert np.array_equal(r["gathered"], inp.pool[g["union"]])
 
 
+def check_step_topk_hand(O):
+    """One decode step's top-k over the resident subset, on the hand example."""
+    for kdt in ("f32", "fp8"):
+        for k in ("2", "5"):
+            g, inp = hand_inputs(kdt, int(k))
+            st = g["step"]
+            h_step = [np.array([st["h"][l]], np.float32) for l in range(2)]
+            r = O.step_topk(inp, h_step, [np.array(g["union"], np.int64)])
+            for l in range(2):
+                tk, y = r[(0, l)]
+                assert np.array_equal(y, st["y"][l]), (kdt, l, y)
+                assert tk.tolist() == st["topk"][k][l], (kdt, k, l, tk)
+
+
 ALL_CHECKS = [
     check_hand_scores, check_hand_topk, check_hand_projection, check_sigmoid_closed_forms,
     check_threshold, check_bf16_decode, check_e4m3fn, check_brute_force, check_special_cases,
     check_union_compact, check_topk_properties, check_gather, check_same_query_topk,
-    check_fp8_scale_hand, check_run_path_hand,
+    check_fp8_scale_hand, check_run_path_hand, check_step_topk_hand,
 ]

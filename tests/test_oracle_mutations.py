@@ -155,13 +155,26 @@ def _mut_path_first_layer_h(m):
     _from_source(m, "run_path", "decode_act(inp.h[l][b:b + 1]", "decode_act(inp.h[0][b:b + 1]")
 
 
+def _mut_step_mem_weights(m):
+    _from_source(m, "step_topk", "nw = inp.nat_w[l]", "nw = inp.mem_w[l]")
+
+
+def _mut_step_trigger_h(m):
+    _from_source(m, "step_topk", "decode_act(h_step[l][b:b + 1]", "decode_act(inp.h[l][b:b + 1]")
+
+
+def _mut_step_whole_sequence(m):  # ranks every entry instead of the resident subset
+    _from_source(m, "step_topk", "idx = np.asarray(lists[b], dtype=np.int64)",
+                 "idx = np.arange(s1 - s0, dtype=np.int64)")
+
+
 MUTANTS = [_mut_no_relu, _mut_relu_after_gate, _mut_sum_then_relu, _mut_strict_threshold,
            _mut_threshold_sign, _mut_union_and, _mut_topk_tie_high, _mut_topk_score_order,
            _mut_topk_smallest, _mut_proj_no_transpose_q, _mut_proj_gate_from_c, _mut_bf16_low_half,
            _mut_e4m3_bias8, _mut_e4m3_no_subnormal, _mut_sigmoid_sign, _mut_compact_descending,
            _mut_gather_offset, _mut_fp8_divide_scale, _mut_fp8_scale_wrong_axis, _mut_fp8_scale_ignored,
            _mut_path_mem_query_topk, _mut_path_other_layer_keys, _mut_path_topk_over_own_selection,
-           _mut_path_first_layer_h]
+           _mut_path_first_layer_h, _mut_step_mem_weights, _mut_step_trigger_h, _mut_step_whole_sequence]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__)
