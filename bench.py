@@ -108,29 +108,89 @@ def algorithmic_bytes(w, lengths) -> dict:
     return {"per_entry_bytes": per_entry + 0.125, "bytes_per_launch": total, "entries_per_launch": w.L * n}
 
 
+PEAK_BF16_FLOPS = 2.5e15  # MI355X dense bf16 matrix cores, published peak
+
+
+def spread(v) -> dict:
+    """Median, p10, p90 and mean of a list of durations."""
+    a = np.asarray(v, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90)),
+            "mean": float(a.mean()), "n": int(a.size)}
+
+
+def project_rates(w, seconds: float) -> dict:
+    """The projection stage (memory-indexer and native queries, 2L layer projections): its weight
+    stream against HBM peak, and its matrix-core work against the dense bf16 peak. The work of one
+    layer projection is 2 B (d r + r n_h d_h + d n_h) flops; the up-projection's c enters the matrix
+    cores as hi + lo, which issues its part twice."""
+    proj = 2 * w.L
+    wbytes = proj * (w.r * w.d + w.n_h * w.d_h * w.r + w.n_h * w.d) * 2
+    flops = proj * 2 * w.B * (w.d * w.r + w.r * w.n_h * w.d_h + w.d * w.n_h)
+    issued = proj * 2 * w.B * (w.d * w.r + 2 * w.r * w.n_h * w.d_h + w.d * w.n_h)
+    return {"us": seconds * 1e6, "weight_bytes": wbytes, "hbm_GBs": wbytes / seconds / 1e9,
+            "hbm_frac": wbytes / seconds / 1e9 / PEAK_HBM_GBS, "flops": flops,
+            "mfma_util": flops / seconds / PEAK_BF16_FLOPS, "mfma_util_issued": issued / seconds / PEAK_BF16_FLOPS,
+            "note": "B rows per projection: a weight stream, bound by HBM; the matrix-core fraction is small by "
+                    "construction"}
+
+
+def host_facts() -> dict:
+    """The host the CPU baselines run on: CPU model, logical CPUs, CPUs this process may use, BLAS threads."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+            "blas_threads": int(blas)}
+
+
+class CpuClock:
+    """Wall time and the process's CPU time over a region: cpu / wall is the number of cores it kept busy."""
+
+    def __enter__(self):
+        self.t0, self.c0 = time.perf_counter(), os.times()
+        return self
+
+    def __exit__(self, *exc):
+        c1 = os.times()
+        self.wall = time.perf_counter() - self.t0
+        self.cpu = (c1.user - self.c0.user) + (c1.system - self.c0.system)
+        return False
+
+    @property
+    def cores(self) -> int:
+        return max(1, int(round(self.cpu / max(self.wall, 1e-9))))
+
+
 def cpu_baseline(inp, budget_s: float):
     """The CPU oracle as it stands, timed over whole sequences of the same workload until about `budget_s`."""
     from oracle import lsa_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     w = inp.workload
     done_entries = 0
     seqs = 0
-    t0 = time.perf_counter()
     # whole sequences, in order, repeating the workload until the budget is spent
-    while time.perf_counter() - t0 < budget_s:
-        b = seqs % w.B
-        O.run_path(inp, sequences=[b])
-        done_entries += int(inp.lengths[b]) * w.L
-        seqs += 1
-    el = time.perf_counter() - t0
-    return {"value": done_entries / el, "unit": "entries/s", "cores": int(threads), "kind": "oracle",
+    with CpuClock() as clk:
+        while time.perf_counter() - clk.t0 < budget_s:
+            b = seqs % w.B
+            O.run_path(inp, sequences=[b])
+            done_entries += int(inp.lengths[b]) * w.L
+            seqs += 1
+    el = clk.wall
+    return {"value": done_entries / el, "unit": "entries/s", "cores": clk.cores, "kind": "oracle",
             "sample": f"{seqs} sequence passes ({seqs / w.B:.2f} x the {w.B} sequences) x {w.L} layers of the "
                       f"{w.name} workload, full path (project, score, select, union, compact, top-k, gather), "
-                      f"{el:.1f} s"}
+                      f"{el:.1f} s",
+            "cpu_seconds": clk.cpu, "host": host_facts()}
 
 
 GOLDEN_WORKLOAD = "golden_t64_l21_n125k"
@@ -150,17 +210,18 @@ def golden_cpu_baseline(inp, budget_s: float) -> dict:
     """The golden-label oracle as it stands, over whole tokens of the window (all layers) until about budget_s."""
     from oracle import golden_oracle as G
     w = inp.workload
-    t0 = time.perf_counter()
     toks = 0
     entries = 0
-    while time.perf_counter() - t0 < budget_s and toks < w.T:
-        n = int(inp.n_valid[toks])
-        G.votes(inp.logits[toks], n, w.p)
-        entries += n * w.L
-        toks += 1
-    el = time.perf_counter() - t0
-    return {"value": entries / el, "unit": "entries/s", "cores": 1, "kind": "oracle",
-            "sample": f"{toks} of the {w.T} tokens x {w.L} layers (softmax, nucleus, vote per token), {el:.1f} s"}
+    with CpuClock() as clk:
+        while time.perf_counter() - clk.t0 < budget_s and toks < w.T:
+            n = int(inp.n_valid[toks])
+            G.votes(inp.logits[toks], n, w.p)
+            entries += n * w.L
+            toks += 1
+    el = clk.wall
+    return {"value": entries / el, "unit": "entries/s", "cores": clk.cores, "kind": "oracle",
+            "sample": f"{toks} of the {w.T} tokens x {w.L} layers (softmax, nucleus, vote per token), {el:.1f} s",
+            "cpu_seconds": clk.cpu}
 
 
 def golden_measure(steps: int, warmup: int, cpu_budget: float | None) -> dict:
@@ -297,18 +358,18 @@ def train_measure(steps: int, warmup: int, cpu_budget: float | None) -> dict:
         from oracle import lsa_oracle as O
         from oracle import train_oracle as TO
         n_seq = 0
-        t0 = time.perf_counter()
         H = O.decode_act(inp.h[0], "bf16")
         Ws = [O.decode_act(m, "bf16") for m in (mw.w_dq, mw.w_iuq, mw.w_w)]
         done = 0
-        while n_seq < w.B and time.perf_counter() - t0 < cpu_budget:
-            s0, s1 = int(inp.key_offsets[n_seq]), int(inp.key_offsets[n_seq + 1])
-            TO.train_step(H[n_seq:n_seq + 1], *Ws, [O.decode_keys(inp.keys[0][s0:s1], "bf16")], [lab[s0:s1]],
-                          w.n_h, w.d_h)
-            done += s1 - s0
-            n_seq += 1
-        el = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": done / el, "unit": "entries/s", "cores": torch.get_num_threads(),
+        with CpuClock() as clk:
+            while n_seq < w.B and time.perf_counter() - clk.t0 < cpu_budget:
+                s0, s1 = int(inp.key_offsets[n_seq]), int(inp.key_offsets[n_seq + 1])
+                TO.train_step(H[n_seq:n_seq + 1], *Ws, [O.decode_keys(inp.keys[0][s0:s1], "bf16")], [lab[s0:s1]],
+                              w.n_h, w.d_h)
+                done += s1 - s0
+                n_seq += 1
+        el = clk.wall
+        out["cpu_baseline"] = {"value": done / el, "unit": "entries/s", "cores": clk.cores,
                                "kind": "oracle",
                                "sample": f"{n_seq} of the {w.B} sequences, each as a one-sequence step "
                                          f"(float64 numpy, decoding included), {el:.1f} s"}
@@ -380,8 +441,8 @@ def main():
         p.gather(); e[5].record(stream)
     torch.cuda.synchronize()
     ms_per_step_eager = (time.perf_counter() - t0) * 1e3 / args.steps
-    stage_ms = {n: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
-                for i, n in enumerate(names)}
+    stage_all = {n: [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)] for i, n in enumerate(names)}
+    stage_ms = {n: float(np.mean(v)) for n, v in stage_all.items()}
 
     # Whole steps: run() as an application calls it (the gather on a second stream,
     # overlapping the top-k stages), K steps between two synchronisations.
@@ -405,6 +466,69 @@ def main():
         graph.replay()
     torch.cuda.synchronize()
     ms_per_step_graph = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    def timed(fn, reps):
+        """Per-launch durations (us) of fn() on the launch stream, HIP events around each launch."""
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        out_us = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out_us.append(e0.elapsed_time(e1) * 1e3)
+        return out_us
+
+    # The score pass in its variants: the step's mask-only pass, mask + sigmoid scores (the full
+    # pass), the hi-only first pass with per-tile completion, and the wave-pair kernel.
+    log("[bench] score pass variants")
+    p.scores = [torch.empty(max(p.rows, 1), dtype=torch.float32, device="cuda") for _ in range(w.L)]
+    p.masks_scored = [torch.empty(max(p.words, 1), dtype=torch.int64, device="cuda") for _ in range(w.L)]
+    variants = {"mask_only": lambda: p.score_select(),
+                "mask_and_score": lambda: p.score_with_sigmoid()}
+    if w.key_dtype != "f32":
+        variants["mask_only_guard"] = lambda: p._score_call(p.masks, None, {"guard": 1}, None)
+    variants["mask_only_pair_kernel"] = lambda: p._score_call(p.masks, None, {"kernel": "pairs"}, None)
+    score_variants = {k_: spread(timed(f_, args.steps)) for k_, f_ in variants.items()}
+    p.scores = p.masks_scored = None
+
+    # Decode steps after the trigger: each layer's union rows of keys packed once, then per step the
+    # native query of the step's hidden state and the top-k over the packed subset (lsa_topk_step).
+    log("[bench] decode steps")
+    p.alloc_steps()
+    p.run()
+    p.pack_subset_keys()
+    hs = synth.step_hidden(inp, 4)
+    p.set_step_hidden(hs[0])
+    torch.cuda.synchronize()
+    pack_us = timed(lambda: p.pack_subset_keys(), 5)
+    step_us = timed(lambda: p.step(), args.steps)
+    step_topk_us = timed(lambda: p.step_topk(), args.steps)
+    union_rows = int(p.count.sum())
+    kb = w.d_h * {"f32": 4, "bf16": 2, "fp8": 1}[w.key_dtype] + (4 if w.key_dtype == "fp8" else 0)
+    step_bytes = w.L * union_rows * (kb + 4 + 4 + 4) + w.L * w.B * w.k * 8
+    st_med = float(np.median(step_topk_us))
+    decode_steps = {
+        "what": "per decode step: the native query of the step's h (lsa_project_packed) and lsa_topk_step over "
+                "each layer's union rows of keys, packed once per trigger (lsa_gather)",
+        "subset_rows_per_layer": union_rows, "k": w.k,
+        "us_per_step": spread(step_us), "topk_step_us": spread(step_topk_us),
+        "pack_once_per_trigger_us": spread(pack_us),
+        "us_per_window_of_64_steps": 64 * float(np.median(step_us)),
+        "topk_step_bytes": step_bytes, "topk_step_GBs": step_bytes / (st_med * 1e-6) / 1e9,
+        "note": "topk_step_bytes: the packed keys (and fp8 scales) once, the list index, the workspace score "
+                "written and read, and the k outputs"}
+    p.keys_sub = None
+    torch.cuda.empty_cache()
+
+    # The plain streaming read of the same number of bytes as the score pass: the achievable ceiling.
+    from sparse_kv_retrieval_amd import profiling as PR
+    log("[bench] streaming-read reference")
+    ab0 = algorithmic_bytes(w, inp.lengths)
+    stream_ref = PR.stream_read_rate(ab0["bytes_per_launch"], reps=args.steps)
 
     host_fetch = None
     if not args.no_host_fetch and inp.pool is not None:
@@ -460,8 +584,16 @@ def main():
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "score_stream_kernel" if w.key_dtype in ("bf16", "fp8") else "score_select_kernel",
                      "bytes_per_launch": ab["bytes_per_launch"], "per_entry_bytes": ab["per_entry_bytes"],
-                     "avg_launch_us": stage_ms["score_select"] * 1e3},
+                     "avg_launch_us": stage_ms["score_select"] * 1e3,
+                     "launch_us": spread([v * 1e3 for v in stage_all["score_select"]]),
+                     "stream_read_ceiling_GBs": stream_ref["GB_per_s"],
+                     "frac_of_stream_read": achieved / stream_ref["GB_per_s"],
+                     "stream_read": {k_: v_ for k_, v_ in stream_ref.items() if k_ != "sweep"}},
         "stages_us": {k: v * 1e3 for k, v in stage_ms.items()},
+        "stages_us_spread": {k: spread([x * 1e3 for x in v]) for k, v in stage_all.items()},
+        "score_select_variants_us": score_variants,
+        "project": project_rates(w, stage_ms["project"] * 1e-3),
+        "decode_steps": decode_steps,
         "ms_per_step_sequential": ms_per_step_eager,
         "ms_per_step_graph": ms_per_step_graph,
         "selection": {"union_fraction": float(counts.sum()) / rows, "union_per_seq_mean": float(counts.mean())},

@@ -15,6 +15,8 @@
  *                                                    [BLOG] §4.2, [HYPER] 方法
  *   lsa_topk           native Lightning-Indexer top-k inside the subset
  *                                                    [BLOG] §2.2, §3.2
+ *   lsa_topk_step      the same at every decode step, over the subset's keys
+ *                      packed once per trigger              [BLOG] §3.2
  *   lsa_gather         copy the selected compressed-KV rows into a compact buffer
  *                                                    [HYPER] 方法 (load C^MemComp)
  *   lsa_fetch_host     the same copy from a pool in pinned host memory
@@ -64,7 +66,7 @@ extern "C" {
 
 #define LSA_MAX_LAYERS 8
 #define LSA_MAX_HEADS 64
-#define LSA_VERSION 1
+#define LSA_VERSION 2
 #define LSA_GOLDEN_MAX_ROW (1 << 28)  /* entries per (token, layer) logit row */
 
 typedef enum {
@@ -169,6 +171,9 @@ lsa_status lsa_project_packed(const lsa_proj_layer* layers /* host [L] */, int32
  * as fp32 for every entry. mask_out receives the selection bits (see "Masks").
  * Supported: d_h in {32, 64, 128}; 1 <= n_h <= 64; 0 < threshold < 1.
  * Sequences with N_b = 0 are allowed and write nothing.
+ * Precision: with fp32 keys the contraction is fp32. With bf16 or fp8 keys, q
+ * enters the bf16 matrix cores as hi + lo parts (about 16 significant bits),
+ * with fp32 accumulation.
  * ---------------------------------------------------------------------- */
 typedef struct {
   const float* q;          /* dev [B, n_h, d_h] fp32 */
@@ -186,6 +191,45 @@ lsa_status lsa_score_select(const lsa_score_layer* layers /* host [L] */, int32_
                             const int64_t* mask_word_offsets_host /* host [B+1] */,
                             int32_t n_h, int32_t d_h, lsa_dtype key_dtype, float threshold,
                             hipStream_t stream);
+
+/* lsa_score_select_ex: lsa_score_select with an explicit choice of launch
+ * variant, for tests and tuning. lsa_score_select is this call with
+ * options == NULL, which means every field 0. Results agree with
+ * lsa_score_select's to the precision stated there; masks outside rounding of
+ * the threshold are identical.
+ *   kernel       LSA_SCORE_KERNEL_AUTO (0): one wave per 32-entry tile for bf16
+ *                and fp8 keys, the wave-pair kernel for fp32 keys;
+ *                LSA_SCORE_KERNEL_STREAM (1): one wave per tile (bf16 keys with
+ *                d_h 32/64/128, fp8 keys with d_h 64/128; else
+ *                LSA_ERR_UNSUPPORTED); LSA_SCORE_KERNEL_PAIRS (2): two waves
+ *                share each tile (every key dtype).
+ *   chunk_words  mask words (64 entries each) a wave takes at a time in the
+ *                one-wave-per-tile kernel: 0 (default, 4) or 2..64.
+ *   ring         LDS ring depth of that kernel in half tiles: 0 (default), 4,
+ *                or 8 (8 only for rows of at most 128 bytes).
+ *   guard        1 (one-wave-per-tile kernel, masks only): score each 32-entry
+ *                tile with the bf16 hi part of q alone first, and complete
+ *                with the lo part only the tiles in which some entry's logit
+ *                lies within a computed bound of the threshold (the bound
+ *                covers everything the lo part can change), so every decision
+ *                equals the full computation's. Ignored when a layer asks for
+ *                scores. 0 (default): every tile with hi + lo.
+ * Other values return LSA_ERR_INVALID_ARG. */
+enum { LSA_SCORE_KERNEL_AUTO = 0, LSA_SCORE_KERNEL_STREAM = 1, LSA_SCORE_KERNEL_PAIRS = 2 };
+typedef struct {
+  int32_t kernel;
+  int32_t chunk_words;
+  int32_t ring;
+  int32_t guard;
+} lsa_score_options;
+
+lsa_status lsa_score_select_ex(const lsa_score_layer* layers /* host [L] */, int32_t L, int32_t B,
+                               const int64_t* key_offsets /* dev [B+1] */,
+                               const int64_t* key_offsets_host /* host [B+1] */,
+                               const int64_t* mask_word_offsets /* dev [B+1] */,
+                               const int64_t* mask_word_offsets_host /* host [B+1] */,
+                               int32_t n_h, int32_t d_h, lsa_dtype key_dtype, float threshold,
+                               const lsa_score_options* options /* host, or NULL */, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * lsa_union_compact: OR-mode routing over the indexer layers. Entry s is
@@ -223,9 +267,13 @@ lsa_status lsa_union_compact(const uint64_t* const* masks /* host [L] of dev poi
  * lsa_union_compact writes.
  *
  * The workspace must hold at least lsa_topk_workspace_size(...) bytes of
- * device memory. Its contents on entry do not matter. It holds the subset
- * scores, one fp32 per (layer, row). Supported: 1 <= k <= 65536; B <= 4096;
- * the key dtypes and head shapes of lsa_score_select.
+ * device memory, 256-byte aligned. Its contents on entry do not matter. It
+ * holds the subset scores, one fp32 per (layer, row), and per (layer,
+ * sequence) a 2048-bin count of the scores by their top 11 bits (sign,
+ * exponent and two mantissa bits of an order-preserving key), which the
+ * selection uses to find the k-th score's bin without sampling. Supported:
+ * 1 <= k <= 65536; B <= 4096; the key dtypes and head shapes of
+ * lsa_score_select.
  * ---------------------------------------------------------------------- */
 typedef struct {
   const float* q;          /* dev [B, n_h, d_h] fp32 (native query q') */
@@ -267,6 +315,33 @@ lsa_status lsa_topk_select(const lsa_topk_layer* layers /* host [L] */, int32_t 
                            const int32_t* idx /* dev [rows] */, const int32_t* count /* dev [B] */,
                            int32_t k, int32_t* topk_count_out /* dev [L, B] */, void* workspace /* dev */,
                            size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * lsa_topk_step: the native indexer's top-k at one decode step, over the
+ * subset that is already resident ([BLOG] §3.2: the memory indexer loads
+ * C^MemComp once per trigger, and inside it the native Lightning Indexer
+ * selects its top-k at every decode step; [HYPER] 方法).
+ *
+ * Same result and arguments as lsa_topk, except that each layer's `keys`
+ * points to that layer's subset keys packed in list order: row
+ * P_b + i is the key of list entry i of sequence b, where
+ * P_b = count[0] + ... + count[b-1] (lsa_gather in packed mode, with the
+ * layer's key array as the pool, row_bytes = d_h times the key size, and the
+ * union lists, writes exactly this). The packed rows are read contiguously,
+ * with no index load before them. For fp8 keys, key_scale is still the full
+ * per-entry scale array of the layer ([rows], read through the lists). q and
+ * w are the step's native query and gates. Call it once per decode step; the
+ * lists, counts and packed keys stay the same over the steps of a trigger.
+ * Supported: as lsa_topk, with B <= 1024 and at most 2^31 - 1 list entries
+ * over all sequences. The workspace is lsa_topk_workspace_size(L, B, rows, k).
+ * ---------------------------------------------------------------------- */
+lsa_status lsa_topk_step(const lsa_topk_layer* layers /* host [L]; keys = packed subset keys */, int32_t L,
+                         int32_t B, const int64_t* key_offsets /* dev [B+1] */,
+                         const int64_t* key_offsets_host /* host [B+1] */,
+                         const int32_t* idx /* dev [rows] */, const int32_t* count /* dev [B] */,
+                         int32_t n_h, int32_t d_h, lsa_dtype key_dtype, int32_t k,
+                         int32_t* topk_count_out /* dev [L, B] */, void* workspace /* dev */,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * lsa_gather: load the selected entries' compressed-KV rows into a compact

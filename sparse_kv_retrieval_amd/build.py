@@ -13,6 +13,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["score.hip", "score_stream.hip", "union.hip", "topk.hip", "gather.hip", "project.hip", "golden.hip", "train.hip", "lsa_api.hip"]
 OUT = os.path.join(HERE, "liblsa.so")
+# the streaming-read reference of the rooflines: a separate library, not part of lsa.h
+PROBE_SOURCE = "probe.hip"
+PROBE_OUT = os.path.join(HERE, "libprobe.so")
 
 BUILD_DIR = os.path.join(HERE, "_build")
 HIPCC_FLAGS = [
@@ -49,10 +52,44 @@ def build(verbose: bool = False) -> str:
     _run([[hipcc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(s, []), *inc, "-c", os.path.join(HERE, "csrc", s), "-o", o]
           for s, o in zip(SOURCES, objs)], verbose)
     tmp = OUT + ".tmp"
-    _run([[hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]], verbose)
+    ptmp = PROBE_OUT + ".tmp"
+    _run([[hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
+          [hipcc, *HIPCC_FLAGS, "-shared", os.path.join(HERE, "csrc", PROBE_SOURCE), "-o", ptmp]], verbose)
     os.replace(tmp, OUT)
+    os.replace(ptmp, PROBE_OUT)
     return OUT
+
+
+# Host-side sanitizers for the C-ABI validation layer: lsa_api.hip with AddressSanitizer and
+# UndefinedBehaviorSanitizer on its host code only (the GPU code is built as usual), linked with
+# the kernel objects into a separate copy of the package. Only a CPU test loads it, with the
+# sanitizer runtime preloaded; the product library is untouched.
+SAN_DIR = os.path.join(BUILD_DIR, "san")
+SAN_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized_host(verbose: bool = False) -> str:
+    """Build <SAN_DIR>/sparse_kv_retrieval_amd (liblsa.so with a sanitized host layer, and the binding)."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objs = [os.path.join(BUILD_DIR, s.replace(".hip", ".o")) for s in SOURCES if s != "lsa_api.hip"]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    pkg = os.path.join(SAN_DIR, "sparse_kv_retrieval_amd")
+    os.makedirs(pkg, exist_ok=True)
+    api = os.path.join(SAN_DIR, "lsa_api_san.o")
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + SAN_FLAGS
+    _run([[hipcc, *flags, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(HERE, "csrc", "lsa_api.hip"),
+           "-o", api]], verbose)
+    _run([[hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, api, "-o", os.path.join(pkg, "liblsa.so")]],
+         verbose)
+    for f in ("__init__.py", "lsa.py"):
+        with open(os.path.join(HERE, f), "rb") as src, open(os.path.join(pkg, f), "wb") as dst:
+            dst.write(src.read())
+    return pkg
 
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    if "--sanitized-host" in sys.argv:
+        print(build_sanitized_host(verbose=True))

@@ -43,6 +43,13 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// c + a.lo * b.lo + a.hi * b.hi for two packed bfloat16 pairs (v_dot2_f32_bf16).
+// bf16 products are exact in fp32; the sum rounds once or twice.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 // ------------------------------------------------------------- e4m3fn -> bf16
 // Widening of 4 OCP e4m3fn bytes (one dword) to 4 bfloat16 values (two
 // dwords, byte i -> element i) with the gfx950 conversion instruction

@@ -14,32 +14,35 @@
 // uint32 image of the crossing entry's logit) and an index cut such that an
 // entry is kept iff key > T, or key == T and index <= cut.
 //
-// Kernel 1, one 512-thread block per (token, layer) row, three blocks per CU.
+// Four kernels, in order:
 //
-// Pass F reads the row from HBM once. Each lane keeps online softmax
-// statistics of its entries (its maximum m and sum s of exp(y - m), in fp64),
-// and the block keeps in LDS a list of every entry whose key is at or above a
-// filter key tau. The first filter is the smallest of the waves' 4th largest
-// lane maxima over the first block chunk; whenever the list passes half its
-// capacity, a count histogram of it by value raises tau so that about a
-// quarter of the capacity stays, and the list is compacted. At the end the list holds every entry with key >=
-// tau, M and Z follow from the lanes' statistics, and if the list's mass at
-// or above tau reaches p * Z the nucleus lies inside it: a radix select by
-// mass over the list finds T (levels of 9, 9, 9 and 5 bits, fp64 weights),
-// the number of entries equal to T that are kept follows from their common
-// mass, and a count select over their indices finds the cut when not all of
-// them are. The row's mask is cleared and the kept entries' bits are set.
-//
-// Fallback, when the list overflowed or holds too little mass: a second read
-// builds a 4096-bin fp64 mass histogram over the top 12 key bits (LDS
-// atomics) and finds the crossing bin b1; a third read writes the mask bits of
-// the entries above b1 and lists the entries of b1; levels of 9, 9 and 2 bits
-// over that list (or over the row, if it does not fit) find T, and the kept entries
-// of b1 are OR-ed into the mask (or, when b1 did not fit, a last read rewrites
-// the whole mask).
-//
-// Kernel 2 (vote and union): per (token, mask word), a bit-sliced count of the
-// layers' mask bits, compared with theta, and OR-ed over the window's tokens.
+// 1. segment_kernel: one 512-thread block per segment (SEG entries) of a
+//    (token, layer) row. It reads the logits once. Each lane keeps online
+//    softmax statistics of its entries (its maximum m and the fp64 sum of
+//    exp(y - m)). Each wave keeps its own list of the entries whose key is at
+//    or above its filter, in its own LDS region, with a register count: pushes
+//    need no atomics and no barriers. The first filter is the smallest of the
+//    waves' second largest lane maxima over the first chunk; a wave whose list
+//    passes half its region keeps its largest keys and raises its filter. The
+//    segment's record (M, Z, the common filter, the entries at or above it)
+//    goes to the workspace.
+// 2. resolve_kernel: one 256-thread block per row. It merges the row's
+//    segment records into an LDS list (every entry at or above the largest of
+//    the segments' filters), buckets the list by distance below the row
+//    maximum (fp64 masses), finds the bucket where the running mass crosses p,
+//    ranks that bucket's entries exactly by (key descending, index ascending),
+//    walks their masses to the crossing, and writes the row's mask. A row it
+//    cannot finish that way (a list that overflowed or does not hold mass p, a
+//    crowded crossing bucket) is flagged in the workspace.
+// 3. fallback_kernel: one block per row; only flagged rows work. A second read
+//    builds a 4096-bin fp64 mass histogram over the top 12 key bits (LDS
+//    atomics) and finds the crossing bin; a third read writes the mask bits of
+//    the entries above it and lists the bin's entries; radix levels of 9, 9 and
+//    2 bits over that list (or over the row, when the bin does not fit) find T,
+//    and a count select over indices finds the cut among equal keys.
+// 4. vote_union_kernel: per (token, mask word), a bit-sliced count of the
+//    layers' mask bits in 7 bit planes, compared with theta plane by plane,
+//    and OR-ed over the window's tokens.
 #include <type_traits>
 
 #include "kernels.hpp"

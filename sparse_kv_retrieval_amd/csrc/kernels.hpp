@@ -5,6 +5,7 @@
 #include "common.hpp"
 
 #define LSA_TOPK_MAX_B 4096
+#define TOPK_CONTIG_MAX_B 1024  // sequences of one per-step top-k call over packed subset keys
 
 namespace lsa {
 
@@ -27,12 +28,20 @@ struct ScoreArgs {
   int32_t chunk_words;
 };
 
+// Histogram of the subset scores per (layer, sequence): bin = top TOPK_HBITS bits
+// of the order-preserving key of y. The scoring kernel fills it; the select
+// reads the k-th largest score's bin from it.
+constexpr int TOPK_HBITS = 11;
+constexpr int TOPK_BINS = 1 << TOPK_HBITS;
+
 struct TopkScoreArgs {
   const float* q[LSA_MAX_LAYERS];
   const float* w[LSA_MAX_LAYERS];
-  const void* keys[LSA_MAX_LAYERS];
+  const void* keys[LSA_MAX_LAYERS];     // full key arrays (gathered through idx), or
+  const void* sub_keys[LSA_MAX_LAYERS]; // the union rows packed in list order (contiguous mode)
   const float* scale[LSA_MAX_LAYERS];
   float* ys;                // workspace scores [L][rows_total]
+  uint32_t* hist;           // workspace [L][B][TOPK_BINS] counts (zeroed before the launch)
   const int32_t* idx;       // union lists, region b at key_off[b]
   const int32_t* count;     // [B]
   const int64_t* key_off;   // [B+1]
@@ -42,6 +51,7 @@ struct TopkScoreArgs {
 
 struct TopkSelectArgs {
   const float* ys;
+  const uint32_t* hist;     // the scoring kernel's histograms
   const int32_t* idx;
   const int32_t* count;
   const int64_t* key_off;
@@ -51,6 +61,13 @@ struct TopkSelectArgs {
   int64_t rows_total;
   int32_t B, k;
 };
+
+// Bytes of the top-k workspace: the scores [L][rows], then (256-byte aligned)
+// the histograms [L][B][TOPK_BINS].
+inline size_t topk_hist_offset(int L, int64_t rows) { return ((size_t)L * (size_t)rows * 4 + 255) & ~(size_t)255; }
+inline size_t topk_workspace_bytes(int L, int B, int64_t rows) {
+  return topk_hist_offset(L, rows) + (size_t)L * (size_t)B * TOPK_BINS * 4;
+}
 
 struct UnionArgs {
   const uint64_t* mask[LSA_MAX_LAYERS];
@@ -133,8 +150,12 @@ struct TrainArgs {
 hipError_t launch_score_select(const ScoreArgs& a, int key_kind, int d_h, int pairs, int depth, hipStream_t st);
 // one wave per tile, keys loaded straight into LDS (bf16 and fp8 keys)
 bool score_stream_supported(int key_kind, int d_h);
-hipError_t launch_score_stream(const ScoreArgs& a, int key_kind, int d_h, int waves, int ring, hipStream_t st);
-hipError_t launch_topk_score(const TopkScoreArgs& a, int key_kind, int d_h, int grid, int depth, hipStream_t st);
+// guard: the hi-only pass with a per-tile refine (no sigmoid scores)
+hipError_t launch_score_stream(const ScoreArgs& a, int key_kind, int d_h, int waves, int ring, bool guard,
+                               hipStream_t st);
+// contig: the keys come from sub_keys (packed union rows), else gathered through idx
+hipError_t launch_topk_score(const TopkScoreArgs& a, int key_kind, int d_h, int grid, bool contig, hipStream_t st);
+hipError_t launch_topk_hist_zero(uint32_t* hist, int64_t n, hipStream_t st);
 hipError_t launch_topk_select(const TopkSelectArgs& a, int L, hipStream_t st);
 hipError_t launch_union_compact(const UnionArgs& a, int B, int64_t max_words, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, int grid, int rows_per_wave, hipStream_t st);

@@ -5,7 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <cstdlib>
+#include <cstring>
 #include <string>
 
 #include "kernels.hpp"
@@ -44,12 +44,13 @@ int cu_count() {
   return cache[dev];
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  if (!v || !*v) return dflt;
-  const int x = std::atoi(v);
-  return x > 0 ? x : dflt;
-}
+// Launch shapes, measured on MI355X (see the design notes): fixed at compile time.
+constexpr int kScoreChunkWords = 4;    // mask words per chunk a score wave claims
+constexpr int kScorePairsPerCu = 4;    // pair kernel (fp32 keys): wave pairs per CU
+constexpr int kTopkPairsPerCu = 4;     // top-k scoring: wave pairs per CU
+constexpr int kGatherRows = 8;         // rows per wave in flight (HBM gather)
+constexpr int kFetchRows = 16;         // rows per wave in flight (host-pool fetch)
+constexpr int kCopyWavesPerCu = 16;    // waves per CU of the gather and the fetch
 
 // Checks an offsets mirror: off[0] >= 0 and non-decreasing. Also returns the total.
 lsa_status check_offsets(const int64_t* off_host, int32_t B, const char* name) {
@@ -83,12 +84,22 @@ lsa_status check_heads(int32_t n_h, int32_t d_h) {
   return LSA_OK;
 }
 
-lsa_status key_kind_of(lsa_dtype dt, int* kind) {
+// The integer a caller passed for a dtype. A C caller may pass any int, and reading a value
+// that names no enumerator as the enum type would be undefined behaviour in C++, so every entry
+// point takes the bits of its dtype argument first and works with the integer.
+static_assert(sizeof(lsa_dtype) == sizeof(int32_t), "lsa_dtype is an int");
+int32_t dtype_value(const lsa_dtype& d) {
+  int32_t v;
+  std::memcpy(&v, &d, sizeof v);
+  return v;
+}
+
+lsa_status key_kind_of(int32_t dt, int* kind) {
   switch (dt) {
     case LSA_F32: *kind = KEY_F32; return LSA_OK;
     case LSA_BF16: *kind = KEY_BF16; return LSA_OK;
     case LSA_FP8_E4M3: *kind = KEY_FP8; return LSA_OK;
-    default: return fail(LSA_ERR_UNSUPPORTED, "unknown key dtype %d", (int)dt);
+    default: return fail(LSA_ERR_UNSUPPORTED, "unknown key dtype %d", dt);
   }
 }
 
@@ -106,13 +117,16 @@ lsa_status check_key_bytes(int32_t B, const int64_t* key_offsets_host, int32_t d
 // The two stages of the top-k share their checks. Scoring needs the queries,
 // keys and key dtype; selection needs k and the outputs; both need the lists
 // and the workspace.
+// contig: the layers' `keys` are the union rows packed in list order (lsa_topk_step).
 lsa_status topk_stages(const lsa_topk_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
                        const int64_t* key_offsets_host, const int32_t* idx, const int32_t* count, int32_t n_h,
-                       int32_t d_h, lsa_dtype key_dtype, int32_t k, int32_t* topk_count_out, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream, bool do_score, bool do_select) {
+                       int32_t d_h, int32_t key_dtype, int32_t k, int32_t* topk_count_out, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, bool do_score, bool do_select,
+                       bool contig = false) {
   if (!layers) return fail(LSA_ERR_INVALID_ARG, "layers is NULL");
   if (L < 1 || L > LSA_MAX_LAYERS) return fail(LSA_ERR_INVALID_ARG, "L must be in [1, %d] (got %d)", LSA_MAX_LAYERS, L);
-  if (B < 1 || B > LSA_TOPK_MAX_B) return fail(LSA_ERR_UNSUPPORTED, "B must be in [1, %d] (got %d)", LSA_TOPK_MAX_B, B);
+  const int32_t max_b = contig ? TOPK_CONTIG_MAX_B : LSA_TOPK_MAX_B;
+  if (B < 1 || B > max_b) return fail(LSA_ERR_UNSUPPORTED, "B must be in [1, %d] (got %d)", max_b, B);
   if (!key_offsets) return fail(LSA_ERR_INVALID_ARG, "key_offsets is NULL");
   lsa_status s;
   if ((s = check_offsets(key_offsets_host, B, "key_offsets")) != LSA_OK) return s;
@@ -130,9 +144,12 @@ lsa_status topk_stages(const lsa_topk_layer* layers, int32_t L, int32_t B, const
   const int64_t rows = key_offsets_host[B];
   for (int32_t b = 0; b < B; ++b)
     if (key_offsets_host[b + 1] - key_offsets_host[b] > INT32_MAX) return fail(LSA_ERR_UNSUPPORTED, "sequence too long");
+  if (contig && rows - key_offsets_host[0] > INT32_MAX)
+    return fail(LSA_ERR_UNSUPPORTED, "the packed subset rows are counted in int32 (at most 2^31-1 rows in all)");
   const size_t need = lsa_topk_workspace_size(L, B, rows, do_select ? k : 1);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(LSA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(LSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   TopkScoreArgs sa{};
   TopkSelectArgs ta{};
   for (int l = 0; l < L; ++l) {
@@ -144,19 +161,26 @@ lsa_status topk_stages(const lsa_topk_layer* layers, int32_t L, int32_t B, const
       if (!aligned16(p.q) || !aligned16(p.keys)) return fail(LSA_ERR_INVALID_ARG, "layer %d: q and keys must be 16-byte aligned", l);
     }
     if (do_select && !p.topk_idx_out) return fail(LSA_ERR_INVALID_ARG, "layer %d: topk_idx_out must be set", l);
-    sa.q[l] = p.q; sa.w[l] = p.w; sa.keys[l] = p.keys; sa.scale[l] = p.key_scale;
+    sa.q[l] = p.q; sa.w[l] = p.w; sa.scale[l] = p.key_scale;
+    if (contig) sa.sub_keys[l] = p.keys; else sa.keys[l] = p.keys;
     ta.out_idx[l] = p.topk_idx_out; ta.out_score[l] = p.topk_score_out;
   }
-  sa.ys = (float*)workspace; sa.idx = idx; sa.count = count; sa.key_off = key_offsets; sa.rows_total = rows;
-  sa.B = B; sa.L = L; sa.n_h = n_h;
-  ta.ys = (const float*)workspace; ta.idx = idx; ta.count = count; ta.key_off = key_offsets;
+  uint32_t* hist = (uint32_t*)((char*)workspace + topk_hist_offset(L, rows));
+  sa.ys = (float*)workspace; sa.hist = hist; sa.idx = idx; sa.count = count; sa.key_off = key_offsets;
+  sa.rows_total = rows; sa.B = B; sa.L = L; sa.n_h = n_h;
+  ta.ys = (const float*)workspace; ta.hist = hist; ta.idx = idx; ta.count = count; ta.key_off = key_offsets;
   ta.out_count = topk_count_out; ta.rows_total = rows; ta.B = B; ta.k = k;
   hipError_t e;
+  if (do_score) {
+    // the histograms are counted by the scoring kernel, from zero
+    if ((e = launch_topk_hist_zero(hist, (int64_t)L * B * TOPK_BINS, stream)) != hipSuccess)
+      return hip_fail("lsa_topk histogram clear", e);
+  }
   if (do_score && rows > 0) {
     int64_t tiles = 0;
     for (int32_t b = 0; b < B; ++b) tiles += (key_offsets_host[b + 1] - key_offsets_host[b] + 31) / 32;
-    const int64_t pairs = std::max<int64_t>(1, std::min<int64_t>(tiles * L, (int64_t)cu_count() * env_int("LSA_TOPK_PAIRS_PER_CU", 4)));
-    if ((e = launch_topk_score(sa, kind, d_h, (int)pairs, env_int("LSA_TOPK_DEPTH", 0), stream)) != hipSuccess)
+    const int64_t pairs = std::max<int64_t>(1, std::min<int64_t>(tiles * L, (int64_t)cu_count() * kTopkPairsPerCu));
+    if ((e = launch_topk_score(sa, kind, d_h, (int)pairs, contig, stream)) != hipSuccess)
       return hip_fail("lsa_topk score launch", e);
   }
   if (do_select && (e = launch_topk_select(ta, L, stream)) != hipSuccess) return hip_fail("lsa_topk select launch", e);
@@ -172,7 +196,8 @@ const char* lsa_last_error(void) { return g_err.c_str(); }
 int32_t lsa_version(void) { return LSA_VERSION; }
 
 lsa_status lsa_project(const lsa_proj_layer* layers, int32_t L, int32_t B, int32_t d, int32_t r, int32_t n_h,
-                       int32_t d_h, lsa_dtype dtype, hipStream_t stream) {
+                       int32_t d_h, lsa_dtype dtype_arg, hipStream_t stream) {
+  const int32_t dtype = dtype_value(dtype_arg);
   if (!layers) return fail(LSA_ERR_INVALID_ARG, "layers is NULL");
   if (L < 1 || L > LSA_MAX_LAYERS) return fail(LSA_ERR_INVALID_ARG, "L must be in [1, %d] (got %d)", LSA_MAX_LAYERS, L);
   if (B < 1 || B > 128) return fail(LSA_ERR_UNSUPPORTED, "B must be in [1, 128] (got %d)", B);
@@ -244,10 +269,13 @@ lsa_status lsa_project_packed(const lsa_proj_layer* layers, int32_t L, int32_t B
   return e == hipSuccess ? LSA_OK : hip_fail("lsa_project_packed launch", e);
 }
 
-lsa_status lsa_score_select(const lsa_score_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
-                            const int64_t* key_offsets_host, const int64_t* mask_word_offsets,
-                            const int64_t* mask_word_offsets_host, int32_t n_h, int32_t d_h, lsa_dtype key_dtype,
-                            float threshold, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+lsa_status score_select_impl(const lsa_score_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
+                             const int64_t* key_offsets_host, const int64_t* mask_word_offsets,
+                             const int64_t* mask_word_offsets_host, int32_t n_h, int32_t d_h, int32_t key_dtype,
+                             float threshold, const lsa_score_options* options, hipStream_t stream) {
   if (!layers) return fail(LSA_ERR_INVALID_ARG, "layers is NULL");
   if (L < 1 || L > LSA_MAX_LAYERS) return fail(LSA_ERR_INVALID_ARG, "L must be in [1, %d] (got %d)", LSA_MAX_LAYERS, L);
   lsa_status s;
@@ -257,7 +285,22 @@ lsa_status lsa_score_select(const lsa_score_layer* layers, int32_t L, int32_t B,
   if ((s = key_kind_of(key_dtype, &kind)) != LSA_OK) return s;
   if ((s = check_key_bytes(B, key_offsets_host, d_h, kind)) != LSA_OK) return s;
   if (!(threshold > 0.0f && threshold < 1.0f)) return fail(LSA_ERR_INVALID_ARG, "threshold must lie in (0, 1)");
+  lsa_score_options opt{LSA_SCORE_KERNEL_AUTO, 0, 0, 0};
+  if (options) {
+    opt = *options;
+    if (opt.kernel < LSA_SCORE_KERNEL_AUTO || opt.kernel > LSA_SCORE_KERNEL_PAIRS)
+      return fail(LSA_ERR_INVALID_ARG, "options->kernel must be 0, 1 or 2 (got %d)", opt.kernel);
+    if (opt.chunk_words != 0 && (opt.chunk_words < 2 || opt.chunk_words > 64))
+      return fail(LSA_ERR_INVALID_ARG, "options->chunk_words must be 0 or in [2, 64] (got %d)", opt.chunk_words);
+    if (opt.ring != 0 && opt.ring != 4 && opt.ring != 8)
+      return fail(LSA_ERR_INVALID_ARG, "options->ring must be 0, 4 or 8 (got %d)", opt.ring);
+    if (opt.guard != 0 && opt.guard != 1) return fail(LSA_ERR_INVALID_ARG, "options->guard must be 0 or 1");
+  }
+  const bool stream_ok = score_stream_supported(kind, d_h);
+  if (opt.kernel == LSA_SCORE_KERNEL_STREAM && !stream_ok)
+    return fail(LSA_ERR_UNSUPPORTED, "the one-wave-per-tile kernel takes bf16 keys (d_h 32, 64, 128) or fp8 keys (d_h 64, 128)");
   ScoreArgs a{};
+  bool scores = false;
   for (int l = 0; l < L; ++l) {
     const lsa_score_layer& p = layers[l];
     if (!p.q || !p.w || !p.keys || !p.mask_out) return fail(LSA_ERR_INVALID_ARG, "layer %d: q, w, keys and mask_out must be set", l);
@@ -266,6 +309,7 @@ lsa_status lsa_score_select(const lsa_score_layer* layers, int32_t L, int32_t B,
     if (!aligned16(p.q) || !aligned16(p.keys)) return fail(LSA_ERR_INVALID_ARG, "layer %d: q and keys must be 16-byte aligned", l);
     a.q[l] = p.q; a.w[l] = p.w; a.keys[l] = p.keys; a.scale[l] = p.key_scale;
     a.mask[l] = p.mask_out; a.score[l] = p.score_out;
+    scores |= p.score_out != nullptr;
   }
   const double t = std::log((double)threshold / (1.0 - (double)threshold));
   a.key_off = key_offsets; a.mwo = mask_word_offsets;
@@ -274,21 +318,42 @@ lsa_status lsa_score_select(const lsa_score_layer* layers, int32_t L, int32_t B,
   a.total_words = a.words_per_layer * L;
   a.B = B; a.n_h = n_h; a.L = L; a.thr = (float)t;
   if (a.total_words == 0) return LSA_OK;
-  if (score_stream_supported(kind, d_h) && env_int("LSA_SCORE_PAIRS", 0) == 0) {
+  if (stream_ok && opt.kernel != LSA_SCORE_KERNEL_PAIRS) {
     // one block of 8 waves per CU, each block a contiguous run of mask words
     // that its waves take in chunks of a few words
-    a.chunk_words = std::max(2, env_int("LSA_SCORE_CHUNK", 4));
-    const int64_t waves = std::min<int64_t>((a.total_words + 7) / 8, (int64_t)cu_count() * env_int("LSA_SCORE_BLOCKS_PER_CU", 1));
+    a.chunk_words = opt.chunk_words ? opt.chunk_words : kScoreChunkWords;
+    const int64_t waves = std::min<int64_t>((a.total_words + 7) / 8, (int64_t)cu_count());
     a.group = 1;
-    const hipError_t e = launch_score_stream(a, kind, d_h, (int)waves, env_int("LSA_SCORE_RING", 0), stream);
+    // the hi-only first pass decides masks only; the sigmoid scores need the full pass everywhere
+    const bool guard = !scores && opt.guard;
+    const hipError_t e = launch_score_stream(a, kind, d_h, (int)waves, opt.ring, guard, stream);
     return e == hipSuccess ? LSA_OK : hip_fail("lsa_score_select launch", e);
   }
-  // One block per pair of waves. Groups of `group` pairs take interleaved words of a contiguous run.
-  int64_t pairs = std::min<int64_t>(a.total_words, (int64_t)cu_count() * env_int("LSA_SCORE_PAIRS_PER_CU", 4));
-  a.group = (int32_t)std::max<int64_t>(1, std::min<int64_t>(env_int("LSA_SCORE_GROUP", 1), pairs));
-  pairs = std::max<int64_t>(a.group, pairs / a.group * a.group);
-  const hipError_t e = launch_score_select(a, kind, d_h, (int)pairs, env_int("LSA_SCORE_DEPTH", 0), stream);
+  // One block per pair of waves over a contiguous run of words.
+  const int64_t pairs = std::min<int64_t>(a.total_words, (int64_t)cu_count() * kScorePairsPerCu);
+  a.group = 1;
+  const hipError_t e = launch_score_select(a, kind, d_h, (int)pairs, 0, stream);
   return e == hipSuccess ? LSA_OK : hip_fail("lsa_score_select launch", e);
+}
+
+}  // namespace
+
+extern "C" {
+
+lsa_status lsa_score_select_ex(const lsa_score_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
+                               const int64_t* key_offsets_host, const int64_t* mask_word_offsets,
+                               const int64_t* mask_word_offsets_host, int32_t n_h, int32_t d_h, lsa_dtype key_dtype,
+                               float threshold, const lsa_score_options* options, hipStream_t stream) {
+  return score_select_impl(layers, L, B, key_offsets, key_offsets_host, mask_word_offsets, mask_word_offsets_host,
+                           n_h, d_h, dtype_value(key_dtype), threshold, options, stream);
+}
+
+lsa_status lsa_score_select(const lsa_score_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
+                            const int64_t* key_offsets_host, const int64_t* mask_word_offsets,
+                            const int64_t* mask_word_offsets_host, int32_t n_h, int32_t d_h, lsa_dtype key_dtype,
+                            float threshold, hipStream_t stream) {
+  return score_select_impl(layers, L, B, key_offsets, key_offsets_host, mask_word_offsets, mask_word_offsets_host,
+                           n_h, d_h, dtype_value(key_dtype), threshold, nullptr, stream);
 }
 
 lsa_status lsa_union_compact(const uint64_t* const* masks, int32_t L, int32_t B, const int64_t* key_offsets,
@@ -315,24 +380,32 @@ lsa_status lsa_union_compact(const uint64_t* const* masks, int32_t L, int32_t B,
 }
 
 size_t lsa_topk_workspace_size(int32_t L, int32_t B, int64_t total_rows, int32_t k) {
-  (void)B; (void)k;
-  if (L < 1 || total_rows < 0) return 0;
-  return (size_t)L * (size_t)total_rows * sizeof(float);
+  (void)k;
+  if (L < 1 || B < 1 || total_rows < 0) return 0;
+  return topk_workspace_bytes(L, B, total_rows);
 }
 
 lsa_status lsa_topk(const lsa_topk_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
                     const int64_t* key_offsets_host, const int32_t* idx, const int32_t* count, int32_t n_h, int32_t d_h,
                     lsa_dtype key_dtype, int32_t k, int32_t* topk_count_out, void* workspace, size_t workspace_bytes,
                     hipStream_t stream) {
-  return topk_stages(layers, L, B, key_offsets, key_offsets_host, idx, count, n_h, d_h, key_dtype, k, topk_count_out,
-                     workspace, workspace_bytes, stream, true, true);
+  return topk_stages(layers, L, B, key_offsets, key_offsets_host, idx, count, n_h, d_h, dtype_value(key_dtype), k,
+                     topk_count_out, workspace, workspace_bytes, stream, true, true);
 }
 
 lsa_status lsa_topk_score(const lsa_topk_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
                           const int64_t* key_offsets_host, const int32_t* idx, const int32_t* count, int32_t n_h,
                           int32_t d_h, lsa_dtype key_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return topk_stages(layers, L, B, key_offsets, key_offsets_host, idx, count, n_h, d_h, key_dtype, 1, nullptr,
-                     workspace, workspace_bytes, stream, true, false);
+  return topk_stages(layers, L, B, key_offsets, key_offsets_host, idx, count, n_h, d_h, dtype_value(key_dtype), 1,
+                     nullptr, workspace, workspace_bytes, stream, true, false);
+}
+
+lsa_status lsa_topk_step(const lsa_topk_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
+                         const int64_t* key_offsets_host, const int32_t* idx, const int32_t* count, int32_t n_h,
+                         int32_t d_h, lsa_dtype key_dtype, int32_t k, int32_t* topk_count_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  return topk_stages(layers, L, B, key_offsets, key_offsets_host, idx, count, n_h, d_h, dtype_value(key_dtype), k,
+                     topk_count_out, workspace, workspace_bytes, stream, true, true, true);
 }
 
 lsa_status lsa_topk_select(const lsa_topk_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
@@ -379,11 +452,8 @@ lsa_status lsa_gather(const void* pool, int64_t row_bytes, int32_t B, const int6
                       const int64_t* pool_row_offsets_host, const int32_t* idx, const int64_t* idx_offsets,
                       const int32_t* count, void* out, const int64_t* out_row_offsets, int64_t out_capacity_rows,
                       hipStream_t stream) {
-  int rows = env_int("LSA_GATHER_ROWS", 8);
-  if (rows != 8 && rows != 16 && rows != 32) rows = 8;
   return gather_call("lsa_gather launch", pool, row_bytes, B, pool_row_offsets, pool_row_offsets_host, idx, idx_offsets,
-                     count, out, out_row_offsets, out_capacity_rows, rows,
-                     std::max(1, env_int("LSA_GATHER_WAVES_PER_CU", 16)), stream);
+                     count, out, out_row_offsets, out_capacity_rows, kGatherRows, kCopyWavesPerCu, stream);
 }
 
 lsa_status lsa_fetch_host(const void* pool_host, int64_t row_bytes, int32_t B, const int64_t* pool_row_offsets,
@@ -402,11 +472,8 @@ lsa_status lsa_fetch_host(const void* pool_host, int64_t row_bytes, int32_t B, c
   const char* dev_view = attr.hostPointer
                              ? (const char*)attr.devicePointer + ((const char*)pool_host - (const char*)attr.hostPointer)
                              : (const char*)attr.devicePointer;
-  int rows = env_int("LSA_FETCH_ROWS", 16);
-  if (rows != 8 && rows != 16 && rows != 32) rows = 16;
   return gather_call("lsa_fetch_host launch", dev_view, row_bytes, B, pool_row_offsets, pool_row_offsets_host, idx,
-                     idx_offsets, count, out, out_row_offsets, out_capacity_rows, rows,
-                     std::max(1, env_int("LSA_FETCH_WAVES_PER_CU", 16)), stream);
+                     idx_offsets, count, out, out_row_offsets, out_capacity_rows, kFetchRows, kCopyWavesPerCu, stream);
 }
 
 size_t lsa_golden_workspace_size(int32_t T, int32_t L, int64_t row_stride) {

@@ -9,6 +9,8 @@
 // when it crosses into another (layer, sequence). Each word is two 32-entry
 // MFMA tiles, and the wave ballot of the two tiles' selections is the 64-bit
 // mask word.
+#include <algorithm>
+
 #include "kernels.hpp"
 #include "scorer.hpp"
 #include "cursor.hpp"
@@ -296,54 +298,93 @@ struct TileCursor {
   int64_t base;       // first row of sequence b (also where its list starts)
   int32_t cnt;        // entries in b's list
   int32_t nrow;       // rows of sequence b
+  int32_t rbase;      // contiguous mode: first packed row of sequence b's list
   const char* keys;   // layer l's keys and fp8 scales (past the last layer: the last layer's, unused)
   const float* scale;
+  template <bool CONTIG>
   __device__ __forceinline__ void load_layer(const TopkScoreArgs& a) {
     const int ll = l < a.L ? l : a.L - 1;
-    keys = (const char*)a.keys[ll];
+    keys = (const char*)(CONTIG ? a.sub_keys[ll] : a.keys[ll]);
     scale = a.scale[ll];
   }
-  __device__ __forceinline__ void load_seq(const TopkScoreArgs& a, const int32_t* tp) {
+  __device__ __forceinline__ void load_seq(const TopkScoreArgs& a, const int32_t* tp, const int32_t* rp) {
     nt = uni(tp[b + 1]) - uni(tp[b]);
     base = uni(a.key_off[b]);
     nrow = (int32_t)(uni(a.key_off[b + 1]) - base);
     cnt = uni(a.count[b]);
+    rbase = rp ? uni(rp[b]) : 0;
   }
-  __device__ __forceinline__ void place(const TopkScoreArgs& a, const int32_t* tp, int64_t t) {
+  template <bool CONTIG>
+  __device__ __forceinline__ void place(const TopkScoreArgs& a, const int32_t* tp, const int32_t* rp, int64_t t) {
     const int64_t tpl = uni(tp[a.B]);
     l = uni((int32_t)(t / tpl));
     const int32_t tt = (int32_t)(t - (int64_t)l * tpl);
     b = uni(upper_seq(tp, a.B, tt));
     jt = tt - uni(tp[b]);
-    load_seq(a, tp);
-    load_layer(a);
+    load_seq(a, tp, rp);
+    load_layer<CONTIG>(a);
   }
-  __device__ __forceinline__ void next(const TopkScoreArgs& a, const int32_t* tp) {
+  template <bool CONTIG>
+  __device__ __forceinline__ void next(const TopkScoreArgs& a, const int32_t* tp, const int32_t* rp) {
     if (++jt < nt) return;
     jt = 0;
     do {
       if (++b == a.B) {
         b = 0;
         ++l;
-        load_layer(a);
+        load_layer<CONTIG>(a);
       }
     } while (uni(tp[b + 1]) == uni(tp[b]));
-    load_seq(a, tp);
+    load_seq(a, tp, rp);
   }
 };
 
-template <int KT, int DH, int D>
+// tp[b] = tiles of the lists before b, rp[b] = entries of the lists before b
+// (b = 0..B; the caller keeps the totals below 2^31).
+__device__ __forceinline__ void block_list_prefix(const int32_t* __restrict__ count, int B, int32_t* tp, int32_t* rp) {
+  const int nt = blockDim.x, tid = threadIdx.x;
+  const int per = (B + nt - 1) / nt;
+  const int lo = min(B, tid * per), hi = min(B, lo + per);
+  int64_t s = 0;
+  for (int b = lo; b < hi; ++b) s += ((int64_t)(count[b] + 31) >> 5) << 32 | (uint32_t)count[b];
+  int64_t tot;
+  int64_t run = block_exclusive_scan(s, &tot);  // tiles in the high word, entries in the low word
+  for (int b = lo; b < hi; ++b) {
+    tp[b] = (int32_t)(run >> 32);
+    rp[b] = (int32_t)(uint32_t)run;
+    run += ((int64_t)(count[b] + 31) >> 5) << 32 | (uint32_t)count[b];
+  }
+  if (tid == 0) {
+    tp[B] = (int32_t)(tot >> 32);
+    rp[B] = (int32_t)(uint32_t)tot;
+  }
+  __syncthreads();
+}
+
+// CONTIG: the keys of the lists are packed in list order in sub_keys (list
+// entry i of sequence b is row rp[b] + i), so every tile is 32 consecutive
+// rows and no index load precedes the key loads (fp8 scales are still read
+// through the list from the full scale array). Used for the per-step top-k
+// over the resident subset. At most TOPK_CONTIG_MAX_B sequences.
+template <int KT, int DH, int D, bool CONTIG>
 __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) {
   using IO = TileIO<KT, DH>;
   using S_t = Scorer<KT == KEY_F32 ? KEY_F32 : KEY_BF16, DH, 1, TileIO<KT, DH>::ROT>;
   static_assert(IO::GRB == 16 * (IO::GRB / 16), "row size");
+  constexpr int MAXB = CONTIG ? TOPK_CONTIG_MAX_B : LSA_TOPK_MAX_B;
   __shared__ __attribute__((aligned(16))) char stage[2][IO::LSUB];
   __shared__ float xpart[2][32];
-  __shared__ int32_t tp[LSA_TOPK_MAX_B + 1];
+  __shared__ int32_t tp[MAXB + 1];
+  __shared__ int32_t rps[CONTIG ? MAXB + 1 : 1];
+  // this block's counts for the histogram of one (layer, sequence): two 16-bit bins per word
+  __shared__ uint32_t lh[TOPK_BINS / 2];
+  const int32_t* rp = CONTIG ? rps : nullptr;
+  for (int i = threadIdx.x; i < TOPK_BINS / 2; i += blockDim.x) lh[i] = 0u;
 
   const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
   const int h = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  block_tile_prefix(a.count, a.B, tp);
+  if constexpr (CONTIG) block_list_prefix(a.count, a.B, tp, rps);
+  else block_tile_prefix(a.count, a.B, tp);
   const int64_t total = (int64_t)tp[a.B] * a.L;
   const int64_t np = gridDim.x;
   const int64_t t0 = (int64_t)blockIdx.x * total / np;
@@ -366,7 +407,7 @@ __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) 
   int32_t IX[2 * D][IO::NLW];  // list entries of the rows this lane loads, 2D tiles deep
   int32_t IXS[2 * D];          // (fp8) list entry of row n, for the scale
   TileCursor xc, ic, cc;       // index, key and compute cursors
-  xc.place(a, tp, t0);
+  xc.place<CONTIG>(a, tp, rp, t0);
   ic = xc;
   cc = xc;
 
@@ -379,23 +420,33 @@ __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) 
     const bool live_ = (LIVE);                                                                 \
     const uint32_t e_ = (uint32_t)xc.jt * 32;                                                  \
     const auto ri_ = buf_rsrc(a.idx + xc.base, (uint32_t)xc.cnt * 4);                          \
-    _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i)                                        \
-      IX[SLOT][i] = (int32_t)buf_load4(ri_, live_ ? (e_ + lrow[i]) * 4 : BUF_OOB);             \
+    if constexpr (!CONTIG) {                                                                   \
+      _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i)                                      \
+        IX[SLOT][i] = (int32_t)buf_load4(ri_, live_ ? (e_ + lrow[i]) * 4 : BUF_OOB);           \
+    }                                                                                          \
     if constexpr (KT == KEY_FP8) IXS[SLOT] = (int32_t)buf_load4(ri_, live_ ? (e_ + n) * 4 : BUF_OOB); \
-    if (live_) xc.next(a, tp);                                                                 \
+    if (live_) xc.next<CONTIG>(a, tp, rp);                                                     \
   } while (0)
 #define LSA_LOAD_KEYS(SLOT, XSLOT, LIVE)                                                       \
   do {                                                                                         \
     const bool live_ = (LIVE);                                                                 \
-    const auto rk_ = buf_rsrc(ic.keys + ic.base * IO::GRB, (uint32_t)ic.nrow * IO::GRB);          \
-    _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i)                                        \
-      R[SLOT][i] = buf_load16_nt(                                                              \
-          rk_, live_ && loads ? (uint32_t)IX[XSLOT][i] * IO::GRB + lchunk[i] * 16 : BUF_OOB);   \
+    if constexpr (CONTIG) {                                                                    \
+      const auto rk_ = buf_rsrc(ic.keys + (int64_t)ic.rbase * IO::GRB, (uint32_t)ic.cnt * IO::GRB); \
+      const uint32_t e_ = (uint32_t)ic.jt * 32;                                                \
+      _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i)                                      \
+        R[SLOT][i] = buf_load16_nt(                                                            \
+            rk_, live_ && loads ? (e_ + lrow[i]) * IO::GRB + lchunk[i] * 16 : BUF_OOB);        \
+    } else {                                                                                   \
+      const auto rk_ = buf_rsrc(ic.keys + ic.base * IO::GRB, (uint32_t)ic.nrow * IO::GRB);     \
+      _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i)                                      \
+        R[SLOT][i] = buf_load16_nt(                                                            \
+            rk_, live_ && loads ? (uint32_t)IX[XSLOT][i] * IO::GRB + lchunk[i] * 16 : BUF_OOB); \
+    }                                                                                          \
     if constexpr (KT == KEY_FP8) {                                                             \
       const auto rs_ = buf_rsrc(ic.scale + ic.base, (uint32_t)ic.nrow * 4);                    \
       SC[SLOT] = __uint_as_float(buf_load4(rs_, live_ ? (uint32_t)IXS[XSLOT] * 4 : BUF_OOB));  \
     }                                                                                          \
-    if (live_) ic.next(a, tp);                                                                 \
+    if (live_) ic.next<CONTIG>(a, tp, rp);                                                     \
   } while (0)
 
   // prologue: indices for tiles 0 .. 2D-1 and keys for tiles 0 .. D-1, issued
@@ -418,6 +469,40 @@ __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) 
   float pprev = 0.0f;
   bool vprev = false;
   int64_t oprev = 0;
+  int64_t hprev = 0;  // histogram of the previous tile's (layer, sequence)
+  // Wave 0 writes every score and counts it in lh, the block's histogram of the current
+  // (layer, sequence) hcur. The counts go to the global histogram (non-zero bins, one
+  // atomic each) when the (layer, sequence) changes, before a 16-bit count could
+  // overflow, and at the end: far fewer global atomics than one per score, which would
+  // serialise on the few bins that hold most scores.
+  int64_t hcur = -1;
+  uint32_t since = 0;  // scores counted in lh since its last flush (at most 65535 per bin)
+  auto flush = [&]() {
+    if (hcur >= 0 && a.hist) {
+      for (int i = lane; i < TOPK_BINS / 2; i += 64) {
+        const uint32_t v = lh[i];
+        if (v) {
+          if (v & 0xFFFFu) atomicAdd(a.hist + hcur + 2 * i, v & 0xFFFFu);
+          if (v >> 16) atomicAdd(a.hist + hcur + 2 * i + 1, v >> 16);
+          lh[i] = 0u;
+        }
+      }
+    }
+    since = 0;
+  };
+  // wave 0, every lane: the score of list position o when `on`, in (layer, sequence) hb
+  auto put = [&](bool on, int64_t o, int64_t hb, float y) {
+    if (hb != hcur || since > 65535u - 64u) {  // uniform
+      flush();
+      hcur = hb;
+    }
+    since += (uint32_t)__popcll(__ballot(on));
+    if (on) {
+      a.ys[o] = y;
+      const uint32_t bin = order_key(y) >> (32 - TOPK_HBITS);
+      atomicAdd(&lh[bin >> 1], 1u << (16 * (bin & 1)));
+    }
+  };
 
   // Whole groups of 2D slots, no early exit (see score_select): a slot past the
   // last tile only issues its out-of-range refills.
@@ -455,7 +540,7 @@ __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) 
       S.read_keys_lds(st);
       if (h == 0 && j > 0) {
         const float y = pprev + xpart[(j - 1) & 1][n];
-        if (g == 0 && vprev) a.ys[oprev] = y;
+        put(g == 0 && vprev, oprev, hprev, y);
       }
       if (cc.l != cur_l || cc.b != cur_b) {
         S.load_query(a.q[cc.l], a.w[cc.l], cc.b, a.n_h, 32 * h);
@@ -474,8 +559,9 @@ __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) 
         pprev = p;
         vprev = e < cc.cnt;
         oprev = (int64_t)cc.l * a.rows_total + cc.base + e;
+        hprev = ((int64_t)cc.l * a.B + cc.b) * TOPK_BINS;
       }
-      cc.next(a, tp);
+      cc.next<CONTIG>(a, tp, rp);
     }
   }
 #undef LSA_LOAD_IDX
@@ -483,8 +569,20 @@ __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) 
   lds_barrier();
   if (h == 0) {
     const float y = pprev + xpart[(J - 1) & 1][n];
-    if (g == 0 && vprev) a.ys[oprev] = y;
+    put(g == 0 && vprev, oprev, hprev, y);
+    flush();
   }
+}
+
+__global__ void topk_hist_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+hipError_t launch_topk_hist_zero(uint32_t* hist, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(topk_hist_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, hist, n);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ launch
@@ -509,23 +607,14 @@ static hipError_t launch_score_t(const ScoreArgs& a, int pairs, int depth, hipSt
   }
   return launch_score_d<KT, DH, DDEF>(a, pairs, st);
 }
-template <int KT, int DH, int D>
-static hipError_t launch_tscore_d(const TopkScoreArgs& a, int pairs, hipStream_t st) {
-  hipLaunchKernelGGL((topk_score_kernel<KT, DH, D>), dim3(pairs), dim3(128), 0, st, a);
-  return hipGetLastError();
-}
 template <int KT, int DH>
-static hipError_t launch_tscore_t(const TopkScoreArgs& a, int pairs, int depth, hipStream_t st) {
-  constexpr int DDEF = TileIO<KT, DH>::GSUB >= 8192 ? 2 : 4;
-  if constexpr (DH == 128) {
-    switch (depth) {
-      case 1: return launch_tscore_d<KT, DH, 1>(a, pairs, st);
-      case 2: return launch_tscore_d<KT, DH, 2>(a, pairs, st);
-      case 4: return launch_tscore_d<KT, DH, 4>(a, pairs, st);
-      default: break;
-    }
-  }
-  return launch_tscore_d<KT, DH, DDEF>(a, pairs, st);
+static hipError_t launch_tscore_t(const TopkScoreArgs& a, int pairs, bool contig, hipStream_t st) {
+  constexpr int D = TileIO<KT, DH>::GSUB >= 8192 ? 2 : 4;  // about 16 KiB of key loads in flight per wave pair
+  if (contig)
+    hipLaunchKernelGGL((topk_score_kernel<KT, DH, D, true>), dim3(pairs), dim3(128), 0, st, a);
+  else
+    hipLaunchKernelGGL((topk_score_kernel<KT, DH, D, false>), dim3(pairs), dim3(128), 0, st, a);
+  return hipGetLastError();
 }
 
 #define LSA_DISPATCH(FN, KT_, DH_, ...)                                                   \
@@ -549,8 +638,8 @@ hipError_t launch_score_select(const ScoreArgs& a, int key_kind, int d_h, int pa
   LSA_DISPATCH(launch_score_t, key_kind, d_h, a, pairs, depth, st);
 }
 
-hipError_t launch_topk_score(const TopkScoreArgs& a, int key_kind, int d_h, int grid, int depth, hipStream_t st) {
-  LSA_DISPATCH(launch_tscore_t, key_kind, d_h, a, grid, depth, st);
+hipError_t launch_topk_score(const TopkScoreArgs& a, int key_kind, int d_h, int grid, bool contig, hipStream_t st) {
+  LSA_DISPATCH(launch_tscore_t, key_kind, d_h, a, grid, contig, st);
 }
 
 }  // namespace lsa

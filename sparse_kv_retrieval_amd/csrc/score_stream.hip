@@ -10,8 +10,9 @@
 //  - Keys go from HBM straight into LDS (buffer_load ... lds). No registers
 //    hold keys in flight, and no instruction copies them into LDS.
 //  - The LDS holds a ring of RU half tiles (16 key rows each). A tile is two
-//    consecutive half tiles; while the wave scores tile j, the loads of the
-//    next RU - 2 half tiles are in flight.
+//    consecutive half tiles. As soon as the wave has read tile j out of LDS,
+//    it issues the loads of tile j + RU/2 into the slots tile j leaves, so
+//    while it scores tile j the loads of the next RU/2 tiles are in flight.
 //
 // A block is the WPB waves of one CU. It owns a contiguous run of mask words
 // (64 entries, two tiles each), cut into chunks of a few words, and its waves
@@ -109,6 +110,19 @@ __device__ __forceinline__ void lds_read_tile(u32x4 (&r)[N], const uint32_t (&ad
 }
 #undef LSA_RD
 
+// MFMA B operand of k-step s from a lane's half row read out of LDS: bf16 keys
+// as they are; fp8 keys (half (s & 1) of chunk s / 2) widened exactly to bf16.
+template <int KT, int NCH>
+__device__ __forceinline__ bf16x8 key_step_t(const u32x4 (&kr)[NCH], int s) {
+  if constexpr (KT == KEY_BF16) {
+    return as_bf16x8(kr[s]);
+  } else {
+    const u32x4& c = kr[s >> 1];
+    const u32x2 lo = e4m3x4_to_bf16x4(c[2 * (s & 1)]), hi = e4m3x4_to_bf16x4(c[2 * (s & 1) + 1]);
+    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+  }
+}
+
 // Atomic increment of an LDS counter, returning the old value. From an asm
 // block for the same reason as the reads above (a plain LDS atomic would
 // first wait for every load in flight); the block waits for its own result.
@@ -119,7 +133,17 @@ __device__ __forceinline__ uint32_t lds_fetch_inc(uint32_t addr) {
   return old;
 }
 
-template <int KT, int DH, int NHB, int RU, int WPB>
+// GUARD: the guard-band variant. Every tile first runs the MFMAs with the bf16 hi
+// part of the query alone (half the matrix work) and forms x_hi. The entries
+// whose decision x_hi >= thr the lo part could still change are those with
+// |x_hi - thr| <= C ||K_s|| (Scorer::guard_c2 gives C^2; ||K_s||^2 comes from
+// bf16 dot products of the key with itself, on the operands the MFMAs read).
+// If any entry of the tile is that close, the wave re-reads the tile from LDS
+// (this variant refills the tile's ring slots only after that) and adds the lo-part
+// MFMAs to the same accumulators, which is the full computation. Otherwise
+// every decision of the tile is already the full computation's. Not used when
+// the sigmoid score is written: scores need the full precision everywhere.
+template <int KT, int DH, int NHB, int RU, int WPB, bool GUARD>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void score_stream_kernel(const ScoreArgs a) {
   static_assert(KT == KEY_BF16 || KT == KEY_FP8, "bf16 or fp8 keys");
@@ -135,7 +159,7 @@ void score_stream_kernel(const ScoreArgs a) {
   constexpr int STEPS = DH / 16;         // MFMA k-steps per head block
   using S_t = Scorer<KEY_BF16, DH, NHB>;
 
-  __shared__ __attribute__((aligned(1024))) char rings[WPB][RU][UNIT];
+  __shared__ __attribute__((aligned(1024))) char rings[WPB][RU][UNIT];  // slots 1 KiB aligned
   __shared__ float srings[WPB][KT == KEY_FP8 ? RU : 1][64];
   __shared__ uint32_t next_chunk;
 
@@ -144,13 +168,14 @@ void score_stream_kernel(const ScoreArgs a) {
   char (&ring)[RU][UNIT] = rings[wv];
   float (&sring)[KT == KEY_FP8 ? RU : 1][64] = srings[wv];
   const SeqTab t(a.key_off, a.mwo);
+  const auto key_step = [](const u32x4 (&kr_)[NCH], int s_) { return key_step_t<KT, NCH>(kr_, s_); };
   if (threadIdx.x == 0) next_chunk = 0;
   __syncthreads();
 
   // this block's words, in chunks of CW words; the last chunk also takes the
   // remainder, so that every chunk a wave moves on to is longer than ic's
-  // lead over cc (at most three tiles, CW >= 2 words = 4 tiles) and ic never
-  // claims a second chunk while cc has yet to start the first
+  // lead over cc (RU/2 tiles; the launcher keeps 2 CW >= RU/2 + 1) and ic
+  // never claims a second chunk while cc has yet to start the first
   const int64_t nblk = gridDim.x;
   const int64_t bw0 = (int64_t)blockIdx.x * a.total_words / nblk;
   const int64_t bw1 = ((int64_t)blockIdx.x + 1) * a.total_words / nblk;
@@ -172,11 +197,17 @@ void score_stream_kernel(const ScoreArgs a) {
   if (first >= 0) {
     // Per-lane offsets: the HBM chunk each lane loads for LDS position
     // k*1024 + 16*lane, and where chunk i of this lane's half row sits in LDS.
-    uint32_t doff[NI], roff[NCH];
-#pragma unroll
-    for (int k = 0; k < NI; ++k) doff[k] = stream_swz(k * 1024 + lane * 16);
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) roff[i] = stream_swz((n & 15) * GRB + 16 * (g * NCH + i));
+    // Both are one register XOR-ed with a constant:
+    //  - load k: line 4k + lane/16, chunk lane % 16, so stream_swz(k*1024 +
+    //    16*lane) = doff0 ^ (k*1024 + k*64) for k < 4 (the bit fields do not
+    //    overlap);
+    //  - read i: rows never cross a 256-byte line (GRB divides 256) and chunk i
+    //    of the lane's half row sits at chunk-in-line p0 | i before the swizzle,
+    //    so its LDS offset is roff0 ^ 16*i. Ring slots are 256-byte aligned, so
+    //    the XOR also holds after the slot base is added.
+    static_assert(NI <= 4 && 256 % GRB == 0, "offset identities");
+    const uint32_t doff0 = stream_swz(lane * 16);
+    const uint32_t roff0 = stream_swz((n & 15) * GRB + 16 * (g * NCH));
 
     // ic: the half tiles being loaded (runs ahead); cc: the tile being scored.
     // ic always reaches the end of a chunk first; it claims the next chunk and
@@ -201,7 +232,7 @@ void score_stream_kernel(const ScoreArgs a) {
     const uint32_t nr_ = ic_live ? (uint32_t)uni(max(0, min(16, ic.nb - e_))) : 0u;              \
     const auto rk_ = buf_rsrc(ic.keys + (ic.row0 + e_) * GRB, nr_ * GRB);                         \
     _Pragma("unroll") for (int k = 0; k < NI; ++k)                                                \
-      dma_lds16(rk_, &ring[us][k * 1024], doff[k]);                                              \
+      dma_lds16(rk_, &ring[us][k * 1024], doff0 ^ (uint32_t)(k * 1088));                         \
     if constexpr (KT == KEY_FP8) {                                                                \
       const auto rs_ = buf_rsrc(ic.scale + ic.row0 + e_, nr_ * 4);                                \
       dma_lds4(rs_, &sring[us][0], lane * 4);                                                    \
@@ -227,53 +258,86 @@ void score_stream_kernel(const ScoreArgs a) {
   } while (0)
 
 #pragma unroll
-    for (int u = 0; u < RU - 2; ++u) LSA_ISSUE();
+    for (int u = 0; u < RU; ++u) LSA_ISSUE();
 
     S_t S;
     int cur_l = -1, cur_b = -1;
     uint32_t bits0 = 0;
+    float c2 = 0.0f;  // GUARD: C^2 of the current query
     for (int j = 0;; j ^= 1) {  // j: tile parity within the mask word
-      LSA_ISSUE();
-      LSA_ISSUE();
-      stream_vm_wait<(RU - 2) * IPU>();  // the current tile is in LDS
+      stream_vm_wait<(RU - 2) * IPU>();  // the current tile is in LDS (the next RU/2 - 1 tiles may be in flight)
       if (cc.l != cur_l || cc.b != cur_b) {
         S.load_query(a.q[cc.l], a.w[cc.l], cc.b, a.n_h, 0);
+        if constexpr (GUARD) c2 = S.guard_c2(a.w[cc.l], cc.b, a.n_h, 0);
         cur_l = cc.l;
         cur_b = cc.b;
       }
       const int c1 = cs + 1 == RU ? 0 : cs + 1;
       const int slot = n < 16 ? cs : c1;
-      const uint32_t base = lds_addr(&ring[0][0]) + slot * UNIT;
+      const uint32_t a0 = lds_addr(&ring[0][0]) + slot * UNIT + roff0;
       uint32_t ad[NCH];
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) ad[i] = base + roff[i];
+      for (int i = 0; i < NCH; ++i) ad[i] = a0 ^ (uint32_t)(16 * i);
       u32x4 kr[NCH];
       float scale = 1.0f;
       lds_read_tile<NCH, KT == KEY_FP8>(kr, ad, lds_addr(&sring[0][0]) + (slot * 64 + (n & 15)) * 4, scale);
+      // The reads have returned, so the tile's two ring slots are free: refill them with the tile
+      // RU/2 tiles ahead now, rather than at the next iteration, so that every tile's loads are
+      // in flight for RU/2 - 1 whole iterations. (The guard variant may read the tile again for
+      // its lo pass, so it refills the slots after that.)
+      if constexpr (!GUARD) {
+        LSA_ISSUE();
+        LSA_ISSUE();
+      }
       f32x16 acc[NHB];
 #pragma unroll
       for (int mb = 0; mb < NHB; ++mb) acc[mb] = f32x16{};
+      float kn0 = 0.0f, kn1 = 0.0f;  // GUARD: this lane's share of ||K_s||^2
 #pragma unroll
       for (int s = 0; s < STEPS; ++s) {
-        bf16x8 kb;
-        if constexpr (KT == KEY_BF16) {
-          kb = as_bf16x8(kr[s]);
-        } else {
-          // k-step s reads 8 fp8 values: half (s & 1) of chunk s / 2, widened exactly
-          const u32x4& c = kr[s >> 1];
-          const u32x2 lo = e4m3x4_to_bf16x4(c[2 * (s & 1)]), hi = e4m3x4_to_bf16x4(c[2 * (s & 1) + 1]);
-          kb = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        const bf16x8 kb = key_step(kr, s);
+        if constexpr (GUARD) {
+          const u32x4 kd = __builtin_bit_cast(u32x4, kb);
+          kn0 = dot2_bf16(kd[0], kd[0], kn0);
+          kn1 = dot2_bf16(kd[1], kd[1], kn1);
+          kn0 = dot2_bf16(kd[2], kd[2], kn0);
+          kn1 = dot2_bf16(kd[3], kd[3], kn1);
         }
 #pragma unroll
         for (int mb = 0; mb < NHB; ++mb) {
           acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(S.qa[mb][s][0], kb, acc[mb], 0, 0, 0);
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(S.qa[mb][s][1], kb, acc[mb], 0, 0, 0);
+          if constexpr (!GUARD) acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(S.qa[mb][s][1], kb, acc[mb], 0, 0, 0);
         }
       }
       float x = sum_halves(S.partial(acc));
       if constexpr (KT == KEY_FP8) x *= scale;
       const int32_t se = cc.e0 + j * 32 + n;
       const bool valid = se < cc.nb;
+      if constexpr (GUARD) {
+        // |x - x_hi| <= C ||K_s|| (times the scale for fp8). The 2^-118 floor keeps
+        // the bound above the lo part's effect when the squares of a tiny key
+        // underflow (every |K_i| < 2^-63 gives ||K_s|| < 2^-59).
+        const float kn2 = sum_halves(kn0 + kn1) + 0x1p-118f;
+        const float dlt = x - a.thr;
+        float lim = c2 * kn2;
+        if constexpr (KT == KEY_FP8) lim *= scale * scale;
+        if (__ballot(valid && dlt * dlt <= lim) != 0) {
+          u32x4 kr2[NCH];
+          float unused;
+          lds_read_tile<NCH, false>(kr2, ad, 0, unused);
+#pragma unroll
+          for (int s = 0; s < STEPS; ++s) {
+            const bf16x8 kb = key_step(kr2, s);
+#pragma unroll
+            for (int mb = 0; mb < NHB; ++mb)
+              acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(S.qa[mb][s][1], kb, acc[mb], 0, 0, 0);
+          }
+          x = sum_halves(S.partial(acc));
+          if constexpr (KT == KEY_FP8) x *= scale;
+        }
+        LSA_ISSUE();
+        LSA_ISSUE();
+      }
       const uint32_t bits = (uint32_t)__ballot(valid && x >= a.thr);
       if (cc.score != nullptr && g == 0 && valid) cc.score[cc.row0 + se] = 1.0f / (1.0f + __expf(-x));
       cs = c1 + 1 == RU ? 0 : c1 + 1;
@@ -300,24 +364,32 @@ void score_stream_kernel(const ScoreArgs a) {
 
 constexpr int STREAM_WPB = 8;  // waves per block: two per SIMD of one CU
 
-template <int KT, int DH, int NHB, int RU>
-static hipError_t launch_stream_r(const ScoreArgs& a, int blocks, hipStream_t st) {
-  hipLaunchKernelGGL((score_stream_kernel<KT, DH, NHB, RU, STREAM_WPB>), dim3(blocks), dim3(64 * STREAM_WPB), 0, st, a);
+template <int KT, int DH, int NHB, int RU, bool GUARD>
+static hipError_t launch_stream_r(const ScoreArgs& a0, int blocks, hipStream_t st) {
+  // chunks must be longer than the loading cursor's lead of RU/2 tiles (two tiles per word)
+  ScoreArgs a = a0;
+  a.chunk_words = a.chunk_words > RU / 4 + 1 ? a.chunk_words : RU / 4 + 1;
+  hipLaunchKernelGGL((score_stream_kernel<KT, DH, NHB, RU, STREAM_WPB, GUARD>), dim3(blocks), dim3(64 * STREAM_WPB), 0,
+                     st, a);
   return hipGetLastError();
 }
 
+template <int KT, int DH, int NHB, int RU>
+static hipError_t launch_stream_g(const ScoreArgs& a, int blocks, bool guard, hipStream_t st) {
+  return guard ? launch_stream_r<KT, DH, NHB, RU, true>(a, blocks, st) : launch_stream_r<KT, DH, NHB, RU, false>(a, blocks, st);
+}
+
 template <int KT, int DH, int NHB>
-static hipError_t launch_stream_h(const ScoreArgs& a, int waves, int ring, hipStream_t st) {
+static hipError_t launch_stream_h(const ScoreArgs& a, int waves, int ring, bool guard, hipStream_t st) {
   // default ring: the 8 waves of a block fit in a CU's 160 KiB of LDS
   constexpr int UNIT = 16 * DH * (KT == KEY_BF16 ? 2 : 1);
   constexpr int RDEF = UNIT >= 4096 ? 4 : 8;
   switch (ring) {
-    case 4: return launch_stream_r<KT, DH, NHB, 4>(a, waves, st);
-    case 6: if constexpr (UNIT <= 2048) return launch_stream_r<KT, DH, NHB, 6>(a, waves, st); break;
-    case 8: if constexpr (UNIT <= 2048) return launch_stream_r<KT, DH, NHB, 8>(a, waves, st); break;
+    case 4: return launch_stream_g<KT, DH, NHB, 4>(a, waves, guard, st);
+    case 8: if constexpr (UNIT <= 2048) return launch_stream_g<KT, DH, NHB, 8>(a, waves, guard, st); break;
     default: break;
   }
-  return launch_stream_r<KT, DH, NHB, RDEF>(a, waves, st);
+  return launch_stream_g<KT, DH, NHB, RDEF>(a, waves, guard, st);
 }
 
 bool score_stream_supported(int key_kind, int d_h) {
@@ -326,11 +398,12 @@ bool score_stream_supported(int key_kind, int d_h) {
   return false;
 }
 
-hipError_t launch_score_stream(const ScoreArgs& a, int key_kind, int d_h, int waves, int ring, hipStream_t st) {
+hipError_t launch_score_stream(const ScoreArgs& a, int key_kind, int d_h, int waves, int ring, bool guard,
+                               hipStream_t st) {
   const bool two = a.n_h > 32;
 #define LSA_STREAM_CASE(KT, DH)                                                         \
   if (key_kind == KT && d_h == DH)                                                      \
-    return two ? launch_stream_h<KT, DH, 2>(a, waves, ring, st) : launch_stream_h<KT, DH, 1>(a, waves, ring, st);
+    return two ? launch_stream_h<KT, DH, 2>(a, waves, ring, guard, st) : launch_stream_h<KT, DH, 1>(a, waves, ring, guard, st);
   LSA_STREAM_CASE(KEY_BF16, 128)
   LSA_STREAM_CASE(KEY_BF16, 64)
   LSA_STREAM_CASE(KEY_BF16, 32)

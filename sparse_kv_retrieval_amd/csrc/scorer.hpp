@@ -81,6 +81,48 @@ struct Scorer {
     }
   }
 
+  // Bound constant of the hi-only score (split query only). A pass that feeds the
+  // MFMAs the bf16 hi parts alone computes x_hi; the full pass adds the lo parts
+  // to the same accumulators and computes x. For every entry with key K_s,
+  //   |x - x_hi| <= sum_j |w_j| (||lo_j|| + 2^-13 ||q_j||) ||K_s|| = C ||K_s||:
+  // ReLU is 1-Lipschitz, |lo_j . K_s| <= ||lo_j|| ||K_s|| (Cauchy-Schwarz), and the
+  // fp32 rounding of both passes (at most 384 products per dot and 65 gated
+  // terms, u = 2^-24) stays below 2^-15 ||q_j|| ||K_s|| per head, which the
+  // 2^-13 ||q_j|| term covers four times over. Returns C^2, the same in every
+  // lane. Heads at or past n_h have q = 0 and w = 0 and add nothing.
+  __device__ __forceinline__ float guard_c2(const float* __restrict__ w, int b, int n_h, int head0 = 0) const {
+    static_assert(SPLIT, "the bound needs the split query");
+    const int lane = threadIdx.x & 63, n = lane & 31;
+    float c = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < NHB; ++mb) {
+      float sh = 0.0f, sl = 0.0f;
+#pragma unroll
+      for (int t = 0; t < STEPS; ++t) {
+        const u32x4 hv = __builtin_bit_cast(u32x4, qa[mb][t][0]);
+        const u32x4 lv = __builtin_bit_cast(u32x4, qa[mb][t][1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sh = dot2_bf16(hv[i], hv[i], sh);
+          sl = dot2_bf16(lv[i], lv[i], sl);
+        }
+      }
+      // lanes l and l ^ 32 hold the two halves of head (head0 + 32 mb + n)
+      sh = sum_halves(sh);
+      sl = sum_halves(sl);
+      const int head = head0 + mb * 32 + n;
+      const float wj = head < n_h ? fabsf(w[(int64_t)b * n_h + head]) : 0.0f;
+      // hi rounds each element of q to nearest, so ||q_j|| <= ||hi_j|| / (1 - 2^-9) < 1.0117 ||hi_j||
+      c += wj * (__builtin_sqrtf(sl) + 0x1.03p-13f * __builtin_sqrtf(sh));
+    }
+    // sum over the 32 heads of each block: every head is held twice (lanes n and n + 32)
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) c += __shfl_xor(c, o);
+    c *= 0.5f;
+    // the fp32 sums above round by a relative 2^-17 at most; the margin in the q term covers it
+    return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(c * c)));
+  }
+
   // Load this lane's half of one key row (row pointer already at the half).
   __device__ __forceinline__ void load_keys(const char* __restrict__ p, bool valid) {
 #pragma unroll

@@ -3,7 +3,8 @@
 // Indexer picks the final top-k core entries inside C^MemComp).
 //
 // One block per (sequence, layer). The scores y are in the workspace, in
-// subset order, which is ascending entry order. A radix select over
+// subset order, which is ascending entry order, with a histogram of their top
+// 11 key bits that the scoring kernel built. A radix select over
 // order-preserving uint32 keys finds T, the key of the k-th largest score, and
 // how many entries equal to T must be kept. The output keeps every entry above
 // T plus the lowest-index entries equal to it, in list order, which matches
@@ -125,8 +126,34 @@ __device__ __forceinline__ void table_exclusive_scan(uint32_t* tab, int n) {
 // per-(v, w) counts held in a small LDS table. One such scan ranks the entries
 // equal to T, which settles ties toward the lower index. A second one places
 // each kept entry at its ascending output position.
+//
+// With the scoring kernel's histogram (hist_bl, the 2048 counts of the list's
+// keys by their top 11 bits), T is found without the three radix passes: the
+// histogram gives the bin d of the k-th largest key and its rank inside the
+// bin; the keys of bin d (a few hundred, typically) are appended to an LDS
+// list while the scores are loaded; and one wave finds T among them bit by bit
+// (no barrier), or, for a crowded bin, the block runs the last two radix
+// levels on that list.
+__device__ __forceinline__ void lds_select(const uint32_t* keys, int n, uint32_t rank, uint32_t* hist,
+                                           uint32_t* sh_digit, uint32_t* sh_krem, uint32_t& T, uint32_t& krem,
+                                           int passes, int first_pass, uint32_t prefix);
+static constexpr int TS_CCAP = 4096;  // keys of the k-th bin held in LDS
+static constexpr int TS_WCAP = 512;   // at most this many: one wave finds T
+
+// LDS of the in-register select (one copy per block, whichever list length is instantiated)
+struct RegSelectSmem {
+  uint32_t hist[2048];
+  uint32_t tab[TS_VMAX * (TS_THREADS / 64)], tab2[TS_VMAX * (TS_THREADS / 64)];
+  uint32_t cand[TS_CCAP];
+  uint32_t sh_digit, sh_krem, ncand;
+};
+
+// VM: values per thread held in registers (the list has at most TS_THREADS * VM entries).
+template <int VM>
 __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys, const int32_t* __restrict__ idx,
-                                                    int32_t M, int32_t k, int32_t* out, float* outs) {
+                                                    int32_t M, int32_t k, int32_t* out, float* outs,
+                                                    const uint32_t* __restrict__ hist_bl, RegSelectSmem& sm) {
+  static_assert(VM % 8 == 0 && VM <= TS_VMAX, "values per thread");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   constexpr int NW = TS_THREADS / 64;
   const int V = (M + TS_THREADS - 1) / TS_THREADS;
@@ -134,9 +161,9 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
   // -inf, maps to 0x007FFFFF), so padding never reaches the selected bins or
   // the output, and the passes need no bounds test.
   // Loads go in chunks of 8 with clamped addresses, so each chunk is one round trip.
-  uint32_t key[TS_VMAX];
+  uint32_t key[VM];
 #pragma unroll
-  for (int c = 0; c < TS_VMAX; c += 8) {
+  for (int c = 0; c < VM; c += 8) {
     if (c < V) {
       float y[8];
 #pragma unroll
@@ -146,18 +173,83 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
     }
   }
 
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t tab[TS_VMAX * NW], tab2[TS_VMAX * NW];
-  __shared__ uint32_t sh_digit, sh_krem;
+  uint32_t* hist = sm.hist;
+  uint32_t* tab = sm.tab;
+  uint32_t* tab2 = sm.tab2;
+  uint32_t* cand = sm.cand;
+  uint32_t& sh_digit = sm.sh_digit;
+  uint32_t& sh_krem = sm.sh_krem;
+  uint32_t& ncand = sm.ncand;
   uint32_t prefix = 0, pmask = 0, krem = (uint32_t)k;
+  bool found = false;
+  if (hist_bl) {
+    for (int i = tid; i < 2048; i += TS_THREADS) hist[i] = hist_bl[i];
+    if (tid == 0) ncand = 0;
+    __syncthreads();
+    find_digit(hist, 2048, (uint32_t)k, &sh_digit, &sh_krem);
+    const uint32_t d = sh_digit, bin_rank = sh_krem, nd = hist[d];
+    if (nd <= (uint32_t)TS_CCAP) {  // uniform
+      // the keys of bin d, in any order (a wave-wide append per register)
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
+      for (int v = 0; v < VM; ++v)
+        if (v < V) {
+          const bool in = tid + TS_THREADS * v < M && (key[v] >> 21) == d;
+          const uint64_t m = __ballot(in);
+          if (m) {  // uniform
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&ncand, (uint32_t)__popcll(m));
+            base = __builtin_amdgcn_readfirstlane(base);
+            if (in) cand[base + lanes_below(m)] = key[v];
+          }
+        }
+      __syncthreads();
+      const uint32_t nc = ncand;
+      if (nc <= (uint32_t)TS_WCAP) {
+        if (w == 0) {
+          // the bin_rank-th largest of the nc keys, bit by bit below the bin's 11 bits
+          uint32_t kk[TS_WCAP / 64];
+#pragma unroll
+          for (int u = 0; u < TS_WCAP / 64; ++u) {
+            const uint32_t j = 64u * u + lane;
+            kk[u] = j < nc ? cand[j] : 0u;  // key 0 ranks below every value tried
+          }
+          uint32_t t = d << 21;
+          for (int b = 20; b >= 0; --b) {
+            const uint32_t c = t | (1u << b);
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int u = 0; u < TS_WCAP / 64; ++u) cnt += (uint32_t)__popcll(__ballot(kk[u] >= c));
+            if (cnt >= bin_rank) t = c;
+          }
+          uint32_t gt = 0;
+#pragma unroll
+          for (int u = 0; u < TS_WCAP / 64; ++u) gt += (uint32_t)__popcll(__ballot(kk[u] > t));
+          if (lane == 0) {
+            sh_digit = t;
+            sh_krem = bin_rank - gt;
+          }
+        }
+        __syncthreads();
+        prefix = sh_digit;
+        krem = sh_krem;
+      } else {
+        uint32_t Tb, kb;
+        lds_select(cand, (int)nc, bin_rank, hist, &sh_digit, &sh_krem, Tb, kb, 3, 1, d << 21);
+        prefix = Tb;
+        krem = kb;
+      }
+      found = true;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int pass = 0; pass < (found ? 0 : 3); ++pass) {
     const int sh = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const int nb = pass == 2 ? 1024 : 2048;
     for (int i = tid; i < 2048; i += TS_THREADS) hist[i] = 0;
     __syncthreads();
 #pragma unroll
-    for (int v = 0; v < TS_VMAX; ++v)
+    for (int v = 0; v < VM; ++v)
       if (v < V && (key[v] & pmask) == prefix) atomicAdd(&hist[(key[v] >> sh) & (nb - 1)], 1u);
     __syncthreads();
     find_digit(hist, nb, krem, &sh_digit, &sh_krem);
@@ -172,7 +264,7 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
   // tab holds per-(v, w) counts of entries equal to T, then their exclusive scan;
   // tab2 the same for kept entries.
 #pragma unroll
-  for (int v = 0; v < TS_VMAX; ++v)
+  for (int v = 0; v < VM; ++v)
     if (v < V) {
       const uint64_t m = __ballot(key[v] == T);
       if (lane == 0) tab[v * NW + w] = (uint32_t)__popcll(m);
@@ -180,7 +272,7 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
   __syncthreads();
   table_exclusive_scan(tab, V * NW);
 #pragma unroll
-  for (int v = 0; v < TS_VMAX; ++v)
+  for (int v = 0; v < VM; ++v)
     if (v < V) {
       const uint64_t meq = __ballot(key[v] == T);
       const bool take = key[v] > T || (key[v] == T && tab[v * NW + w] + lanes_below(meq) < krem);
@@ -191,7 +283,7 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
   table_exclusive_scan(tab2, V * NW);
   // output in chunks of 8: positions first, then all the loads, then all the stores
 #pragma unroll
-  for (int c = 0; c < TS_VMAX; c += 8) {
+  for (int c = 0; c < VM; c += 8) {
     if (c < V) {
       int32_t pos[8];
 #pragma unroll
@@ -215,7 +307,7 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (pos[u] >= 0) {
+        if (pos[u] >= 0 && pos[u] < k) {  // exactly k are taken; the bound only guards a mismatched workspace
           out[pos[u]] = iv[u];
           if (outs) outs[pos[u]] = yv[u];
         }
@@ -300,15 +392,16 @@ __device__ __forceinline__ void select_streaming(const float* __restrict__ ys, c
 // `rank` (the rest of those equal to T rank after them). Thread t handles
 // keys t, t + TS_THREADS, ...
 static constexpr int TS_FCAP = 4096;     // candidates kept after the filter
-static constexpr int TS_SAMPLE = 4096;   // sampled scores for the threshold estimate
 
+// With first_pass = 1 the top 11 bits are already known: prefix holds them and
+// only keys with those bits take part (rank counts among them).
 __device__ __forceinline__ void lds_select(const uint32_t* keys, int n, uint32_t rank, uint32_t* hist,
                                            uint32_t* sh_digit, uint32_t* sh_krem, uint32_t& T, uint32_t& krem,
-                                           int passes = 3) {
+                                           int passes, int first_pass, uint32_t prefix) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, pmask = 0;
+  uint32_t pmask = first_pass ? 0xFFE00000u : 0u;
   krem = rank;
-  for (int pass = 0; pass < passes; ++pass) {
+  for (int pass = first_pass; pass < passes; ++pass) {
     const int sh = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const int nb = pass == 2 ? 1024 : 2048;
     for (int i = tid; i < 2048; i += TS_THREADS) hist[i] = 0;
@@ -327,19 +420,19 @@ __device__ __forceinline__ void lds_select(const uint32_t* keys, int n, uint32_t
   T = prefix;
 }
 
-// Select through a threshold estimated from a sample. TS_SAMPLE scores at
-// evenly spaced list positions give t, the sample key of rank
-// r = ceil(k S / M) * 5/4 + 32: about 1.25 k + 32 M/S entries of the list are
-// expected at or above it, so at least k with a wide margin. One pass keeps
-// the entries with key >= t, in list order (each thread owns a contiguous run
-// of the list, so one block scan places them), as long as they number between
-// k and TS_FCAP. The exact select then runs on those. Every entry of the top k
-// has key >= the k-th key >= t whenever at least k keys are >= t, so the
-// result is the exact top-k. Returns false, having written nothing, when the
-// kept count falls outside [k, TS_FCAP]; the caller then runs a full select.
+// Select through the k-th key's histogram bin. The scoring kernel counted the
+// list's keys by their top 11 bits, so the bin d holding the k-th largest key
+// and the number of keys in higher bins are known exactly. One pass keeps the
+// entries with key >= t = d << 21 (the bin and everything above it), in list
+// order (each thread owns a contiguous run of the list, so one block scan
+// places them); there are between k and k + hist[d] of them. The exact select
+// then ranks only the keys of bin d, on their lower 21 bits. Returns false,
+// having written nothing, when the kept entries do not fit in TS_FCAP; the
+// caller then runs a full select.
 #define LSA_GLOBAL __attribute__((address_space(1)))
 __device__ __attribute__((noinline)) bool select_filtered(const float* __restrict__ ys_, const int32_t* __restrict__ idx_,
-                                                int32_t M, int32_t k, int32_t* out_, float* outs_) {
+                                                int32_t M, int32_t k, int32_t* out_, float* outs_,
+                                                const uint32_t* __restrict__ hist_) {
   // This function is not inlined, so its pointer arguments lose the knowledge
   // that they point to global memory; generic (flat) accesses would make every
   // load wait for all outstanding memory and LDS operations. Restore it.
@@ -348,22 +441,26 @@ __device__ __attribute__((noinline)) bool select_filtered(const float* __restric
   LSA_GLOBAL int32_t* out = (LSA_GLOBAL int32_t*)out_;
   LSA_GLOBAL float* outs = (LSA_GLOBAL float*)outs_;
   const int tid = threadIdx.x;
-  __shared__ uint32_t fkey[TS_FCAP];    // sampled keys, then the kept keys
+  __shared__ uint32_t fkey[TS_FCAP];    // the kept keys
   __shared__ int32_t fpos[TS_FCAP];     // list positions of the kept keys
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t sh_digit, sh_krem;
   __shared__ uint32_t wt[TS_THREADS / 64];
 
-  // 1. threshold estimate from the sample. Two radix passes fix the top 22
-  // bits of the rank-r sample key; t (those bits, the rest zero) is at most
-  // that key, so at least as many entries pass as with the exact key.
-  for (int j = tid; j < TS_SAMPLE; j += TS_THREADS)
-    fkey[j] = order_key(ys[(int32_t)((int64_t)j * M / TS_SAMPLE)]);
+  // 1. the bin of the k-th largest key, from the scoring kernel's histogram
+  // of the top 11 key bits: t = the bin's smallest key. Exactly `above`
+  // entries lie in higher bins and hist[d] in the bin, so the kept count is
+  // known before the pass.
+  const LSA_GLOBAL uint32_t* hg = (const LSA_GLOBAL uint32_t*)hist_;
+  for (int j = tid; j < 2048; j += TS_THREADS) hist[j] = hg[j];
   __syncthreads();
-  const uint32_t est = (uint32_t)(((int64_t)k * TS_SAMPLE + M - 1) / M);
-  const uint32_t r = min((uint32_t)TS_SAMPLE, est + est / 4 + 32);
-  uint32_t t, tk;
-  lds_select(fkey, TS_SAMPLE, r, hist, &sh_digit, &sh_krem, t, tk, 2);
+  find_digit(hist, 2048, (uint32_t)k, &sh_digit, &sh_krem);
+  const uint32_t d = sh_digit;
+  const uint32_t bin_krem = sh_krem;  // rank of the k-th key among the keys of its bin
+  const uint32_t kept = (uint32_t)k - bin_krem + hist[d];
+  __syncthreads();
+  if (kept > (uint32_t)TS_FCAP) return false;  // uniform
+  const uint32_t t = d << 21;
 
   // 2. keep the entries with key >= t, in list order. Rounds of TS_THREADS x 8
   // entries; thread j owns entries 8j .. 8j+7 of a round, so the loads of a
@@ -411,9 +508,9 @@ __device__ __attribute__((noinline)) bool select_filtered(const float* __restric
   if (c < k) return false;
   __syncthreads();
 
-  // 3. exact select among the kept entries
+  // 3. exact select among the kept entries of the k-th bin (the top 11 bits are d)
   uint32_t T, krem;
-  lds_select(fkey, c, (uint32_t)k, hist, &sh_digit, &sh_krem, T, krem);
+  lds_select(fkey, c, bin_krem, hist, &sh_digit, &sh_krem, T, krem, 3, 1, t);
 
   // 4. output: keys above T, and the first krem keys equal to T, in list order
   const int32_t q = (c + TS_THREADS - 1) / TS_THREADS;
@@ -457,7 +554,7 @@ __device__ __attribute__((noinline)) bool select_filtered(const float* __restric
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    if (u < nt) {
+    if (u < nt && pos + u < k) {  // exactly k are taken; the bound only guards a mismatched workspace
       out[pos + u] = iv[u];
       if (outs) outs[pos + u] = yo[u];
     }
@@ -465,6 +562,7 @@ __device__ __attribute__((noinline)) bool select_filtered(const float* __restric
 }
 
 __global__ __launch_bounds__(TS_THREADS) void topk_select_kernel(const TopkSelectArgs a) {
+  __shared__ RegSelectSmem rsm;
   const int b = blockIdx.x, l = blockIdx.y, tid = threadIdx.x;
   const int64_t base = a.key_off[b];
   const int32_t M = a.count[b];
@@ -478,10 +576,15 @@ __global__ __launch_bounds__(TS_THREADS) void topk_select_kernel(const TopkSelec
       out[i] = i < M ? idx[i] : -1;
       if (outs) outs[i] = i < M ? ys[i] : -INFINITY;
     }
-  } else if (M >= 2 * TS_SAMPLE && (int64_t)k * 4 <= TS_FCAP * 3 && select_filtered(ys, idx, M, k, out, outs)) {
-    // done through the sample threshold
   } else if (M <= TS_THREADS * TS_VMAX) {
-    select_in_registers(ys, idx, M, k, out, outs);
+    const uint32_t* hb = a.hist + ((int64_t)l * a.B + b) * TOPK_BINS;
+    if (M <= TS_THREADS * 8) select_in_registers<8>(ys, idx, M, k, out, outs, hb, rsm);
+    else if (M <= TS_THREADS * 16) select_in_registers<16>(ys, idx, M, k, out, outs, hb, rsm);
+    else if (M <= TS_THREADS * 32) select_in_registers<32>(ys, idx, M, k, out, outs, hb, rsm);
+    else select_in_registers<TS_VMAX>(ys, idx, M, k, out, outs, hb, rsm);
+  } else if ((int64_t)k * 2 <= TS_FCAP &&
+             select_filtered(ys, idx, M, k, out, outs, a.hist + ((int64_t)l * a.B + b) * TOPK_BINS)) {
+    // done through the histogram's bin of the k-th key
   } else {
     select_streaming(ys, idx, M, k, out, outs);
   }

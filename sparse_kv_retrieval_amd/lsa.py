@@ -46,6 +46,13 @@ class ScoreLayer(ctypes.Structure):
                 ("mask_out", _vp), ("score_out", _vp)]
 
 
+class ScoreOptions(ctypes.Structure):
+    _fields_ = [("kernel", _i32), ("chunk_words", _i32), ("ring", _i32), ("guard", _i32)]
+
+
+SCORE_KERNELS = {"auto": 0, "stream": 1, "pairs": 2}
+
+
 class TopkLayer(ctypes.Structure):
     _fields_ = [("q", _vp), ("w", _vp), ("keys", _vp), ("key_scale", _vp),
                 ("topk_idx_out", _vp), ("topk_score_out", _vp)]
@@ -65,6 +72,8 @@ _project_packed = _sig("lsa_project_packed", _i32, [ctypes.POINTER(ProjLayer), _
                                                      _vp])
 _score_select = _sig("lsa_score_select", _i32, [ctypes.POINTER(ScoreLayer), _i32, _i32, _vp, _vp, _vp, _vp,
                                                  _i32, _i32, _i32, _f32, _vp])
+_score_select_ex = _sig("lsa_score_select_ex", _i32, [ctypes.POINTER(ScoreLayer), _i32, _i32, _vp, _vp, _vp, _vp,
+                                                       _i32, _i32, _i32, _f32, ctypes.POINTER(ScoreOptions), _vp])
 _union_compact = _sig("lsa_union_compact", _i32, [ctypes.POINTER(_vp), _i32, _i32, _vp, _vp, _vp, _vp,
                                                    _vp, _vp, _vp, _vp])
 _topk_ws = _sig("lsa_topk_workspace_size", _sz, [_i32, _i32, _i64, _i32])
@@ -72,6 +81,8 @@ _topk = _sig("lsa_topk", _i32, [ctypes.POINTER(TopkLayer), _i32, _i32, _vp, _vp,
                                  _i32, _vp, _vp, _sz, _vp])
 _topk_score = _sig("lsa_topk_score", _i32, [ctypes.POINTER(TopkLayer), _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32,
                                              _i32, _vp, _sz, _vp])
+_topk_step = _sig("lsa_topk_step", _i32, [ctypes.POINTER(TopkLayer), _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32,
+                                           _i32, _i32, _vp, _vp, _sz, _vp])
 _topk_select = _sig("lsa_topk_select", _i32, [ctypes.POINTER(TopkLayer), _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
                                                _vp, _sz, _vp])
 _gather = _sig("lsa_gather", _i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp])
@@ -86,6 +97,7 @@ _last_error = _sig("lsa_last_error", ctypes.c_char_p, [])
 _version = _sig("lsa_version", _i32, [])
 
 EXPORTED = ("lsa_project", "lsa_pack_weights_size", "lsa_pack_weights", "lsa_project_packed", "lsa_score_select",
+            "lsa_score_select_ex", "lsa_topk_step",
             "lsa_topk_score", "lsa_topk_select", "lsa_union_compact", "lsa_topk_workspace_size", "lsa_topk",
             "lsa_gather", "lsa_fetch_host", "lsa_golden_workspace_size", "lsa_golden_labels", "lsa_train_workspace_size",
             "lsa_train_step", "lsa_last_error",
@@ -165,15 +177,23 @@ def project_packed(layers, *, B, d, r, n_h, d_h, stream=None):
 
 
 def score_select(layers, *, B, key_offsets, key_offsets_host, mask_word_offsets, mask_word_offsets_host,
-                 n_h, d_h, key_dtype, threshold=0.5, stream=None):
-    """lsa_score_select. `layers`: dicts with q, w, keys, key_scale (fp8), mask_out, score_out (optional)."""
+                 n_h, d_h, key_dtype, threshold=0.5, options=None, stream=None):
+    """lsa_score_select. `layers`: dicts with q, w, keys, key_scale (fp8), mask_out, score_out (optional).
+
+    With `options` (a dict with any of kernel ("auto", "stream", "pairs"), chunk_words, ring, guard),
+    lsa_score_select_ex with those launch options instead."""
     arr = (ScoreLayer * len(layers))(*[ScoreLayer(_p(x["q"]), _p(x["w"]), _p(x["keys"]), _p(x.get("key_scale")),
                                                   _p(x["mask_out"]), _p(x.get("score_out"))) for x in layers])
     ko, kop = _host64(key_offsets_host)
     mo, mop = _host64(mask_word_offsets_host)
-    _check("lsa_score_select", _score_select(arr, len(layers), B, _p(key_offsets), kop, _p(mask_word_offsets), mop,
-                                             n_h, d_h, DTYPES.get(key_dtype, key_dtype), float(threshold),
-                                             _stream(stream)))
+    args = (arr, len(layers), B, _p(key_offsets), kop, _p(mask_word_offsets), mop, n_h, d_h,
+            DTYPES.get(key_dtype, key_dtype), float(threshold))
+    if options is None:
+        _check("lsa_score_select", _score_select(*args, _stream(stream)))
+        return
+    o = ScoreOptions(SCORE_KERNELS.get(options.get("kernel", 0), options.get("kernel", 0)),
+                     int(options.get("chunk_words", 0)), int(options.get("ring", 0)), int(options.get("guard", 0)))
+    _check("lsa_score_select_ex", _score_select_ex(*args, ctypes.byref(o), _stream(stream)))
 
 
 def union_compact(masks, *, B, key_offsets, key_offsets_host, mask_word_offsets, mask_word_offsets_host,
@@ -201,6 +221,18 @@ def topk(layers, *, B, key_offsets, key_offsets_host, idx, count, n_h, d_h, key_
     _check("lsa_topk", _topk(arr, len(layers), B, _p(key_offsets), kop, _p(idx), _p(count), n_h, d_h,
                              DTYPES.get(key_dtype, key_dtype), k, _p(topk_count_out), _p(workspace), nbytes,
                              _stream(stream)))
+
+
+def topk_step(layers, *, B, key_offsets, key_offsets_host, idx, count, n_h, d_h, key_dtype, k, topk_count_out,
+              workspace, stream=None):
+    """lsa_topk_step: as topk, with each layer's `keys` the packed subset keys (one decode step)."""
+    arr = (TopkLayer * len(layers))(*[TopkLayer(_p(x["q"]), _p(x["w"]), _p(x["keys"]), _p(x.get("key_scale")),
+                                                _p(x["topk_idx_out"]), _p(x.get("topk_score_out"))) for x in layers])
+    ko, kop = _host64(key_offsets_host)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("lsa_topk_step", _topk_step(arr, len(layers), B, _p(key_offsets), kop, _p(idx), _p(count), n_h, d_h,
+                                       DTYPES.get(key_dtype, key_dtype), k, _p(topk_count_out), _p(workspace),
+                                       nbytes, _stream(stream)))
 
 
 def _topk_layers(layers):

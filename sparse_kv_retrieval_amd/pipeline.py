@@ -8,13 +8,18 @@ and joins at the end):
 
   lsa_project        memory-indexer and native query/gates for every layer (one call, 2L layers);
                      with bf16 weights, lsa_project_packed on weights packed once at set-up
-  lsa_score_select   masks (and optional sigmoid scores) for every (layer, sequence)
+  lsa_score_select   masks for every (layer, sequence) (score_with_sigmoid: a pass that also
+                     writes the sigmoid scores)
   lsa_union_compact  OR over the layers -> ascending index list + count per sequence
   lsa_topk           native top-k inside the union, per (layer, sequence)
                      (run() calls its two stages, lsa_topk_score and lsa_topk_select)
   lsa_gather         the union rows of the compressed-KV pool -> packed compact buffer
                      (with host_pool=True, lsa_fetch_host reads them from a copy of the
                      pool in pinned host memory instead: the cold pool)
+
+After a trigger, alloc_steps() / pack_subset_keys() / step() run the decode steps: each
+layer's union rows of keys are packed once (lsa_gather), and every step projects its own
+native query and calls lsa_topk_step over them.
 
 This module only wires buffers. All arithmetic happens in the HIP kernels.
 """
@@ -97,7 +102,11 @@ class Pipeline:
         self.q = [out((B, w.n_h, w.d_h), f32) for _ in range(2 * L)]
         self.g = [out((B, w.n_h), f32) for _ in range(2 * L)]
         self.masks = [out((max(self.words, 1),), i64) for _ in range(L)]
+        # with_scores: buffers for a separate score pass that also writes the sigmoid scores
+        # (score_with_sigmoid); run() itself writes masks only
         self.scores = [out((max(self.rows, 1),), f32) for _ in range(L)] if with_scores else None
+        self.masks_scored = [out((max(self.words, 1),), i64) for _ in range(L)] if with_scores else None
+        self.score_options = None  # launch options of run()'s score pass (lsa_score_select_ex), None = defaults
         self.idx = out((max(self.rows, 1),), i32)
         self.count = out((B,), i32)
         self.union_mask = out((max(self.words, 1),), i64)
@@ -109,6 +118,24 @@ class Pipeline:
         self.gather_capacity = self.rows if gather_capacity is None else int(gather_capacity)
         if self.pool is not None:
             self.gathered = out((max(self.gather_capacity, 1), w.pool_dim), i16)
+        # decode steps (allocated by alloc_steps): each layer's union rows of keys packed once per
+        # trigger, the step's native query and gates, and the step's top-k outputs
+        self.keys_sub = None
+
+    def alloc_steps(self):
+        """Buffers of the per-step top-k over the resident subset (lsa_topk_step)."""
+        w, L, B = self.w, self.w.L, self.w.B
+        f32, i32 = torch.float32, torch.int32
+        kdt = {"f32": torch.float32, "bf16": torch.int16, "fp8": torch.uint8}[w.key_dtype]
+        self.key_row_bytes = w.d_h * {"f32": 4, "bf16": 2, "fp8": 1}[w.key_dtype]
+        self.keys_sub = [self._out((max(self.rows, 1), w.d_h), kdt) for _ in range(L)]
+        self.h_step = [self._out((B, w.d), torch.int16 if w.act_dtype == "bf16" else f32) for _ in range(L)]
+        self.c_step = [self._out((B, w.r), f32) for _ in range(L)]
+        self.q_step = [self._out((B, w.n_h, w.d_h), f32) for _ in range(L)]
+        self.g_step = [self._out((B, w.n_h), f32) for _ in range(L)]
+        self.step_idx = [self._out((B, w.k), i32) for _ in range(L)]
+        self.step_score = [self._out((B, w.k), f32) for _ in range(L)]
+        self.step_count = self._out((L, B), i32)
 
     def _out(self, shape, dtype):
         """An output buffer. With guard=True it sits between two GUARD_BYTES canary bands."""
@@ -147,12 +174,20 @@ class Pipeline:
             lsa.project(layers, B=w.B, d=w.d, r=w.r, n_h=w.n_h, d_h=w.d_h, dtype=w.act_dtype, stream=stream)
 
     def score_select(self, stream=None):
+        """The step's score pass: masks only, with score_options if set."""
+        self._score_call(self.masks, None, self.score_options, stream)
+
+    def score_with_sigmoid(self, stream=None, options=None):
+        """A score pass that also writes the sigmoid scores (into scores and masks_scored)."""
+        self._score_call(self.masks_scored, self.scores, options, stream)
+
+    def _score_call(self, masks, scores, options, stream):
         w = self.w
-        layers = [dict(q=self.q[l], w=self.g[l], keys=self.keys[l], key_scale=self.scale[l], mask_out=self.masks[l],
-                       score_out=None if self.scores is None else self.scores[l]) for l in range(w.L)]
+        layers = [dict(q=self.q[l], w=self.g[l], keys=self.keys[l], key_scale=self.scale[l], mask_out=masks[l],
+                       score_out=None if scores is None else scores[l]) for l in range(w.L)]
         lsa.score_select(layers, B=w.B, key_offsets=self.key_off, key_offsets_host=self.key_off_h,
                          mask_word_offsets=self.mwo, mask_word_offsets_host=self.mwo_h, n_h=w.n_h, d_h=w.d_h,
-                         key_dtype=w.key_dtype, threshold=w.threshold, stream=stream)
+                         key_dtype=w.key_dtype, threshold=w.threshold, options=options, stream=stream)
 
     def union_compact(self, stream=None):
         w = self.w
@@ -200,6 +235,42 @@ class Pipeline:
         lsa.fetch_host(self.pool_host, row_bytes=w.pool_dim * 2, B=w.B, pool_row_offsets=self.key_off,
                        pool_row_offsets_host=self.key_off_h, idx=self.idx, idx_offsets=self.key_off, count=self.count,
                        out=self.gathered, out_capacity_rows=self.gather_capacity, stream=stream)
+
+    # ------------------------------------------------------------- decode steps
+    def pack_subset_keys(self, stream=None):
+        """Once per trigger: each layer's keys of the union rows, packed in list order (lsa_gather)."""
+        w = self.w
+        for l in range(w.L):
+            lsa.gather(self.keys[l], row_bytes=self.key_row_bytes, B=w.B, pool_row_offsets=self.key_off,
+                       pool_row_offsets_host=self.key_off_h, idx=self.idx, idx_offsets=self.key_off, count=self.count,
+                       out=self.keys_sub[l], out_capacity_rows=self.rows, stream=stream)
+
+    def set_step_hidden(self, h_step):
+        """Copy one decode step's hidden states ([layer] -> [B, d] stored values) into HBM."""
+        for l, hl in enumerate(h_step):
+            a = np.ascontiguousarray(hl)
+            self.h_step[l].copy_(torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a))
+
+    def step(self, stream=None):
+        """One decode step: the native query and gates of the step's h (lsa_project with the native
+        weights), then lsa_topk_step over the packed subset keys."""
+        w, L = self.w, self.w.L
+        layers = [dict(h=self.h_step[l], w_dq=self.nat[l][0], w_iuq=self.nat[l][1], w_w=self.nat[l][2],
+                       c_out=self.c_step[l], q_out=self.q_step[l], w_out=self.g_step[l]) for l in range(L)]
+        if self.packed:
+            lsa.project_packed(layers, B=w.B, d=w.d, r=w.r, n_h=w.n_h, d_h=w.d_h, stream=stream)
+        else:
+            lsa.project(layers, B=w.B, d=w.d, r=w.r, n_h=w.n_h, d_h=w.d_h, dtype=w.act_dtype, stream=stream)
+        self.step_topk(stream)
+
+    def step_topk(self, stream=None):
+        """lsa_topk_step with the step's native query (q_step, g_step) over the packed subset keys."""
+        w, L = self.w, self.w.L
+        tl = [dict(q=self.q_step[l], w=self.g_step[l], keys=self.keys_sub[l], key_scale=self.scale[l],
+                   topk_idx_out=self.step_idx[l], topk_score_out=self.step_score[l]) for l in range(L)]
+        lsa.topk_step(tl, B=w.B, key_offsets=self.key_off, key_offsets_host=self.key_off_h, idx=self.idx,
+                      count=self.count, n_h=w.n_h, d_h=w.d_h, key_dtype=w.key_dtype, k=w.k,
+                      topk_count_out=self.step_count, workspace=self.workspace, stream=stream)
 
     def load(self, stream=None):
         """The load step: from the host pool when there is one, else from HBM."""
@@ -261,8 +332,6 @@ class Pipeline:
         """Every output buffer of run(), for comparisons between runs."""
         out = self.c + self.q + self.g + self.masks + [self.idx, self.count, self.union_mask, self.topk_count]
         out += self.topk_idx
-        if self.scores is not None:
-            out += self.scores
         if self.topk_score is not None:
             out += self.topk_score
         if self.pool is not None:
@@ -270,9 +339,9 @@ class Pipeline:
         return out
 
     # ------------------------------------------------------------- readback
-    def masks_bool(self, l):
-        """Unpack layer l's mask words into one bool array per sequence."""
-        words = self.masks[l][: self.words].cpu().numpy().view(np.uint64)
+    def masks_bool(self, l, scored=False):
+        """Unpack layer l's mask words (of run(), or of score_with_sigmoid) into one bool array per sequence."""
+        words = (self.masks_scored if scored else self.masks)[l][: self.words].cpu().numpy().view(np.uint64)
         return self._unpack(words)
 
     def union_bool(self):

@@ -7,6 +7,11 @@ Usage (each step's output is plain text, suitable for a short summary file):
       counters: run it under `rocprofv3 --pmc FETCH_SIZE` (then WRITE_SIZE)
       and compare the counter with the bytes the copy must move.
 
+  python -m sparse_kv_retrieval_amd.profiling stream --mib 768 --reps 10
+      The plain streaming-read kernel (probe.hip, libprobe.so) over a buffer of
+      that size: the achievable read rate that the score pass's key stream is
+      compared with.
+
   python -m sparse_kv_retrieval_amd.profiling stats <dir>
       Per-kernel call count and average / min / max duration from a
       `rocprofv3 --kernel-trace --output-format csv` run (its
@@ -22,7 +27,8 @@ Usage (each step's output is plain text, suitable for a short summary file):
       per dispatch) divided by what the same counters read per byte for the
       plain copy of M MiB.
 
-Nothing here launches the selection kernels; the copy uses torch.
+Nothing here launches the selection kernels; the copy uses torch, the stream
+probe its own kernel.
 """
 from __future__ import annotations
 
@@ -93,6 +99,66 @@ def copy_run(mib: int, reps: int) -> None:
     print(f"copied {mib} MiB x {reps}", flush=True)
 
 
+PROBE_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libprobe.so")
+
+
+def stream_read_rate(nbytes: int, reps: int = 10, copies: int = 2) -> dict:
+    """Read rate of the plain streaming-read kernel (probe.hip) over `nbytes`, in GB/s.
+
+    `copies` buffers of nbytes each are read in turn, so no launch finds its
+    buffer in the 256 MB Infinity Cache when nbytes is large. The probe's
+    access patterns (grid-stride or one contiguous range per block, plain or
+    non-temporal loads), loads in flight per thread (8 or 16) and blocks per
+    compute unit (2, 4, 8) are swept; the fastest configuration's median over
+    `reps` launches (HIP events on the launch stream) is the ceiling. The
+    whole sweep is returned too."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(PROBE_LIB)
+    fn = lib.probe_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_void_p]
+    nbytes = (int(nbytes) + 15) // 16 * 16
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    for b in bufs:
+        b.fill_(3)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(8 * cus, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    sweep = []
+    for mode in (0, 1, 2):
+        for u in (8, 16):
+            for bpc in (2, 4, 8):
+                blocks = bpc * cus
+
+                def launch(i):
+                    r = fn(bufs[i % copies].data_ptr(), nbytes, sink.data_ptr(), blocks, mode, u,
+                           ctypes.c_void_p(st.cuda_stream))
+                    assert r == 0, r
+                for i in range(3):
+                    launch(i)
+                torch.cuda.synchronize()
+                us = []
+                for i in range(reps):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(st)
+                    launch(i)
+                    e1.record(st)
+                    torch.cuda.synchronize()
+                    us.append(e0.elapsed_time(e1) * 1e3)
+                us.sort()
+                sweep.append({"mode": ["grid_stride", "block_range", "block_range_nt"][mode], "loads_in_flight": u,
+                              "blocks_per_cu": bpc, "median_us": us[len(us) // 2], "min_us": us[0],
+                              "GB_per_s": nbytes / (us[len(us) // 2] * 1e-6) / 1e9})
+    del bufs
+    torch.cuda.empty_cache()
+    best = max(sweep, key=lambda r: r["GB_per_s"])
+    return {"bytes": nbytes, "GB_per_s": best["GB_per_s"], "median_us": best["median_us"], "best": best,
+            "sweep": sweep}
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(prog="python -m sparse_kv_retrieval_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -104,6 +170,9 @@ def main(argv=None) -> None:
     p = sub.add_parser("pmc")
     p.add_argument("dir")
     p.add_argument("--kernel")
+    r = sub.add_parser("stream")
+    r.add_argument("--mib", type=int, default=768)
+    r.add_argument("--reps", type=int, default=10)
     t = sub.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write", "kernel"):
         t.add_argument("--" + k.replace("_", "-"), required=True)
@@ -112,6 +181,17 @@ def main(argv=None) -> None:
 
     if a.cmd == "copy":
         copy_run(a.mib, a.reps)
+    elif a.cmd == "stream":
+        r_ = stream_read_rate(a.mib << 20, a.reps)
+        print(f"streaming read of {a.mib} MiB ({r_['bytes']} bytes), median of {a.reps} launches per configuration")
+        print("| pattern | loads in flight per thread | blocks per CU | median us | GB/s |")
+        print("|---|---:|---:|---:|---:|")
+        for c in r_["sweep"]:
+            print(f"| {c['mode']} | {c['loads_in_flight']} | {c['blocks_per_cu']} | {c['median_us']:.1f} | "
+                  f"{c['GB_per_s']:.0f} |")
+        b_ = r_["best"]
+        print(f"ceiling: {r_['GB_per_s']:.0f} GB/s ({b_['mode']}, {b_['loads_in_flight']} loads, "
+              f"{b_['blocks_per_cu']} blocks per CU)", flush=True)
     elif a.cmd == "stats":
         print("| kernel | calls | avg us | min us | max us |")
         print("|---|---:|---:|---:|---:|")

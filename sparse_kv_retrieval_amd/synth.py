@@ -286,6 +286,28 @@ def make(w: Workload, *, with_pool: bool = True) -> Inputs:
     return Inputs(w, n, key_offsets, mwo, hs, mem, nat, keys, scales, pool, planted)
 
 
+# ---------------------------------------------------------------- decode steps
+def step_hidden(inp: Inputs, steps: int) -> list:
+    """Hidden states of `steps` decode steps after the trigger: [step][layer] -> [B, d].
+
+    Each step's h is drawn like the trigger's (the massive-activation channel
+    plus N(0, 1) noise), from its own seed, and stored in the workload's
+    activation dtype. They feed the native indexer's per-step query."""
+    w = inp.workload
+    out = []
+    for t in range(steps):
+        per = []
+        for l in range(w.L):
+            hl = np.empty((w.B, w.d), np.float32)
+            for b in range(w.B):
+                hl[b] = _rng(w, 8, t, l, b).standard_normal(w.d, dtype=np.float32)
+            if w.structured and not w.random_init:
+                hl[:, 0] = KAPPA
+            per.append(_store_act(w, hl))
+        out.append(per)
+    return out
+
+
 # ---------------------------------------------------------------- training labels
 def pack_mask_words(bits: np.ndarray, key_offsets: np.ndarray, mask_word_offsets: np.ndarray) -> np.ndarray:
     """Lay out per-entry booleans [rows] as the selection path's u64 mask words.

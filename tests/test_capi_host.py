@@ -28,7 +28,7 @@ def test_header_declares_the_five_calls():
     fns = declared_functions()
     for f in ("lsa_project", "lsa_score_select", "lsa_union_compact", "lsa_topk", "lsa_gather",
               "lsa_topk_workspace_size", "lsa_pack_weights_size", "lsa_pack_weights", "lsa_project_packed",
-              "lsa_topk_score", "lsa_topk_select",
+              "lsa_topk_score", "lsa_topk_select", "lsa_score_select_ex", "lsa_topk_step",
               "lsa_last_error", "lsa_version"):
         assert f in fns
 
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lsa):
 
 
 def test_version(lsa):
-    assert lsa.version() == 1
+    assert lsa.version() == 2
 
 
 def _offs(n):
@@ -95,6 +95,13 @@ def test_score_select_validation(lsa):
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.score_select, [_score_layer(keys=FAKE + 4)], **base, match="aligned")
     _expect(lsa, lsa.ERR_INVALID_ARG, lsa.score_select, [_score_layer()], **{**base, "B": 0})
     assert "B must" in lsa.last_error()
+    # lsa_score_select_ex: the same checks, then the options
+    _expect(lsa, lsa.ERR_INVALID_ARG, lsa.score_select, [_score_layer(q=None)], **base, options={}, match="must be set")
+    for bad_opt, what in (({"kernel": 3}, "kernel"), ({"chunk_words": 1}, "chunk_words"),
+                          ({"chunk_words": 65}, "chunk_words"), ({"ring": 6}, "ring"), ({"guard": 2}, "guard")):
+        _expect(lsa, lsa.ERR_INVALID_ARG, lsa.score_select, [_score_layer()], **base, options=bad_opt, match=what)
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.score_select, [_score_layer()], **{**base, "key_dtype": "f32"},
+            options={"kernel": "stream"}, match="one-wave-per-tile")
 
 
 def test_project_validation(lsa):
@@ -150,7 +157,14 @@ def test_union_topk_gather_validation(lsa):
             return FAKE
     _expect(lsa, lsa.ERR_WORKSPACE, lsa.topk, [tl], **tb, workspace=_WS(), match="workspace")
     _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.topk, [tl], **{**tb, "k": 0}, workspace=_WS())
-    assert lsa.topk_workspace_size(3, 2, 30, 2048) == 3 * 30 * 4
+    # scores [L][rows] fp32, then (256-byte aligned) 2048-bin histograms per (layer, sequence)
+    assert lsa.topk_workspace_size(3, 2, 30, 2048) == 512 + 3 * 2 * 2048 * 4
+    assert lsa.topk_workspace_size(3, 0, 30, 2048) == 0
+    # the per-step top-k over packed subset keys: the same checks, and at most 1024 sequences
+    _expect(lsa, lsa.ERR_WORKSPACE, lsa.topk_step, [tl], **tb, workspace=_WS(), match="workspace")
+    ko1025 = np.arange(1026, dtype=np.int64)
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.topk_step, [tl], **{**tb, "B": 1025, "key_offsets_host": ko1025},
+            workspace=_WS(), match="B must")
     # the two stages of the top-k check what each reads
     class _WSBig(_WS):  # a workspace stand-in that is large enough
         def numel(self):

@@ -46,7 +46,7 @@ def test_fetch_host_full_size(torch_cuda):
     p.run()
     torch_cuda.cuda.synchronize()
     _, lists = P.gpu_union_lists(p, inp)
-    P.check_gather(p, inp, lists, sample=2048, rng=np.random.default_rng(3))
+    P.check_gather(p, inp, lists)
     # the HBM gather of the same rows writes the same bytes
     fetched = p.gathered.clone()
     p.gathered.zero_()

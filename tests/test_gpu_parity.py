@@ -2,9 +2,8 @@
 
 Small cases span several tiles, ragged tails, empty and one-entry sequences,
 k above and below the subset size, and every key dtype and head shape.
-The full-size cases run the five workloads at their real sizes, with the
-launch configuration that bench.py times. There the oracle checks sampled
-outputs, and properties that hold at any size cover the rest.
+The full-size cases run the workloads at their real sizes, with the launch
+configuration that bench.py times, and compare every output with the oracle.
 """
 import dataclasses
 
@@ -31,6 +30,14 @@ SMALL = {
         synth.scaled(W["three_layer_b8"], N=(777, 64), k=50), key_dtype="f32", act_dtype="f32", n_h=48, d=256,
         r=128, L=2, name="f32h48"),
     "single_k_ge_count": synth.scaled(W["three_layer_b8"], N=(600, 200), k=4096),
+    # other loading thresholds: the comparison is x >= ln(theta / (1 - theta))
+    "three_layer_theta03": dataclasses.replace(synth.scaled(W["three_layer_b8"], N=(4000, 129, 0, 2500), k=128),
+                                               threshold=0.3, name="theta03"),
+    "fp8_theta07": dataclasses.replace(synth.scaled(W["fp8_1m"], N=(3000, 700), k=200), threshold=0.7,
+                                       name="fp8_theta07"),
+    "bf16_d64_theta07": dataclasses.replace(
+        synth.scaled(W["three_layer_b8"], N=(1500, 65), k=64), n_h=16, d_h=64, d=512, r=256, threshold=0.7,
+        name="h16d64_theta07"),
 }
 
 
@@ -56,28 +63,29 @@ def test_small_parity(case, torch_cuda):
           f"band_mismatch={st['mismatch_in_band']} max_dI={st['max_dI']:.2e}")
 
 
-# Launch variants of the score pass, chosen by environment knobs the library
-# reads at each call: the pair kernel (two waves per tile), and the
-# one-wave-per-tile kernel with other chunk sizes and LDS rings.
+# Launch variants of the score pass, passed to lsa_score_select_ex: the pair
+# kernel (two waves per tile), the one-wave-per-tile kernel with other chunk
+# sizes and LDS rings, and the full hi + lo pass on every tile.
 SCORE_VARIANTS = {
-    "pairs": {"LSA_SCORE_PAIRS": "1"},
-    "chunk2": {"LSA_SCORE_CHUNK": "2"},
-    "chunk3_ring8": {"LSA_SCORE_CHUNK": "3", "LSA_SCORE_RING": "8"},
-    "chunk5": {"LSA_SCORE_CHUNK": "5"},
+    "pairs": {"kernel": "pairs"},
+    "chunk2": {"kernel": "stream", "chunk_words": 2},
+    "chunk3_ring8": {"chunk_words": 3, "ring": 8},
+    "chunk5": {"chunk_words": 5},
+    "guard": {"guard": 1},
+    "guard_chunk2": {"guard": 1, "chunk_words": 2},
 }
 
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("variant", list(SCORE_VARIANTS))
 @pytest.mark.parametrize("case", ["three_layer_mixed", "fp8_two_seq", "ragged_small", "bf16_16heads_d64"])
-def test_score_variants(case, variant, torch_cuda, monkeypatch):
+def test_score_variants(case, variant, torch_cuda):
     from sparse_kv_retrieval_amd.pipeline import Pipeline
-    for k, v in SCORE_VARIANTS[variant].items():
-        monkeypatch.setenv(k, v)
     w = SMALL[case]
     P.say(f"[variant] case={case} variant={variant}")
     inp = synth.make(w)
     p = Pipeline(inp, "cuda", with_scores=True, guard=True)
+    p.score_options = SCORE_VARIANTS[variant]
     p.run()
     torch_cuda.cuda.synchronize()
     assert p.check_guards() == [], f"writes outside an output buffer: {p.check_guards()}"
@@ -95,8 +103,9 @@ def test_repeat_is_deterministic(torch_cuda):
     snaps = []
     for _ in range(2):
         p.run()
+        p.score_with_sigmoid()
         torch_cuda.cuda.synchronize()
-        snaps.append([t.clone() for t in (p.masks + p.scores + [p.idx[: p.rows], p.count, p.topk_count]
+        snaps.append([t.clone() for t in (p.masks + p.masks_scored + p.scores + [p.idx[: p.rows], p.count, p.topk_count]
                                           + p.topk_idx + p.topk_score + [p.gathered])])
     for a, b in zip(*snaps):
         assert torch_cuda.equal(a, b)
@@ -169,8 +178,12 @@ def test_graph_replay_matches_eager(torch_cuda):
             assert torch_cuda.equal(a, b), f"replay {rep} differs"
 
 
-def _full_sampled(name, torch_cuda, sample=2048):
-    from oracle import lsa_oracle as O
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", ["single_layer_500k", "three_layer_b8", "fp8_1m", "ragged_b32"])
+def test_full_size(name, torch_cuda):
+    """The workloads at their full sizes, in the launch configuration bench.py times, against the
+    oracle on every output: every entry's mask bit (both score passes) and sigmoid score, every
+    union list, every (layer, sequence)'s top-k, every gathered row."""
     from sparse_kv_retrieval_amd.pipeline import Pipeline
     w = W[name]
     P.say(f"[full] case={name}: generating")
@@ -180,57 +193,8 @@ def _full_sampled(name, torch_cuda, sample=2048):
     p.run()
     torch_cuda.cuda.synchronize()
     assert p.check_guards() == [], f"writes outside an output buffer: {p.check_guards()}"
-    P.say(f"[full] case={name}: checking")
-    rng = np.random.default_rng(0)
-    masks = [p.masks_bool(l) for l in range(w.L)]
-    # sampled entries of every (sequence, layer) against the oracle, one by one
-    checked = 0
-    for b in range(w.B):
-        s0, s1 = int(inp.key_offsets[b]), int(inp.key_offsets[b + 1])
-        n = s1 - s0
-        if n == 0:
-            continue
-        ent = np.unique(np.concatenate([rng.choice(n, min(n, sample), replace=False), np.arange(min(n, 64)),
-                                        np.arange(max(0, n - 64), n)]))
-        for l in range(w.L):
-            mw = inp.mem_w[l]
-            H = O.decode_act(inp.h[l][b:b + 1], w.act_dtype)
-            _, q, g = O.project(H, O.decode_act(mw.w_dq, w.act_dtype), O.decode_act(mw.w_iuq, w.act_dtype),
-                                O.decode_act(mw.w_w, w.act_dtype), w.n_h, w.d_h)
-            sc = None if inp.key_scale[l] is None else inp.key_scale[l][s0 + ent]
-            K = O.decode_keys(inp.keys[l][s0 + ent], w.key_dtype, sc)
-            x = O.logits(q[0], g[0], K)
-            band = np.abs(x) <= P.BAND
-            m, tail = masks[l][b]
-            assert not tail.any()
-            assert np.array_equal(m[ent][~band], O.select(x, w.threshold)[~band]), f"mask b={b} l={l}"
-            I = p.scores[l][s0 + ent].cpu().numpy() if len(ent) else np.zeros(0)
-            assert np.abs(I - O.sigmoid(x)).max() <= P.SCORE_TOL
-            checked += len(ent)
-    # compaction is integer work: bit-exact against the GPU's own masks, all sequences
-    counts, lists = P.gpu_union_lists(p, inp)
-    for b in range(w.B):
-        U = O.union([masks[l][b][0] for l in range(w.L)])
-        assert np.array_equal(lists[b], O.compact(U))
-    # top-k against the oracle for the first and last sequence (full subset re-scored)
-    sel = sorted({0, w.B - 1})
-    ref = {}
-    for b in sel:
-        s0, s1 = int(inp.key_offsets[b]), int(inp.key_offsets[b + 1])
-        ref[b] = {"qn": {}, "wn": {}}
-        for l in range(w.L):
-            nw = inp.nat_w[l]
-            H = O.decode_act(inp.h[l][b:b + 1], w.act_dtype)
-            _, qn, wn = O.project(H, O.decode_act(nw.w_dq, w.act_dtype), O.decode_act(nw.w_iuq, w.act_dtype),
-                                  O.decode_act(nw.w_w, w.act_dtype), w.n_h, w.d_h)
-            ref[b]["qn"][l], ref[b]["wn"][l] = qn[0], wn[0]
-    P.check_topk(p, inp, ref, lists)
-    P.check_gather(p, inp, lists, sample=512, rng=rng)
+    P.say(f"[full] case={name}: checking against the oracle")
+    st, counts = P.full_check(p, inp)
     frac = counts.sum() / max(1, int(inp.key_offsets[-1]))
-    P.say(f"[full] case={name}: ok, {checked} sampled entries, union fraction {frac:.4f}")
-
-
-@pytest.mark.gpu
-@pytest.mark.parametrize("name", ["single_layer_500k", "three_layer_b8", "fp8_1m", "ragged_b32"])
-def test_full_size_sampled(name, torch_cuda):
-    _full_sampled(name, torch_cuda)
+    P.say(f"[full] case={name}: ok, union fraction {frac:.4f}, band={st['band']} "
+          f"band_mismatch={st['mismatch_in_band']} run_vs_scored={st['run_vs_scored']} max_dI={st['max_dI']:.2e}")

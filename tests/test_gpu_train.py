@@ -244,7 +244,9 @@ def test_train_label_and_logit_extremes(torch_cuda, kind):
 def test_train_on_mined_labels(torch_cuda):
     """Labels straight from golden-label mining: lsa_golden_labels writes the window's label set in the
     same bit layout that lsa_train_step reads, so the mined words feed the training step on the device.
-    The oracle side mines its own labels (the golden-label oracle) and trains on those."""
+    The mined set is judged as the mining tests judge it (the golden-label oracle's bounds: entries whose
+    nucleus mass lies within rounding of p may fall either way), and the training oracle then trains on
+    the GPU's mined labels, so the training comparison does not depend on how those entries fell."""
     from oracle import golden_oracle as G
     from sparse_kv_retrieval_amd import lsa
     from sparse_kv_retrieval_amd import synth_golden as SG
@@ -259,10 +261,13 @@ def test_train_on_mined_labels(torch_cuda):
                       workspace=torch_cuda.empty(lsa.golden_workspace_size(gw.T, gw.L, gw.row_stride),
                                                  dtype=torch_cuda.uint8, device=dev))
     torch_cuda.cuda.synchronize()
-    lab = G.golden_labels(gi.logits, gi.n_valid, gw.p, gw.theta)       # the oracle's own label set
-    N = lab.size
-    mined = np.unpackbits(golden.cpu().numpy().view(np.uint8), bitorder="little").astype(bool)[:N]
-    assert np.array_equal(mined, lab), "mined label set differs from the oracle's on this window"
+    sure, never = G.golden_bounds(gi.logits, gi.n_valid, gw.p, gw.theta, 1e-5)
+    N = sure.size
+    bits = np.unpackbits(golden.cpu().numpy().view(np.uint8), bitorder="little").astype(bool)
+    mined = bits[:N]
+    assert not (sure & ~mined).any() and not (never & mined).any() and not bits[N:W * 64].any(), \
+        "mined label set outside the oracle's bounds"
+    lab = mined  # the GPU's labels feed both sides of the training comparison
     w = _workload((N,), name="train_mined", seed=26)
     say(f"train_on_mined_labels: N={N}, {int(lab.sum())} golden")
     inp = S.make(w, with_pool=False)
