@@ -344,6 +344,30 @@ lsa_status lsa_topk_step(const lsa_topk_layer* layers /* host [L]; keys = packed
                          size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * lsa_topk_step_noalloc: lsa_topk_step for callers that cannot allocate or
+ * hold device memory of their own: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. It takes no workspace and allocates
+ * nothing; its scratch (the subset scores and the score histograms) is a fixed
+ * array of LSA_NOALLOC_SCRATCH_BYTES in device memory, one copy on every GPU
+ * the library runs on, held until the process ends.
+ *
+ * Arguments, results and errors are those of lsa_topk_step. A call whose
+ * scratch, lsa_topk_workspace_size(L, B, key_offsets_host[B], k), exceeds
+ * LSA_NOALLOC_SCRATCH_BYTES returns LSA_ERR_UNSUPPORTED before any HIP call.
+ * Each call clears what it needs cleared, and leaves the array holding its own
+ * scratch. Calls on one GPU share the array: two calls that may overlap in
+ * time on one GPU (on different streams, or from different threads without
+ * ordering) race and give wrong results; order them on one stream.
+ * ---------------------------------------------------------------------- */
+#define LSA_NOALLOC_SCRATCH_BYTES (32 << 20)
+lsa_status lsa_topk_step_noalloc(const lsa_topk_layer* layers /* host [L]; keys = packed subset keys */,
+                                 int32_t L, int32_t B, const int64_t* key_offsets /* dev [B+1] */,
+                                 const int64_t* key_offsets_host /* host [B+1] */,
+                                 const int32_t* idx /* dev [rows] */, const int32_t* count /* dev [B] */,
+                                 int32_t n_h, int32_t d_h, lsa_dtype key_dtype, int32_t k,
+                                 int32_t* topk_count_out /* dev [L, B] */, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * lsa_gather: load the selected entries' compressed-KV rows into a compact
  * device buffer ([HYPER] 方法: the subset C^MemComp is loaded into GPU memory).
  * Here the pool is already in device memory, so this is an HBM-to-HBM row copy.

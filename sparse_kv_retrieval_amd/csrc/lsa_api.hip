@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <cstring>
 #include <string>
 
@@ -406,6 +407,58 @@ lsa_status lsa_topk_step(const lsa_topk_layer* layers, int32_t L, int32_t B, con
                          size_t workspace_bytes, hipStream_t stream) {
   return topk_stages(layers, L, B, key_offsets, key_offsets_host, idx, count, n_h, d_h, dtype_value(key_dtype), k,
                      topk_count_out, workspace, workspace_bytes, stream, true, true, true);
+}
+
+}  // extern "C"
+
+// Scratch of lsa_topk_step_noalloc: a fixed array in device memory, one copy on
+// every GPU the library runs on, held until the process ends. Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in); it
+// takes the device's address of its copy from hipGetSymbolAddress, once per
+// device, and passes that.
+static __device__ __align__(256) char scratch[LSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {nullptr};
+
+// The current device's address of `scratch` (looked up on the first call on that device).
+lsa_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("lsa_topk_step_noalloc: hipGetDevice", e);
+  if (dev < 0 || dev >= 64) return fail(LSA_ERR_UNSUPPORTED, "lsa_topk_step_noalloc: device %d (at most 64)", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail("lsa_topk_step_noalloc: hipGetSymbolAddress", e);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+lsa_status lsa_topk_step_noalloc(const lsa_topk_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,
+                                 const int64_t* key_offsets_host, const int32_t* idx, const int32_t* count,
+                                 int32_t n_h, int32_t d_h, lsa_dtype key_dtype, int32_t k, int32_t* topk_count_out,
+                                 hipStream_t stream) {
+  // the size check needs only host values, and runs before any HIP call
+  if (L < 1 || L > LSA_MAX_LAYERS) return fail(LSA_ERR_INVALID_ARG, "L must be in [1, %d] (got %d)", LSA_MAX_LAYERS, L);
+  if (B < 1 || B > TOPK_CONTIG_MAX_B) return fail(LSA_ERR_UNSUPPORTED, "B must be in [1, %d] (got %d)", TOPK_CONTIG_MAX_B, B);
+  lsa_status s;
+  if ((s = check_offsets(key_offsets_host, B, "key_offsets")) != LSA_OK) return s;
+  const size_t need = lsa_topk_workspace_size(L, B, key_offsets_host[B], k);
+  if (need > (size_t)LSA_NOALLOC_SCRATCH_BYTES)
+    return fail(LSA_ERR_UNSUPPORTED, "lsa_topk_step_noalloc: the call needs %zu bytes of scratch, more than the %d the "
+                                     "library holds (use lsa_topk_step with a workspace)", need, LSA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((s = scratch_for_current_device(&ws)) != LSA_OK) return s;
+  return topk_stages(layers, L, B, key_offsets, key_offsets_host, idx, count, n_h, d_h, dtype_value(key_dtype), k,
+                     topk_count_out, ws, (size_t)LSA_NOALLOC_SCRATCH_BYTES, stream, true, true, true);
 }
 
 lsa_status lsa_topk_select(const lsa_topk_layer* layers, int32_t L, int32_t B, const int64_t* key_offsets,

@@ -83,6 +83,8 @@ _topk_score = _sig("lsa_topk_score", _i32, [ctypes.POINTER(TopkLayer), _i32, _i3
                                              _i32, _vp, _sz, _vp])
 _topk_step = _sig("lsa_topk_step", _i32, [ctypes.POINTER(TopkLayer), _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32,
                                            _i32, _i32, _vp, _vp, _sz, _vp])
+_topk_step_noalloc = _sig("lsa_topk_step_noalloc", _i32, [ctypes.POINTER(TopkLayer), _i32, _i32, _vp, _vp, _vp, _vp,
+                                                           _i32, _i32, _i32, _i32, _vp, _vp])
 _topk_select = _sig("lsa_topk_select", _i32, [ctypes.POINTER(TopkLayer), _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp,
                                                _vp, _sz, _vp])
 _gather = _sig("lsa_gather", _i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp])
@@ -97,7 +99,7 @@ _last_error = _sig("lsa_last_error", ctypes.c_char_p, [])
 _version = _sig("lsa_version", _i32, [])
 
 EXPORTED = ("lsa_project", "lsa_pack_weights_size", "lsa_pack_weights", "lsa_project_packed", "lsa_score_select",
-            "lsa_score_select_ex", "lsa_topk_step",
+            "lsa_score_select_ex", "lsa_topk_step", "lsa_topk_step_noalloc",
             "lsa_topk_score", "lsa_topk_select", "lsa_union_compact", "lsa_topk_workspace_size", "lsa_topk",
             "lsa_gather", "lsa_fetch_host", "lsa_golden_workspace_size", "lsa_golden_labels", "lsa_train_workspace_size",
             "lsa_train_step", "lsa_last_error",
@@ -233,6 +235,20 @@ def topk_step(layers, *, B, key_offsets, key_offsets_host, idx, count, n_h, d_h,
     _check("lsa_topk_step", _topk_step(arr, len(layers), B, _p(key_offsets), kop, _p(idx), _p(count), n_h, d_h,
                                        DTYPES.get(key_dtype, key_dtype), k, _p(topk_count_out), _p(workspace),
                                        nbytes, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def topk_step_noalloc(layers, *, B, key_offsets, key_offsets_host, idx, count, n_h, d_h, key_dtype, k,
+                      topk_count_out, stream=None):
+    """lsa_topk_step_noalloc: as topk_step, with the library's own fixed scratch instead of a workspace."""
+    arr = (TopkLayer * len(layers))(*[TopkLayer(_p(x["q"]), _p(x["w"]), _p(x["keys"]), _p(x.get("key_scale")),
+                                                _p(x["topk_idx_out"]), _p(x.get("topk_score_out"))) for x in layers])
+    ko, kop = _host64(key_offsets_host)
+    _check("lsa_topk_step_noalloc", _topk_step_noalloc(arr, len(layers), B, _p(key_offsets), kop, _p(idx), _p(count),
+                                                       n_h, d_h, DTYPES.get(key_dtype, key_dtype), k,
+                                                       _p(topk_count_out), _stream(stream)))
 
 
 def _topk_layers(layers):

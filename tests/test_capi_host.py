@@ -29,6 +29,7 @@ def test_header_declares_the_five_calls():
     for f in ("lsa_project", "lsa_score_select", "lsa_union_compact", "lsa_topk", "lsa_gather",
               "lsa_topk_workspace_size", "lsa_pack_weights_size", "lsa_pack_weights", "lsa_project_packed",
               "lsa_topk_score", "lsa_topk_select", "lsa_score_select_ex", "lsa_topk_step",
+              "lsa_topk_step_noalloc",
               "lsa_last_error", "lsa_version"):
         assert f in fns
 
@@ -160,6 +161,11 @@ def test_union_topk_gather_validation(lsa):
     # scores [L][rows] fp32, then (256-byte aligned) 2048-bin histograms per (layer, sequence)
     assert lsa.topk_workspace_size(3, 2, 30, 2048) == 512 + 3 * 2 * 2048 * 4
     assert lsa.topk_workspace_size(3, 0, 30, 2048) == 0
+    # the allocation-free variant refuses a call whose scratch exceeds its fixed array, before any HIP call
+    big = np.array([0, 5_000_000, 10_000_000], np.int64)
+    nb = {k_: v for k_, v in tb.items() if k_ not in ("key_offsets_host",)}
+    assert lsa.topk_workspace_size(1, 2, 10_000_000, 2048) > lsa.NOALLOC_SCRATCH_BYTES
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.topk_step_noalloc, [tl], **nb, key_offsets_host=big, match="scratch")
     # the per-step top-k over packed subset keys: the same checks, and at most 1024 sequences
     _expect(lsa, lsa.ERR_WORKSPACE, lsa.topk_step, [tl], **tb, workspace=_WS(), match="workspace")
     ko1025 = np.arange(1026, dtype=np.int64)
