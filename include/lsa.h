@@ -42,7 +42,9 @@
  *    dtype returns LSA_ERR_UNSUPPORTED. In both cases nothing is launched and
  *    lsa_last_error() describes the problem. A failed launch returns
  *    LSA_ERR_HIP. Device-side values such as indices, counts and offsets are
- *    not range-checked beyond what each call states.
+ *    not range-checked beyond what each call states. A debug build of the
+ *    library (LSA_DEBUG_CHECKS) checks every list entry that addresses a row
+ *    against N_b; see lsa_debug_range_errors.
  *  - Sequences: B sequences are stored back to back. Sequence b owns rows
  *    [key_offsets[b], key_offsets[b+1]) of every per-entry buffer. Entry indices
  *    are sequence-local int32 values in [0, N_b), where
@@ -509,6 +511,21 @@ lsa_status lsa_train_step(const void* h /* dev */, const void* w_dq /* dev */, c
                           float* g_dq /* dev [r, d] */, float* g_iuq /* dev [n_h*d_h, r] */,
                           float* g_w /* dev [n_h, d] */, void* workspace /* dev */, size_t workspace_bytes,
                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * lsa_debug_range_errors: in a debug build (compiled with LSA_DEBUG_CHECKS=1),
+ * the number of out-of-range list entries that the gather, the cold-pool
+ * fetch and the top-k scoring of gathered rows have met since the previous
+ * call. Such an entry (an index outside [0, N_b) of its sequence) is counted
+ * and its row is not read: its gathered row is not written, and its top-k score
+ * is that of an all-zero key. One entry may be counted more than once. The
+ * count is cleared by the call.
+ *
+ * Unlike every other call it synchronises: it waits for `stream` and copies the
+ * count to the host. Counts are per device and shared by all streams.
+ * A release build returns LSA_ERR_UNSUPPORTED and leaves *count_out alone.
+ * ---------------------------------------------------------------------- */
+lsa_status lsa_debug_range_errors(hipStream_t stream, int64_t* count_out /* host [1] */);
 
 /* Text describing the last non-OK status returned on the calling thread. */
 const char* lsa_last_error(void);

@@ -89,7 +89,35 @@ def build_sanitized_host(verbose: bool = False) -> str:
     return pkg
 
 
+# Debug build: the kernels that address rows through list entries check them against N_b
+# (LSA_DEBUG_CHECKS=1; see lsa_debug_range_errors), in a separate copy of the package so that
+# the product library is untouched. GPU tests load it in a child process.
+DEBUG_DIR = os.path.join(HERE, "_debug")
+DEBUG_SOURCES = ["score.hip", "gather.hip", "lsa_api.hip"]
+
+
+def build_debug(verbose: bool = False) -> str:
+    """Build <DEBUG_DIR>/sparse_kv_retrieval_amd (liblsa.so with the device range checks, and the binding)."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objs = [os.path.join(BUILD_DIR, s.replace(".hip", ".o")) for s in SOURCES if s not in DEBUG_SOURCES]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    pkg = os.path.join(DEBUG_DIR, "sparse_kv_retrieval_amd")
+    os.makedirs(pkg, exist_ok=True)
+    dobjs = [os.path.join(DEBUG_DIR, s.replace(".hip", "_debug.o")) for s in DEBUG_SOURCES]
+    _run([[hipcc, *HIPCC_FLAGS, "-DLSA_DEBUG_CHECKS=1", "-I", os.path.join(ROOT, "include"), "-c",
+           os.path.join(HERE, "csrc", s), "-o", o] for s, o in zip(DEBUG_SOURCES, dobjs)], verbose)
+    tmp = os.path.join(pkg, "liblsa.so.tmp")
+    _run([[hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, *dobjs, "-o", tmp]], verbose)
+    os.replace(tmp, os.path.join(pkg, "liblsa.so"))
+    for f in ("__init__.py", "lsa.py"):
+        with open(os.path.join(HERE, f), "rb") as src, open(os.path.join(pkg, f), "wb") as dst:
+            dst.write(src.read())
+    return pkg
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_debug(verbose=True))
     if "--sanitized-host" in sys.argv:
         print(build_sanitized_host(verbose=True))

@@ -20,6 +20,10 @@
 namespace lsa {
 
 static constexpr int GA_THREADS = 256;
+
+#if LSA_DEBUG_CHECKS
+static __device__ unsigned int g_gather_range_errors;
+#endif
 static constexpr int GA_TAB = 1024;  // sequences whose offsets are cached in LDS
 
 // Dynamic LDS: pre[B+1], then (for B <= GA_TAB) t_pool[B], t_idx[B], t_out[B], all int64.
@@ -82,7 +86,14 @@ __global__ __launch_bounds__(GA_THREADS) void gather_kernel(const GatherArgs a) 
         const int64_t io = cached ? t_idx[b] : a.idx_off[b];
         dst_row = a.out_off ? (cached ? t_out[b] : a.out_off[b]) + i : r;
         ok = dst_row < a.out_capacity;
-        src_row = po + a.idx[io + i];
+        const int32_t e = a.idx[io + i];
+        src_row = po + e;
+#if LSA_DEBUG_CHECKS
+        if (ok && (e < 0 || e >= a.pool_off[b + 1] - po)) {
+          atomicAdd(&g_gather_range_errors, 1u);
+          ok = 0;
+        }
+#endif
       }
     }
     const char* src[GA_ROWS];
@@ -104,6 +115,18 @@ __global__ __launch_bounds__(GA_THREADS) void gather_kernel(const GatherArgs a) 
         if (okr[u]) __builtin_nontemporal_store(v[u], (u32x4*)dst[u] + j);
     }
   }
+}
+
+hipError_t gather_take_range_errors(unsigned int* out) {
+#if LSA_DEBUG_CHECKS
+  hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_gather_range_errors), sizeof(unsigned int));
+  if (e != hipSuccess) return e;
+  const unsigned int zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_gather_range_errors), &zero, sizeof(unsigned int));
+#else
+  *out = 0;
+  return hipSuccess;
+#endif
 }
 
 hipError_t launch_gather(const GatherArgs& a, int grid, int rows_per_wave, hipStream_t st) {

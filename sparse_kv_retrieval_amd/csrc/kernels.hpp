@@ -4,6 +4,13 @@
 
 #include "common.hpp"
 
+// Debug builds (-DLSA_DEBUG_CHECKS=1) check every list entry that addresses a row (the
+// gather and the top-k scoring of gathered rows) against its sequence's row count, skip
+// the access when it is out of range, and count it; lsa_debug_range_errors reports the
+// count. Release builds compile none of this.
+#ifndef LSA_DEBUG_CHECKS
+#define LSA_DEBUG_CHECKS 0
+#endif
 #define LSA_TOPK_MAX_B 4096
 #define TOPK_CONTIG_MAX_B 1024  // sequences of one per-step top-k call over packed subset keys
 
@@ -159,6 +166,10 @@ hipError_t launch_topk_hist_zero(uint32_t* hist, int64_t n, hipStream_t st);
 hipError_t launch_topk_select(const TopkSelectArgs& a, int L, hipStream_t st);
 hipError_t launch_union_compact(const UnionArgs& a, int B, int64_t max_words, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, int grid, int rows_per_wave, hipStream_t st);
+// Debug builds: the out-of-range list entries each file's kernels have skipped since the last
+// call (the count is read, then cleared; synchronous).
+hipError_t gather_take_range_errors(unsigned int* out);
+hipError_t topk_take_range_errors(unsigned int* out);
 hipError_t launch_project(const ProjArgs& a, int L, bool f32, hipStream_t st);
 hipError_t launch_project_packed(const ProjArgs& a, int L, hipStream_t st);
 // One bf16 layer with each reduction split over two blocks that add into zeroed outputs (a grid of

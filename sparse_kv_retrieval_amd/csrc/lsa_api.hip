@@ -194,6 +194,23 @@ extern "C" {
 
 const char* lsa_last_error(void) { return g_err.c_str(); }
 
+lsa_status lsa_debug_range_errors(hipStream_t stream, int64_t* count_out) {
+#if LSA_DEBUG_CHECKS
+  if (!count_out) return fail(LSA_ERR_INVALID_ARG, "count_out is NULL");
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail("lsa_debug_range_errors: stream", e);
+  unsigned int ng = 0, nt = 0;
+  if ((e = gather_take_range_errors(&ng)) != hipSuccess) return hip_fail("lsa_debug_range_errors: gather count", e);
+  if ((e = topk_take_range_errors(&nt)) != hipSuccess) return hip_fail("lsa_debug_range_errors: top-k count", e);
+  *count_out = (int64_t)ng + (int64_t)nt;
+  return LSA_OK;
+#else
+  (void)stream;
+  (void)count_out;
+  return fail(LSA_ERR_UNSUPPORTED, "this build has no device range checks (build with LSA_DEBUG_CHECKS=1)");
+#endif
+}
+
 int32_t lsa_version(void) { return LSA_VERSION; }
 
 lsa_status lsa_project(const lsa_proj_layer* layers, int32_t L, int32_t B, int32_t d, int32_t r, int32_t n_h,

@@ -366,6 +366,25 @@ __device__ __forceinline__ void block_list_prefix(const int32_t* __restrict__ co
 // rows and no index load precedes the key loads (fp8 scales are still read
 // through the list from the full scale array). Used for the per-step top-k
 // over the resident subset. At most TOPK_CONTIG_MAX_B sequences.
+#if LSA_DEBUG_CHECKS
+static __device__ unsigned int g_topk_range_errors;
+__device__ __forceinline__ void range_error() { atomicAdd(&g_topk_range_errors, 1u); }
+#else
+__device__ __forceinline__ void range_error() {}
+#endif
+
+hipError_t topk_take_range_errors(unsigned int* out) {
+#if LSA_DEBUG_CHECKS
+  hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_topk_range_errors), sizeof(unsigned int));
+  if (e != hipSuccess) return e;
+  const unsigned int zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_topk_range_errors), &zero, sizeof(unsigned int));
+#else
+  *out = 0;
+  return hipSuccess;
+#endif
+}
+
 template <int KT, int DH, int D, bool CONTIG>
 __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) {
   using IO = TileIO<KT, DH>;
@@ -438,13 +457,18 @@ __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) 
             rk_, live_ && loads ? (e_ + lrow[i]) * IO::GRB + lchunk[i] * 16 : BUF_OOB);        \
     } else {                                                                                   \
       const auto rk_ = buf_rsrc(ic.keys + ic.base * IO::GRB, (uint32_t)ic.nrow * IO::GRB);     \
-      _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i)                                      \
+      _Pragma("unroll") for (int i = 0; i < IO::NLW; ++i) {                                    \
+        const bool in_ = LSA_DEBUG_CHECKS == 0 || (uint32_t)IX[XSLOT][i] < (uint32_t)ic.nrow;    \
+        if (LSA_DEBUG_CHECKS && live_ && loads && !in_) range_error();                         \
         R[SLOT][i] = buf_load16_nt(                                                            \
-            rk_, live_ && loads ? (uint32_t)IX[XSLOT][i] * IO::GRB + lchunk[i] * 16 : BUF_OOB); \
+            rk_, live_ && loads && in_ ? (uint32_t)IX[XSLOT][i] * IO::GRB + lchunk[i] * 16 : BUF_OOB); \
+      }                                                                                        \
     }                                                                                          \
     if constexpr (KT == KEY_FP8) {                                                             \
       const auto rs_ = buf_rsrc(ic.scale + ic.base, (uint32_t)ic.nrow * 4);                    \
-      SC[SLOT] = __uint_as_float(buf_load4(rs_, live_ ? (uint32_t)IXS[XSLOT] * 4 : BUF_OOB));  \
+      const bool ins_ = LSA_DEBUG_CHECKS == 0 || (uint32_t)IXS[XSLOT] < (uint32_t)ic.nrow;     \
+      if (LSA_DEBUG_CHECKS && live_ && !ins_) range_error();                                   \
+      SC[SLOT] = __uint_as_float(buf_load4(rs_, live_ && ins_ ? (uint32_t)IXS[XSLOT] * 4 : BUF_OOB)); \
     }                                                                                          \
     if (live_) ic.next<CONTIG>(a, tp, rp);                                                     \
   } while (0)

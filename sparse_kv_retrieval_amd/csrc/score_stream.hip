@@ -157,7 +157,11 @@ void score_stream_kernel(const ScoreArgs a) {
   constexpr int CPR = GRB / 16;          // 16-byte chunks per row
   constexpr int NCH = CPR / 2;           // chunks of a lane's half row
   constexpr int STEPS = DH / 16;         // MFMA k-steps per head block
-  using S_t = Scorer<KEY_BF16, DH, NHB>;
+  // KS: a ring unit is one half of every row of a 32-row tile (bytes 0..127 or 128..255 of
+  // 256-byte bf16 rows) rather than 16 whole rows, so the first half's k-steps run while the
+  // second half is still landing, and each wait leaves three units in flight rather than two.
+  constexpr bool KS = KT == KEY_BF16 && GRB == 256 && !GUARD;
+  using S_t = Scorer<KEY_BF16, DH, NHB, false, KS>;
 
   __shared__ __attribute__((aligned(1024))) char rings[WPB][RU][UNIT];  // slots 1 KiB aligned
   __shared__ float srings[WPB][KT == KEY_FP8 ? RU : 1][64];
@@ -206,8 +210,15 @@ void score_stream_kernel(const ScoreArgs a) {
     //    so its LDS offset is roff0 ^ 16*i. Ring slots are 256-byte aligned, so
     //    the XOR also holds after the slot base is added.
     static_assert(NI <= 4 && 256 % GRB == 0, "offset identities");
-    const uint32_t doff0 = stream_swz(lane * 16);
-    const uint32_t roff0 = stream_swz((n & 15) * GRB + 16 * (g * NCH));
+    // KS: unit position P = 1024 k + 16 lane holds row 8k + lane/8 of the tile, chunk
+    // (lane % 8) ^ x(row) of the row's half, with x(row) = (row / 2) % 8 (every 16 lanes of an
+    // operand read then hit 16 distinct bank groups). For load k that is HBM offset
+    // (8k + lane/8) * 256 + 16 ((lane % 8) ^ ((4k + lane/16) % 8)) = dks0 ^ 64 (k % 2) ^ 2048 k.
+    // Lane (n, g) reads chunk 2s + g of row n (k-step s of the half) at
+    // 128 n + 16 ((2s + g) ^ x(n)) = rks0 ^ 32 s.
+    const uint32_t doff0 = KS ? (uint32_t)((lane >> 3) * 256 + 16 * ((lane & 7) ^ (lane >> 4))) : stream_swz(lane * 16);
+    const uint32_t roff0 = KS ? (uint32_t)(n * 128 + 16 * (g ^ ((n >> 1) & 7)))
+                              : stream_swz((n & 15) * GRB + 16 * (g * NCH));
 
     // ic: the half tiles being loaded (runs ahead); cc: the tile being scored.
     // ic always reaches the end of a chunk first; it claims the next chunk and
@@ -228,14 +239,22 @@ void score_stream_kernel(const ScoreArgs a) {
     // every iteration issues the same instructions.
 #define LSA_ISSUE()                                                                               \
   do {                                                                                            \
-    const int32_t e_ = ic.e0 + 16 * iq;                                                           \
-    const uint32_t nr_ = ic_live ? (uint32_t)uni(max(0, min(16, ic.nb - e_))) : 0u;              \
-    const auto rk_ = buf_rsrc(ic.keys + (ic.row0 + e_) * GRB, nr_ * GRB);                         \
-    _Pragma("unroll") for (int k = 0; k < NI; ++k)                                                \
-      dma_lds16(rk_, &ring[us][k * 1024], doff0 ^ (uint32_t)(k * 1088));                         \
-    if constexpr (KT == KEY_FP8) {                                                                \
-      const auto rs_ = buf_rsrc(ic.scale + ic.row0 + e_, nr_ * 4);                                \
-      dma_lds4(rs_, &sring[us][0], lane * 4);                                                    \
+    if constexpr (KS) {                                                                           \
+      const int32_t e_ = ic.e0 + 32 * (iq >> 1);                                                  \
+      const uint32_t nr_ = ic_live ? (uint32_t)uni(max(0, min(32, ic.nb - e_))) : 0u;            \
+      const auto rk_ = buf_rsrc(ic.keys + (ic.row0 + e_) * GRB + 128 * (iq & 1), nr_ ? nr_ * GRB - 128 : 0u); \
+      _Pragma("unroll") for (int k = 0; k < NI; ++k)                                              \
+        dma_lds16(rk_, &ring[us][k * 1024], doff0 ^ (uint32_t)((k & 1) * 64 + k * 2048));         \
+    } else {                                                                                      \
+      const int32_t e_ = ic.e0 + 16 * iq;                                                         \
+      const uint32_t nr_ = ic_live ? (uint32_t)uni(max(0, min(16, ic.nb - e_))) : 0u;            \
+      const auto rk_ = buf_rsrc(ic.keys + (ic.row0 + e_) * GRB, nr_ * GRB);                       \
+      _Pragma("unroll") for (int k = 0; k < NI; ++k)                                              \
+        dma_lds16(rk_, &ring[us][k * 1024], doff0 ^ (uint32_t)(k * 1088));                       \
+      if constexpr (KT == KEY_FP8) {                                                              \
+        const auto rs_ = buf_rsrc(ic.scale + ic.row0 + e_, nr_ * 4);                              \
+        dma_lds4(rs_, &sring[us][0], lane * 4);                                                  \
+      }                                                                                           \
     }                                                                                             \
     us = us + 1 == RU ? 0 : us + 1;                                                               \
     if (ic_live && ++iq == 4) {                                                                   \
@@ -265,7 +284,8 @@ void score_stream_kernel(const ScoreArgs a) {
     uint32_t bits0 = 0;
     float c2 = 0.0f;  // GUARD: C^2 of the current query
     for (int j = 0;; j ^= 1) {  // j: tile parity within the mask word
-      stream_vm_wait<(RU - 2) * IPU>();  // the current tile is in LDS (the next RU/2 - 1 tiles may be in flight)
+      // the current tile is in LDS (the next RU/2 - 1 tiles may be in flight); KS: its first half
+      stream_vm_wait<(RU - (KS ? 1 : 2)) * IPU>();
       if (cc.l != cur_l || cc.b != cur_b) {
         S.load_query(a.q[cc.l], a.w[cc.l], cc.b, a.n_h, 0);
         if constexpr (GUARD) c2 = S.guard_c2(a.w[cc.l], cc.b, a.n_h, 0);
@@ -273,6 +293,53 @@ void score_stream_kernel(const ScoreArgs a) {
         cur_b = cc.b;
       }
       const int c1 = cs + 1 == RU ? 0 : cs + 1;
+      if constexpr (KS) {
+        // first half of the rows: read it, refill its slot, and run its k-steps while the
+        // second half lands; then the same for the second half
+        f32x16 acc[NHB];
+#pragma unroll
+        for (int mb = 0; mb < NHB; ++mb) acc[mb] = f32x16{};
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          if (hf == 1) stream_vm_wait<(RU - 1) * IPU>();
+          const uint32_t a0 = lds_addr(&ring[0][0]) + (hf ? c1 : cs) * UNIT + roff0;
+          uint32_t ad[STEPS / 2];
+#pragma unroll
+          for (int i = 0; i < STEPS / 2; ++i) ad[i] = a0 ^ (uint32_t)(32 * i);
+          u32x4 kr[STEPS / 2];
+          float unused;
+          lds_read_tile<STEPS / 2, false>(kr, ad, 0, unused);
+          LSA_ISSUE();
+#pragma unroll
+          for (int s = 0; s < STEPS / 2; ++s) {
+            const bf16x8 kb = as_bf16x8(kr[s]);
+#pragma unroll
+            for (int mb = 0; mb < NHB; ++mb) {
+              acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(S.qa[mb][hf * STEPS / 2 + s][0], kb, acc[mb], 0, 0, 0);
+              acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(S.qa[mb][hf * STEPS / 2 + s][1], kb, acc[mb], 0, 0, 0);
+            }
+          }
+        }
+        const float x = sum_halves(S.partial(acc));
+        const int32_t se = cc.e0 + j * 32 + n;
+        const bool valid = se < cc.nb;
+        const uint32_t bits = (uint32_t)__ballot(valid && x >= a.thr);
+        if (cc.score != nullptr && g == 0 && valid) cc.score[cc.row0 + se] = 1.0f / (1.0f + __expf(-x));
+        cs = c1 + 1 == RU ? 0 : c1 + 1;
+        if (j == 0) {
+          bits0 = bits;
+          continue;
+        }
+        if (lane == 0) cc.mask[cc.word] = (uint64_t)bits0 | ((uint64_t)bits << 32);
+        if (--cc_left > 0) {
+          cc.next(a, t);
+        } else {
+          if (pend < 0) break;
+          cc.jump(a, t, bw0 + pend * CW);
+          cc_left = LSA_CHUNK_WORDS(pend);
+        }
+        continue;
+      }
       const int slot = n < 16 ? cs : c1;
       const uint32_t a0 = lds_addr(&ring[0][0]) + slot * UNIT + roff0;
       uint32_t ad[NCH];

@@ -26,10 +26,14 @@
 
 namespace lsa {
 
-template <int KT, int DH, int NHB, bool ROT = false>
+// ILV: lane group g takes the interleaved 16-byte chunks 2t + g of the head
+// dimension (k-step t) instead of the contiguous half [g*d_h/2, (g+1)*d_h/2),
+// so that k-steps 0 .. STEPS/2 - 1 use only the first half of every key row.
+template <int KT, int DH, int NHB, bool ROT = false, bool ILV = false>
 struct Scorer {
   static_assert(DH == 32 || DH == 64 || DH == 128, "d_h");
   static_assert(NHB == 1 || NHB == 2, "heads per block");
+  static_assert(!ILV || KT == KEY_BF16, "the interleaved layout is for the split bf16 query");
   static_assert(KT == KEY_F32 || KT == KEY_BF16, "fp8 keys are widened to bf16 before the scorer");
   static constexpr int HALF = DH / 2;                         // k values per lane group
   static constexpr int ESZ = KT == KEY_F32 ? 4 : (KT == KEY_BF16 ? 2 : 1);
@@ -54,13 +58,14 @@ struct Scorer {
     for (int mb = 0; mb < NHB; ++mb) {
       const int head = head0 + mb * 32 + n;
       const bool ok = head < n_h;
-      const float* qrow = q + ((int64_t)b * n_h + (ok ? head : 0)) * DH + g * HALF;
+      const float* qrow = q + ((int64_t)b * n_h + (ok ? head : 0)) * DH + (ILV ? 8 * g : g * HALF);
       if constexpr (SPLIT) {
+        constexpr int QS = ILV ? 16 : 8;  // elements between the chunks of consecutive k-steps
 #pragma unroll
         for (int t = 0; t < STEPS; ++t) {
           float v[8];
-          f32x4 v0 = ok ? *(const f32x4*)(qrow + 8 * t) : f32x4{0, 0, 0, 0};
-          f32x4 v1 = ok ? *(const f32x4*)(qrow + 8 * t + 4) : f32x4{0, 0, 0, 0};
+          f32x4 v0 = ok ? *(const f32x4*)(qrow + QS * t) : f32x4{0, 0, 0, 0};
+          f32x4 v1 = ok ? *(const f32x4*)(qrow + QS * t + 4) : f32x4{0, 0, 0, 0};
 #pragma unroll
           for (int i = 0; i < 4; ++i) { v[i] = v0[i]; v[4 + i] = v1[i]; }
           split8(v, qa[mb][t][0], qa[mb][t][1]);

@@ -102,51 +102,86 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, uint
   __syncthreads();
 }
 
-// Exclusive scan, in place, of an LDS table of n <= 2 * TS_THREADS counts.
-__device__ __forceinline__ void table_exclusive_scan(uint32_t* tab, int n) {
-  const int tid = threadIdx.x;
-  const int j0 = 2 * tid;
-  const uint32_t a0 = j0 < n ? tab[j0] : 0u, a1 = j0 + 1 < n ? tab[j0 + 1] : 0u;
-  __shared__ uint32_t wt[TS_THREADS / 64];
-  uint32_t tot;
-  const uint32_t ex = block_prefix_small<8>(a0 + a1, wt, tot);  // a0, a1 <= 64
-  if (j0 < n) tab[j0] = ex;
-  if (j0 + 1 < n) tab[j0 + 1] = ex + a0;
-  __syncthreads();
-}
-
 // Radix select over a list held in registers.
 //
 // Thread t = 64 w + lane holds the list entries i = t + 1024 v (v < V), so
-// every load is coalesced. Three histogram passes over bits 31..21, 20..10
-// and 9..0 of the keys touch only registers and a 2048-bin LDS histogram, and
-// find T, the key of the k-th largest score. The list order is (v, w, lane).
-// An entry's rank among the entries before it is therefore a count of lanes
-// below it in its wave (ballot + mbcnt) plus an exclusive scan of the
-// per-(v, w) counts held in a small LDS table. One such scan ranks the entries
-// equal to T, which settles ties toward the lower index. A second one places
-// each kept entry at its ascending output position.
+// every load is coalesced; all of a thread's loads (and its share of the
+// histogram) are issued before any is used, so the list costs one memory round
+// trip. The list order is (v, w, lane): an entry's rank among the entries
+// before it is a count of lanes below it in its wave (ballot + mbcnt) plus an
+// exclusive scan of per-(v, w) counts held in a small LDS table.
 //
-// With the scoring kernel's histogram (hist_bl, the 2048 counts of the list's
-// keys by their top 11 bits), T is found without the three radix passes: the
-// histogram gives the bin d of the k-th largest key and its rank inside the
-// bin; the keys of bin d (a few hundred, typically) are appended to an LDS
-// list while the scores are loaded; and one wave finds T among them bit by bit
-// (no barrier), or, for a crowded bin, the block runs the last two radix
-// levels on that list.
+// T, the key of the k-th largest score, comes from the scoring kernel's
+// histogram (hist_bl, the 2048 counts of the list's keys by their top 11
+// bits): it gives the bin d of the k-th largest key and its rank inside the
+// bin; the keys of bin d are appended to an LDS list (one LDS atomic per wave);
+// and one wave finds T among them bit by bit (no barrier), or, for a crowded
+// bin, the block runs the last two radix levels on that list. Without a usable
+// histogram, three histogram passes over bits 31..21, 20..10 and 9..0 of the
+// keys find T.
+//
+// The output keeps every key above T and the first krem keys equal to T in
+// list order, which settles ties toward the lower index. One scan of the
+// per-(v, w) counts of keys above T and keys equal to T places them all: the
+// taken entries before an entry number (above before) + min(equal before,
+// krem). For k <= TS_OCAP the list positions of the taken entries go to LDS
+// by output position first, so the index loads are one round trip and the
+// stores are coalesced.
 __device__ __forceinline__ void lds_select(const uint32_t* keys, int n, uint32_t rank, uint32_t* hist,
                                            uint32_t* sh_digit, uint32_t* sh_krem, uint32_t& T, uint32_t& krem,
                                            int passes, int first_pass, uint32_t prefix);
 static constexpr int TS_CCAP = 4096;  // keys of the k-th bin held in LDS
 static constexpr int TS_WCAP = 512;   // at most this many: one wave finds T
+static constexpr int TS_OCAP = 4096;  // outputs placed through LDS
 
 // LDS of the in-register select (one copy per block, whichever list length is instantiated)
 struct RegSelectSmem {
   uint32_t hist[2048];
   uint32_t tab[TS_VMAX * (TS_THREADS / 64)], tab2[TS_VMAX * (TS_THREADS / 64)];
   uint32_t cand[TS_CCAP];
+  int32_t osrc[TS_OCAP];
+  uint32_t wt[2][TS_THREADS / 64];
   uint32_t sh_digit, sh_krem, ncand;
 };
+
+// Exclusive scan, in place, of two LDS tables of n <= 2 * TS_THREADS counts each (counts <= 64).
+__device__ __forceinline__ void table_exclusive_scan2(uint32_t* ta, uint32_t* te, int n, uint32_t (&wt)[2][16]) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int j0 = 2 * tid;
+  const uint32_t a0 = j0 < n ? ta[j0] : 0u, a1 = j0 + 1 < n ? ta[j0 + 1] : 0u;
+  const uint32_t e0 = j0 < n ? te[j0] : 0u, e1 = j0 + 1 < n ? te[j0 + 1] : 0u;
+  // both prefixes bit-sliced at once: per-thread sums are at most 128 (8 bits)
+  const uint32_t va = a0 + a1, ve = e0 + e1;
+  uint32_t pa = 0, pe = 0, sa = 0, se = 0;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const uint64_t ma = __ballot((va >> b) & 1u), me = __ballot((ve >> b) & 1u);
+    pa += lanes_below(ma) << b;
+    pe += lanes_below(me) << b;
+    sa += (uint32_t)__popcll(ma) << b;
+    se += (uint32_t)__popcll(me) << b;
+  }
+  if (lane == 0) {
+    wt[0][w] = sa;
+    wt[1][w] = se;
+  }
+  __syncthreads();
+  uint32_t oa = 0, oe = 0;
+#pragma unroll
+  for (int i = 0; i < TS_THREADS / 64; ++i) {
+    oa += i < w ? wt[0][i] : 0u;
+    oe += i < w ? wt[1][i] : 0u;
+  }
+  if (j0 < n) {
+    ta[j0] = oa + pa;
+    te[j0] = oe + pe;
+  }
+  if (j0 + 1 < n) {
+    ta[j0 + 1] = oa + pa + a0;
+    te[j0 + 1] = oe + pe + e0;
+  }
+  __syncthreads();
+}
 
 // VM: values per thread held in registers (the list has at most TS_THREADS * VM entries).
 template <int VM>
@@ -159,17 +194,22 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
   const int V = (M + TS_THREADS - 1) / TS_THREADS;
   // Key 0 pads the tail. It sorts below every real key (the smallest real key,
   // -inf, maps to 0x007FFFFF), so padding never reaches the selected bins or
-  // the output, and the passes need no bounds test.
-  // Loads go in chunks of 8 with clamped addresses, so each chunk is one round trip.
+  // the output, and the passes need no bounds test. Every load is issued first
+  // (clamped addresses, no branch), then the keys are formed.
+  // Lists of up to 32 values per thread load in one round trip; longer ones in round trips of 16.
+  constexpr int LC = VM <= 32 ? VM : 16;
   uint32_t key[VM];
+  uint32_t hv[2048 / TS_THREADS];
 #pragma unroll
-  for (int c = 0; c < VM; c += 8) {
+  for (int u = 0; u < 2048 / TS_THREADS; ++u) hv[u] = hist_bl ? hist_bl[tid + TS_THREADS * u] : 0u;
+#pragma unroll
+  for (int c = 0; c < VM; c += LC) {
     if (c < V) {
-      float y[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) y[u] = ys[min(tid + TS_THREADS * (c + u), M - 1)];
+      for (int v = c; v < c + LC; ++v) key[v] = __float_as_uint(ys[min(tid + TS_THREADS * v, M - 1)]);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) key[c + u] = (c + u < V && tid + TS_THREADS * (c + u) < M) ? order_key(y[u]) : 0u;
+      for (int v = c; v < c + LC; ++v)
+        key[v] = (v < V && tid + TS_THREADS * v < M) ? order_key(__uint_as_float(key[v])) : 0u;
     }
   }
 
@@ -183,24 +223,28 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
   uint32_t prefix = 0, pmask = 0, krem = (uint32_t)k;
   bool found = false;
   if (hist_bl) {
-    for (int i = tid; i < 2048; i += TS_THREADS) hist[i] = hist_bl[i];
+#pragma unroll
+    for (int u = 0; u < 2048 / TS_THREADS; ++u) hist[tid + TS_THREADS * u] = hv[u];
     if (tid == 0) ncand = 0;
     __syncthreads();
     find_digit(hist, 2048, (uint32_t)k, &sh_digit, &sh_krem);
     const uint32_t d = sh_digit, bin_rank = sh_krem, nd = hist[d];
     if (nd <= (uint32_t)TS_CCAP) {  // uniform
-      // the keys of bin d, in any order (a wave-wide append per register)
+      // the keys of bin d, in any order: one LDS atomic per wave reserves the wave's run
+      uint32_t wc = 0;
+#pragma unroll
+      for (int v = 0; v < VM; ++v)
+        if (v < V) wc += (uint32_t)__popcll(__ballot((key[v] >> 21) == d && key[v] != 0u));
+      uint32_t base = 0;
+      if (lane == 0 && wc) base = atomicAdd(&ncand, wc);
+      base = __builtin_amdgcn_readfirstlane(base);
 #pragma unroll
       for (int v = 0; v < VM; ++v)
         if (v < V) {
-          const bool in = tid + TS_THREADS * v < M && (key[v] >> 21) == d;
+          const bool in = (key[v] >> 21) == d && key[v] != 0u;
           const uint64_t m = __ballot(in);
-          if (m) {  // uniform
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&ncand, (uint32_t)__popcll(m));
-            base = __builtin_amdgcn_readfirstlane(base);
-            if (in) cand[base + lanes_below(m)] = key[v];
-          }
+          if (in) cand[base + lanes_below(m)] = key[v];
+          base += (uint32_t)__popcll(m);
         }
       __syncthreads();
       const uint32_t nc = ncand;
@@ -260,43 +304,64 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
   }
   const uint32_t T = prefix;
 
-  // Ballots are recomputed in each loop rather than kept, so registers hold only the keys.
-  // tab holds per-(v, w) counts of entries equal to T, then their exclusive scan;
-  // tab2 the same for kept entries.
+  // tab: per-(v, w) counts of keys above T, tab2: of keys equal to T; then one scan of both.
+  // (Ballots are recomputed in each loop rather than kept, so registers hold only the keys.)
 #pragma unroll
   for (int v = 0; v < VM; ++v)
     if (v < V) {
-      const uint64_t m = __ballot(key[v] == T);
-      if (lane == 0) tab[v * NW + w] = (uint32_t)__popcll(m);
+      const uint64_t ma = __ballot(key[v] > T), me = __ballot(key[v] == T);
+      if (lane == 0) {
+        tab[v * NW + w] = (uint32_t)__popcll(ma);
+        tab2[v * NW + w] = (uint32_t)__popcll(me);
+      }
     }
   __syncthreads();
-  table_exclusive_scan(tab, V * NW);
+  table_exclusive_scan2(tab, tab2, V * NW, sm.wt);
+  // output position of entry (v, w, lane) if it is taken, else -1
+  auto place = [&](int v) -> int32_t {
+    const uint64_t ma = __ballot(key[v] > T), me = __ballot(key[v] == T);
+    const uint32_t ab = tab[v * NW + w] + lanes_below(ma), eb = tab2[v * NW + w] + lanes_below(me);
+    const bool take = key[v] > T || (key[v] == T && eb < krem);
+    return take ? (int32_t)(ab + min(eb, krem)) : -1;
+  };
+  if (k <= TS_OCAP) {
+    // the list position of every output, by output position, then one round trip for the loads
 #pragma unroll
-  for (int v = 0; v < VM; ++v)
-    if (v < V) {
-      const uint64_t meq = __ballot(key[v] == T);
-      const bool take = key[v] > T || (key[v] == T && tab[v * NW + w] + lanes_below(meq) < krem);
-      const uint64_t mt = __ballot(take);
-      if (lane == 0) tab2[v * NW + w] = (uint32_t)__popcll(mt);
+    for (int v = 0; v < VM; ++v)
+      if (v < V) {
+        const int32_t pos = place(v);
+        if (pos >= 0 && pos < k) sm.osrc[pos] = tid + TS_THREADS * v;
+      }
+    __syncthreads();
+    constexpr int PO = TS_OCAP / TS_THREADS;
+    int32_t iv[PO];
+    float yv[PO];
+#pragma unroll
+    for (int u = 0; u < PO; ++u) {
+      const int p = tid + TS_THREADS * u;
+      // (clamped: a workspace whose histogram does not match its scores must not send a load astray)
+      const int32_t src = p < k ? min(max(sm.osrc[p], 0), M - 1) : 0;
+      iv[u] = p < k ? idx[src] : 0;
+      yv[u] = (outs && p < k) ? ys[src] : 0.0f;
     }
-  __syncthreads();
-  table_exclusive_scan(tab2, V * NW);
-  // output in chunks of 8: positions first, then all the loads, then all the stores
+#pragma unroll
+    for (int u = 0; u < PO; ++u) {
+      const int p = tid + TS_THREADS * u;
+      if (p < k) {
+        out[p] = iv[u];
+        if (outs) outs[p] = yv[u];
+      }
+    }
+    return;
+  }
+  // larger k: each thread stores its own taken entries, in chunks of 8: positions first, then
+  // all the loads, then all the stores
 #pragma unroll
   for (int c = 0; c < VM; c += 8) {
     if (c < V) {
       int32_t pos[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int v = c + u;
-        pos[u] = -1;
-        if (v < V) {
-          const uint64_t meq = __ballot(key[v] == T);
-          const bool take = key[v] > T || (key[v] == T && tab[v * NW + w] + lanes_below(meq) < krem);
-          const uint64_t mt = __ballot(take);
-          if (take) pos[u] = (int32_t)(tab2[v * NW + w] + lanes_below(mt));
-        }
-      }
+      for (int u = 0; u < 8; ++u) pos[u] = c + u < V ? place(c + u) : -1;
       int32_t iv[8];
       float yv[8];
 #pragma unroll

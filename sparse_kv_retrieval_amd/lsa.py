@@ -95,6 +95,7 @@ _golden = _sig("lsa_golden_labels", _i32, [_vp, _i64, _i32, _i32, _vp, _f32, _i3
 _train_ws = _sig("lsa_train_workspace_size", _sz, [_i32, _vp, _i32])
 _train = _sig("lsa_train_step", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                        _i32, _f32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
+_debug_range_errors = _sig("lsa_debug_range_errors", _i32, [_vp, ctypes.POINTER(_i64)])
 _last_error = _sig("lsa_last_error", ctypes.c_char_p, [])
 _version = _sig("lsa_version", _i32, [])
 
@@ -102,7 +103,7 @@ EXPORTED = ("lsa_project", "lsa_pack_weights_size", "lsa_pack_weights", "lsa_pro
             "lsa_score_select_ex", "lsa_topk_step", "lsa_topk_step_noalloc",
             "lsa_topk_score", "lsa_topk_select", "lsa_union_compact", "lsa_topk_workspace_size", "lsa_topk",
             "lsa_gather", "lsa_fetch_host", "lsa_golden_workspace_size", "lsa_golden_labels", "lsa_train_workspace_size",
-            "lsa_train_step", "lsa_last_error",
+            "lsa_train_step", "lsa_debug_range_errors", "lsa_last_error",
             "lsa_version")
 
 
@@ -112,6 +113,14 @@ def last_error() -> str:
 
 def version() -> int:
     return int(_version())
+
+
+def debug_range_errors(stream=None) -> int:
+    """lsa_debug_range_errors: out-of-range list entries met since the last call (debug builds only;
+    waits for the stream)."""
+    n = _i64(0)
+    _check("lsa_debug_range_errors", _debug_range_errors(_stream(stream), ctypes.byref(n)))
+    return int(n.value)
 
 
 def _p(t):

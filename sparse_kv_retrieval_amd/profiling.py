@@ -109,7 +109,8 @@ def stream_read_rate(nbytes: int, reps: int = 10, copies: int = 2) -> dict:
     buffer in the 256 MB Infinity Cache when nbytes is large. The probe's
     access patterns (grid-stride or one contiguous range per block, plain or
     non-temporal loads), loads in flight per thread (8 or 16) and blocks per
-    compute unit (2, 4, 8) are swept; the fastest configuration's median over
+    compute unit (2, 4, 8) are swept, plus the LDS-ring pattern of the key scan
+    (one block of 8 waves per CU); the fastest configuration's median over
     `reps` launches (HIP events on the launch stream) is the ceiling. The
     whole sweep is returned too."""
     import ctypes
@@ -128,30 +129,31 @@ def stream_read_rate(nbytes: int, reps: int = 10, copies: int = 2) -> dict:
     sink = torch.zeros(8 * cus, dtype=torch.int32, device="cuda")
     st = torch.cuda.current_stream()
     sweep = []
-    for mode in (0, 1, 2):
-        for u in (8, 16):
-            for bpc in (2, 4, 8):
-                blocks = bpc * cus
+    # (mode, loads in flight, blocks per CU); the LDS-ring mode runs one block of 8 waves per CU
+    configs = [(m, u, bpc) for m in (0, 1, 2) for u in (8, 16) for bpc in (2, 4, 8)] + [(3, 8, 1)]
+    for mode, u, bpc in configs:
+        blocks = bpc * cus
 
-                def launch(i):
-                    r = fn(bufs[i % copies].data_ptr(), nbytes, sink.data_ptr(), blocks, mode, u,
-                           ctypes.c_void_p(st.cuda_stream))
-                    assert r == 0, r
-                for i in range(3):
-                    launch(i)
-                torch.cuda.synchronize()
-                us = []
-                for i in range(reps):
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(st)
-                    launch(i)
-                    e1.record(st)
-                    torch.cuda.synchronize()
-                    us.append(e0.elapsed_time(e1) * 1e3)
-                us.sort()
-                sweep.append({"mode": ["grid_stride", "block_range", "block_range_nt"][mode], "loads_in_flight": u,
-                              "blocks_per_cu": bpc, "median_us": us[len(us) // 2], "min_us": us[0],
-                              "GB_per_s": nbytes / (us[len(us) // 2] * 1e-6) / 1e9})
+        def launch(i):
+            r = fn(bufs[i % copies].data_ptr(), nbytes, sink.data_ptr(), blocks, mode, u,
+                   ctypes.c_void_p(st.cuda_stream))
+            assert r == 0, r
+        for i in range(3):
+            launch(i)
+        torch.cuda.synchronize()
+        us = []
+        for i in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            launch(i)
+            e1.record(st)
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3)
+        us.sort()
+        sweep.append({"mode": ["grid_stride", "block_range", "block_range_nt", "lds_ring_nt"][mode],
+                      "loads_in_flight": u if mode < 3 else 16,  # the ring: 4 slots x 4 loads per wave
+                      "blocks_per_cu": bpc, "median_us": us[len(us) // 2], "min_us": us[0],
+                      "GB_per_s": nbytes / (us[len(us) // 2] * 1e-6) / 1e9})
     del bufs
     torch.cuda.empty_cache()
     best = max(sweep, key=lambda r: r["GB_per_s"])

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -29,7 +30,7 @@ def test_header_declares_the_five_calls():
     for f in ("lsa_project", "lsa_score_select", "lsa_union_compact", "lsa_topk", "lsa_gather",
               "lsa_topk_workspace_size", "lsa_pack_weights_size", "lsa_pack_weights", "lsa_project_packed",
               "lsa_topk_score", "lsa_topk_select", "lsa_score_select_ex", "lsa_topk_step",
-              "lsa_topk_step_noalloc",
+              "lsa_topk_step_noalloc", "lsa_debug_range_errors",
               "lsa_last_error", "lsa_version"):
         assert f in fns
 
@@ -46,6 +47,20 @@ def test_library_exports_every_declared_symbol(lsa):
 
 def test_version(lsa):
     assert lsa.version() == 2
+
+
+def test_release_build_has_no_range_checks(lsa):
+    # the product library compiles no device range checks, and the query says so before any HIP call
+    _expect(lsa, lsa.ERR_UNSUPPORTED, lsa.debug_range_errors, stream=0, match="range checks")
+
+
+def test_debug_build_exports_every_declared_symbol():
+    lib = os.path.join(ROOT, "sparse_kv_retrieval_amd", "_debug", "sparse_kv_retrieval_amd", "liblsa.so")
+    if not os.path.exists(lib):
+        subprocess.run([sys.executable, "-c", "from sparse_kv_retrieval_amd import build; build.build_debug()"],
+                       cwd=ROOT, check=True)
+    out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True).stdout
+    assert set(re.findall(r"\bT (lsa_\w+)", out)) == set(declared_functions())
 
 
 def _offs(n):
