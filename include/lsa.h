@@ -206,7 +206,7 @@ lsa_status lsa_score_select(const lsa_score_layer* layers /* host [L] */, int32_
  *                LSA_ERR_UNSUPPORTED); LSA_SCORE_KERNEL_PAIRS (2): two waves
  *                share each tile (every key dtype).
  *   chunk_words  mask words (64 entries each) a wave takes at a time in the
- *                one-wave-per-tile kernel: 0 (default, 4) or 2..64.
+ *                one-wave-per-tile kernel: 0 (default, 2) or 2..64.
  *   ring         LDS ring depth of that kernel in half tiles: 0 (default), 4,
  *                or 8 (8 only for rows of at most 128 bytes).
  *   guard        1 (one-wave-per-tile kernel, masks only): score each 32-entry

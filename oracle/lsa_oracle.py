@@ -23,8 +23,8 @@ Sources. Section names refer to these pages:
           Sparse Attention", §2.1 (I >= 0.5 fetch; top-k inside the subset)
           and §2.4 (OR union).
 
-Readings where the pages leave a step open. The same list is kept with the
-design notes.
+Readings where the pages leave a step open, numbered as in the design notes'
+list (R10-R14 there are about the GPU side and the workloads).
   R1  The per-head ReLU stays inside the sum and the sigmoid wraps the head sum
       ([BLOG] §3.1 score formula). The threshold replaces the native top-k.
   R2  The gates are linear: w = h W^w, with no softmax and no 1/sqrt scale.
@@ -40,7 +40,7 @@ design notes.
   R7  The compacted list is in ascending entry order.
   R8  For fp8 keys, K_s = scale_s * e4m3fn(K8_s). Scales are positive, so the
       scale commutes with the ReLU.
-  R9  At every decode step after a trigger, the native indexer's own query for
+  R15 At every decode step after a trigger, the native indexer's own query for
       that step (its projections of the step's hidden state) ranks the entries
       of the subset loaded at the trigger, with that layer's keys ([BLOG] §3.2
       second level; [HYPER] 方法). The subset is an input of the step.
@@ -247,7 +247,7 @@ def run_path(inp, *, sequences=None, layers=None, want_scores=True):
 
 
 def step_topk(inp, h_step, lists, *, layers=None):
-    """The native top-k of one decode step over the resident subset (R9).
+    """The native top-k of one decode step over the resident subset (R15).
 
     `h_step[l]` holds the step's hidden states [B, d] (stored values) for
     layer l, and `lists[b]` the subset of sequence b (ascending entry indices,

@@ -170,6 +170,7 @@ hipError_t launch_gather(const GatherArgs& a, int grid, int rows_per_wave, hipSt
 // call (the count is read, then cleared; synchronous).
 hipError_t gather_take_range_errors(unsigned int* out);
 hipError_t topk_take_range_errors(unsigned int* out);
+
 hipError_t launch_project(const ProjArgs& a, int L, bool f32, hipStream_t st);
 hipError_t launch_project_packed(const ProjArgs& a, int L, hipStream_t st);
 // One bf16 layer with each reduction split over two blocks that add into zeroed outputs (a grid of
@@ -211,6 +212,28 @@ __device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* tota
   __syncthreads();
   if (total) *total = tot;
   return off + x - v;
+}
+
+// tp[b] = tiles of the lists before b, rp[b] = entries of the lists before b
+// (b = 0..B; the caller keeps the totals below 2^31).
+__device__ __forceinline__ void block_list_prefix(const int32_t* __restrict__ count, int B, int32_t* tp, int32_t* rp) {
+  const int nt = blockDim.x, tid = threadIdx.x;
+  const int per = (B + nt - 1) / nt;
+  const int lo = min(B, tid * per), hi = min(B, lo + per);
+  int64_t s = 0;
+  for (int b = lo; b < hi; ++b) s += ((int64_t)(count[b] + 31) >> 5) << 32 | (uint32_t)count[b];
+  int64_t tot;
+  int64_t run = block_exclusive_scan(s, &tot);  // tiles in the high word, entries in the low word
+  for (int b = lo; b < hi; ++b) {
+    tp[b] = (int32_t)(run >> 32);
+    rp[b] = (int32_t)(uint32_t)run;
+    run += ((int64_t)(count[b] + 31) >> 5) << 32 | (uint32_t)count[b];
+  }
+  if (tid == 0) {
+    tp[B] = (int32_t)(tot >> 32);
+    rp[B] = (int32_t)(uint32_t)tot;
+  }
+  __syncthreads();
 }
 
 // tp[b] = sum over b' < b of ceil(count[b'] / 32), for b = 0..B (B <= LSA_TOPK_MAX_B).

@@ -46,7 +46,7 @@ int cu_count() {
 }
 
 // Launch shapes, measured on MI355X (see the design notes): fixed at compile time.
-constexpr int kScoreChunkWords = 4;    // mask words per chunk a score wave claims
+constexpr int kScoreChunkWords = 2;    // mask words per chunk a score wave claims
 constexpr int kScorePairsPerCu = 4;    // pair kernel (fp32 keys): wave pairs per CU
 constexpr int kTopkPairsPerCu = 4;     // top-k scoring: wave pairs per CU
 constexpr int kGatherRows = 8;         // rows per wave in flight (HBM gather)

@@ -339,28 +339,6 @@ struct TileCursor {
   }
 };
 
-// tp[b] = tiles of the lists before b, rp[b] = entries of the lists before b
-// (b = 0..B; the caller keeps the totals below 2^31).
-__device__ __forceinline__ void block_list_prefix(const int32_t* __restrict__ count, int B, int32_t* tp, int32_t* rp) {
-  const int nt = blockDim.x, tid = threadIdx.x;
-  const int per = (B + nt - 1) / nt;
-  const int lo = min(B, tid * per), hi = min(B, lo + per);
-  int64_t s = 0;
-  for (int b = lo; b < hi; ++b) s += ((int64_t)(count[b] + 31) >> 5) << 32 | (uint32_t)count[b];
-  int64_t tot;
-  int64_t run = block_exclusive_scan(s, &tot);  // tiles in the high word, entries in the low word
-  for (int b = lo; b < hi; ++b) {
-    tp[b] = (int32_t)(run >> 32);
-    rp[b] = (int32_t)(uint32_t)run;
-    run += ((int64_t)(count[b] + 31) >> 5) << 32 | (uint32_t)count[b];
-  }
-  if (tid == 0) {
-    tp[B] = (int32_t)(tot >> 32);
-    rp[B] = (int32_t)(uint32_t)tot;
-  }
-  __syncthreads();
-}
-
 // CONTIG: the keys of the lists are packed in list order in sub_keys (list
 // entry i of sequence b is row rp[b] + i), so every tile is 32 consecutive
 // rows and no index load precedes the key loads (fp8 scales are still read

@@ -284,14 +284,16 @@ void score_stream_kernel(const ScoreArgs a) {
     uint32_t bits0 = 0;
     float c2 = 0.0f;  // GUARD: C^2 of the current query
     for (int j = 0;; j ^= 1) {  // j: tile parity within the mask word
-      // the current tile is in LDS (the next RU/2 - 1 tiles may be in flight); KS: its first half
-      stream_vm_wait<(RU - (KS ? 1 : 2)) * IPU>();
+      // A new (layer, sequence)'s query, before the wait for the tile: its loads wait for every
+      // load in flight (they are issued after the ring's), so the two latencies overlap.
       if (cc.l != cur_l || cc.b != cur_b) {
         S.load_query(a.q[cc.l], a.w[cc.l], cc.b, a.n_h, 0);
         if constexpr (GUARD) c2 = S.guard_c2(a.w[cc.l], cc.b, a.n_h, 0);
         cur_l = cc.l;
         cur_b = cc.b;
       }
+      // the current tile is in LDS (the next RU/2 - 1 tiles may be in flight); KS: its first half
+      stream_vm_wait<(RU - (KS ? 1 : 2)) * IPU>();
       const int c1 = cs + 1 == RU ? 0 : cs + 1;
       if constexpr (KS) {
         // first half of the rows: read it, refill its slot, and run its k-steps while the

@@ -87,20 +87,28 @@ __global__ __launch_bounds__(UC_THREADS) void union_compact_kernel(const UnionAr
   const uint32_t pos = (uint32_t)(carry + (ex & 0xFFFFFFFFll));  // < N_b < 2^31
   const int64_t chunk_total = tot & 0xFFFFFFFFll;
 
-  // coalesced writes, one word of the wave at a time (words past the end are 0)
-  int32_t* out = a.idx_out + row0;
+  // One word of the wave at a time (words past the end are 0): for word j, every lane whose bit
+  // is set writes its entry index at the word's position + (set bits in the lanes below it): one
+  // coalesced store of consecutive indices per word. Eight words at a time: their broadcasts
+  // first, then eight buffer stores in which a lane without its bit stores out of range (the
+  // store is dropped), so there is no branch and the stores overlap (with one wave per SIMD
+  // there is little else to hide their latency).
+  const auto ro = buf_rsrc(a.idx_out + row0, (uint32_t)nb * 4u);
   const int32_t wave_e0 = (int32_t)((wl - lane) * 64);  // the wave's first entry
-#pragma unroll 4
-  for (int j = 0; j < 64; ++j) {
-    const uint32_t ulo = __builtin_amdgcn_readlane((uint32_t)u, j);
-    const uint32_t uhi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), j);
-    if ((ulo | uhi) == 0u) continue;  // uniform
-    const uint32_t pj = __builtin_amdgcn_readlane(pos, j);
-    const uint64_t word = ((uint64_t)uhi << 32) | ulo;
-    if ((word >> lane) & 1ull) {
+  for (int j0 = 0; j0 < 64; j0 += 8) {
+    uint32_t off[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t ulo = __builtin_amdgcn_readlane((uint32_t)u, j0 + i);
+      const uint32_t uhi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), j0 + i);
+      const uint32_t pj = __builtin_amdgcn_readlane(pos, j0 + i);
+      const uint32_t mine = lane < 32 ? (ulo >> lane) & 1u : (uhi >> (lane - 32)) & 1u;
       const uint32_t below = __builtin_amdgcn_mbcnt_hi(uhi, __builtin_amdgcn_mbcnt_lo(ulo, 0u));
-      out[pj + below] = wave_e0 + j * 64 + lane;
+      off[i] = mine ? (pj + below) * 4u : BUF_OOB;
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(wave_e0 + (j0 + i) * 64 + lane), ro, (int)off[i], 0, 0);
   }
   if (chunk0 + UC_THREADS >= nwords && tid == 0) a.count_out[b] = (int32_t)(carry + chunk_total);
 }

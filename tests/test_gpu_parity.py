@@ -73,6 +73,8 @@ SCORE_VARIANTS = {
     "chunk5": {"chunk_words": 5},
     "guard": {"guard": 1},
     "guard_chunk2": {"guard": 1, "chunk_words": 2},
+    "chunk4": {"chunk_words": 4},
+    "chunk8": {"chunk_words": 8},
 }
 
 
