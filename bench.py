@@ -193,6 +193,53 @@ def cpu_baseline(inp, budget_s: float):
             "cpu_seconds": clk.cpu, "host": host_facts()}
 
 
+def single_scan(steps: int, copies: int = 16) -> dict:
+    """score_select on one 125,000-entry sequence of one layer (single_layer_500k: 32 MB of keys),
+    timed per launch with HIP events: with the same keys every launch (they stay in the 256 MB
+    Infinity Cache), and rotating over `copies` copies of the keys (512 MB), so that every launch
+    reads its keys from HBM."""
+    import torch
+    from sparse_kv_retrieval_amd import lsa
+    from sparse_kv_retrieval_amd import synth
+    from sparse_kv_retrieval_amd.pipeline import Pipeline
+    w = synth.WORKLOADS["single_layer_500k"]
+    log(f"[bench] single scan: generating {w.name}")
+    inp = synth.make(w, with_pool=False)
+    p = Pipeline(inp, "cuda:0")
+    p.run()
+    keys = [p.keys[0]] + [p.keys[0].clone() for _ in range(copies - 1)]
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        layers = [dict(q=p.q[0], w=p.g[0], keys=keys[i % copies], key_scale=p.scale[0], mask_out=p.masks[0])]
+        lsa.score_select(layers, B=w.B, key_offsets=p.key_off, key_offsets_host=p.key_off_h,
+                         mask_word_offsets=p.mwo, mask_word_offsets_host=p.mwo_h, n_h=w.n_h, d_h=w.d_h,
+                         key_dtype=w.key_dtype, threshold=w.threshold, stream=stream)
+
+    ab = algorithmic_bytes(w, inp.lengths)
+    out = {"workload": w.name, "entries": int(np.sum(inp.lengths)), "bytes_per_launch": ab["bytes_per_launch"],
+           "copies_rotated": copies}
+    for tag, rot in (("same_keys", False), ("rotated_keys", True)):
+        for i in range(3):
+            call(i if rot else 0)
+        torch.cuda.synchronize()
+        us = []
+        for i in range(max(steps, 10)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call(i + 3 if rot else 0)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3)
+        med = float(np.median(us))
+        gbs = ab["bytes_per_launch"] / (med * 1e-6) / 1e9
+        out[tag] = {"launch_us": spread(us), "GB_per_s": gbs, "frac": gbs / PEAK_HBM_GBS,
+                    "entries_per_s": out["entries"] / (med * 1e-6)}
+    del keys, p
+    torch.cuda.empty_cache()
+    return out
+
+
 GOLDEN_WORKLOAD = "golden_t64_l21_n125k"
 GOLDEN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "golden_segment_traffic_{}.txt")
 GOLDEN_SOURCES = ["csrc/golden.hip", "csrc/common.hpp", "csrc/kernels.hpp", "build.py"]
@@ -390,6 +437,8 @@ def main():
     ap.add_argument("--no-golden", action="store_true", help="skip the golden-label mining measurement")
     ap.add_argument("--golden-only", action="store_true", help="only the golden-label mining measurement")
     ap.add_argument("--no-train", action="store_true", help="skip the training-step measurement")
+    ap.add_argument("--no-single-scan", action="store_true",
+                    help="skip the one-sequence scan (single_layer_500k, cache-resident and rotated keys)")
     ap.add_argument("--train-only", action="store_true", help="only the training-step measurement")
     args = ap.parse_args()
 
@@ -600,8 +649,12 @@ def main():
     }
     if host_fetch is not None:
         out["host_fetch"] = host_fetch
+    if not args.no_single_scan and args.workload != "single_layer_500k":
+        p = None
+        torch.cuda.empty_cache()
+        out["single_scan"] = single_scan(args.steps)
     if not args.no_golden:
-        del p
+        p = None
         torch.cuda.empty_cache()
         out["golden_labels"] = golden_measure(args.steps, args.warmup, None if args.no_cpu_baseline else 3.0)
     if not args.no_train:

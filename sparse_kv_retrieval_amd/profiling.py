@@ -65,7 +65,11 @@ def kernel_stats(run_dir: str) -> list[dict]:
 
 
 def pmc_means(run_dir: str, kernel: str | None = None) -> dict:
-    """{(kernel, counter): mean value per dispatch} from a counter-collection csv."""
+    """{(kernel, counter): (median value per dispatch, dispatches)} from a counter-collection csv.
+
+    The median, not the mean: a run may launch a few dispatches of the same kernel
+    with other options (the bench's score-writing variant of the selection pass),
+    and those must not shift the figure of the timed step's dispatches."""
     path = _one(os.path.join(run_dir, "**", "*counter_collection.csv"))
     vals = defaultdict(list)
     rx = re.compile(kernel) if kernel else None
@@ -74,7 +78,7 @@ def pmc_means(run_dir: str, kernel: str | None = None) -> dict:
             if rx and not rx.search(r["Kernel_Name"]):
                 continue
             vals[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
-    return {k: (statistics.mean(v), len(v)) for k, v in vals.items()}
+    return {k: (statistics.median(v), len(v)) for k, v in vals.items()}
 
 
 def _counter(run_dir: str, kernel: str, counter: str) -> float:
@@ -209,7 +213,7 @@ def main(argv=None) -> None:
         kf = _counter(a.fetch, a.kernel, "FETCH_SIZE") * 1024
         kw = _counter(a.write, a.kernel, "WRITE_SIZE") * 1024
         print(f"copy calibration: FETCH_SIZE reads {cf:.4f} x the copied bytes, WRITE_SIZE {cw:.4f} x")
-        print(f"kernel /{a.kernel}/: FETCH_SIZE {kf / 1e6:.2f} MB, WRITE_SIZE {kw / 1e6:.2f} MB per dispatch (raw)")
+        print(f"kernel /{a.kernel}/: FETCH_SIZE {kf / 1e6:.2f} MB, WRITE_SIZE {kw / 1e6:.2f} MB per dispatch (raw, median)")
         print(f"traffic_bytes_per_launch: {kf / cf + kw / cw:.0f}")
         print(f"fetch_bytes_per_launch: {kf / cf:.0f}")
         print(f"write_bytes_per_launch: {kw / cw:.0f}")
