@@ -14,7 +14,9 @@
 namespace lsa {
 
 static constexpr int TS_THREADS = 1024;
-static constexpr int TS_VMAX = 80;  // values per thread held in registers (lists up to 81,920)
+static constexpr int TS_VMAX = 32;  // values per thread held in registers (lists up to 32,768)
+static constexpr int TS_RMAX = 128; // values per thread of the reloading select (lists up to 131,072)
+static constexpr int TS_RC = 16;    // values per thread per round trip of the reloading select
 
 // Number of set bits of m in the lanes below this one.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
@@ -137,9 +139,10 @@ static constexpr int TS_OCAP = 4096;  // outputs placed through LDS
 // LDS of the in-register select (one copy per block, whichever list length is instantiated)
 struct RegSelectSmem {
   uint32_t hist[2048];
-  uint32_t tab[TS_VMAX * (TS_THREADS / 64)], tab2[TS_VMAX * (TS_THREADS / 64)];
+  uint32_t tab[TS_RMAX * (TS_THREADS / 64)], tab2[TS_RMAX * (TS_THREADS / 64)];
   uint32_t cand[TS_CCAP];
   int32_t osrc[TS_OCAP];
+  uint64_t bal[2][TS_RMAX * (TS_THREADS / 64)];  // the reloading select: ballots of keys above and equal to T
   uint32_t wt[2][TS_THREADS / 64];
   uint32_t sh_digit, sh_krem, ncand;
 };
@@ -381,6 +384,195 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
   }
 }
 
+// Lists longer than the in-register select holds (up to TS_THREADS x TS_RMAX
+// entries): the same steps, with the scores read again from memory, TS_RC per
+// thread at a time, wherever the keys are needed, instead of held in
+// registers. Thread t handles entries t + TS_THREADS v as before. The pass
+// that compares every key with T keeps its ballots in LDS, so the placement
+// needs no third read. When the histogram bin of the k-th key holds more than
+// TS_CCAP keys, one more read counts their next 11 bits and narrows the
+// candidates to a 22-bit prefix. Returns false, having written nothing, when
+// even that prefix is shared by more than TS_CCAP keys (massive ties); the
+// caller then runs the streaming select.
+__device__ __forceinline__ void reload_keys(const float* __restrict__ ys, int32_t M, int c, int V,
+                                            uint32_t (&kv)[TS_RC]) {
+  const int tid = threadIdx.x;
+  float y[TS_RC];
+#pragma unroll
+  for (int u = 0; u < TS_RC; ++u) y[u] = ys[min(tid + TS_THREADS * (c + u), M - 1)];
+#pragma unroll
+  for (int u = 0; u < TS_RC; ++u)
+    kv[u] = (c + u < V && tid + TS_THREADS * (c + u) < M) ? order_key(y[u]) : 0u;
+}
+
+__device__ __forceinline__ bool select_reload(const float* __restrict__ ys, const int32_t* __restrict__ idx,
+                                              int32_t M, int32_t k, int32_t* out, float* outs,
+                                              const uint32_t* __restrict__ hist_bl, RegSelectSmem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int NW = TS_THREADS / 64;
+  const int V = (M + TS_THREADS - 1) / TS_THREADS;
+  for (int i = tid; i < 2048; i += TS_THREADS) sm.hist[i] = hist_bl[i];
+  if (tid == 0) sm.ncand = 0;
+  __syncthreads();
+  find_digit(sm.hist, 2048, (uint32_t)k, &sm.sh_digit, &sm.sh_krem);
+  const uint32_t d = sm.sh_digit, nd = sm.hist[d];
+  // the k-th key has the top bits `pre` (under `pmask`) and is the rank-th largest of the keys that do
+  uint32_t pre = d << 21, pmask = 0xFFE00000u, rank = sm.sh_krem;
+  int low = 21;  // bits below the known prefix
+  __syncthreads();
+  if (nd > (uint32_t)TS_CCAP) {  // uniform
+    // a crowded bin: one more level, the counts of bits 20..10 of the bin's keys
+    for (int i = tid; i < 2048; i += TS_THREADS) sm.hist[i] = 0u;
+    __syncthreads();
+    for (int c = 0; c < TS_RMAX; c += TS_RC) {
+      if (c >= V) break;  // uniform
+      uint32_t kv[TS_RC];
+      reload_keys(ys, M, c, V, kv);
+#pragma unroll
+      for (int u = 0; u < TS_RC; ++u)
+        if ((kv[u] & pmask) == pre && kv[u] != 0u) atomicAdd(&sm.hist[(kv[u] >> 10) & 2047u], 1u);
+    }
+    __syncthreads();
+    find_digit(sm.hist, 2048, rank, &sm.sh_digit, &sm.sh_krem);
+    const uint32_t d2 = sm.sh_digit, n2 = sm.hist[d2];
+    rank = sm.sh_krem;
+    __syncthreads();
+    if (n2 > (uint32_t)TS_CCAP) return false;  // uniform: massive ties
+    pre |= d2 << 10;
+    pmask = 0xFFFFFC00u;
+    low = 10;
+  }
+
+  // the keys with the prefix, in any order: one LDS atomic per wave and round reserves the wave's run
+  for (int c = 0; c < TS_RMAX; c += TS_RC) {
+    if (c >= V) break;  // uniform
+    uint32_t kv[TS_RC];
+    reload_keys(ys, M, c, V, kv);
+#pragma unroll
+    for (int u = 0; u < TS_RC; ++u) {
+      const bool in = (kv[u] & pmask) == pre && kv[u] != 0u;
+      const uint64_t m = __ballot(in);
+      if (m) {  // uniform within the wave
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&sm.ncand, (uint32_t)__popcll(m));
+        base = __builtin_amdgcn_readfirstlane(base);
+        const uint32_t j = base + lanes_below(m);
+        if (in && j < (uint32_t)TS_CCAP) sm.cand[j] = kv[u];  // (bounded: a histogram that does not match the scores)
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t nc = min(sm.ncand, (uint32_t)TS_CCAP);
+  uint32_t T, krem;
+  if (nc <= (uint32_t)TS_WCAP) {
+    if (w == 0) {
+      // the bin_rank-th largest of the nc keys, bit by bit below the bin's 11 bits
+      uint32_t kk[TS_WCAP / 64];
+#pragma unroll
+      for (int u = 0; u < TS_WCAP / 64; ++u) {
+        const uint32_t j = 64u * u + lane;
+        kk[u] = j < nc ? sm.cand[j] : 0u;
+      }
+      uint32_t t = pre;
+      for (int b = low - 1; b >= 0; --b) {
+        const uint32_t c = t | (1u << b);
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int u = 0; u < TS_WCAP / 64; ++u) cnt += (uint32_t)__popcll(__ballot(kk[u] >= c));
+        if (cnt >= rank) t = c;
+      }
+      uint32_t gt = 0;
+#pragma unroll
+      for (int u = 0; u < TS_WCAP / 64; ++u) gt += (uint32_t)__popcll(__ballot(kk[u] > t));
+      if (lane == 0) {
+        sm.sh_digit = t;
+        sm.sh_krem = rank - gt;
+      }
+    }
+    __syncthreads();
+    T = sm.sh_digit;
+    krem = sm.sh_krem;
+  } else {
+    lds_select(sm.cand, (int)nc, rank, sm.hist, &sm.sh_digit, &sm.sh_krem, T, krem, 3, low == 21 ? 1 : 2, pre);
+  }
+
+  // per-(v, w) counts of keys above T and equal to T, and their ballots, then one scan of the counts
+  for (int c = 0; c < TS_RMAX; c += TS_RC) {
+    if (c >= V) break;  // uniform
+    uint32_t kv[TS_RC];
+    reload_keys(ys, M, c, V, kv);
+#pragma unroll
+    for (int u = 0; u < TS_RC; ++u) {
+      const uint64_t ma = __ballot(kv[u] > T), me = __ballot(kv[u] == T);
+      if (lane == 0 && c + u < V) {
+        const int j = (c + u) * NW + w;
+        sm.tab[j] = (uint32_t)__popcll(ma);
+        sm.tab2[j] = (uint32_t)__popcll(me);
+        sm.bal[0][j] = ma;
+        sm.bal[1][j] = me;
+      }
+    }
+  }
+  __syncthreads();
+  table_exclusive_scan2(sm.tab, sm.tab2, V * NW, sm.wt);
+  // output position of entry (v, w, lane) if it is taken, else -1
+  auto place = [&](int v) -> int32_t {
+    const int j = v * NW + w;
+    const uint64_t ma = sm.bal[0][j], me = sm.bal[1][j];
+    const bool above = (ma >> lane) & 1u, equal = (me >> lane) & 1u;
+    const uint32_t ab = sm.tab[j] + lanes_below(ma), eb = sm.tab2[j] + lanes_below(me);
+    const bool take = above || (equal && eb < krem);
+    return take ? (int32_t)(ab + min(eb, krem)) : -1;
+  };
+  if (k <= TS_OCAP) {
+    for (int v = 0; v < V; ++v) {
+      const int32_t pos = place(v);
+      if (pos >= 0 && pos < k) sm.osrc[pos] = tid + TS_THREADS * v;
+    }
+    __syncthreads();
+    constexpr int PO = TS_OCAP / TS_THREADS;
+    int32_t iv[PO];
+    float yv[PO];
+#pragma unroll
+    for (int u = 0; u < PO; ++u) {
+      const int p = tid + TS_THREADS * u;
+      const int32_t src = p < k ? min(max(sm.osrc[p], 0), M - 1) : 0;
+      iv[u] = p < k ? idx[src] : 0;
+      yv[u] = (outs && p < k) ? ys[src] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < PO; ++u) {
+      const int p = tid + TS_THREADS * u;
+      if (p < k) {
+        out[p] = iv[u];
+        if (outs) outs[p] = yv[u];
+      }
+    }
+    return true;
+  }
+  // larger k: each thread stores its own taken entries, 8 values at a time
+  for (int c = 0; c < V; c += 8) {
+    int32_t pos[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pos[u] = c + u < V ? place(c + u) : -1;
+    int32_t iv[8];
+    float yv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = min(tid + TS_THREADS * (c + u), M - 1);
+      iv[u] = pos[u] >= 0 ? idx[i] : 0;
+      yv[u] = (outs && pos[u] >= 0) ? ys[i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (pos[u] >= 0 && pos[u] < k) {
+        out[pos[u]] = iv[u];
+        if (outs) outs[pos[u]] = yv[u];
+      }
+  }
+  return true;
+}
+
 // Radix select that re-reads the scores from memory on every pass (lists of
 // any length): four 8-bit passes, then an ordered output pass in chunks of
 // 1024 entries.
@@ -458,13 +650,14 @@ __device__ __forceinline__ void select_streaming(const float* __restrict__ ys, c
 // keys t, t + TS_THREADS, ...
 static constexpr int TS_FCAP = 4096;     // candidates kept after the filter
 
-// With first_pass = 1 the top 11 bits are already known: prefix holds them and
-// only keys with those bits take part (rank counts among them).
+// With first_pass = 1 the top 11 bits are already known (first_pass = 2: the top
+// 22 bits): prefix holds them and only keys with those bits take part (rank
+// counts among them).
 __device__ __forceinline__ void lds_select(const uint32_t* keys, int n, uint32_t rank, uint32_t* hist,
                                            uint32_t* sh_digit, uint32_t* sh_krem, uint32_t& T, uint32_t& krem,
                                            int passes, int first_pass, uint32_t prefix) {
   const int tid = threadIdx.x;
-  uint32_t pmask = first_pass ? 0xFFE00000u : 0u;
+  uint32_t pmask = first_pass == 0 ? 0u : (first_pass == 1 ? 0xFFE00000u : 0xFFFFFC00u);
   krem = rank;
   for (int pass = first_pass; pass < passes; ++pass) {
     const int sh = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
@@ -495,12 +688,11 @@ __device__ __forceinline__ void lds_select(const uint32_t* keys, int n, uint32_t
 // having written nothing, when the kept entries do not fit in TS_FCAP; the
 // caller then runs a full select.
 #define LSA_GLOBAL __attribute__((address_space(1)))
-__device__ __attribute__((noinline)) bool select_filtered(const float* __restrict__ ys_, const int32_t* __restrict__ idx_,
+__device__ __forceinline__ bool select_filtered(const float* __restrict__ ys_, const int32_t* __restrict__ idx_,
                                                 int32_t M, int32_t k, int32_t* out_, float* outs_,
                                                 const uint32_t* __restrict__ hist_) {
-  // This function is not inlined, so its pointer arguments lose the knowledge
-  // that they point to global memory; generic (flat) accesses would make every
-  // load wait for all outstanding memory and LDS operations. Restore it.
+  // Global-memory pointers: the accesses below are global loads and stores, never generic
+  // (flat) ones, which would wait for every outstanding memory and LDS operation.
   const LSA_GLOBAL float* ys = (const LSA_GLOBAL float*)ys_;
   const LSA_GLOBAL int32_t* idx = (const LSA_GLOBAL int32_t*)idx_;
   LSA_GLOBAL int32_t* out = (LSA_GLOBAL int32_t*)out_;
@@ -597,17 +789,20 @@ __device__ __attribute__((noinline)) bool select_filtered(const float* __restric
   uint32_t tot_take;
   int32_t pos = (int32_t)block_prefix_small<3>((uint32_t)ntake, wt, tot_take);   // ntake <= 4
   // this thread's (at most 4) outputs: positions, then all the loads, then the stores
-  int32_t src[4];
+  // (slot s of src takes the s-th taken entry; every index is a constant, so src stays in registers)
+  int32_t src[4] = {0, 0, 0, 0};
   int nt = 0;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int32_t j = j0 + u;
-    src[u] = 0;
     if (j < j1) {
       const uint32_t kv = fkey[j];
       const bool take = kv > T || (kv == T && eq_before < (int64_t)krem);
       if (kv == T) ++eq_before;
-      if (take) src[nt++] = fpos[j];
+      const int32_t fp = fpos[j];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) src[s] = (take && nt == s) ? fp : src[s];
+      nt += take ? 1 : 0;
     }
   }
   int32_t iv[4];
@@ -645,8 +840,10 @@ __global__ __launch_bounds__(TS_THREADS) void topk_select_kernel(const TopkSelec
     const uint32_t* hb = a.hist + ((int64_t)l * a.B + b) * TOPK_BINS;
     if (M <= TS_THREADS * 8) select_in_registers<8>(ys, idx, M, k, out, outs, hb, rsm);
     else if (M <= TS_THREADS * 16) select_in_registers<16>(ys, idx, M, k, out, outs, hb, rsm);
-    else if (M <= TS_THREADS * 32) select_in_registers<32>(ys, idx, M, k, out, outs, hb, rsm);
     else select_in_registers<TS_VMAX>(ys, idx, M, k, out, outs, hb, rsm);
+  } else if (M <= TS_THREADS * TS_RMAX &&
+             select_reload(ys, idx, M, k, out, outs, a.hist + ((int64_t)l * a.B + b) * TOPK_BINS, rsm)) {
+    // done with the scores read again from memory
   } else if ((int64_t)k * 2 <= TS_FCAP &&
              select_filtered(ys, idx, M, k, out, outs, a.hist + ((int64_t)l * a.B + b) * TOPK_BINS)) {
     // done through the histogram's bin of the k-th key

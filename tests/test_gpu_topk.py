@@ -2,9 +2,11 @@
 
 With one head, gate 1, query e_0 and bf16 keys, the native score of entry s is
 y_s = ReLU(K_s[0]) exactly, so the expected top-k is the oracle's (-y, s) order
-on known values. The cases reach every branch of the select: the
-sample-threshold filter, its fall-backs (too few entries above the estimate,
-too many) and the in-register and streaming radix selects.
+on known values. The cases reach every branch of the select: the in-register
+select (lists up to 32,768 entries), the select that reads the scores again
+(up to 131,072), with its outputs placed through LDS or stored directly (k
+above 4,096), the histogram-bin filter for longer lists, and the fall-backs
+to the streaming radix select (a crowded bin of the k-th key).
 """
 import numpy as np
 import pytest
@@ -19,7 +21,10 @@ def _bf16_exact(v):
     return bits, synth.bf16_bits_to_f32(bits).astype(np.float64)
 
 
-def _run(torch, y_target, k, M_list=None):
+def _run(torch, y_target, k, M_list=None, fine=False):
+    """fine: each score is the sum of two bf16 key components (query e_0 + e_1), so the scores take
+    up to 16 significant bits rather than bf16's 8. The caller keeps the targets on a grid that
+    makes both parts exact in bf16 and their sum exact in fp32."""
     from oracle import lsa_oracle as O
     from sparse_kv_retrieval_amd import lsa
     M = len(y_target)
@@ -27,6 +32,10 @@ def _run(torch, y_target, k, M_list=None):
     bits, y = _bf16_exact(y_target)
     keys = np.zeros((M, d_h), np.uint16)
     keys[:, 0] = bits
+    if fine:
+        lo_bits, lo = _bf16_exact(np.asarray(y_target, np.float64) - y)
+        keys[:, 1] = lo_bits
+        y = y + lo
     y = np.maximum(y, 0.0)                         # the ReLU
     n = M if M_list is None else M_list
     idx = np.arange(n, dtype=np.int32)             # the union list: the first n entries
@@ -34,6 +43,8 @@ def _run(torch, y_target, k, M_list=None):
     t_keys = torch.from_numpy(keys.view(np.int16)).to(dev)
     q = torch.zeros(1, 1, d_h, dtype=torch.float32, device=dev)
     q[0, 0, 0] = 1.0
+    if fine:
+        q[0, 0, 1] = 1.0
     w = torch.ones(1, 1, dtype=torch.float32, device=dev)
     ko_h = np.array([0, M], np.int64)
     ko = torch.from_numpy(ko_h).to(dev)
@@ -81,14 +92,27 @@ def test_topk_all_equal(torch):
 
 @pytest.mark.gpu
 def test_topk_heavy_ties(torch):
-    """Sixteen distinct scores over 50,000 entries: the k-th key is shared by thousands of entries."""
+    """Sixteen distinct scores over 50,000 entries: the k-th key is shared by thousands of entries
+    (more than the bin buffer holds, so the streaming select runs)."""
     P.say("[topk] heavy ties")
     rng = np.random.default_rng(5)
     _run(torch, rng.integers(0, 16, 50000).astype(np.float64), 2048)
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("M", [8192, 50000, 90000, 200000])
+@pytest.mark.parametrize("M", [20000, 80000])
+def test_topk_crowded_bin(M, torch):
+    """Scores packed into a narrow range (100 +- a few): the bin of the k-th key by its top 11 bits
+    holds nearly every entry, so the select narrows it with the next 11 bits (lists past the
+    in-register select) or with register passes."""
+    P.say(f"[topk] crowded bin M={M}")
+    rng = np.random.default_rng(M + 1)
+    y = np.round((100.0 + 0.5 * rng.standard_normal(M)) * 512.0) / 512.0  # 16 bits from 2^6 to 2^-9
+    _run(torch, y, 2048, fine=True)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M", [8192, 32768, 32769, 50000, 90000, 131072, 131073, 200000])
 def test_topk_random(M, torch):
     """Random scores (many exact ties in bf16): the filtered path, and the long lists past the register path."""
     P.say(f"[topk] random M={M}")
@@ -97,7 +121,7 @@ def test_topk_random(M, torch):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("n,k", [(5000, 2048), (2048, 2048), (1, 32), (7000, 7000), (30000, 3072)])
+@pytest.mark.parametrize("n,k", [(5000, 2048), (2048, 2048), (1, 32), (7000, 7000), (30000, 3072), (60000, 5000)])
 def test_topk_shapes(n, k, torch):
     """Lists shorter than, equal to and longer than k, and the largest k the filter takes."""
     P.say(f"[topk] n={n} k={k}")
