@@ -126,9 +126,8 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, uint
 // list order, which settles ties toward the lower index. One scan of the
 // per-(v, w) counts of keys above T and keys equal to T places them all: the
 // taken entries before an entry number (above before) + min(equal before,
-// krem). For k <= TS_OCAP the list positions of the taken entries go to LDS
-// by output position first, so the index loads are one round trip and the
-// stores are coalesced.
+// krem). The list's entry indices are loaded with the scores, so each thread
+// stores its taken entries (index and score) straight from registers.
 __device__ __forceinline__ void lds_select(const uint32_t* keys, int n, uint32_t rank, uint32_t* hist,
                                            uint32_t* sh_digit, uint32_t* sh_krem, uint32_t& T, uint32_t& krem,
                                            int passes, int first_pass, uint32_t prefix);
@@ -200,8 +199,11 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
   // the output, and the passes need no bounds test. Every load is issued first
   // (clamped addresses, no branch), then the keys are formed.
   // Lists of up to 32 values per thread load in one round trip; longer ones in round trips of 16.
+  // The entry indices of the list come in the same round trip, so the taken entries are stored
+  // straight from registers at the end.
   constexpr int LC = VM <= 32 ? VM : 16;
   uint32_t key[VM];
+  int32_t ent[VM];
   uint32_t hv[2048 / TS_THREADS];
 #pragma unroll
   for (int u = 0; u < 2048 / TS_THREADS; ++u) hv[u] = hist_bl ? hist_bl[tid + TS_THREADS * u] : 0u;
@@ -209,7 +211,10 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
   for (int c = 0; c < VM; c += LC) {
     if (c < V) {
 #pragma unroll
-      for (int v = c; v < c + LC; ++v) key[v] = __float_as_uint(ys[min(tid + TS_THREADS * v, M - 1)]);
+      for (int v = c; v < c + LC; ++v) {
+        key[v] = __float_as_uint(ys[min(tid + TS_THREADS * v, M - 1)]);
+        ent[v] = idx[min(tid + TS_THREADS * v, M - 1)];
+      }
 #pragma unroll
       for (int v = c; v < c + LC; ++v)
         key[v] = (v < V && tid + TS_THREADS * v < M) ? order_key(__uint_as_float(key[v])) : 0u;
@@ -327,61 +332,19 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
     const bool take = key[v] > T || (key[v] == T && eb < krem);
     return take ? (int32_t)(ab + min(eb, krem)) : -1;
   };
-  if (k <= TS_OCAP) {
-    // the list position of every output, by output position, then one round trip for the loads
+  // every taken entry straight from registers: its index, and its score (the inverse of order_key)
 #pragma unroll
-    for (int v = 0; v < VM; ++v)
-      if (v < V) {
-        const int32_t pos = place(v);
-        if (pos >= 0 && pos < k) sm.osrc[pos] = tid + TS_THREADS * v;
-      }
-    __syncthreads();
-    constexpr int PO = TS_OCAP / TS_THREADS;
-    int32_t iv[PO];
-    float yv[PO];
-#pragma unroll
-    for (int u = 0; u < PO; ++u) {
-      const int p = tid + TS_THREADS * u;
-      // (clamped: a workspace whose histogram does not match its scores must not send a load astray)
-      const int32_t src = p < k ? min(max(sm.osrc[p], 0), M - 1) : 0;
-      iv[u] = p < k ? idx[src] : 0;
-      yv[u] = (outs && p < k) ? ys[src] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < PO; ++u) {
-      const int p = tid + TS_THREADS * u;
-      if (p < k) {
-        out[p] = iv[u];
-        if (outs) outs[p] = yv[u];
-      }
-    }
-    return;
-  }
-  // larger k: each thread stores its own taken entries, in chunks of 8: positions first, then
-  // all the loads, then all the stores
-#pragma unroll
-  for (int c = 0; c < VM; c += 8) {
-    if (c < V) {
-      int32_t pos[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) pos[u] = c + u < V ? place(c + u) : -1;
-      int32_t iv[8];
-      float yv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = min(tid + TS_THREADS * (c + u), M - 1);
-        iv[u] = pos[u] >= 0 ? idx[i] : 0;
-        yv[u] = (outs && pos[u] >= 0) ? ys[i] : 0.0f;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (pos[u] >= 0 && pos[u] < k) {  // exactly k are taken; the bound only guards a mismatched workspace
-          out[pos[u]] = iv[u];
-          if (outs) outs[pos[u]] = yv[u];
+  for (int v = 0; v < VM; ++v)
+    if (v < V) {
+      const int32_t pos = place(v);
+      if (pos >= 0 && pos < k) {  // exactly k are taken; the bound only guards a mismatched workspace
+        out[pos] = ent[v];
+        if (outs) {
+          const uint32_t kv = key[v];
+          outs[pos] = __uint_as_float((kv & 0x80000000u) ? (kv & 0x7FFFFFFFu) : ~kv);
         }
       }
     }
-  }
 }
 
 // Lists longer than the in-register select holds (up to TS_THREADS x TS_RMAX
