@@ -142,6 +142,7 @@ struct RegSelectSmem {
   uint32_t cand[TS_CCAP];
   int32_t osrc[TS_OCAP];
   uint64_t bal[2][TS_RMAX * (TS_THREADS / 64)];  // the reloading select: ballots of keys above and equal to T
+  int32_t cpos[TS_CCAP];                          // the reloading select: list positions of the candidates
   uint32_t wt[2][TS_THREADS / 64];
   uint32_t sh_digit, sh_krem, ncand;
 };
@@ -351,8 +352,10 @@ __device__ __forceinline__ void select_in_registers(const float* __restrict__ ys
 // entries): the same steps, with the scores read again from memory, TS_RC per
 // thread at a time, wherever the keys are needed, instead of held in
 // registers. Thread t handles entries t + TS_THREADS v as before. The pass
-// that compares every key with T keeps its ballots in LDS, so the placement
-// needs no third read. When the histogram bin of the k-th key holds more than
+// that collects the candidates (the keys that share the k-th key's prefix)
+// also keeps, in LDS, the ballots of the keys with a higher prefix, which are
+// all taken; once T is known the candidates above and equal to T set their own
+// bits from their list positions, so no further read is needed. When the histogram bin of the k-th key holds more than
 // TS_CCAP keys, one more read counts their next 11 bits and narrows the
 // candidates to a 22-bit prefix. Returns false, having written nothing, when
 // even that prefix is shared by more than TS_CCAP keys (massive ties); the
@@ -406,21 +409,33 @@ __device__ __forceinline__ bool select_reload(const float* __restrict__ ys, cons
     low = 10;
   }
 
-  // the keys with the prefix, in any order: one LDS atomic per wave and round reserves the wave's run
+  // the keys with the prefix, in any order: one LDS atomic per wave and round trip reserves the
+  // wave's run (one per value would serialise on the shared counter)
   for (int c = 0; c < TS_RMAX; c += TS_RC) {
     if (c >= V) break;  // uniform
     uint32_t kv[TS_RC];
     reload_keys(ys, M, c, V, kv);
+    uint32_t wc = 0;
+#pragma unroll
+    for (int u = 0; u < TS_RC; ++u) wc += (uint32_t)__popcll(__ballot((kv[u] & pmask) == pre && kv[u] != 0u));
+    uint32_t base = 0;
+    if (lane == 0 && wc) base = atomicAdd(&sm.ncand, wc);
+    base = __builtin_amdgcn_readfirstlane(base);
 #pragma unroll
     for (int u = 0; u < TS_RC; ++u) {
       const bool in = (kv[u] & pmask) == pre && kv[u] != 0u;
       const uint64_t m = __ballot(in);
-      if (m) {  // uniform within the wave
-        uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&sm.ncand, (uint32_t)__popcll(m));
-        base = __builtin_amdgcn_readfirstlane(base);
-        const uint32_t j = base + lanes_below(m);
-        if (in && j < (uint32_t)TS_CCAP) sm.cand[j] = kv[u];  // (bounded: a histogram that does not match the scores)
+      const uint32_t j = base + lanes_below(m);
+      if (in && j < (uint32_t)TS_CCAP) {  // (bounded: a histogram that does not match the scores)
+        sm.cand[j] = kv[u];
+        sm.cpos[j] = tid + TS_THREADS * (c + u);
+      }
+      base += (uint32_t)__popcll(m);
+      // keys whose prefix is above the k-th key's are all taken; the candidates add their own bits later
+      const uint64_t ma = __ballot((kv[u] & pmask) > pre);
+      if (lane == 0 && c + u < V) {
+        sm.bal[0][(c + u) * NW + w] = ma;
+        sm.bal[1][(c + u) * NW + w] = 0ull;
       }
     }
   }
@@ -459,22 +474,20 @@ __device__ __forceinline__ bool select_reload(const float* __restrict__ ys, cons
     lds_select(sm.cand, (int)nc, rank, sm.hist, &sm.sh_digit, &sm.sh_krem, T, krem, 3, low == 21 ? 1 : 2, pre);
   }
 
-  // per-(v, w) counts of keys above T and equal to T, and their ballots, then one scan of the counts
-  for (int c = 0; c < TS_RMAX; c += TS_RC) {
-    if (c >= V) break;  // uniform
-    uint32_t kv[TS_RC];
-    reload_keys(ys, M, c, V, kv);
-#pragma unroll
-    for (int u = 0; u < TS_RC; ++u) {
-      const uint64_t ma = __ballot(kv[u] > T), me = __ballot(kv[u] == T);
-      if (lane == 0 && c + u < V) {
-        const int j = (c + u) * NW + w;
-        sm.tab[j] = (uint32_t)__popcll(ma);
-        sm.tab2[j] = (uint32_t)__popcll(me);
-        sm.bal[0][j] = ma;
-        sm.bal[1][j] = me;
-      }
+  // the candidates above and equal to T set their bits (a key with a higher prefix has its bit
+  // already); then the per-(v, w) counts, and one scan of them
+  for (uint32_t j = tid; j < nc; j += TS_THREADS) {
+    const uint32_t kv = sm.cand[j];
+    if (kv >= T) {
+      const int32_t p = sm.cpos[j];
+      atomicOr((unsigned long long*)&sm.bal[kv > T ? 0 : 1][(p / TS_THREADS) * NW + (p % TS_THREADS) / 64],
+               1ull << (p % 64));
     }
+  }
+  __syncthreads();
+  for (int e = tid; e < V * NW; e += TS_THREADS) {
+    sm.tab[e] = (uint32_t)__popcll(sm.bal[0][e]);
+    sm.tab2[e] = (uint32_t)__popcll(sm.bal[1][e]);
   }
   __syncthreads();
   table_exclusive_scan2(sm.tab, sm.tab2, V * NW, sm.wt);
@@ -488,9 +501,14 @@ __device__ __forceinline__ bool select_reload(const float* __restrict__ ys, cons
     return take ? (int32_t)(ab + min(eb, krem)) : -1;
   };
   if (k <= TS_OCAP) {
-    for (int v = 0; v < V; ++v) {
-      const int32_t pos = place(v);
-      if (pos >= 0 && pos < k) sm.osrc[pos] = tid + TS_THREADS * v;
+    // 8 values at a time, so that their LDS reads are in flight together
+    for (int v0 = 0; v0 < V; v0 += 8) {
+      int32_t pos[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pos[u] = v0 + u < V ? place(v0 + u) : -1;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (pos[u] >= 0 && pos[u] < k) sm.osrc[pos[u]] = tid + TS_THREADS * (v0 + u);
     }
     __syncthreads();
     constexpr int PO = TS_OCAP / TS_THREADS;
