@@ -84,6 +84,7 @@ struct UnionArgs {
   int32_t* count_out;
   uint64_t* union_out;
   int32_t L;
+  int32_t chunk_words;  // mask words per block: 64, 128, 192 or 256 (set by the launcher)
 };
 
 struct GatherArgs {
@@ -164,7 +165,7 @@ hipError_t launch_score_stream(const ScoreArgs& a, int key_kind, int d_h, int wa
 hipError_t launch_topk_score(const TopkScoreArgs& a, int key_kind, int d_h, int grid, bool contig, hipStream_t st);
 hipError_t launch_topk_hist_zero(uint32_t* hist, int64_t n, hipStream_t st);
 hipError_t launch_topk_select(const TopkSelectArgs& a, int L, hipStream_t st);
-hipError_t launch_union_compact(const UnionArgs& a, int B, int64_t max_words, hipStream_t st);
+hipError_t launch_union_compact(const UnionArgs& a, int B, int64_t max_words, int cus, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, int grid, int rows_per_wave, hipStream_t st);
 // Debug builds: the out-of-range list entries each file's kernels have skipped since the last
 // call (the count is read, then cleared; synchronous).

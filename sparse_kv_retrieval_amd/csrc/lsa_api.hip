@@ -393,7 +393,7 @@ lsa_status lsa_union_compact(const uint64_t* const* masks, int32_t L, int32_t B,
   for (int b = 0; b < B; ++b) max_words = std::max(max_words, mask_word_offsets_host[b + 1] - mask_word_offsets_host[b]);
   a.key_off = key_offsets; a.mwo = mask_word_offsets; a.idx_out = idx_out; a.count_out = count_out;
   a.union_out = union_mask_out; a.L = L;
-  const hipError_t e = launch_union_compact(a, B, max_words, stream);
+  const hipError_t e = launch_union_compact(a, B, max_words, cu_count(), stream);
   return e == hipSuccess ? LSA_OK : hip_fail("lsa_union_compact launch", e);
 }
 

@@ -3,9 +3,10 @@
 Integer work, so the result must be bit-exact: the union word of every sequence is the OR of the
 layers' words with the bits at or beyond N_b cleared, the list holds the set bits' entry indices in
 ascending order, and the count is their number. The masks here are random bit patterns, including
-set bits past N_b (which the union must drop), dense chunks (more selected entries in one
-16,384-entry chunk than the kernel stages in LDS, so its direct-store path runs), empty sequences
-and sequences longer than eight chunks (the carry-in takes two rounds of loads).
+set bits past N_b (which the union must drop), dense chunks, empty sequences, sequences with more
+than 2048 words before their last chunk (the carry-in takes several rounds of loads), and enough
+sequences that the kernel's chunks grow from 64 words to 128, 192 and 256 (it keeps its grid at
+one block per compute unit where it can: 256 on this device).
 """
 import numpy as np
 import pytest
@@ -28,6 +29,12 @@ CASES = {
     "eight_layers": ((9_000, 70_000, 333), 8, 0.03),
     "five_layers": ((1200, 64, 130), 5, 0.2),
     "single_entry": ((1,), 4, 0.5),
+    # 256 compute units: 469 words x 40 sequences needs 128-word chunks, 1600 x 20 needs 192,
+    # 1024 x 64 needs 256, and 200 ragged sequences stay at the 256-word maximum
+    "chunks_128": ((30_000,) * 40, 3, 0.1),
+    "chunks_192": ((102_400,) * 20, 3, 0.05),
+    "chunks_256": ((65_536,) * 64, 2, 0.05),
+    "chunks_256_capped": ((40_000, 1, 0, 39_999) * 50, 3, 0.1),
 }
 
 
