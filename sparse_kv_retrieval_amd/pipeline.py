@@ -25,10 +25,55 @@ This module only wires buffers. All arithmetic happens in the HIP kernels.
 """
 from __future__ import annotations
 
+import ctypes
+import os
+
 import numpy as np
 import torch
 
 from . import lsa
+
+
+class _DeviceEvent:
+    """A HIP event for ordering two streams of one device: no timing, and no system-scope
+    fence when it is recorded or waited on (the device-scope ordering of the two streams is all
+    the fork and join need; host visibility comes from the caller's own synchronisation). A
+    default event's system-scope fence left the GPU idle for several microseconds at each
+    fork and join. The runtime is the one the library is linked against, already loaded."""
+
+    _DISABLE_TIMING = 0x2
+    _DISABLE_SYSTEM_FENCE = 0x20000000
+    _hip = None
+
+    def __init__(self):
+        if _DeviceEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD)
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            _DeviceEvent._hip = hip
+        self._h = ctypes.c_void_p()
+        self._check(self._hip.hipEventCreateWithFlags(ctypes.byref(self._h),
+                                                      self._DISABLE_TIMING | self._DISABLE_SYSTEM_FENCE),
+                    "hipEventCreateWithFlags")
+
+    @staticmethod
+    def _check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def record(self, stream):
+        self._check(self._hip.hipEventRecord(self._h, ctypes.c_void_p(stream.cuda_stream)), "hipEventRecord")
+
+    def wait(self, stream):
+        """Make `stream` wait for the work before this event's last record."""
+        self._check(self._hip.hipStreamWaitEvent(ctypes.c_void_p(stream.cuda_stream), self._h, 0),
+                    "hipStreamWaitEvent")
+
+    def __del__(self):
+        if self._hip is not None and self._h:
+            self._hip.hipEventDestroy(self._h)
 
 
 def _dev(a: np.ndarray, device) -> torch.Tensor:
@@ -57,8 +102,8 @@ class Pipeline:
         self.overlap = overlap
         self.early_fork = early_fork  # fork the load step before the top-k scoring (else after it)
         self._side = torch.cuda.Stream(device=dev)  # default priority
-        self._fork = torch.cuda.Event()
-        self._join = torch.cuda.Event()
+        self._fork = _DeviceEvent()
+        self._join = _DeviceEvent()
         B, L = w.B, w.L
         self.rows = int(inp.key_offsets[-1])
         self.words = int(inp.mask_word_offsets[-1])
@@ -298,17 +343,17 @@ class Pipeline:
             return
         if self.early_fork:
             self._fork.record(main)
-            self._side.wait_event(self._fork)
+            self._fork.wait(self._side)
             self.load(self._side)
             self.topk_score_stage(main)
         else:
             self.topk_score_stage(main)
             self._fork.record(main)
-            self._side.wait_event(self._fork)
+            self._fork.wait(self._side)
             self.load(self._side)
         self.topk_select_stage(main)
         self._join.record(self._side)
-        main.wait_event(self._join)
+        self._join.wait(main)
 
     def capture(self):
         """Record one run() into a HIP graph and return it (replay with .replay()).
