@@ -201,7 +201,7 @@ def single_scan(steps: int, copies: int = 16) -> dict:
     import torch
     from sparse_kv_retrieval_amd import lsa
     from sparse_kv_retrieval_amd import synth
-    from sparse_kv_retrieval_amd.pipeline import Pipeline
+    from sparse_kv_retrieval_amd.pipeline import DeviceEvent, Pipeline
     w = synth.WORKLOADS["single_layer_500k"]
     log(f"[bench] single scan: generating {w.name}")
     inp = synth.make(w, with_pool=False)
@@ -225,7 +225,7 @@ def single_scan(steps: int, copies: int = 16) -> dict:
         torch.cuda.synchronize()
         us = []
         for i in range(max(steps, 10)):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = DeviceEvent(timing=True), DeviceEvent(timing=True)
             e0.record(stream)
             call(i + 3 if rot else 0)
             e1.record(stream)
@@ -276,6 +276,7 @@ def golden_measure(steps: int, warmup: int, cpu_budget: float | None) -> dict:
     import torch
     from sparse_kv_retrieval_amd import lsa
     from sparse_kv_retrieval_amd import synth_golden as SG
+    from sparse_kv_retrieval_amd.pipeline import DeviceEvent
     w = SG.WORKLOADS[GOLDEN_WORKLOAD]
     log(f"[bench] golden labels: generating {w.name}")
     inp = SG.make(w)
@@ -296,7 +297,7 @@ def golden_measure(steps: int, warmup: int, cpu_budget: float | None) -> dict:
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = DeviceEvent(timing=True), DeviceEvent(timing=True)
     e0.record(stream)
     for _ in range(steps):
         call()
@@ -356,6 +357,7 @@ def train_measure(steps: int, warmup: int, cpu_budget: float | None) -> dict:
     import torch
     from sparse_kv_retrieval_amd import lsa
     from sparse_kv_retrieval_amd import synth
+    from sparse_kv_retrieval_amd.pipeline import DeviceEvent
     w = synth.WORKLOADS[TRAIN_WORKLOAD]
     log(f"[bench] training step: generating {w.name}")
     inp = synth.make(w, with_pool=False)
@@ -381,7 +383,7 @@ def train_measure(steps: int, warmup: int, cpu_budget: float | None) -> dict:
     for _ in range(warmup):
         lsa.train_step(**args, stream=stream)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = DeviceEvent(timing=True), DeviceEvent(timing=True)
     e0.record(stream)
     for _ in range(steps):
         lsa.train_step(**args, stream=stream)
@@ -449,7 +451,7 @@ def main():
 
     import torch
     from sparse_kv_retrieval_amd import synth
-    from sparse_kv_retrieval_amd.pipeline import Pipeline
+    from sparse_kv_retrieval_amd.pipeline import DeviceEvent, Pipeline
 
     if args.golden_only:
         g = golden_measure(args.steps, args.warmup, None if args.no_cpu_baseline else 3.0)
@@ -476,7 +478,7 @@ def main():
 
     # Per-stage launch durations: eager calls with HIP events between them, on the launch stream.
     names = ["project", "score_select", "union_compact", "topk", "gather"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    ev = [[DeviceEvent(timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} eager steps (per stage)")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -523,7 +525,7 @@ def main():
         torch.cuda.synchronize()
         out_us = []
         for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = DeviceEvent(timing=True), DeviceEvent(timing=True)
             e0.record(stream)
             fn()
             e1.record(stream)

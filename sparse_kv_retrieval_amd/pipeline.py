@@ -34,29 +34,31 @@ import torch
 from . import lsa
 
 
-class _DeviceEvent:
-    """A HIP event for ordering two streams of one device: no timing, and no system-scope
-    fence when it is recorded or waited on (the device-scope ordering of the two streams is all
-    the fork and join need; host visibility comes from the caller's own synchronisation). A
-    default event's system-scope fence left the GPU idle for several microseconds at each
-    fork and join. The runtime is the one the library is linked against, already loaded."""
+class DeviceEvent:
+    """A HIP event for ordering or timing work on the streams of one device, with no
+    system-scope fence when it is recorded or waited on. The fork and join of run() need only
+    device-scope ordering (host visibility comes from the caller's own synchronisation), and a
+    default event's system-scope fence left the GPU idle for several microseconds at each fork
+    and join. As a timing event (timing=True) it adds less to the interval it brackets than a
+    default event, for the same reason. The runtime is the one the library is linked against,
+    already loaded."""
 
     _DISABLE_TIMING = 0x2
     _DISABLE_SYSTEM_FENCE = 0x20000000
     _hip = None
 
-    def __init__(self):
-        if _DeviceEvent._hip is None:
+    def __init__(self, timing: bool = False):
+        if DeviceEvent._hip is None:
             hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD)
             hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
             hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
             hip.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
             hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-            _DeviceEvent._hip = hip
+            DeviceEvent._hip = hip
         self._h = ctypes.c_void_p()
-        self._check(self._hip.hipEventCreateWithFlags(ctypes.byref(self._h),
-                                                      self._DISABLE_TIMING | self._DISABLE_SYSTEM_FENCE),
-                    "hipEventCreateWithFlags")
+        flags = self._DISABLE_SYSTEM_FENCE | (0 if timing else self._DISABLE_TIMING)
+        self._check(self._hip.hipEventCreateWithFlags(ctypes.byref(self._h), flags), "hipEventCreateWithFlags")
 
     @staticmethod
     def _check(rc, what):
@@ -70,6 +72,12 @@ class _DeviceEvent:
         """Make `stream` wait for the work before this event's last record."""
         self._check(self._hip.hipStreamWaitEvent(ctypes.c_void_p(stream.cuda_stream), self._h, 0),
                     "hipStreamWaitEvent")
+
+    def elapsed_time(self, end: "DeviceEvent") -> float:
+        """Milliseconds from this event to `end` (both recorded with timing=True and complete)."""
+        ms = ctypes.c_float()
+        self._check(self._hip.hipEventElapsedTime(ctypes.byref(ms), self._h, end._h), "hipEventElapsedTime")
+        return ms.value
 
     def __del__(self):
         if self._hip is not None and self._h:
@@ -102,8 +110,8 @@ class Pipeline:
         self.overlap = overlap
         self.early_fork = early_fork  # fork the load step before the top-k scoring (else after it)
         self._side = torch.cuda.Stream(device=dev)  # default priority
-        self._fork = _DeviceEvent()
-        self._join = _DeviceEvent()
+        self._fork = DeviceEvent()
+        self._join = DeviceEvent()
         B, L = w.B, w.L
         self.rows = int(inp.key_offsets[-1])
         self.words = int(inp.mask_word_offsets[-1])

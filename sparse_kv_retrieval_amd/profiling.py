@@ -115,11 +115,13 @@ def stream_read_rate(nbytes: int, reps: int = 10, copies: int = 2) -> dict:
     non-temporal loads), loads in flight per thread (8 or 16) and blocks per
     compute unit (2, 4, 8) are swept, plus the LDS-ring pattern of the key scan
     (one block of 8 waves per CU); the fastest configuration's median over
-    `reps` launches (HIP events on the launch stream) is the ceiling. The
+    `reps` launches (HIP events on the launch stream, as the kernels are timed) is the ceiling. The
     whole sweep is returned too."""
     import ctypes
 
     import torch
+
+    from .pipeline import DeviceEvent
     lib = ctypes.CDLL(PROBE_LIB)
     fn = lib.probe_stream_read
     fn.restype = ctypes.c_int
@@ -147,7 +149,7 @@ def stream_read_rate(nbytes: int, reps: int = 10, copies: int = 2) -> dict:
         torch.cuda.synchronize()
         us = []
         for i in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = DeviceEvent(timing=True), DeviceEvent(timing=True)
             e0.record(st)
             launch(i)
             e1.record(st)
