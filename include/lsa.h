@@ -273,7 +273,10 @@ lsa_status lsa_union_compact(const uint64_t* const* masks /* host [L] of dev poi
  * holds the subset scores, one fp32 per (layer, row), and per (layer,
  * sequence) a 2048-bin count of the scores by their top 11 bits (sign,
  * exponent and two mantissa bits of an order-preserving key), which the
- * selection uses to find the k-th score's bin without sampling. Supported:
+ * selection uses to find the k-th score's bin without sampling. The counts
+ * are kept only when some sequence has more than 131,072 rows; otherwise the
+ * selection counts the bins of each list itself and that part of the
+ * workspace is left untouched. Supported:
  * 1 <= k <= 65536; B <= 4096; the key dtypes and head shapes of
  * lsa_score_select.
  * ---------------------------------------------------------------------- */

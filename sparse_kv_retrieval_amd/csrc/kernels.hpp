@@ -40,6 +40,11 @@ struct ScoreArgs {
 // reads the k-th largest score's bin from it.
 constexpr int TOPK_HBITS = 11;
 constexpr int TOPK_BINS = 1 << TOPK_HBITS;
+// Longest sequence (rows) for which the top-k runs without that histogram: every list then fits
+// the select's register or reload paths, which count the keys' bins themselves from the scores
+// they read anyway, so the scorer keeps no histogram and nothing has to clear one. Calls with a
+// longer sequence pass the histogram (hist non-null in both argument blocks).
+constexpr int64_t TOPK_NOHIST_MAX_ROWS = 131072;
 
 struct TopkScoreArgs {
   const float* q[LSA_MAX_LAYERS];
@@ -48,7 +53,7 @@ struct TopkScoreArgs {
   const void* sub_keys[LSA_MAX_LAYERS]; // the union rows packed in list order (contiguous mode)
   const float* scale[LSA_MAX_LAYERS];
   float* ys;                // workspace scores [L][rows_total]
-  uint32_t* hist;           // workspace [L][B][TOPK_BINS] counts (zeroed before the launch)
+  uint32_t* hist;           // workspace [L][B][TOPK_BINS] counts (zeroed before the launch), or null
   const int32_t* idx;       // union lists, region b at key_off[b]
   const int32_t* count;     // [B]
   const int64_t* key_off;   // [B+1]
@@ -58,7 +63,7 @@ struct TopkScoreArgs {
 
 struct TopkSelectArgs {
   const float* ys;
-  const uint32_t* hist;     // the scoring kernel's histograms
+  const uint32_t* hist;     // the scoring kernel's histograms, or null (the select counts the bins)
   const int32_t* idx;
   const int32_t* count;
   const int64_t* key_off;

@@ -166,13 +166,18 @@ lsa_status topk_stages(const lsa_topk_layer* layers, int32_t L, int32_t B, const
     if (contig) sa.sub_keys[l] = p.keys; else sa.keys[l] = p.keys;
     ta.out_idx[l] = p.topk_idx_out; ta.out_score[l] = p.topk_score_out;
   }
-  uint32_t* hist = (uint32_t*)((char*)workspace + topk_hist_offset(L, rows));
+  // The scorer's histogram of each list's keys is only needed by lists too long for the select's
+  // register and reload paths; a call whose sequences are all short enough skips it (and its
+  // clear). The scoring and the select calls of one top-k decide the same way from the offsets.
+  int64_t max_nb = 0;
+  for (int32_t b = 0; b < B; ++b) max_nb = std::max<int64_t>(max_nb, key_offsets_host[b + 1] - key_offsets_host[b]);
+  uint32_t* hist = max_nb > TOPK_NOHIST_MAX_ROWS ? (uint32_t*)((char*)workspace + topk_hist_offset(L, rows)) : nullptr;
   sa.ys = (float*)workspace; sa.hist = hist; sa.idx = idx; sa.count = count; sa.key_off = key_offsets;
   sa.rows_total = rows; sa.B = B; sa.L = L; sa.n_h = n_h;
   ta.ys = (const float*)workspace; ta.hist = hist; ta.idx = idx; ta.count = count; ta.key_off = key_offsets;
   ta.out_count = topk_count_out; ta.rows_total = rows; ta.B = B; ta.k = k;
   hipError_t e;
-  if (do_score) {
+  if (do_score && hist) {
     // the histograms are counted by the scoring kernel, from zero
     if ((e = launch_topk_hist_zero(hist, (int64_t)L * B * TOPK_BINS, stream)) != hipSuccess)
       return hip_fail("lsa_topk histogram clear", e);

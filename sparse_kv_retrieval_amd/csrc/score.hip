@@ -501,8 +501,10 @@ __global__ __launch_bounds__(128) void topk_score_kernel(const TopkScoreArgs a) 
     since += (uint32_t)__popcll(__ballot(on));
     if (on) {
       a.ys[o] = y;
-      const uint32_t bin = order_key(y) >> (32 - TOPK_HBITS);
-      atomicAdd(&lh[bin >> 1], 1u << (16 * (bin & 1)));
+      if (a.hist) {
+        const uint32_t bin = order_key(y) >> (32 - TOPK_HBITS);
+        atomicAdd(&lh[bin >> 1], 1u << (16 * (bin & 1)));
+      }
     }
   };
 

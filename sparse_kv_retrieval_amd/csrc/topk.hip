@@ -17,6 +17,7 @@ static constexpr int TS_THREADS = 1024;
 static constexpr int TS_VMAX = 32;  // values per thread held in registers (lists up to 32,768)
 static constexpr int TS_RMAX = 128; // values per thread of the reloading select (lists up to 131,072)
 static constexpr int TS_RC = 16;    // values per thread per round trip of the reloading select
+static_assert((int64_t)TS_THREADS * TS_RMAX == TOPK_NOHIST_MAX_ROWS, "lists without the scorer's histogram");
 
 // Number of set bits of m in the lanes below this one.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
@@ -377,7 +378,21 @@ __device__ __forceinline__ bool select_reload(const float* __restrict__ ys, cons
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   constexpr int NW = TS_THREADS / 64;
   const int V = (M + TS_THREADS - 1) / TS_THREADS;
-  for (int i = tid; i < 2048; i += TS_THREADS) sm.hist[i] = hist_bl[i];
+  if (hist_bl) {
+    for (int i = tid; i < 2048; i += TS_THREADS) sm.hist[i] = hist_bl[i];
+  } else {
+    // no histogram from the scorer: count the keys' top 11 bits in one more read of the list
+    for (int i = tid; i < 2048; i += TS_THREADS) sm.hist[i] = 0u;
+    __syncthreads();
+    for (int c = 0; c < TS_RMAX; c += TS_RC) {
+      if (c >= V) break;  // uniform
+      uint32_t kv[TS_RC];
+      reload_keys(ys, M, c, V, kv);
+#pragma unroll
+      for (int u = 0; u < TS_RC; ++u)
+        if (kv[u] != 0u) atomicAdd(&sm.hist[kv[u] >> 21], 1u);
+    }
+  }
   if (tid == 0) sm.ncand = 0;
   __syncthreads();
   find_digit(sm.hist, 2048, (uint32_t)k, &sm.sh_digit, &sm.sh_krem);
@@ -812,21 +827,20 @@ __global__ __launch_bounds__(TS_THREADS) void topk_select_kernel(const TopkSelec
   const int32_t* idx = a.idx + base;
   int32_t* out = a.out_idx[l] + (int64_t)b * k;
   float* outs = a.out_score[l] ? a.out_score[l] + (int64_t)b * k : nullptr;
+  const uint32_t* hb = a.hist ? a.hist + ((int64_t)l * a.B + b) * TOPK_BINS : nullptr;
   if (M <= k) {
     for (int32_t i = tid; i < k; i += TS_THREADS) {
       out[i] = i < M ? idx[i] : -1;
       if (outs) outs[i] = i < M ? ys[i] : -INFINITY;
     }
   } else if (M <= TS_THREADS * TS_VMAX) {
-    const uint32_t* hb = a.hist + ((int64_t)l * a.B + b) * TOPK_BINS;
+    // without the scorer's histogram the register select counts the bins itself (radix passes)
     if (M <= TS_THREADS * 8) select_in_registers<8>(ys, idx, M, k, out, outs, hb, rsm);
     else if (M <= TS_THREADS * 16) select_in_registers<16>(ys, idx, M, k, out, outs, hb, rsm);
     else select_in_registers<TS_VMAX>(ys, idx, M, k, out, outs, hb, rsm);
-  } else if (M <= TS_THREADS * TS_RMAX &&
-             select_reload(ys, idx, M, k, out, outs, a.hist + ((int64_t)l * a.B + b) * TOPK_BINS, rsm)) {
+  } else if (M <= TS_THREADS * TS_RMAX && select_reload(ys, idx, M, k, out, outs, hb, rsm)) {
     // done with the scores read again from memory
-  } else if ((int64_t)k * 2 <= TS_FCAP &&
-             select_filtered(ys, idx, M, k, out, outs, a.hist + ((int64_t)l * a.B + b) * TOPK_BINS)) {
+  } else if (hb && (int64_t)k * 2 <= TS_FCAP && select_filtered(ys, idx, M, k, out, outs, hb)) {
     // done through the histogram's bin of the k-th key
   } else {
     select_streaming(ys, idx, M, k, out, outs);

@@ -6,7 +6,10 @@ on known values. The cases reach every branch of the select: the in-register
 select (lists up to 32,768 entries), the select that reads the scores again
 (up to 131,072), with its outputs placed through LDS or stored directly (k
 above 4,096), the histogram-bin filter for longer lists, and the fall-backs
-to the streaming radix select (a crowded bin of the k-th key).
+to the streaming radix select (a crowded bin of the k-th key). A call whose
+sequences all have at most 131,072 rows runs without the scorer's histogram
+(the select counts the bins itself); the cases with a longer sequence and a
+shorter list run the register and reload paths from the scorer's histogram.
 """
 import numpy as np
 import pytest
@@ -127,3 +130,23 @@ def test_topk_shapes(n, k, torch):
     P.say(f"[topk] n={n} k={k}")
     rng = np.random.default_rng(n + k)
     _run(torch, rng.standard_normal(n + 100) * 4.0, k, M_list=n)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M", [20000, 80000, 131072])
+def test_topk_lists_with_histogram(M, torch):
+    """A 140,000-row sequence whose list holds its first M entries: the scorer counts the list's
+    histogram and the register or reload select starts from it."""
+    P.say(f"[topk] histogram mode M={M}")
+    rng = np.random.default_rng(M + 3)
+    _run(torch, rng.standard_normal(140_000) * 4.0, 2048, M_list=M)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M", [20000, 80000])
+def test_topk_crowded_bin_with_histogram(M, torch):
+    """The crowded-bin case of test_topk_crowded_bin in a 140,000-row sequence (histogram mode)."""
+    P.say(f"[topk] crowded bin, histogram mode M={M}")
+    rng = np.random.default_rng(M + 1)
+    y = np.round((100.0 + 0.5 * rng.standard_normal(140_000)) * 512.0) / 512.0
+    _run(torch, y, 2048, M_list=M, fine=True)
