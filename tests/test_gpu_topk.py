@@ -78,7 +78,8 @@ def torch():
 
 @pytest.mark.gpu
 def test_topk_sample_misses_the_top(torch):
-    """The highest scores sit only at positions the sample never reads: the filter keeps too few, fall back."""
+    """The highest scores sit only at the odd positions (every other entry), 64 distinct values in runs
+    of ties, the lower half of the list all equal."""
     P.say("[topk] sample misses the top")
     M, k = 8192, 2048
     y = np.full(M, 1.0)
