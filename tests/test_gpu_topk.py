@@ -77,13 +77,13 @@ def torch():
 
 
 @pytest.mark.gpu
-def test_topk_sample_misses_the_top(torch):
+def test_topk_alternating_scores(torch):
     """The highest scores sit only at the odd positions (every other entry), 64 distinct values in runs
     of ties, the lower half of the list all equal."""
-    P.say("[topk] sample misses the top")
+    P.say("[topk] alternating scores")
     M, k = 8192, 2048
     y = np.full(M, 1.0)
-    y[1::2] = 64.0 + (np.arange(M // 2) % 64)      # odd positions high; the sample reads even positions
+    y[1::2] = 64.0 + (np.arange(M // 2) % 64)      # odd positions high, even positions low
     _run(torch, y, k)
 
 
