@@ -27,6 +27,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 
 import numpy as np
 import torch
@@ -80,7 +81,8 @@ class DeviceEvent:
         return ms.value
 
     def __del__(self):
-        if self._hip is not None and self._h:
+        # at interpreter exit the runtime may already be torn down; the process frees the event
+        if self._hip is not None and self._h and not sys.is_finalizing():
             self._hip.hipEventDestroy(self._h)
 
 
