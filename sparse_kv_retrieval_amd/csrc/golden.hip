@@ -33,8 +33,8 @@
 //    ranks that bucket's entries exactly by (key descending, index ascending),
 //    walks their masses to the crossing, and writes the row's mask. A row it
 //    cannot finish that way (a list that overflowed or does not hold mass p, a
-//    crowded crossing bucket) is flagged in the workspace.
-// 3. fallback_kernel: one block per row; only flagged rows work. A second read
+//    crowded crossing bucket) is appended to a list in the workspace.
+// 3. fallback_kernel: a small grid over the rows resolve listed. A second read
 //    builds a 4096-bin fp64 mass histogram over the top 12 key bits (LDS
 //    atomics) and finds the crossing bin; a third read writes the mask bits of
 //    the entries above it and lists the bin's entries; radix levels of 9, 9 and
@@ -421,11 +421,12 @@ __device__ uint32_t wave_kth_key(const uint32_t* keys, uint32_t m, uint32_t R, u
   return v;
 }
 
-// Per-row fallback flags, after the segment records in the workspace.
-__device__ __forceinline__ uint32_t* row_flags(const GoldenArgs& a) {
+// The rows the resolve kernel leaves to the fallback, after the segment records in the
+// workspace: a count (cleared by the segment kernel), then the rows in any order.
+__device__ __forceinline__ uint32_t* fallback_count(const GoldenArgs& a) {
   return (uint32_t*)(a.ws + (int64_t)a.T * a.L * a.S * SEG_BYTES);
 }
-__device__ __forceinline__ bool row_flag(const GoldenArgs& a, int row) { return row_flags(a)[row] != 0; }
+__device__ __forceinline__ uint32_t* fallback_rows(const GoldenArgs& a) { return fallback_count(a) + 1; }
 
 // Kernel 1: one block per segment of SEG entries of a (token, layer) row.
 // Each wave keeps its own part of the list (LW entries of LDS, a register
@@ -445,6 +446,8 @@ void segment_kernel(const GoldenArgs a) {
   const uint32_t wv = uni((int32_t)(t >> 6));  // wave-uniform
   const uint32_t lane = t & 63;
   const int row = blockIdx.y, seg = blockIdx.x;
+  // the fallback list starts empty (the resolve kernel, next on the stream, appends to it)
+  if (row == 0 && seg == 0 && t == 0) *fallback_count(a) = 0u;
   const int tok = row / a.L;
   const int32_t nv = a.n_valid[tok];
   const uint32_t nrow = (uint32_t)min((int64_t)max(nv, 0), a.row_stride);
@@ -618,7 +621,7 @@ void segment_kernel(const GoldenArgs a) {
 // segments' filters), finds the crossing bucket of the mass by distance below
 // M, ranks that bucket's entries exactly, and writes the row's mask. A row it
 // cannot finish that way (a list that overflowed or does not hold mass p, a
-// crowded bucket) is flagged for the fallback kernel.
+// crowded bucket) is listed for the fallback kernel.
 constexpr int RT = 256;           // threads per resolve block
 constexpr int RW = RT / 64;
 constexpr int NBR = RT;           // buckets: one per thread
@@ -654,16 +657,12 @@ __global__ __launch_bounds__(RT) void resolve_kernel(const GoldenArgs a) {
   const uint32_t n = (uint32_t)min((int64_t)max(nv, 0), a.row_stride);
   const uint32_t nw = (n + 63) >> 6;
   uint64_t* words = a.row_mask + (int64_t)row * a.W;
-  uint32_t* flag = row_flags(a) + row;
 
   if (row == 0)
     for (int64_t j = t; j < a.W; j += RT) a.golden[j] = 0;  // the vote kernel ORs into it
   for (uint32_t j = nw + t; j < (uint32_t)a.W; j += RT) words[j] = 0;
   if (n == 0) {
-    if (t == 0) {
-      *flag = 0;
-      if (a.nucleus_size) a.nucleus_size[row] = 0;
-    }
+    if (t == 0 && a.nucleus_size) a.nucleus_size[row] = 0;
     return;
   }
 
@@ -847,21 +846,19 @@ __global__ __launch_bounds__(RT) void resolve_kernel(const GoldenArgs a) {
       }
     }
   }
-  if (t == 0) *flag = fb ? 1u : 0u;
+  if (t == 0 && fb) fallback_rows(a)[atomicAdd(fallback_count(a), 1u)] = (uint32_t)row;
   if (!fb && a.nucleus_size) {
     block_scan_f64_n<RW>((double)kept, sm.wsum, ex, in, tot);
     if (t == 0) a.nucleus_size[row] = (int32_t)tot;
   }
 }
 
-// Kernel 3: the fallback, one block per row; only rows the resolve kernel
-// flagged do any work. M comes from the segment records again.
-__global__ __launch_bounds__(GT) void fallback_kernel(const GoldenArgs a) {
-  __shared__ GoldenSmem sm;
+// Kernel 3: the fallback, for the rows the resolve kernel listed. M comes from
+// the segment records again. One row at a time per block.
+__device__ __forceinline__ void fallback_row(const GoldenArgs& a, const int row, GoldenSmem& sm) {
   const int t = threadIdx.x;
   const uint32_t wv = uni((int32_t)(t >> 6));  // wave-uniform
   const uint32_t lane = t & 63;
-  const int row = blockIdx.x;
   const int tok = row / a.L;
   const int32_t nv = a.n_valid[tok];
   const uint32_t n = (uint32_t)min((int64_t)max(nv, 0), a.row_stride);
@@ -871,7 +868,7 @@ __global__ __launch_bounds__(GT) void fallback_kernel(const GoldenArgs a) {
   const auto rs = buf_rsrc(y, n * 4u);
   const uint32_t nit = (n + GBC - 1) / GBC;
 
-  if (n == 0 || !row_flag(a, row)) return;
+  if (n == 0) return;
 
   // ---- the row maximum from the segment records
   const uint32_t nseg = (n + SEG - 1) / SEG;
@@ -1015,6 +1012,17 @@ __global__ __launch_bounds__(GT) void fallback_kernel(const GoldenArgs a) {
   }
 }
 
+// A small grid walks the list (empty on most calls, so the launch costs little).
+constexpr int FB_BLOCKS = 256;
+__global__ __launch_bounds__(GT) void fallback_kernel(const GoldenArgs a) {
+  __shared__ GoldenSmem sm;
+  const uint32_t nf = *fallback_count(a);
+  for (uint32_t i = blockIdx.x; i < nf; i += gridDim.x) {
+    fallback_row(a, (int)fallback_rows(a)[i], sm);
+    __syncthreads();  // the next row reuses sm
+  }
+}
+
 // Per (token, word): count the L layers' bits in 7 bit planes, keep the bits
 // with count >= theta, store the token's word if asked, and OR the block's
 // tokens into the window's word.
@@ -1072,8 +1080,8 @@ __global__ __launch_bounds__(VT) void vote_union_kernel(const GoldenArgs a) {
 }  // namespace
 
 size_t golden_workspace_bytes(int64_t rows, int64_t row_stride) {
-  // segment records, then one fallback flag per row
-  return (size_t)rows * (size_t)((row_stride + SEG - 1) / SEG) * (size_t)SEG_BYTES + (size_t)rows * 4;
+  // segment records, then the fallback list: its count and up to one entry per row
+  return (size_t)rows * (size_t)((row_stride + SEG - 1) / SEG) * (size_t)SEG_BYTES + (size_t)(rows + 1) * 4;
 }
 
 hipError_t launch_golden(const GoldenArgs& a0, hipStream_t st) {
@@ -1086,7 +1094,7 @@ hipError_t launch_golden(const GoldenArgs& a0, hipStream_t st) {
   hipLaunchKernelGGL(resolve_kernel, dim3(rows), dim3(RT), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fallback_kernel, dim3(rows), dim3(GT), 0, st, a);
+  hipLaunchKernelGGL(fallback_kernel, dim3((unsigned)std::min(rows, FB_BLOCKS)), dim3(GT), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 g((unsigned)((a.W + 63) / 64), (unsigned)((a.T + VTOK - 1) / VTOK));
