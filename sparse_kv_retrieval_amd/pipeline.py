@@ -342,7 +342,9 @@ class Pipeline:
         the three-layer workload: the scoring and the gather share HBM better than they
         queue. Projecting the native indexer on the second stream while the memory indexer
         scores is 6 us slower per step: score_select is the HBM-bound stage and loses more
-        than the projection gains.)"""
+        than the projection gains. Projecting it after the union instead, on this stream while
+        the load runs on the other, is 24 us slower on the three-layer workload: that phase is
+        already bound by HBM, and the split adds a second pair of projection launches.)"""
         main = torch.cuda.current_stream() if stream is None else stream
         self.project(main)
         self.score_select(main)
